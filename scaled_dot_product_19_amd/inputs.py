@@ -1,0 +1,252 @@
+"""Seeded synthetic inputs for the SDPA forward path.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic.  Both the HIP path's tests/benchmark and the fp64 oracle
+consume what it produces.
+
+Every workload is drawn on the CPU from ``torch.Generator().manual_seed(seed)``
+in a fixed order -- lengths, Q, K (or the K pool), V (or the V pool), the K page
+permutation, the V page permutation -- with values N(0, 1) in fp32, then rounded
+to bf16 (round-to-nearest-even) unless the workload is fp32.
+
+Shapes follow the packed THD layout (token, head, dim; dim innermost) and the
+paged pool layout (page, token-in-page, head, dim) of the serving path the
+cuDNN Frontend release notes describe (v1.30.0 Release Notes, "New: the
+FlashInfer serving path runs on FROST"; v1.31.0 Release Notes, "SDPA: paged KV,
+split-KV, and engine selection").
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+CHUNK_ELEMS = 1 << 26  # draw big tensors in pieces to bound host memory
+
+
+def _randn(g: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    """N(0,1) fp32 draws, rounded to ``dtype``; drawn piecewise along dim 0."""
+    shape = tuple(int(s) for s in shape)
+    out = torch.empty(shape, dtype=dtype)
+    if out.numel() == 0:
+        return out
+    row = max(1, out.numel() // max(1, shape[0]))
+    step = max(1, CHUNK_ELEMS // row)
+    for s in range(0, shape[0], step):
+        e = min(shape[0], s + step)
+        out[s:e] = torch.randn((e - s,) + shape[1:], generator=g, dtype=torch.float32).to(dtype)
+    return out
+
+
+@dataclass
+class ThdCase:
+    """Packed THD ragged prefill problem (Q/K/V on the host)."""
+    q: torch.Tensor            # [Tq, Hq, Dqk]
+    k: torch.Tensor            # [Tk, Hkv, Dqk]
+    v: torch.Tensor            # [Tk, Hkv, Dv]
+    cu_q: torch.Tensor         # int32 [B+1]
+    cu_kv: torch.Tensor        # int32 [B+1]
+    lengths_q: List[int]
+    lengths_kv: List[int]
+    hq: int
+    hkv: int
+    scale: float
+    causal: bool = True
+    name: str = ""
+
+    @property
+    def batch(self) -> int:
+        return len(self.lengths_q)
+
+    @property
+    def max_q(self) -> int:
+        return max(self.lengths_q) if self.lengths_q else 0
+
+    @property
+    def max_kv(self) -> int:
+        return max(self.lengths_kv) if self.lengths_kv else 0
+
+
+@dataclass
+class PagedCase:
+    """Paged-KV decode problem (Q and the pools on the host)."""
+    q: torch.Tensor            # [B, sq, Hq, Dqk]
+    k_pool: torch.Tensor       # [P, page, Hkv, Dqk]
+    v_pool: torch.Tensor       # [P, page, Hkv, Dv]
+    pt_k: torch.Tensor         # int32 [B, table_stride]
+    pt_v: torch.Tensor         # int32 [B, table_stride]
+    seq_lens: torch.Tensor     # int32 [B]
+    page_size: int
+    hq: int
+    hkv: int
+    scale: float
+    causal: bool
+    num_splits: int
+    name: str = ""
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def sq(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def max_kv(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.numel() else 0
+
+
+def thd_case(seed: int, hq: int, hkv: int, d_qk: int, d_v: Optional[int] = None,
+             lengths: Optional[List[int]] = None, batch: int = 0, lo: int = 0, hi: int = 0,
+             lengths_kv: Optional[List[int]] = None, dtype: torch.dtype = torch.bfloat16,
+             causal: bool = True, scale: Optional[float] = None, name: str = "") -> ThdCase:
+    """Ragged THD problem.  Lengths are given, or drawn uniform in [lo, hi]."""
+    d_v = d_qk if d_v is None else d_v
+    g = torch.Generator().manual_seed(seed)
+    if lengths is None:
+        lengths = torch.randint(lo, hi + 1, (batch,), generator=g).tolist()
+    lengths = [int(x) for x in lengths]
+    lengths_kv = lengths if lengths_kv is None else [int(x) for x in lengths_kv]
+    tq, tk = sum(lengths), sum(lengths_kv)
+    q = _randn(g, (tq, hq, d_qk), dtype)
+    k = _randn(g, (tk, hkv, d_qk), dtype)
+    v = _randn(g, (tk, hkv, d_v), dtype)
+    cu_q = torch.tensor([0] + list(_cumsum(lengths)), dtype=torch.int32)
+    cu_kv = torch.tensor([0] + list(_cumsum(lengths_kv)), dtype=torch.int32)
+    sc = 1.0 / math.sqrt(d_qk) if scale is None else float(scale)
+    return ThdCase(q, k, v, cu_q, cu_kv, lengths, lengths_kv, hq, hkv, sc, causal, name)
+
+
+def _cumsum(xs):
+    acc = 0
+    for x in xs:
+        acc += x
+        yield acc
+
+
+def paged_case(seed: int, batch: int, sq: int, hq: int, hkv: int, d_qk: int, d_v: int,
+               page_size: int, lo: int = 0, hi: int = 0, lengths: Optional[List[int]] = None,
+               num_splits: int = 1, causal: bool = True, scale: Optional[float] = None,
+               dtype: torch.dtype = torch.bfloat16, poison: bool = False,
+               name: str = "") -> PagedCase:
+    """Paged decode problem with one shared K pool and one shared V pool.
+
+    The pools hold exactly sum_b ceil(L_b / page) pages, filled N(0,1) in pool
+    order.  Logical page p of sequence b (global index gi, sequences in order)
+    lives at perm_k[gi] in the K pool and perm_v[gi] in the V pool: two
+    independent random permutations.  Table stride = ceil(max L / page).
+
+    poison=True appends one NaN page to each pool, points every unused table
+    entry at it, and fills the slots past each sequence's end in its last
+    page with NaN (the capacity-tail hazard).  Otherwise unused entries are 0.
+    """
+    g = torch.Generator().manual_seed(seed)
+    if lengths is None:
+        lengths = torch.randint(lo, hi + 1, (batch,), generator=g).tolist()
+    lengths = [int(x) for x in lengths]
+    batch = len(lengths)
+    q = _randn(g, (batch, sq, hq, d_qk), dtype)
+    pages_b = [(L + page_size - 1) // page_size for L in lengths]
+    n_pages = sum(pages_b)
+    extra = 1 if poison else 0
+    k_pool = _randn(g, (n_pages + extra, page_size, hkv, d_qk), dtype)
+    v_pool = _randn(g, (n_pages + extra, page_size, hkv, d_v), dtype)
+    perm_k = torch.randperm(n_pages, generator=g) if n_pages else torch.zeros(0, dtype=torch.long)
+    perm_v = torch.randperm(n_pages, generator=g) if n_pages else torch.zeros(0, dtype=torch.long)
+    table_stride = max(1, max(pages_b) if pages_b else 1)
+    fill = n_pages if poison else 0
+    pt_k = torch.full((batch, table_stride), fill, dtype=torch.int32)
+    pt_v = torch.full((batch, table_stride), fill, dtype=torch.int32)
+    gi = 0
+    for b, npg in enumerate(pages_b):
+        pt_k[b, :npg] = perm_k[gi:gi + npg].to(torch.int32)
+        pt_v[b, :npg] = perm_v[gi:gi + npg].to(torch.int32)
+        gi += npg
+    if poison:
+        nan = float("nan")
+        k_pool[n_pages] = nan
+        v_pool[n_pages] = nan
+        for b, L in enumerate(lengths):
+            tail = L % page_size
+            if tail and pages_b[b]:
+                last = pages_b[b] - 1
+                k_pool[int(pt_k[b, last]), tail:] = nan
+                v_pool[int(pt_v[b, last]), tail:] = nan
+    sc = 1.0 / math.sqrt(d_qk) if scale is None else float(scale)
+    seq_lens = torch.tensor(lengths, dtype=torch.int32)
+    return PagedCase(q, k_pool, v_pool, pt_k, pt_v, seq_lens, page_size, hq, hkv, sc, causal,
+                     num_splits, name)
+
+
+# ---- the five workloads -----------------------------------------------------
+
+SEED_BASE = 1000      # seed 1000 + k for workload k
+SEED_ALT = 1100       # a second parity seed, 1100 + k
+
+
+def tiny_fp32(seed: int = SEED_BASE + 1) -> ThdCase:
+    """Tiny dense causal fp32 THD: seqlens {5, 17}, 2 Q heads / 1 KV head, D=64."""
+    return thd_case(seed, hq=2, hkv=1, d_qk=64, lengths=[5, 17], dtype=torch.float32,
+                    name="thd_fp32_tiny_5_17_h2x1_d64")
+
+
+def thd_prefill_d128(seed: int = SEED_BASE + 2, batch: int = 8, lo: int = 128,
+                     hi: int = 4096) -> ThdCase:
+    """Packed THD ragged causal prefill bf16: 8 sequences U[128, 4096], 32/8 heads, D=128."""
+    return thd_case(seed, hq=32, hkv=8, d_qk=128, batch=batch, lo=lo, hi=hi,
+                    name="thd_prefill_bf16_b%d_%d-%d_h32x8_d128" % (batch, lo, hi))
+
+
+def paged_decode_d128(seed: int = SEED_BASE + 3, batch: int = 64, lo: int = 512,
+                      hi: int = 32768, poison: bool = False) -> PagedCase:
+    """Paged decode bf16: batch 64, 1 token, 32/8 heads, D=128, page 64, L U[512, 32768], 8 splits."""
+    return paged_case(seed, batch=batch, sq=1, hq=32, hkv=8, d_qk=128, d_v=128, page_size=64,
+                      lo=lo, hi=hi, num_splits=8, causal=True, poison=poison,
+                      name="paged_decode_bf16_b%d_h32x8_d128_p64_%d-%d_s8" % (batch, lo, hi))
+
+
+def dense_prefill_d256(seed: int = SEED_BASE + 4, seqlen: int = 8192) -> ThdCase:
+    """Dense causal prefill bf16 D=256: batch 2 x 8192, 24 Q / 2 KV heads (GQA 12)."""
+    return thd_case(seed, hq=24, hkv=2, d_qk=256, lengths=[seqlen, seqlen],
+                    name="dense_prefill_bf16_2x%d_h24x2_d256" % seqlen)
+
+
+def ragged_prefill_d256(seed: int = SEED_BASE + 4, lengths=(8192, 3000)) -> ThdCase:
+    """The ragged variant of the D=256 workload: seqlens {8192, 3000}, padded LSE."""
+    return thd_case(seed, hq=24, hkv=2, d_qk=256, lengths=list(lengths),
+                    name="ragged_prefill_bf16_%s_h24x2_d256" % "_".join(map(str, lengths)))
+
+
+def mla_decode(seed: int = SEED_BASE + 5, batch: int = 32, lo: int = 4096, hi: int = 16384,
+               poison: bool = False) -> PagedCase:
+    """Absorbed-MLA-shaped paged decode bf16: Dqk 576, Dv 512, 128/1 heads, 2 query tokens."""
+    return paged_case(seed, batch=batch, sq=2, hq=128, hkv=1, d_qk=576, d_v=512, page_size=64,
+                      lo=lo, hi=hi, num_splits=16, causal=True, poison=poison,
+                      name="mla_decode_bf16_b%d_sq2_h128x1_d576-512_p64_%d-%d_s16"
+                      % (batch, lo, hi))
+
+
+def thd_with_capacity(case: ThdCase, extra_rows: int, fill: float = float("nan")):
+    """Copies of Q/K/V with ``extra_rows`` unwritten capacity rows appended (NaN by default)."""
+    def pad(t):
+        tail = torch.full((extra_rows,) + tuple(t.shape[1:]), fill, dtype=t.dtype)
+        return torch.cat([t, tail], 0)
+    return pad(case.q), pad(case.k), pad(case.v)
+
+
+def bf16_bits(t: torch.Tensor):
+    """Raw uint16 bit patterns of a bf16 tensor, as numpy (no copy if contiguous)."""
+    import numpy as np
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def host_array(t: torch.Tensor):
+    """numpy view of a host tensor in the oracle's input format (uint16 bf16 bits or float32)."""
+    if t.dtype == torch.bfloat16:
+        import numpy as np
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -1,0 +1,87 @@
+"""Planted-mistake checks for the oracle's pins (CPU only).
+
+Each case copies the oracle source, plants one plausible mistake (a dropped
+term, a wrong sign or index, a swapped operand or table), compiles the copy
+into a temporary library and runs the pins against it: at least one pin must
+fail.  The product oracle is never modified.
+"""
+import os
+import shutil
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "sdpa_oracle.c")
+
+# (name, original text, planted text)
+MUTATIONS = [
+    ("gqa_head_mapping_mod", "int32_t kvh = h / (c->hq / c->hkv);\n    /* visible",
+     "int32_t kvh = h % c->hkv;\n    /* visible"),
+    ("causal_top_left", "int64_t last = i + lk - lq;", "int64_t last = i;"),
+    ("causal_off_by_one", "n = last + 1 < lk ? last + 1 : lk;", "n = last < lk ? last : lk;"),
+    ("lse_base_two", "*lse = m + log(l);", "*lse = m + log2(l);"),
+    ("scale_dropped", "s[j] = scale * dot;", "s[j] = dot;"),
+    ("exp_sign", "s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
+    ("normalizer_dropped", "for (int d = 0; d < dv; ++d) o[d] /= l;", ""),
+    ("k_strides_swapped", "koff[j] = (c->cu_kv[b] + j) * c->k_st + (int64_t)kvh * c->k_sh;",
+     "koff[j] = (c->cu_kv[b] + j) * c->k_sh + (int64_t)kvh * c->k_st;"),
+    ("v_uses_k_table", "int64_t vpage = c->pt_v[", "int64_t vpage = c->pt_k["),
+    ("merge_weight_uses_max", "double w = exp(ll[sp] - L_all);",
+     "double w = exp(ll[sp] - m_all);"),
+    ("decode_causal_position", "int64_t last = c->causal ? (L - c->sq + tq) : (L - 1);",
+     "int64_t last = c->causal ? (L - 1 - tq) : (L - 1);"),
+    ("combine_lse_dropped_log", "double L = m + log(w_sum);", "double L = m + w_sum;"),
+]
+
+
+def _pin_suite():
+    """Pins run against a variant; returns the names of the pins that failed."""
+    checks = [
+        ("brute_gqa", lambda: pins.test_brute_force_vs_torch(8, 2, 128, 128, True,
+                                                             pins.torch.bfloat16)),
+        ("brute_mla", lambda: pins.test_brute_force_vs_torch(16, 1, 576, 512, True,
+                                                             pins.torch.float32)),
+        ("natural_log", pins.test_lse_is_natural_log),
+        ("rows_sum_to_one", pins.test_softmax_rows_sum_to_one),
+        ("causal_bitwise", pins.test_causal_rows_ignore_future_keys_bitwise),
+        ("scale_zero", pins.test_closed_form_scale_zero),
+        ("first_row", pins.test_closed_form_first_causal_row),
+        ("golden", pins.test_golden_hand_examples),
+        ("empty_rows", pins.test_empty_and_degenerate_rows),
+        ("paged_dense", lambda: pins.test_paged_equals_gathered_dense_bitwise(
+            (4, 2, 8, 2, 64, 64, 16))),
+        ("split_merge", lambda: pins.test_split_merge_equals_unsplit(3)),
+        ("combine_closed", pins.test_combine_closed_forms),
+        ("decode_causal", pins.test_decode_causal_two_tokens),
+    ]
+    failed = []
+    for name, fn in checks:
+        try:
+            fn()
+        except Exception:  # an assertion, or the oracle rejecting / crashing
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _pin_suite() == []
+
+
+@pytest.mark.parametrize("name,orig,planted", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, orig, planted):
+    text = open(SRC).read()
+    assert text.count(orig) == 1, "mutation anchor for %s not unique in the oracle" % name
+    tmp = tempfile.mkdtemp(prefix="oracle_mut_")
+    try:
+        src = os.path.join(tmp, "mut.c")
+        with open(src, "w") as f:
+            f.write(text.replace(orig, planted))
+        lib = oracle.compile_source(src, os.path.join(tmp, "libmut.so"))
+        with oracle.variant(lib):
+            failed = _pin_suite()
+        assert failed, "planted mistake %s passed every pin" % name
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
