@@ -1,0 +1,202 @@
+/*
+ * sdpa.h -- C-ABI of the MI355X (gfx950) fused scaled-dot-product-attention
+ * forward library (libsdpa.so).
+ *
+ * Three operations, each a set of HIP kernels enqueued on the caller's stream:
+ *   sdpa_prefill_thd      packed THD ragged prefill (causal or not), GQA,
+ *                         FP32 natural-log LSE Stats, packed or padded rows;
+ *   sdpa_decode_paged     paged-KV decode through independent K and V page
+ *                         tables, split-KV partials merged by LSE;
+ *   sdpa_splitkv_combine  the LSE merge of split partials on its own.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named q/k/v/o/lse/cu_seqlens/page tables/seq_lens/workspace
+ *     are DEVICE pointers; the caller owns every buffer.  The library never
+ *     allocates device memory, never reads device memory on the host and
+ *     never synchronizes the host (THD metadata is consumed on the device:
+ *     cuDNN Frontend v1.28.0 release notes, "New: FROST SDPA on Ampere,
+ *     Ada/Blackwell-consumer, and Rubin", paragraph "Ragged / THD, with zero
+ *     host reads").
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All
+ *     work, including the -inf seeding of padded LSE rows, is enqueued on it
+ *     in order.
+ *   - Every extent and stride is a runtime argument; strides are in
+ *     ELEMENTS and 64-bit (v1.30.0 Release Notes, "New: prepared launches --
+ *     the execute fast path", int64 stride leaves).  The last (head-dim) axis
+ *     of every tensor is contiguous.
+ *   - All argument checks run before anything is enqueued.  On any error the
+ *     call returns a nonzero sdpa_status_t, enqueues nothing, and
+ *     sdpa_last_error_detail() (thread-local) says why.  Unsupported
+ *     combinations are declined, never served with a silently different
+ *     computation (v1.30.0 "New: decode tiles", Partial PackGQA bullet).
+ *   - scale is always explicit; 0 and negative values are honoured
+ *     (v1.31.0 Release Notes, "Compatibility and numerical behavior";
+ *     v1.32.0 Release Notes, "SDPA: backward and numerical fixes").
+ *   - LSE (softmax Stats) is always FP32 and natural-log: max + ln(sum exp)
+ *     of the scaled logits (v1.28.0 "Updates to Graph API -- SDPA", Stats
+ *     must be FP32; v1.30.0 "New: stats_use_log2 -- LSE in base 2").
+ *     lse == NULL skips the Stats stores.
+ *   - A query row with no visible key gets O = 0 and LSE = -inf (v1.32.0
+ *     "New: Rubin triangle operations").
+ *   - GQA: query head h reads KV head h / (h_q / h_kv); h_q % h_kv must be 0.
+ *   - Causal masks are bottom-right aligned per sequence: query i of a
+ *     sequence with Lq queries and Lk keys sees key j iff j <= i + Lk - Lq
+ *     (v1.28.0 "New: FROST SDPA ...", per-sequence THD bottom-right
+ *     diagonals).
+ *   - Thread-safe: no mutable global state besides the thread-local error
+ *     detail.
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SDPA_OK = 0,
+    SDPA_ERR_NULL = 1,         /* a required pointer is NULL                        */
+    SDPA_ERR_SHAPE = 2,        /* inconsistent or out-of-range extents / strides     */
+    SDPA_ERR_UNSUPPORTED = 3,  /* valid request this build does not serve (declined) */
+    SDPA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required         */
+    SDPA_ERR_LSE_LAYOUT = 5,   /* unknown LSE layout or bad padded-row capacity      */
+    SDPA_ERR_HIP = 6           /* a HIP launch failed                                */
+} sdpa_status_t;
+
+typedef enum {
+    SDPA_BF16 = 0,  /* Q/K/V/O bfloat16, FP32 accumulation (MFMA) */
+    SDPA_FP32 = 1   /* Q/K/V/O float32, FP32 arithmetic (VALU)    */
+} sdpa_dtype_t;
+
+typedef enum {
+    SDPA_LSE_NONE = 0,    /* no Stats written (lse may be NULL)                         */
+    SDPA_LSE_PACKED = 1,  /* token-major packed rows: lse[(cu_seqlens_q[b] + i) * h_q + h] */
+    SDPA_LSE_PADDED = 2   /* per-batch padded rows: lse[(b * lse_s_max + i) * h_q + h];
+                             the library first fills all batch*lse_s_max*h_q entries with
+                             -inf on `stream`, so rows i >= Lq_b read -inf           */
+} sdpa_lse_layout_t;
+
+/*
+ * Packed THD ragged prefill.
+ *
+ * Defines: for every sequence b, query row i in [0, Lq_b) and query head h,
+ *   O[i,h,:] = softmax_j(scale * <Q[i,h,:], K[j,h/G,:]>) V[j,h/G,:] over the
+ *   visible keys j, and LSE[i,h] = natural-log log-sum-exp of those logits.
+ *   Packed THD layout (head dim innermost, then heads, then tokens; the batch
+ *   stride is never read, every sequence base comes from the offset table):
+ *   v1.30.0 Release Notes, "New: the FlashInfer serving path runs on FROST";
+ *   prefix-sum offsets: v1.28.0 "New: FROST SDPA ...", THD paragraph.
+ *
+ * q  [Tq, h_q,  d_qk] at q + t*q_st + h*q_sh   (t = packed token row)
+ * k  [Tk, h_kv, d_qk] at k + t*k_st + h*k_sh
+ * v  [Tk, h_kv, d_v ] at v + t*v_st + h*v_sh
+ * o  [Tq, h_q,  d_v ] at o + t*o_st + h*o_sh   (written for rows of real tokens only)
+ * cu_seqlens_q / cu_seqlens_kv: int32 [batch+1] prefix sums on the device;
+ *   sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key
+ *   rows cu_seqlens_kv[b] .. cu_seqlens_kv[b+1]-1.
+ * max_seqlen_q / max_seqlen_kv: host-known upper bounds of Lq_b / Lk_b (they
+ *   size the grid; a sequence longer than its bound is only partly computed).
+ * causal: 0 or 1 (bottom-right).  lse_layout: sdpa_lse_layout_t; lse_s_max:
+ *   padded row capacity (>= max_seqlen_q) for SDPA_LSE_PADDED, else ignored.
+ * dtype: SDPA_BF16 (d_qk == d_v in {64, 128, 256}; rows 16-byte aligned: base
+ *   pointers 16-byte aligned and strides multiples of 8) or SDPA_FP32
+ *   (d_qk, d_v <= 256; 4-byte aligned).
+ * Reads of K/V stop at each sequence's Lk: unwritten capacity rows past the
+ * last sequence are never read.
+ */
+int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh,
+                     const void* k, int64_t k_st, int64_t k_sh,
+                     const void* v, int64_t v_st, int64_t v_sh,
+                     void* o, int64_t o_st, int64_t o_sh,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t batch,
+                     int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                     int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v,
+                     float scale, int32_t causal,
+                     float* lse, int32_t lse_layout, int32_t lse_s_max,
+                     int32_t dtype, void* stream);
+
+/*
+ * Bytes of caller workspace sdpa_decode_paged needs for these extents
+ * (0 when num_splits == 1).  Caller-owned split workspace: v1.31.0 Release
+ * Notes, "Compatibility and numerical behavior" (direct split-attention calls
+ * require caller workspace; omission is rejected before launch).
+ * Layout: o_part fp32 [num_splits, rows, d_v] at offset 0, then lse_part fp32
+ * [num_splits, rows] at the next 256-byte boundary; rows = batch*s_q*h_q,
+ * row = (b*s_q + t)*h_q + h.
+ */
+size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t d_v,
+                                   int32_t num_splits);
+
+/*
+ * Paged-KV decode with split-KV.
+ *
+ * Defines: query token t of sequence b sits at key position seq_lens[b]-s_q+t
+ * and, per head h, attends to keys j of that sequence (all j < seq_lens[b],
+ * or j <= seq_lens[b]-s_q+t when causal).  Logical key j lives in physical
+ * page page_table_k[b*table_stride + j/page_size] of the K pool (and
+ * page_table_v[...] of the V pool) at slot j % page_size: independent K and
+ * V page tables and pools (v1.31.0 "SDPA: paged KV, split-KV, and engine
+ * selection"; v1.32.0 "SDPA: wider native forward support", Q/K 576 with
+ * V 512 and independent K/V tables and layouts).
+ * The keys of each (b, KV head) are cut into num_splits contiguous chunks of
+ * ceil(ceil(L/S)/page_size)*page_size keys; each chunk's normalized partial
+ * (O_c, LSE_c) goes to the workspace and a second kernel merges them by LSE
+ * (sdpa_splitkv_combine).  num_splits == 1 writes O/LSE directly and needs
+ * no workspace.  seq_lens need not be multiples of anything (v1.30.0 "New:
+ * the FlashInfer serving path ...", split-KV kept for non-128-multiple KV max).
+ *
+ * q       [batch, s_q, h_q, d_qk] dense, bf16.
+ * k_pool  K rows at k_pool + page*k_sp + slot*k_st + head*k_sh, d_qk wide.
+ * v_pool  V rows at v_pool + page*v_sp + slot*v_st + head*v_sh, d_v wide
+ *         (K and V pools may alias).
+ * page_table_k / page_table_v: int32 [batch, table_stride]; entries past a
+ *         sequence's last page are never read.
+ * seq_lens int32 [batch]; max_seqlen_kv: host-known upper bound (must be
+ *         <= table_stride*page_size).
+ * o       [batch, s_q, h_q, d_v] dense bf16; lse [batch, s_q, h_q] fp32 or NULL.
+ * Supported: dtype SDPA_BF16; (d_qk, d_v) in {(64,64), (128,128), (256,256),
+ * (576,512)}; page_size a multiple of 16; 1 <= num_splits <= 256;
+ * s_q * (h_q/h_kv) <= 512 query rows per KV head.
+ */
+int sdpa_decode_paged(const void* q,
+                      const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,
+                      const void* v_pool, int64_t v_sp, int64_t v_st, int64_t v_sh,
+                      const int32_t* page_table_k, const int32_t* page_table_v,
+                      int32_t table_stride, const int32_t* seq_lens, int32_t max_seqlen_kv,
+                      int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv,
+                      int32_t d_qk, int32_t d_v, int32_t page_size,
+                      float scale, int32_t causal, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes,
+                      void* o, float* lse, int32_t dtype, void* stream);
+
+/*
+ * LSE merge of split-KV partials (the merge the notes use but never print;
+ * the textbook log-sum-exp merge is taken):
+ *   M = max_c lse_part[c,r];  LSE[r] = M + ln sum_c exp(lse_part[c,r] - M);
+ *   O[r,:] = sum_c exp(lse_part[c,r] - LSE[r]) * o_part[c,r,:];
+ *   every split empty (-inf) -> O[r,:] = 0, LSE[r] = -inf.
+ * o_part fp32 [num_splits, rows, d_v] (each partial already normalized),
+ * lse_part fp32 [num_splits, rows] natural log; o [rows, d_v] in `dtype`
+ * (SDPA_BF16 or SDPA_FP32); lse fp32 [rows] or NULL.  d_v <= 1024.
+ */
+int sdpa_splitkv_combine(const float* o_part, const float* lse_part, int32_t num_splits,
+                         int64_t rows, int32_t d_v, void* o, float* lse, int32_t dtype,
+                         void* stream);
+
+/* Static description of a status code. */
+const char* sdpa_status_string(int status);
+
+/* Detail of the last error returned on this thread ("" if none). */
+const char* sdpa_last_error_detail(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int sdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */

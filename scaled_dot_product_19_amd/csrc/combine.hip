@@ -1,0 +1,100 @@
+// combine.hip -- LSE merge of split-KV partials, and the -inf seeding of
+// padded LSE rows.
+//
+// Merge (the notes use split-KV partials merged by LSE -- cuDNN Frontend
+// v1.31.0 Release Notes, "SDPA: paged KV, split-KV, and engine selection" --
+// but print no formula; the textbook log-sum-exp merge is taken):
+//   M = max_c LSE_c, LSE = M + ln sum_c exp(LSE_c - M),
+//   O = sum_c exp(LSE_c - LSE) * O_c; every split empty -> O = 0, LSE = -inf.
+// A split with LSE_c = -inf gets weight exactly 0 and its partial is not
+// read, so an empty split never contributes 0 * NaN.
+//
+// -inf seeding: a padded (b, s_max, h) Stats buffer under THD is filled with
+// -inf on the launch stream before the prefill writes the real rows (v1.30.0
+// Release Notes, "New: the FlashInfer serving path runs on FROST").
+#include "sdpa_device.h"
+#include "sdpa_launch.h"
+
+namespace sdpa {
+namespace {
+
+constexpr int kMaxSplits = 256;
+
+// One wave per row; each lane owns columns lane, lane+64, ... (coalesced).
+template <bool OUT_F32>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
+                                                      const float* __restrict__ lse_part,
+                                                      int splits, int64_t rows, int dv, void* o,
+                                                      float* lse) {
+    __shared__ float w_s[4][kMaxSplits];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+    const bool valid = row < rows;  // no early return: every wave reaches the barrier
+    float* w = w_s[wave];
+    float lse_row = neg_inf();
+    if (valid) {
+        float m = neg_inf();
+        for (int c = lane; c < splits; c += 64) m = fmaxf(m, lse_part[(int64_t)c * rows + row]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        if (m == neg_inf()) {
+            for (int c = lane; c < splits; c += 64) w[c] = 0.f;
+        } else {
+            float sum = 0.f;
+            for (int c = lane; c < splits; c += 64)
+                sum += fast_exp2((lse_part[(int64_t)c * rows + row] - m) * kLog2e);
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+            lse_row = m + kLn2 * fast_log2(sum);
+            for (int c = lane; c < splits; c += 64)
+                w[c] = fast_exp2((lse_part[(int64_t)c * rows + row] - lse_row) * kLog2e);
+        }
+    }
+    __syncthreads();
+    if (!valid) return;
+    for (int n = lane; n < dv; n += 64) {
+        float acc = 0.f;
+        for (int c = 0; c < splits; ++c) {
+            const float wc = w[c];
+            if (wc != 0.f) acc = fmaf(wc, o_part[((int64_t)c * rows + row) * dv + n], acc);
+        }
+        if (OUT_F32)
+            static_cast<float*>(o)[row * dv + n] = acc;
+        else
+            static_cast<bf16_t*>(o)[row * dv + n] = (bf16_t)f32_to_bf16_bits(acc);
+    }
+    if (lse != nullptr && lane == 0) lse[row] = lse_row;
+}
+
+__global__ void fill_kernel(float* p, int64_t n, float value) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (; i < n; i += stride) p[i] = value;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,
+                          int64_t rows, int32_t dv, void* o, float* lse, int32_t out_f32,
+                          hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const int64_t blocks = (rows + 3) / 4;
+    if (out_f32)
+        hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, o_part,
+                           lse_part, (int)splits, rows, (int)dv, o, lse);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, o_part,
+                           lse_part, (int)splits, rows, (int)dv, o, lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n,
+                       -__builtin_inff());
+    return hipGetLastError();
+}
+
+}  // namespace sdpa

@@ -1,0 +1,61 @@
+// sdpa_launch.h -- internal host-side launcher interface between the C-ABI
+// layer (sdpa_api.cpp) and the kernel translation units.  Arguments arrive
+// here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+struct PrefillArgs {
+    const void* q;
+    int64_t q_st, q_sh;
+    const void* k;
+    int64_t k_st, k_sh;
+    const void* v;
+    int64_t v_st, v_sh;
+    void* o;
+    int64_t o_st, o_sh;
+    const int32_t* cu_q;
+    const int32_t* cu_kv;
+    int32_t batch, max_q, max_kv;
+    int32_t hq, hkv, dqk, dv;
+    float scale;
+    int32_t causal;
+    float* lse;
+    int32_t lse_layout, lse_s_max;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k_pool;
+    int64_t k_sp, k_st, k_sh;
+    const void* v_pool;
+    int64_t v_sp, v_st, v_sh;
+    const int32_t* pt_k;
+    const int32_t* pt_v;
+    int32_t table_stride;
+    const int32_t* seq_lens;
+    int32_t batch, sq, hq, hkv, dqk, dv, page;
+    float scale;
+    int32_t causal, splits;
+    float* o_part;    // [splits, rows, dv] when splits > 1
+    float* lse_part;  // [splits, rows]
+    void* o;          // final output when splits == 1
+    float* lse;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,
+                          int64_t rows, int32_t dv, void* o, float* lse, int32_t out_f32,
+                          hipStream_t s);
+hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t s);
+
+// Decode row-group geometry shared by the launcher and the workspace query.
+bool decode_supported(int32_t dqk, int32_t dv);
+
+}  // namespace sdpa

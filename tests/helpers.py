@@ -1,0 +1,101 @@
+"""Shared test helpers: device transfer, the parity bar, oracle calls on workloads."""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from scaled_dot_product_19_amd import inputs
+
+# The parity bar: O elementwise |g - o| <= 2e-2 + 2e-2 * |o| (max-abs / rel 2e-2);
+# LSE |g - o| <= 1e-3 where finite, and -inf exactly where the oracle has -inf.
+O_ATOL = 2e-2
+O_RTOL = 2e-2
+LSE_ATOL = 1e-3
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_available() -> bool:
+    return torch.cuda.is_available()
+
+
+def to_dev(t: torch.Tensor) -> torch.Tensor:
+    return t.to("cuda", non_blocking=False)
+
+
+def check_o(gpu: torch.Tensor, ref: np.ndarray, what: str = "O"):
+    g = gpu.detach().float().cpu().numpy().astype(np.float64)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.isfinite(g).all(), "%s has non-finite values" % what
+    err = np.abs(g - ref)
+    bound = O_ATOL + O_RTOL * np.abs(ref)
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d elements out of tolerance, first %s, max abs err %.4g" %
+                             (what, int(bad.sum()), idx.tolist(), float(err.max())))
+    return float(err.max()) if err.size else 0.0
+
+
+def check_lse(gpu: torch.Tensor, ref: np.ndarray, what: str = "LSE"):
+    g = gpu.detach().float().cpu().numpy().astype(np.float64)
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(g), fin), "%s: finite/-inf pattern differs" % what
+    assert np.all(g[~fin] == -np.inf), "%s: empty rows must be exactly -inf" % what
+    if fin.any():
+        err = np.abs(g[fin] - ref[fin])
+        assert err.max() <= LSE_ATOL, "%s: max abs err %.3g > %g" % (what, err.max(), LSE_ATOL)
+        return float(err.max())
+    return 0.0
+
+
+def oracle_prefill(case: inputs.ThdCase, **kw):
+    return oracle.prefill_thd(inputs.host_array(case.q), inputs.host_array(case.k),
+                              inputs.host_array(case.v), case.cu_q.numpy(), case.cu_kv.numpy(),
+                              case.scale, case.causal, **kw)
+
+
+def oracle_decode(pc: inputs.PagedCase, **kw):
+    return oracle.decode_paged(inputs.host_array(pc.q), inputs.host_array(pc.k_pool),
+                               inputs.host_array(pc.v_pool), pc.pt_k.numpy(), pc.pt_v.numpy(),
+                               pc.seq_lens.numpy(), pc.page_size, pc.scale, pc.causal, **kw)
+
+
+def sample_rows(n_total: int, n: int, seed: int, must=()):
+    g = np.random.default_rng(seed)
+    idx = set(int(x) for x in must if 0 <= x < n_total)
+    if n_total > 0:
+        idx.update(int(x) for x in g.integers(0, n_total, size=n))
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def thd_sample(case: inputs.ThdCase, n: int, seed: int):
+    """Sampled (token, head) rows: random ones plus each sequence's first/last rows."""
+    must = []
+    for b in range(case.batch):
+        s, e = int(case.cu_q[b]), int(case.cu_q[b + 1])
+        if e > s:
+            must += [s, e - 1, s + (e - s) // 2]
+    toks = sample_rows(int(case.cu_q[-1]), n, seed, must)
+    g = np.random.default_rng(seed + 1)
+    heads = g.integers(0, case.hq, size=len(toks)).astype(np.int32)
+    # every head appears at least once
+    heads[: min(len(heads), case.hq)] = np.arange(min(len(heads), case.hq), dtype=np.int32)
+    return toks, heads
+
+
+def nproc_for_oracle() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def finite_lse_frac(lse: np.ndarray) -> float:
+    return float(np.isfinite(lse).mean()) if lse.size else math.nan
