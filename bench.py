@@ -1,0 +1,307 @@
+"""Benchmark of the fused SDPA forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of seeded synthetic
+input already resident in HBM:
+  1. packed THD ragged causal prefill, bf16: 8 sequences with lengths uniform
+     in [128, 4096], 32 Q heads / 8 KV heads, D = 128, packed FP32 LSE
+     (sdpa_prefill_thd: one kernel);
+  2. paged-KV decode, bf16: batch 64, one query token, 32 / 8 heads, D = 128,
+     page size 64, KV lengths uniform in [512, 32768], independent randomly
+     permuted K and V page tables, 8 KV splits merged by LSE
+     (sdpa_decode_paged: the split kernel, then the combine kernel).
+
+Reported: prefill attention TFLOP/s (visible (row, key) pairs x 2 (Dqk + Dv))
+against the bf16 dense MFMA peak, and paged-decode KV GB/s against the HBM
+peak, each from HIP events recorded on the launch stream around every call
+of the timed steps.  Beside them, the fp64 CPU oracle timed on a bounded
+sample of the same workloads (``cpu_baseline``).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_flops(lengths_q, lengths_kv, hq, dqk, dv, causal=True):
+    """Visible (row, key) pairs x 2 (Dqk + Dv) x Hq (bottom-right causal)."""
+    pairs = 0
+    for lq, lk in zip(lengths_q, lengths_kv):
+        for_rows = 0
+        if causal:
+            # row i sees min(lk, max(0, i + lk - lq + 1)) keys
+            for_rows = sum(min(lk, max(0, i + lk - lq + 1)) for i in range(lq))
+        else:
+            for_rows = lq * lk
+        pairs += for_rows
+    return pairs * hq * 2 * (dqk + dv)
+
+
+def decode_bytes(pc):
+    """Compulsory HBM bytes of one paged decode call and its K/V share."""
+    lens = [int(x) for x in pc.seq_lens.tolist()]
+    dqk, dv = int(pc.q.shape[3]), int(pc.v_pool.shape[3])
+    kv = sum(lens) * pc.hkv * (dqk + dv) * 2
+    rows = pc.batch * pc.sq * pc.hq
+    q = rows * dqk * 2
+    o = rows * dv * 2
+    lse = rows * 4
+    pages = sum((L + pc.page_size - 1) // pc.page_size for L in lens)
+    tables = 2 * pages * 4 + pc.batch * 4
+    return kv, kv + q + o + lse + tables
+
+
+def host_threads():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline_prefill(case, target_s, threads):
+    """The oracle on a random sample of (token, head) rows; TFLOP/s of the sample."""
+    import numpy as np
+    import oracle
+    from scaled_dot_product_19_amd import inputs
+    cu = case.cu_q.numpy()
+    T = int(cu[-1])
+    rng = np.random.default_rng(7)
+    qa, ka, va = inputs.host_array(case.q), inputs.host_array(case.k), inputs.host_array(case.v)
+
+    def run(n):
+        toks = rng.integers(0, T, size=n).astype(np.int64)
+        heads = rng.integers(0, case.hq, size=n).astype(np.int32)
+        b = np.searchsorted(cu, toks, side="right") - 1
+        i = toks - cu[b]
+        vis = (i + 1).astype(np.float64)  # causal, Lq == Lk
+        flops = float(vis.sum()) * 2 * (case.q.shape[2] + case.v.shape[2])
+        t0 = time.perf_counter()
+        oracle.prefill_thd(qa, ka, va, case.cu_q.numpy(), case.cu_kv.numpy(), case.scale, True,
+                           sel_tok=toks, sel_head=heads, nthreads=threads)
+        return flops, time.perf_counter() - t0
+
+    f, dt = run(8 * threads)
+    n = int(max(8 * threads, min(200000, 8 * threads * target_s / max(dt, 1e-3))))
+    f, dt = run(n)
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d random (token, head) rows of the THD prefill workload, fp64, %.1f s"
+                      % (n, dt)}
+
+
+def cpu_baseline_decode(pc, target_s, threads):
+    """The oracle on random (sequence, KV head) units, all their query rows; KV GB/s."""
+    import numpy as np
+    import oracle
+    from scaled_dot_product_19_amd import inputs
+    rng = np.random.default_rng(11)
+    G = pc.hq // pc.hkv
+    lens = pc.seq_lens.numpy()
+    dqk, dv = int(pc.q.shape[3]), int(pc.v_pool.shape[3])
+    qa, ka, va = (inputs.host_array(pc.q), inputs.host_array(pc.k_pool),
+                  inputs.host_array(pc.v_pool))
+
+    def run(n_units):
+        bs = rng.integers(0, pc.batch, size=n_units)
+        kvs = rng.integers(0, pc.hkv, size=n_units)
+        rows = []
+        for b, kvh in zip(bs, kvs):
+            for t in range(pc.sq):
+                for h in range(kvh * G, (kvh + 1) * G):
+                    rows.append((int(b) * pc.sq + t) * pc.hq + h)
+        kv_bytes = float(sum(int(lens[b]) for b in bs)) * (dqk + dv) * 2
+        t0 = time.perf_counter()
+        oracle.decode_paged(qa, ka, va, pc.pt_k.numpy(), pc.pt_v.numpy(), lens, pc.page_size,
+                            pc.scale, pc.causal, num_splits=pc.num_splits,
+                            sel_rows=np.array(rows, dtype=np.int64), nthreads=threads)
+        return kv_bytes, time.perf_counter() - t0, len(rows)
+
+    by, dt, _ = run(max(2, threads // G))
+    n = int(max(2, min(pc.batch * pc.hkv * 4, max(2, threads // G) * target_s / max(dt, 1e-3))))
+    by, dt, nrows = run(n)
+    return {"value": by / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d random (sequence, KV head) units (%d query rows) of the paged decode "
+                      "workload, 8-way split + LSE merge, fp64, %.1f s" % (n, nrows, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU seconds of each oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the kernels here run on a single MI355X and "
+              "no multi-GPU path is built (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from scaled_dot_product_19_amd import inputs, sdpa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sdpa.load()  # raises if the HIP library is missing; there is no fallback
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    t0 = time.time()
+    case = inputs.thd_prefill_d128()
+    pc = inputs.paged_decode_d128()
+    log("inputs drawn in %.1f s: prefill T=%d lengths=%s; decode pages=%d lens sum=%d"
+        % (time.time() - t0, int(case.cu_q[-1]), case.lengths_q, pc.k_pool.shape[0],
+           int(pc.seq_lens.sum())))
+
+    # --- device-resident inputs and caller-owned outputs -------------------
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    cu_q, cu_kv = case.cu_q.to(dev), case.cu_kv.to(dev)
+    T = int(case.cu_q[-1])
+    o_p = torch.empty((T, case.hq, 128), dtype=torch.bfloat16, device=dev)
+    lse_p = torch.empty((T, case.hq), dtype=torch.float32, device=dev)
+
+    dq, kp, vp = pc.q.to(dev), pc.k_pool.to(dev), pc.v_pool.to(dev)
+    ptk, ptv, sl = pc.pt_k.to(dev), pc.pt_v.to(dev), pc.seq_lens.to(dev)
+    o_d = torch.empty((pc.batch, pc.sq, pc.hq, 128), dtype=torch.bfloat16, device=dev)
+    lse_d = torch.empty((pc.batch, pc.sq, pc.hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(sdpa.decode_workspace_bytes(pc.batch, pc.sq, pc.hq, 128, pc.num_splits),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        sdpa.prefill_thd(q, k, v, cu_q, cu_kv, case.max_q, case.max_kv, case.scale, True,
+                         out=o_p, lse=lse_p, lse_layout=sdpa.LSE_PACKED, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        sdpa.decode_paged(dq, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, pc.causal,
+                          num_splits=pc.num_splits, workspace=ws, out=o_d, lse=lse_d,
+                          stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    total_ms = start.elapsed_time(end)
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    ms_per_step = total_ms / args.steps
+
+    flops = prefill_flops(case.lengths_q, case.lengths_kv, case.hq, 128, 128)
+    kv_bytes, comp_bytes = decode_bytes(pc)
+    pre_tflops = flops / (pre_avg * 1e-3) / 1e12
+    dec_kv_gbs = kv_bytes / (dec_avg * 1e-3) / 1e9
+    dec_comp_gbs = comp_bytes / (dec_avg * 1e-3) / 1e9
+    log("prefill: %.4f ms avg (min %.4f) -> %.1f TFLOP/s (%.1f%% of bf16 peak)"
+        % (pre_avg, min(pre_ms), pre_tflops, 100 * pre_tflops / PEAK_BF16_TFLOPS))
+    log("decode : %.4f ms avg (min %.4f) -> %.1f GB/s K/V, %.1f GB/s compulsory (%.1f%% of HBM)"
+        % (dec_avg, min(dec_ms), dec_kv_gbs, dec_comp_gbs, 100 * dec_comp_gbs / PEAK_HBM_GBS))
+    log("step   : %.4f ms (wall %.4f ms)" % (ms_per_step, 1e3 * wall / args.steps))
+
+    cpu_pre = cpu_dec = None
+    if not args.no_cpu_baseline:
+        threads = host_threads()
+        log("cpu baseline: oracle on %d threads, ~%.0f s per sample" % (threads,
+                                                                      args.cpu_seconds))
+        cpu_pre = cpu_baseline_prefill(case, args.cpu_seconds, threads)
+        log("  prefill oracle: %.3g TFLOP/s (%s)" % (cpu_pre["value"], cpu_pre["sample"]))
+        cpu_dec = cpu_baseline_decode(pc, args.cpu_seconds, threads)
+        log("  decode oracle: %.3g GB/s (%s)" % (cpu_dec["value"], cpu_dec["sample"]))
+
+    line = {
+        "metric": "prefill attn TFLOP/s (% MFMA peak); paged decode KV GB/s (% HBM peak)",
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16; lengths, page permutations drawn per seed)",
+        "config": {
+            "workload": "THD ragged causal prefill bf16 (8 seqs U[128,4096], 32/8 heads, D=128)"
+                        " + paged decode bf16 (B=64, 32/8 heads, D=128, page 64, "
+                        "L U[512,32768], 8 splits + LSE combine)",
+            "prefill_tokens": T,
+            "prefill_lengths": case.lengths_q,
+            "prefill_flop": flops,
+            "prefill_ms": round(pre_avg, 4),
+            "decode_batch": pc.batch,
+            "decode_kv_bytes": kv_bytes,
+            "decode_compulsory_bytes": comp_bytes,
+            "decode_ms": round(dec_avg, 4),
+            "seeds": [inputs.SEED_BASE + 2, inputs.SEED_BASE + 3],
+        },
+        "decode": {
+            "value": round(dec_kv_gbs, 1),
+            "unit": "GB/s",
+            "what": "K/V bytes of live tokens / (split kernel + combine kernel) time",
+        },
+        "roofline": {
+            "kernel": "prefill_bf16_kernel<128, 64>",
+            "bound": "mfma",
+            "achieved": round(pre_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "roofline_decode": {
+            "kernel": "decode_kernel<128, 128, 1, true> + combine_kernel<false>",
+            "bound": "hbm",
+            "achieved": round(dec_comp_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_comp_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu_pre,
+        "cpu_baseline_decode": cpu_dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
