@@ -151,7 +151,8 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  * q       [batch, s_q, h_q, d_qk] dense, bf16.
  * k_pool  K rows at k_pool + page*k_sp + slot*k_st + head*k_sh, d_qk wide.
  * v_pool  V rows at v_pool + page*v_sp + slot*v_st + head*v_sh, d_v wide
- *         (K and V pools may alias).
+ *         (K and V pools may alias).  Token rows of one page must not
+ *         overlap (k_st >= d_qk, v_st >= d_v) and k_st, v_st < 2^26.
  * page_table_k / page_table_v: int32 [batch, table_stride]; entries past a
  *         sequence's last page are never read.
  * seq_lens int32 [batch]; max_seqlen_kv: host-known upper bound (must be

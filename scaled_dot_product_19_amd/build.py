@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libsdpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["sdpa_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip",
-           "combine.hip"]
+           "decode_small.hip", "combine.hip"]
 
 
 def hipcc() -> str:

@@ -1,0 +1,426 @@
+// decode_small.hip -- paged-KV decode for few query rows per KV head
+// (s_q * G <= 16), e.g. single-token GQA decode: the HBM-streaming case.
+//
+// Same result as decode_paged.hip (per (b, KV head, split): the normalized
+// partial O_c and its natural-log LSE_c over the chunk's visible keys, read
+// through independent K and V page tables: cuDNN Frontend v1.31.0 Release
+// Notes, "SDPA: paged KV, split-KV, and engine selection"), but the tile is
+// sized to the live rows (v1.30.0 Release Notes, "New: decode tiles -- SDPA
+// decode stops running the prefill pipeline"): 16 query columns on the
+// 16x16 MFMA instead of 32-row prefill blocks.
+//
+// Work decomposition: one work-group (4 waves) per (b, KV head, split).  The
+// four waves stream disjoint tiles of the chunk (wave w takes tiles w, w+4,
+// ...) with no block-level barrier in the loop, each with its own online
+// softmax state, and merge by LSE through LDS at the end.  Per tile of TK
+// keys (TK * D = 4096, so one tile is 8 KB of K plus 8 KB of V):
+//   - K goes straight from HBM into the MFMA A-operand registers
+//     (S^T = K Q^T: lane (key, d-group) loads 16 contiguous bytes of its key
+//     row), no LDS;
+//   - V is loaded row-coalesced (16 lanes read one 256-byte row), transposed
+//     in registers and written to a wave-private LDS tile V^T[n][key], from
+//     which the second MFMA (O^T += V^T P^T) reads its A operand;
+//   - the next tile's loads are issued before the current tile is computed
+//     (register double buffer) and page ids are fetched two tiles ahead with
+//     scalar loads, so a wave keeps 16 KB in flight.
+#include "sdpa_device.h"
+#include "sdpa_launch.h"
+
+namespace sdpa {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_k16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+struct SmallKArgs {
+    const bf16_t* q;
+    const bf16_t* kp;
+    int64_t k_sp, k_st, k_sh;
+    const bf16_t* vp;
+    int64_t v_sp, v_st, v_sh;
+    const int32_t* pt_k;
+    const int32_t* pt_v;
+    int32_t table_stride;
+    const int32_t* seq_lens;
+    int32_t sq, hq, hkv, group, page, page_shift, splits, rows, n_units;
+    int64_t total_rows;
+    float scale_log2;
+    int32_t causal;
+    float* o_part;
+    float* lse_part;
+    bf16_t* o;
+    float* lse;
+};
+
+constexpr int kWaves = 4;
+
+// Fourth word of a raw buffer resource on gfx9-family parts (CDNA): no
+// swizzle, 32-bit data format; the range check returns zeros past num_records.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Load of a kernel-invariant int32 (page table, lengths) at a wave-uniform
+// index through the constant address space, so it becomes a scalar load.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+template <int D>
+struct SmallCfg {
+    static constexpr int TK = 4096 / D;      // keys per wave tile
+    static constexpr int SB = TK / 16;       // 16-key sub-blocks per tile
+    static constexpr int KK = D / 32;        // k-steps of S^T = K Q^T
+    static constexpr int NB = D / 16;        // 16-row blocks of O^T
+    static constexpr int VP = TK + 4;        // V^T LDS pitch in elements
+    static constexpr int VU = TK * D / 32 / 64;  // V units (4 keys x 8 columns) per lane
+    static constexpr int WAVE_LDS = D * VP;  // elements of one wave's V^T tile
+    static constexpr int MERGE_BYTES = kWaves * 16 * D * 4 + 2 * kWaves * 16 * 4;
+    static constexpr int LDS_BYTES =
+        (kWaves * WAVE_LDS * 2 > MERGE_BYTES) ? kWaves * WAVE_LDS * 2 : MERGE_BYTES;
+    static_assert(SB >= 1 && VU >= 1, "tile shape");
+};
+
+// One wave's registers for one tile: K operands and raw V rows.
+template <int D>
+struct TileRegs {
+    bf16x8 k[SmallCfg<D>::SB][SmallCfg<D>::KK];
+    uint4 v[SmallCfg<D>::VU][4];
+};
+
+template <int D>
+__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(SmallKArgs a) {
+    using C = SmallCfg<D>;
+    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, g = lane >> 4;
+
+    const int unit = blockIdx.x;
+    const int split = unit % a.splits;
+    const int bh = unit / a.splits;
+    const int kvh = bh % a.hkv, b = bh / a.hkv;
+
+    // a length past the table's reach is clamped: the table is never read out of bounds
+    const int L = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
+    int lo = 0, hi = L;
+    if (a.splits > 1) {
+        const int per = (L + a.splits - 1) / a.splits;
+        const int chunk = ((per + a.page - 1) / a.page) * a.page;
+        lo = min(L, split * chunk);
+        hi = min(L, lo + chunk);
+    }
+    // query column c of the tile = row c of this KV head: token c / G, head kvh*G + c % G
+    const bool row_ok = c < a.rows;
+    const int rr = row_ok ? c : 0;
+    const int tok = rr / a.group;
+    const int64_t grow = ((int64_t)b * a.sq + tok) * a.hq + kvh * a.group + rr % a.group;
+    const int lim = min(hi - 1, a.causal ? L - a.sq + tok : L - 1);
+    // keys every live row sees (the first token has the earliest causal limit)
+    const int nomask_end = max(lo, min(hi, a.causal ? L - a.sq + 1 : hi));
+
+    // Q^T operand: lane (q = c, d-group g) holds d = 32 kk + 8 g .. +8 of its row
+    bf16x8 qf[C::KK];
+    {
+        const bf16_t* qrow = a.q + grow * D + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) {
+            uint4 w = {0u, 0u, 0u, 0u};
+            if (row_ok) w = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+            qf[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    f32x4 acc[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = neg_inf(), l = 0.f;
+
+    const int n_tiles = (hi - lo + C::TK - 1) / C::TK;
+    const int32_t* ptk = a.pt_k + (int64_t)b * a.table_stride;
+    const int32_t* ptv = a.pt_v + (int64_t)b * a.table_stride;
+    const char* kbase = reinterpret_cast<const char*>(a.kp + (int64_t)kvh * a.k_sh);
+    const char* vbase = reinterpret_cast<const char*>(a.vp + (int64_t)kvh * a.v_sh);
+    const int64_t k_sp2 = 2 * a.k_sp, v_sp2 = 2 * a.v_sp;
+    const int k_st2 = 2 * (int)a.k_st, v_st2 = 2 * (int)a.v_st;
+    bf16_t* vt = smem + wave * C::WAVE_LDS;
+    // the last key index whose page may be looked up (the table is never read past it)
+    const int last_key = max(hi - 1, 0);
+
+    // Per-lane byte offsets inside a 16-key sub-block; all loop-invariant.
+    //   K (A operand of S^T = K Q^T): lane (key c, d-group g) -> row c, bytes 16 g + 64 kk.
+    //   V (row-coalesced 4 keys x 8 columns units): unit lane + 64 u.
+    const int k_off = c * k_st2 + 16 * g;
+    int v_off[C::VU], v_kt[C::VU], v_n8[C::VU];
+#pragma unroll
+    for (int u = 0; u < C::VU; ++u) {
+        const int unitv = lane + 64 * u;
+        v_n8[u] = unitv % (D / 8);
+        v_kt[u] = 4 * (unitv / (D / 8));           // first key of the unit in the tile
+        v_off[u] = (v_kt[u] & 15) * v_st2 + 16 * v_n8[u];
+    }
+
+    // Buffer resources of one tile's 16-key sub-blocks.  The range of a
+    // sub-block covers exactly its keys below hi, so lanes of masked keys
+    // read zeros and a tile past the chunk moves no data at all.
+    struct Rsrc {
+        __amdgpu_buffer_rsrc_t k[C::SB], v[C::SB];
+    };
+    auto make_rsrc = [&](int t, Rsrc& rs) {
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) {
+            const int ks = lo + t * C::TK + 16 * sb;
+            const int nvalid = min(max(hi - ks, 0), 16);
+            const int kc = min(ks, last_key);
+            const int pidx = a.page_shift >= 0 ? (kc >> a.page_shift) : kc / a.page;
+            const int slot = ks - pidx * a.page;    // in [0, page) whenever nvalid > 0
+            const int32_t pk = load_uniform(ptk, pidx);
+            const int32_t pv = load_uniform(ptv, pidx);
+            const int k_bytes = nvalid > 0 ? (nvalid - 1) * k_st2 + 2 * D : 0;
+            const int v_bytes = nvalid > 0 ? (nvalid - 1) * v_st2 + 2 * D : 0;
+            rs.k[sb] = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(kbase + (int64_t)pk * k_sp2 + (int64_t)slot * k_st2), (short)0, k_bytes,
+                kRsrcWord3);
+            rs.v[sb] = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(vbase + (int64_t)pv * v_sp2 + (int64_t)slot * v_st2), (short)0, v_bytes,
+                kRsrcWord3);
+        }
+    };
+    auto issue = [&](const Rsrc& rs, TileRegs<D>& r) {
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) {
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk)
+                r.k[sb][kk] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs.k[sb], k_off + 64 * kk, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < C::VU; ++u) {
+            const int sb = (64 * u) / (D / 2);   // uniform: every lane's unit is in this sub-block
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                r.v[u][e] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v[sb], v_off[u], e * v_st2, 0));
+        }
+    };
+    auto compute = [&](int t, const TileRegs<D>& r) {
+        const int key0 = lo + t * C::TK;
+        // V rows -> V^T[n][key] in this wave's LDS tile
+#pragma unroll
+        for (int u = 0; u < C::VU; ++u) {
+            const int kt = v_kt[u];
+            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[u][0]);
+            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[u][1]);
+            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[u][2]);
+            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[u][3]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint2 even, odd;
+                even.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);
+                even.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x05040100u);
+                odd.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);
+                odd.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x07060302u);
+                const int n = 8 * v_n8[u] + 2 * j;
+                *reinterpret_cast<uint2*>(vt + n * C::VP + kt) = even;
+                *reinterpret_cast<uint2*>(vt + (n + 1) * C::VP + kt) = odd;
+            }
+        }
+        // S^T = K Q^T: s[sb][r] is key key0 + 16 sb + 4 g + r of query c
+        f32x4 s[C::SB];
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) {
+            s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk) s[sb] = mfma16_k32(r.k[sb][kk], qf[kk], s[sb]);
+        }
+        const bool need_mask = key0 + C::TK > nomask_end;
+        float mt = neg_inf();
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x = s[sb][i] * a.scale_log2;
+                if (need_mask) x = key0 + 16 * sb + 4 * g + i > lim ? neg_inf() : x;
+                s[sb][i] = x;
+                mt = fmaxf(mt, x);
+            }
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m, mt);
+        const float m_use = m_new == neg_inf() ? 0.f : m_new;
+        const float alpha = fast_exp2(m - m_use);
+        m = m_new;
+        float lsum = 0.f;
+        s16x4 pb[C::SB];
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(s[sb][i] - m_use);
+                lsum += p;
+                pb[sb][i] = (short)f32_to_bf16_bits(p);
+            }
+        }
+        l = l * alpha + lsum;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) acc[nb] *= alpha;
+        // the V^T stores of all lanes land before any lane reads them
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // O^T += V^T P^T: A = V^T[n = 16 nb + c][keys 16 sb + 4 g .. +4]
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+            for (int sb = 0; sb < C::SB; ++sb) {
+                const s16x4 va =
+                    *reinterpret_cast<const s16x4*>(vt + (16 * nb + c) * C::VP + 16 * sb + 4 * g);
+                acc[nb] = mfma16_k16(va, pb[sb], acc[nb]);
+            }
+        }
+        // keep the next tile's V^T stores behind this tile's reads
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+
+    // wave-private stream over tiles wave, wave + 4, ...; the loads of the
+    // next tile are in flight while this one is computed.  Loop invariant at
+    // the top: r0 holds (or is loading) tile t, ra is the resource set of
+    // tile t + 4.
+    {
+        TileRegs<D> r0, r1;
+        Rsrc ra, rb;
+        int t = wave;
+        make_rsrc(t, rb);
+        make_rsrc(t + kWaves, ra);
+        issue(rb, r0);
+        while (t < n_tiles) {
+            make_rsrc(t + 2 * kWaves, rb);
+            issue(ra, r1);
+            compute(t, r0);
+            t += kWaves;
+            if (t >= n_tiles) break;
+            // r1 holds tile t, rb the resources of tile t + 4
+            make_rsrc(t + 2 * kWaves, ra);
+            issue(rb, r0);
+            compute(t, r1);
+            t += kWaves;
+        }
+    }
+
+    // ---- merge the four waves by LSE and store -----------------------------
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    __syncthreads();  // every wave is done with its V^T tile
+    float* red_o = reinterpret_cast<float*>(smem);              // [wave][q][n]
+    float* red_m = red_o + kWaves * 16 * D;                      // [wave][q]
+    float* red_l = red_m + kWaves * 16;                          // [wave][q]
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+        *reinterpret_cast<f32x4*>(red_o + (wave * 16 + c) * D + 16 * nb + 4 * g) = acc[nb];
+    if (g == 0) {
+        red_m[wave * 16 + c] = m;
+        red_l[wave * 16 + c] = l;
+    }
+    __syncthreads();
+    const int items = a.rows * (D / 4);
+    for (int it = threadIdx.x; it < items; it += 256) {
+        const int q = it / (D / 4), n = 4 * (it % (D / 4));
+        float mw[kWaves];
+        float M = neg_inf();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            mw[w] = red_m[w * 16 + q];
+            M = fmaxf(M, mw[w]);
+        }
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        float lse = neg_inf();
+        if (M != neg_inf()) {
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float sc = fast_exp2(mw[w] - M);  // exactly 0 for an empty wave
+                tot += sc * red_l[w * 16 + q];
+                o += sc * *reinterpret_cast<const f32x4*>(red_o + (w * 16 + q) * D + n);
+            }
+            o *= 1.f / tot;
+            lse = kLn2 * (M + fast_log2(tot));
+        }
+        const int t2 = q / a.group;
+        const int64_t row = ((int64_t)b * a.sq + t2) * a.hq + kvh * a.group + q % a.group;
+        if (a.splits > 1) {
+            *reinterpret_cast<f32x4*>(a.o_part + ((int64_t)split * a.total_rows + row) * D + n) = o;
+            if (n == 0) a.lse_part[(int64_t)split * a.total_rows + row] = lse;
+        } else {
+            uint2 w;
+            w.x = pack_bf16x2(o[0], o[1]);
+            w.y = pack_bf16x2(o[2], o[3]);
+            *reinterpret_cast<uint2*>(a.o + row * D + n) = w;
+            if (n == 0 && a.lse != nullptr) a.lse[row] = lse;
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_small_d(const SmallKArgs& a, hipStream_t s) {
+    using C = SmallCfg<D>;
+    if (a.n_units == 0) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void*)decode_small_kernel<D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_small_kernel<D>, dim3((unsigned)a.n_units), dim3(256),
+                       (size_t)C::LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows) {
+    return dqk == dv && (dqk == 128 || dqk == 256) && rows <= 16;
+}
+
+hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
+    SmallKArgs a;
+    a.q = static_cast<const bf16_t*>(da.q);
+    a.kp = static_cast<const bf16_t*>(da.k_pool);
+    a.k_sp = da.k_sp;
+    a.k_st = da.k_st;
+    a.k_sh = da.k_sh;
+    a.vp = static_cast<const bf16_t*>(da.v_pool);
+    a.v_sp = da.v_sp;
+    a.v_st = da.v_st;
+    a.v_sh = da.v_sh;
+    a.pt_k = da.pt_k;
+    a.pt_v = da.pt_v;
+    a.table_stride = da.table_stride;
+    a.seq_lens = da.seq_lens;
+    a.sq = da.sq;
+    a.hq = da.hq;
+    a.hkv = da.hkv;
+    a.group = da.hq / da.hkv;
+    a.page = da.page;
+    a.page_shift = -1;
+    for (int sh = 4; sh < 31; ++sh)
+        if (da.page == (1 << sh)) a.page_shift = sh;
+    a.splits = da.splits;
+    a.rows = da.sq * a.group;
+    a.n_units = da.batch * da.hkv * da.splits;
+    a.total_rows = (int64_t)da.batch * da.sq * da.hq;
+    a.scale_log2 = da.scale * kLog2e;
+    a.causal = da.causal;
+    a.o_part = da.o_part;
+    a.lse_part = da.lse_part;
+    a.o = static_cast<bf16_t*>(da.o);
+    a.lse = da.lse;
+    switch (da.dqk) {
+        case 128: return launch_small_d<128>(a, s);
+        case 256: return launch_small_d<256>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sdpa

@@ -191,6 +191,11 @@ int sdpa_decode_paged(const void* q, const void* k_pool, int64_t k_sp, int64_t k
                     max_seqlen_kv, (long long)table_stride * page_size);
     if (k_sp <= 0 || k_st <= 0 || k_sh <= 0 || v_sp <= 0 || v_st <= 0 || v_sh <= 0)
         return fail(SDPA_ERR_SHAPE, "pool strides must be positive");
+    if (k_st < d_qk || v_st < d_v)
+        return fail(SDPA_ERR_SHAPE, "pool token rows overlap: k_st=%lld < d_qk or v_st=%lld < d_v",
+                    (long long)k_st, (long long)v_st);
+    if (k_st >= ((int64_t)1 << 26) || v_st >= ((int64_t)1 << 26))
+        return fail(SDPA_ERR_UNSUPPORTED, "pool token strides must be below 2^26 elements");
     const int64_t st[6] = {k_sp, k_st, k_sh, v_sp, v_st, v_sh};
     for (int64_t x : st)
         if (x % 8 != 0)

@@ -58,4 +58,9 @@ hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t s);
 // Decode row-group geometry shared by the launcher and the workspace query.
 bool decode_supported(int32_t dqk, int32_t dv);
 
+// Few-row decode (s_q * G <= 16 query rows per KV head, d_qk == d_v in
+// {64, 128, 256}): the HBM-streaming kernel of decode_small.hip.
+bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows);
+hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t s);
+
 }  // namespace sdpa
