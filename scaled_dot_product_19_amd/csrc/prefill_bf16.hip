@@ -57,6 +57,10 @@ struct PrefillKArgs {
 
 constexpr int kThreads = 256;
 constexpr float kLazyRescale = 8.f;  // log2 units the running max may lag behind
+constexpr int kWin = 4;              // LDS operand fragments read ahead of the MFMAs
+// Fourth word of a raw buffer resource on gfx9-family parts (CDNA): the
+// range check returns zeros past num_records.
+constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -86,6 +90,12 @@ struct PCfg {
 __device__ __forceinline__ void half_swap(float& a, float& b) {
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
+// 3-input max without the NaN-quieting copies the compiler adds around fmaxf
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 __device__ __forceinline__ float half_max(float v) {
     float a = v, b = v;
     half_swap(a, b);
@@ -112,11 +122,17 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Work items: levels of equal causal row block qt, longest first; inside a
+    // level the batch x head-group items are rotated by the level, so one
+    // sequence's items do not stay on the same XCDs (the dispatcher sends
+    // work-group id g to XCD g % 8) and ragged batches spread over the chip.
     const int bid = blockIdx.x;
-    const int b = bid % a.batch;
-    const int rest = bid / a.batch;
-    const int hg = rest % a.n_hg;
-    const int qt = a.n_qtiles - 1 - rest / a.n_hg;
+    const int n_items = a.batch * a.n_hg;
+    const int level = bid / n_items;
+    const int item = (bid % n_items + level) % n_items;
+    const int b = item / a.n_hg;
+    const int hg = item % a.n_hg;
+    const int qt = a.n_qtiles - 1 - level;
 
     const int q_beg = a.cu_q[b], lq = a.cu_q[b + 1] - q_beg;
     const int kv_beg = a.cu_kv[b], lk = a.cu_kv[b + 1] - kv_beg;
@@ -175,31 +191,39 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     // staging maps: K chunk idx -> (row idx / (D/8), 16-byte column idx % (D/8));
     // V unit idx -> (key quad idx % (BN/4), column chunk idx / (BN/4)).  The V
     // map makes 16 consecutive lanes write one V^T row (no LDS bank conflict).
+    // Tiles are read with raw buffer loads: the resource of a tile starts at
+    // its first row and ends with its last row below kv_end, so rows past the
+    // end read as zeros with no predicate, and every lane offset is fixed.
+    const int k_st2 = 2 * (int)a.k_st, v_st2 = 2 * (int)a.v_st;
+    int k_off[C::KC], v_off[C::VU];
+#pragma unroll
+    for (int cc = 0; cc < C::KC; ++cc) {
+        const int idx = tid + kThreads * cc;
+        k_off[cc] = (idx / (D / 8)) * k_st2 + 16 * (idx % (D / 8));
+    }
+#pragma unroll
+    for (int u = 0; u < C::VU; ++u) {
+        const int idx = tid + kThreads * u;
+        v_off[u] = 4 * (idx % (BN / 4)) * v_st2 + 16 * (idx / (BN / 4));
+    }
     Stage<D, BN> st;
     auto load = [&](int k0) {
-        const bool full = k0 + BN <= kv_end;
+        const int nvalid = min(BN, kv_end - k0);
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kb0 + (int64_t)k0 * a.k_st), (short)0, (nvalid - 1) * k_st2 + 2 * D,
+            kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vb0 + (int64_t)k0 * a.v_st), (short)0, (nvalid - 1) * v_st2 + 2 * D,
+            kRsrcWord3);
 #pragma unroll
-        for (int cc = 0; cc < C::KC; ++cc) {
-            const int idx = tid + kThreads * cc;
-            const int row = idx / (D / 8), ch = idx % (D / 8);
-            uint4 w = {0u, 0u, 0u, 0u};
-            if (full || k0 + row < kv_end)
-                w = *reinterpret_cast<const uint4*>(kb0 + (int64_t)(k0 + row) * a.k_st + 8 * ch);
-            st.k[cc] = w;
-        }
+        for (int cc = 0; cc < C::KC; ++cc)
+            st.k[cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off[cc], 0, 0));
 #pragma unroll
-        for (int u = 0; u < C::VU; ++u) {
-            const int idx = tid + kThreads * u;
-            const int kq = idx % (BN / 4), ch = idx / (BN / 4);
+        for (int u = 0; u < C::VU; ++u)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = k0 + 4 * kq + e;
-                uint4 w = {0u, 0u, 0u, 0u};
-                if (full || key < kv_end)
-                    w = *reinterpret_cast<const uint4*>(vb0 + (int64_t)key * a.v_st + 8 * ch);
-                st.v[u][e] = w;
-            }
-        }
+            for (int e = 0; e < 4; ++e)
+                st.v[u][e] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off[u], e * v_st2, 0));
     };
     auto store = [&](bf16_t* buf) {
 #pragma unroll
@@ -236,31 +260,56 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     // one KV tile for this wave
     auto tile = [&](const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vt, int key0,
                     bool need_mask) {
+        // S^T = K Q^T.  MFMA o works on key block o % NKB (consecutive MFMAs use
+        // independent accumulators) and reads its K fragment kWin steps ahead.
+        constexpr int NQK = C::NKB * (D / 16);
+        auto kfrag = [&](int o) {
+            return *reinterpret_cast<const bf16x8*>(
+                ks + ((o % C::NKB) * 32 + col) * C::KP + 8 * half + 16 * (o / C::NKB));
+        };
         f32x16 s[C::NKB];
+        const f32x16 zero = {};
+        bf16x8 fk[kWin];
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) {
+        for (int w = 0; w < kWin; ++w) fk[w] = kfrag(w);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-            const bf16_t* krow = ks + (kb * 32 + col) * C::KP + 8 * half;
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * kk);
-                s[kb] = mfma_32x32x16(kf, qf[kk], s[kb]);
-            }
+        for (int o = 0; o < NQK; ++o) {
+            // the first MFMA of each key block starts from the constant 0
+            s[o % C::NKB] = mfma_32x32x16(fk[o % kWin], qf[o / C::NKB],
+                                          o < C::NKB ? zero : s[o % C::NKB]);
+            if (o + kWin < NQK) fk[o % kWin] = kfrag(o + kWin);
         }
+        // keep the reads kWin ahead: kWin reads, then alternate MFMA / read
+        __builtin_amdgcn_sched_group_barrier(0x100, kWin, 0);
+#pragma unroll
+        for (int o = 0; o < NQK; ++o) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (o + kWin < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        // the first V^T fragments load while the softmax runs
+        constexpr int NPV = C::NB * (BN / 16);
+        auto vfrag = [&](int o) {
+            return *reinterpret_cast<const bf16x8*>(
+                vt + ((o % C::NB) * 32 + col) * C::VP + 8 * half + 16 * (o / C::NB));
+        };
+        bf16x8 fv[kWin];
+#pragma unroll
+        for (int w = 0; w < kWin; ++w) fv[w] = vfrag(w);
         // raw tile max of this lane's query (masked scores -> -inf)
         float mx = neg_inf();
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
             if (need_mask) {
+                // key = key0 + 4 half + (compile-time offset); masked iff offset > dl
+                const int dl = lim - key0 - 4 * half;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    s[kb][r] = key > lim ? neg_inf() : s[kb][r];
+                    const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+                    s[kb][r] = off > dl ? neg_inf() : s[kb][r];
                 }
             }
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+            for (int r = 0; r < 16; r += 2) mx = max3(mx, s[kb][r], s[kb][r + 1]);
         }
         mx = half_max(mx);
         const float mt = mx == neg_inf() ? neg_inf() : mx * a.c;
@@ -276,7 +325,9 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[nb][r] *= alpha;
         }
-        const float nm = -m;
+        // a lane whose max is still -inf has every key masked: any finite shift
+        // gives p = exp2(-inf) = 0 (c > 0) instead of exp2(-inf + inf) = NaN
+        const float nm = m == neg_inf() ? 0.f : -m;
         float lsum = 0.f;
         bf16x8 pb[BN / 16];
 #pragma unroll
@@ -285,7 +336,7 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
             for (int r = 0; r < 16; r += 2) {
                 float p0 = fast_exp2(__builtin_fmaf(s[kb][r], a.c, nm));
                 float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], a.c, nm));
-                if (need_mask) {  // exact zeros for masked keys (also when c = 0)
+                if (need_mask && a.c == 0.f) {  // c > 0: exp2(-inf) is already 0
                     p0 = s[kb][r] == neg_inf() ? 0.f : p0;
                     p1 = s[kb][r + 1] == neg_inf() ? 0.f : p1;
                 }
@@ -296,14 +347,16 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
             }
         }
         l += lsum;
+        // O^T += V^T P^T: MFMA o works on output block o % NB
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-            const bf16_t* vrow = vt + (nb * 32 + col) * C::VP + 8 * half;
+        for (int o = 0; o < NPV; ++o) {
+            acc[o % C::NB] = mfma_32x32x16(fv[o % kWin], pb[o / C::NB], acc[o % C::NB]);
+            if (o + kWin < NPV) fv[o % kWin] = vfrag(o + kWin);
+        }
 #pragma unroll
-            for (int kst = 0; kst < BN / 16; ++kst) {
-                const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + 16 * kst);
-                acc[nb] = mfma_32x32x16(vf, pb[kst], acc[nb]);
-            }
+        for (int o = 0; o < NPV; ++o) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            if (o + kWin < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
         }
     };
 
