@@ -15,21 +15,28 @@
 // (partial GQA packing: v1.30.0 "New: decode tiles", Partial PackGQA bullet).
 // Work-groups are issued longest causal row block first.
 //
-// Per wave and KV tile of BN keys (v_mfma_f32_32x32x16_bf16, wave64):
-//   S^T[key][q] = K Q^T  -- A = K rows from LDS, B = the wave's Q^T held in
-//                           registers; each lane ends up holding scores of
-//                           ONE query (column lane % 32) for 16 keys per block;
+// K/V staging (gfx950 LDS DMA).  Tiles of BN keys go from HBM straight into
+// LDS with buffer_load_dwordx4 ... lds: each lane's 16 bytes land at
+// LDS base + 16 * lane, so a wave instruction fills 1 KB.  Both tiles stay
+// row-major; bank conflicts are avoided by choosing, per lane, which 16-byte
+// chunk of which row it fetches (an XOR swizzle of the chunk index by the
+// row).  The buffer range of a tile ends with its last row below kv_end, so
+// rows past it arrive as zeros and a tile past the end moves no data.  An
+// S-stage LDS ring keeps S - 1 tiles in flight.
+//
+// Per wave and tile (v_mfma_f32_32x32x16_bf16, wave64):
+//   S^T[key][q] = K Q^T  -- A = K rows (ds_read_b128), B = the wave's Q^T in
+//                           registers; each lane holds the scores of ONE
+//                           query (column lane % 32);
 //   online softmax       -- raw row max (3-input max), one lane-half exchange
 //                           (v_permlane32_swap), p = exp2(s * c - m) as one
-//                           FMA + exp, running sums per lane half; the output
-//                           rescale is lazy: the running max only moves when a
+//                           FMA + exp; the running max only moves when a
 //                           tile's max exceeds it by more than 8 (log2 units),
 //                           which leaves the result exactly the same;
 //   O^T[n][q] += V^T P^T -- B = P^T straight from the score accumulators
-//                           (bf16), A = V^T from LDS, stored transposed with
-//                           the keys of each 16-key step permuted to match.
-// K/V tiles are double-buffered in LDS: the next tile's global loads are in
-// flight while the current one is on the MFMA units.
+//                           (bf16); A = V^T read from the row-major V tile
+//                           with ds_read_b64_tr_b16, which hands each lane
+//                           four consecutive keys of one column.
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 
@@ -59,27 +66,42 @@ constexpr int kThreads = 256;
 constexpr float kLazyRescale = 8.f;  // log2 units the running max may lag behind
 constexpr int kWin = 4;              // LDS operand fragments read ahead of the MFMAs
 // Fourth word of a raw buffer resource on gfx9-family parts (CDNA): the
-// range check returns zeros past num_records.
+// range check returns zeros past num_records (also for loads into LDS).
 constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, int BN>
+template <int D, int BN, int S>
 struct PCfg {
-    static constexpr int KP = D + 8;             // K tile pitch (elements)
-    static constexpr int VP = BN + 8;            // V^T tile pitch (elements)
-    static constexpr int K_ELEMS = BN * KP;
-    static constexpr int V_ELEMS = D * VP;
-    static constexpr int BUF = K_ELEMS + V_ELEMS;
-    static constexpr int LDS_BYTES = 2 * BUF * 2;
-    static constexpr int KC = BN * D / 8 / kThreads;   // 16-byte K chunks per thread
-    static constexpr int VU = BN * D / 32 / kThreads;  // V units (4 keys x 8 columns) per thread
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int ROW_B = 2 * D;                // bytes per row
+    static constexpr int TILE_B = BN * ROW_B;          // bytes of a K (or V) tile
+    static constexpr int STAGE_B = 2 * TILE_B;         // K tile then V tile
+    static constexpr int LDS_BYTES = S * STAGE_B;
+    static constexpr int NI = TILE_B / 1024 / 4;       // LDS DMA instructions per wave per tile
     static constexpr int NKB = BN / 32;                // 32-key blocks of a tile
     static constexpr int NB = D / 32;                  // 32-row blocks of O^T
-    static_assert(KC >= 1 && VU >= 1 && BN % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert((BN / 4) * (D / 8) % kThreads == 0, "V units must tile the work-group");
+    static constexpr int KK = D / 16;                  // k-steps of S^T = K Q^T
+    static_assert(NI >= 1 && TILE_B % 4096 == 0, "tile must fill whole DMA instructions");
+    static_assert(BN % 32 == 0 && D % 32 == 0 && CPR >= 8, "tile shape");
 };
+
+// Swizzled position of 16-byte chunk lc of a K row: 16 lanes reading the
+// same chunk of 16 consecutive rows hit 16 different 16-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row, int lc) {
+    return CPR >= 16 ? (lc ^ (row & 15)) : (lc ^ ((row >> 1) & 7));
+}
+// Swizzled chunk of a V row: the transpose reads of 32 lanes touch 4
+// consecutive rows x 4 consecutive chunks, which then cover all banks.
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row, int lc) {
+    return CPR >= 16 ? (lc ^ (4 * (row & 3))) : (lc ^ (4 * ((row >> 1) & 1)));
+}
 
 // Lane-half exchange with v_permlane32_swap: on two copies a = b = v the
 // swap leaves a = v of lanes 0..31 and b = v of lanes 32..63 in every lane,
@@ -107,25 +129,58 @@ __device__ __forceinline__ float half_sum(float v) {
     return a + b;
 }
 
-template <int D, int BN>
-struct Stage {
-    uint4 k[PCfg<D, BN>::KC];
-    uint4 v[PCfg<D, BN>::VU][4];
-};
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// D <= 128: two work-groups per CU (<= 256 registers per lane).  D = 256:
-// one, with the O^T accumulators in the second half of the register file.
-template <int D, int BN>
+// Raw buffer resource (no stride) over [base, base + nbytes).
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, int nbytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)nbytes, (uint32_t)kRsrcWord3};
+}
+
+// LDS byte address of a pointer into this work-group's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p);
+}
+
+// 16-byte LDS DMA: lane L's 16 bytes at rsrc + voff land at LDS address
+// lds + 16 L.  Issued as inline asm so the compiler does not hold LDS reads
+// back behind every pending DMA (its alias model cannot tell the ring stages
+// apart); completion is awaited explicitly with wait_vmcnt + a barrier.  The
+// s_nop covers the M0-write -> LDS-DMA hazard.  M0 is declared clobbered;
+// nothing else in these kernels keeps a value in M0 (the compiler only uses
+// it for LDS DMA, interpolation and indexed moves, none of which occur).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// D <= 128: two work-groups per CU (<= 256 registers per lane, 2-stage ring).
+// D = 256: one, with a 4-stage ring and the O^T accumulators in AGPRs.
+template <int D, int BN, int S>
 __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_kernel(PrefillKArgs a) {
-    using C = PCfg<D, BN>;
+    using C = PCfg<D, BN, S>;
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    char* const lds = reinterpret_cast<char*>(smem);
+    const uint32_t lds_base = lds_addr(smem);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // Work items: levels of equal causal row block qt, longest first; inside a
-    // level the batch x head-group items are rotated by the level, so one
-    // sequence's items do not stay on the same XCDs (the dispatcher sends
-    // work-group id g to XCD g % 8) and ragged batches spread over the chip.
+    // level the batch x head-group items are rotated by the level so that no
+    // sequence stays on fixed XCDs (the dispatcher sends work-group g to XCD
+    // g % 8) and ragged batches spread over the chip.
     const int bid = blockIdx.x;
     const int n_items = a.batch * a.n_hg;
     const int level = bid / n_items;
@@ -159,13 +214,47 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
         nomask_end = a.causal ? max(0, min(lk, i0 + shift + 1)) : lk;
     }
     const int lim = a.causal ? min(lk - 1, i + shift) : lk - 1;
+    const int n_tiles = (kv_end + BN - 1) / BN;
+
+    // ---- LDS DMA of the K/V tiles -------------------------------------------
+    // Wave w's instruction j fills bytes [(w NI + j) KiB, +1 KiB) of a tile;
+    // lane L of it writes chunk position p = (w NI + j) * 64 + L, i.e. row
+    // p / CPR, physical chunk p % CPR, and so fetches logical chunk
+    // swz(row, p % CPR) of that row.  These byte offsets never change.
+    const bf16_t* kb0 = a.k + (int64_t)kv_beg * a.k_st + (int64_t)kvh * a.k_sh;
+    const bf16_t* vb0 = a.v + (int64_t)kv_beg * a.v_st + (int64_t)kvh * a.v_sh;
+    const int k_st2 = 2 * (int)a.k_st, v_st2 = 2 * (int)a.v_st;
+    int k_src[C::NI], v_src[C::NI];
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) {
+        const int p = (wave * C::NI + j) * 64 + lane;
+        const int row = p / C::CPR, pc = p % C::CPR;
+        k_src[j] = row * k_st2 + 16 * swz_k<C::CPR>(row, pc);
+        v_src[j] = row * v_st2 + 16 * swz_v<C::CPR>(row, pc);
+    }
+    auto issue = [&](int t) {
+        // a tile at or past kv_end gets an empty range: its DMA writes zeros
+        // and reads nothing
+        const int k0 = t * BN;
+        const int nvalid = min(BN, kv_end - k0);
+        const u32x4 kr = make_rsrc(kb0 + (int64_t)k0 * a.k_st, nvalid > 0 ? (nvalid - 1) * k_st2 + 2 * D : 0);
+        const u32x4 vr = make_rsrc(vb0 + (int64_t)k0 * a.v_st, nvalid > 0 ? (nvalid - 1) * v_st2 + 2 * D : 0);
+        const uint32_t st = lds_base + (t % S) * C::STAGE_B + wave * C::NI * 1024;
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) dma16(kr, st + j * 1024, k_src[j]);
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) dma16(vr, st + C::TILE_B + j * 1024, v_src[j]);
+    };
+    // start the first S - 1 tiles before the Q load so they overlap it
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) issue(t);
 
     // Q^T operand: lane (col, half) holds d = 16 kk + 8 half .. +8 of row i
-    bf16x8 qf[D / 16];
+    bf16x8 qf[C::KK];
     {
         const bf16_t* qrow = a.q + (int64_t)(q_beg + i) * a.q_st + (int64_t)h * a.q_sh + 8 * half;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
+        for (int kk = 0; kk < C::KK; ++kk) {
             uint4 w = {0u, 0u, 0u, 0u};
             if (row_ok) w = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
             w.x ^= a.q_sign;
@@ -176,6 +265,32 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
         }
     }
 
+    // ---- per-lane LDS read offsets (bytes within a stage) -------------------
+    // K fragment (A of S^T): lane (key = col, half) reads logical chunk
+    // 2 kk + half of row 32 kb + col.  The swizzle depends on the row only
+    // modulo 16, so block kb adds 32 rows and kk >= 8 adds 16 chunks exactly.
+    constexpr int KKW = C::KK < 8 ? C::KK : 8;
+    int k_rd[KKW];
+#pragma unroll
+    for (int kk = 0; kk < KKW; ++kk)
+        k_rd[kk] = col * C::ROW_B + 16 * swz_k<C::CPR>(col, 2 * kk + half);
+    // V^T fragment (A of O^T), two transpose reads per 16-key step: lane l of
+    // 16-lane group G = l / 16 supplies row 16 kst + 4 half + (l % 16) / 4
+    // (+8 for the second read) and the 4 columns starting at
+    // 32 nb + 16 (G % 2) + 4 (l % 4); it receives 4 consecutive keys of
+    // column 32 nb + l % 32.  The swizzle depends on the row modulo 4 only,
+    // and 32-column blocks nb >= 4 sit 16 chunks further.
+    constexpr int NBW = C::NB < 4 ? C::NB : 4;
+    int v_rd[NBW];
+    {
+        const int r0 = 4 * half + (lane & 15) / 4;
+        const int cg = 2 * ((lane >> 4) & 1) + (lane & 3) / 2;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+            v_rd[nb] = C::TILE_B + r0 * C::ROW_B + 16 * swz_v<C::CPR>(r0, 4 * nb + cg) +
+                       8 * (lane & 1);
+    }
+
     f32x16 acc[C::NB];
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
@@ -184,88 +299,16 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     float m = neg_inf();  // running max (log2 units) of this lane's query
     float l = 0.f;        // this lane half's running sum
 
-    const int n_tiles = (kv_end + BN - 1) / BN;
-    const bf16_t* kb0 = a.k + (int64_t)kv_beg * a.k_st + (int64_t)kvh * a.k_sh;
-    const bf16_t* vb0 = a.v + (int64_t)kv_beg * a.v_st + (int64_t)kvh * a.v_sh;
-
-    // staging maps: K chunk idx -> (row idx / (D/8), 16-byte column idx % (D/8));
-    // V unit idx -> (key quad idx % (BN/4), column chunk idx / (BN/4)).  The V
-    // map makes 16 consecutive lanes write one V^T row (no LDS bank conflict).
-    // Tiles are read with raw buffer loads: the resource of a tile starts at
-    // its first row and ends with its last row below kv_end, so rows past the
-    // end read as zeros with no predicate, and every lane offset is fixed.
-    const int k_st2 = 2 * (int)a.k_st, v_st2 = 2 * (int)a.v_st;
-    int k_off[C::KC], v_off[C::VU];
-#pragma unroll
-    for (int cc = 0; cc < C::KC; ++cc) {
-        const int idx = tid + kThreads * cc;
-        k_off[cc] = (idx / (D / 8)) * k_st2 + 16 * (idx % (D / 8));
-    }
-#pragma unroll
-    for (int u = 0; u < C::VU; ++u) {
-        const int idx = tid + kThreads * u;
-        v_off[u] = 4 * (idx % (BN / 4)) * v_st2 + 16 * (idx / (BN / 4));
-    }
-    Stage<D, BN> st;
-    auto load = [&](int k0) {
-        const int nvalid = min(BN, kv_end - k0);
-        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(kb0 + (int64_t)k0 * a.k_st), (short)0, (nvalid - 1) * k_st2 + 2 * D,
-            kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(vb0 + (int64_t)k0 * a.v_st), (short)0, (nvalid - 1) * v_st2 + 2 * D,
-            kRsrcWord3);
-#pragma unroll
-        for (int cc = 0; cc < C::KC; ++cc)
-            st.k[cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off[cc], 0, 0));
-#pragma unroll
-        for (int u = 0; u < C::VU; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                st.v[u][e] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off[u], e * v_st2, 0));
-    };
-    auto store = [&](bf16_t* buf) {
-#pragma unroll
-        for (int cc = 0; cc < C::KC; ++cc) {
-            const int idx = tid + kThreads * cc;
-            const int row = idx / (D / 8), ch = idx % (D / 8);
-            *reinterpret_cast<uint4*>(buf + row * C::KP + 8 * ch) = st.k[cc];
-        }
-        bf16_t* vt = buf + C::K_ELEMS;
-#pragma unroll
-        for (int u = 0; u < C::VU; ++u) {
-            const int idx = tid + kThreads * u;
-            const int kq = idx % (BN / 4), ch = idx / (BN / 4);
-            const int key0 = 4 * kq;
-            const int pos = (key0 & ~15) + vt_pos(key0 & 15);
-            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.v[u][0]);
-            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.v[u][1]);
-            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.v[u][2]);
-            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.v[u][3]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint2 even, odd;
-                even.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);
-                even.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x05040100u);
-                odd.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);
-                odd.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x07060302u);
-                const int n = 8 * ch + 2 * j;
-                *reinterpret_cast<uint2*>(vt + n * C::VP + pos) = even;
-                *reinterpret_cast<uint2*>(vt + (n + 1) * C::VP + pos) = odd;
-            }
-        }
-    };
-
-    // one KV tile for this wave
-    auto tile = [&](const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vt, int key0,
-                    bool need_mask) {
-        // S^T = K Q^T.  MFMA o works on key block o % NKB (consecutive MFMAs use
-        // independent accumulators) and reads its K fragment kWin steps ahead.
-        constexpr int NQK = C::NKB * (D / 16);
+    // one KV tile for this wave; st: the tile's stage in LDS
+    auto tile = [&](const char* st, int key0, bool need_mask) {
+        // S^T = K Q^T.  MFMA o works on key block o % NKB (consecutive MFMAs
+        // use independent accumulators) and reads its K fragment kWin steps
+        // ahead.
+        constexpr int NQK = C::NKB * C::KK;
         auto kfrag = [&](int o) {
-            return *reinterpret_cast<const bf16x8*>(
-                ks + ((o % C::NKB) * 32 + col) * C::KP + 8 * half + 16 * (o / C::NKB));
+            const int kb = o % C::NKB, kk = o / C::NKB;
+            return *reinterpret_cast<const bf16x8*>(st + k_rd[kk % KKW] + kb * 32 * C::ROW_B +
+                                                    (kk / KKW) * 256);
         };
         f32x16 s[C::NKB];
         const f32x16 zero = {};
@@ -279,18 +322,21 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
                                           o < C::NKB ? zero : s[o % C::NKB]);
             if (o + kWin < NQK) fk[o % kWin] = kfrag(o + kWin);
         }
-        // keep the reads kWin ahead: kWin reads, then alternate MFMA / read
         __builtin_amdgcn_sched_group_barrier(0x100, kWin, 0);
 #pragma unroll
         for (int o = 0; o < NQK; ++o) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (o + kWin < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        // the first V^T fragments load while the softmax runs
+        // V^T fragments: two transpose reads each; the first kWin load while
+        // the softmax runs
         constexpr int NPV = C::NB * (BN / 16);
         auto vfrag = [&](int o) {
-            return *reinterpret_cast<const bf16x8*>(
-                vt + ((o % C::NB) * 32 + col) * C::VP + 8 * half + 16 * (o / C::NB));
+            const int nb = o % C::NB, kst = o / C::NB;
+            const char* vp = st + v_rd[nb % NBW] + (nb / NBW) * 256 + kst * 16 * C::ROW_B;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::ROW_B));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         bf16x8 fv[kWin];
 #pragma unroll
@@ -347,7 +393,7 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
             }
         }
         l += lsum;
-        // O^T += V^T P^T: MFMA o works on output block o % NB
+        // O^T += V^T P^T: MFMA o works on output block o % NB, 16-key step o / NB
 #pragma unroll
         for (int o = 0; o < NPV; ++o) {
             acc[o % C::NB] = mfma_32x32x16(fv[o % kWin], pb[o / C::NB], acc[o % C::NB]);
@@ -356,22 +402,21 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
 #pragma unroll
         for (int o = 0; o < NPV; ++o) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            if (o + kWin < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            if (o + kWin < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
     };
 
-    if (n_tiles > 0) {
-        load(0);
-        store(smem);
-    }
+    // Ring: at iteration t tile t is complete in stage t % S, tiles up to
+    // t + S - 2 are in flight; the DMA of tile t + S - 1 reuses the stage
+    // that tile t - 1 occupied (every wave passed the barrier after it).
+    constexpr int PER_TILE = 2 * C::NI;  // vector-memory operations per tile and wave
+    wait_vmcnt<PER_TILE * (S - 2)>();
     __syncthreads();
     for (int t = 0; t < n_tiles; ++t) {
+        issue(t + S - 1);
         const int key0 = t * BN;
-        const bool more = t + 1 < n_tiles;
-        if (more) load(key0 + BN);  // next tile's HBM loads in flight during the MFMAs
-        const bf16_t* buf = smem + (t & 1) * C::BUF;
-        if (key0 < kv_end_w) tile(buf, buf + C::K_ELEMS, key0, key0 + BN > nomask_end);
-        if (more) store(smem + ((t + 1) & 1) * C::BUF);
+        if (key0 < kv_end_w) tile(lds + (t % S) * C::STAGE_B, key0, key0 + BN > nomask_end);
+        wait_vmcnt<PER_TILE * (S - 2)>();
         __syncthreads();
     }
 
@@ -401,9 +446,9 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     }
 }
 
-template <int D, int BN>
+template <int D, int BN, int S>
 hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
-    using C = PCfg<D, BN>;
+    using C = PCfg<D, BN, S>;
     PrefillKArgs a;
     a.q = static_cast<const bf16_t*>(pa.q);
     a.q_st = pa.q_st;
@@ -434,11 +479,12 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     a.lse_s_max = pa.lse_s_max;
     const int64_t n_wg = (int64_t)a.n_qtiles * a.n_hg * a.batch;
     if (n_wg == 0) return hipSuccess;
+    if (n_wg > INT32_MAX) return hipErrorInvalidValue;
     // more than 64 KiB of dynamic LDS must be requested per kernel
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, BN>,
+    hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, BN, S>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, BN>), dim3((unsigned)n_wg), dim3(kThreads),
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BN, S>), dim3((unsigned)n_wg), dim3(kThreads),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
@@ -447,9 +493,9 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     switch (a.dqk) {
-        case 64: return launch_d<64, 128>(a, s);
-        case 128: return launch_d<128, 64>(a, s);
-        case 256: return launch_d<256, 32>(a, s);
+        case 64: return launch_d<64, 128, 2>(a, s);
+        case 128: return launch_d<128, 64, 2>(a, s);
+        case 256: return launch_d<256, 32, 4>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -91,8 +91,8 @@ int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh, const void* k, i
         if (k_st < d_qk || v_st < d_v)
             return fail(SDPA_ERR_SHAPE, "K/V token rows overlap: k_st=%lld < d_qk or v_st=%lld < d_v",
                         (long long)k_st, (long long)v_st);
-        if (k_st >= ((int64_t)1 << 24) || v_st >= ((int64_t)1 << 24))
-            return fail(SDPA_ERR_UNSUPPORTED, "bf16 prefill K/V token strides must be below 2^24");
+        if (k_st >= ((int64_t)1 << 22) || v_st >= ((int64_t)1 << 22))
+            return fail(SDPA_ERR_UNSUPPORTED, "bf16 prefill K/V token strides must be below 2^22");
         if (d_qk != d_v || (d_qk != 64 && d_qk != 128 && d_qk != 256))
             return fail(SDPA_ERR_UNSUPPORTED,
                         "bf16 prefill serves d_qk == d_v in {64, 128, 256}; got (%d, %d)", d_qk,
