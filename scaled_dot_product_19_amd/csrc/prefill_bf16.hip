@@ -40,6 +40,8 @@
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 
+#include <type_traits>
+
 namespace sdpa {
 namespace {
 
@@ -168,7 +170,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // D <= 128: two work-groups per CU (<= 256 registers per lane, 2-stage ring).
 // D = 256: one, with a 4-stage ring and the O^T accumulators in AGPRs.
-template <int D, int BN, int S>
+// CZ: the scale is 0 (every logit is 0; masked keys need explicit zeros)
+template <int D, int BN, int S, bool CZ>
 __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_kernel(PrefillKArgs a) {
     using C = PCfg<D, BN, S>;
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
         k_src[j] = row * k_st2 + 16 * swz_k<C::CPR>(row, pc);
         v_src[j] = row * v_st2 + 16 * swz_v<C::CPR>(row, pc);
     }
-    auto issue = [&](int t) {
+    auto issue = [&](int t) __attribute__((always_inline)) {
         // a tile at or past kv_end gets an empty range: its DMA writes zeros
         // and reads nothing
         const int k0 = t * BN;
@@ -300,12 +303,12 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     float l = 0.f;        // this lane half's running sum
 
     // one KV tile for this wave; st: the tile's stage in LDS
-    auto tile = [&](const char* st, int key0, bool need_mask) {
+    auto tile = [&](const char* st, int key0, bool need_mask) __attribute__((always_inline)) {
         // S^T = K Q^T.  MFMA o works on key block o % NKB (consecutive MFMAs
         // use independent accumulators) and reads its K fragment kWin steps
         // ahead.
         constexpr int NQK = C::NKB * C::KK;
-        auto kfrag = [&](int o) {
+        auto kfrag = [&](int o) __attribute__((always_inline)) {
             const int kb = o % C::NKB, kk = o / C::NKB;
             return *reinterpret_cast<const bf16x8*>(st + k_rd[kk % KKW] + kb * 32 * C::ROW_B +
                                                     (kk / KKW) * 256);
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
         // V^T fragments: two transpose reads each; the first kWin load while
         // the softmax runs
         constexpr int NPV = C::NB * (BN / 16);
-        auto vfrag = [&](int o) {
+        auto vfrag = [&](int o) __attribute__((always_inline)) {
             const int nb = o % C::NB, kst = o / C::NB;
             const char* vp = st + v_rd[nb % NBW] + (nb / NBW) * 256 + kst * 16 * C::ROW_B;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
             for (int r = 0; r < 16; r += 2) {
                 float p0 = fast_exp2(__builtin_fmaf(s[kb][r], a.c, nm));
                 float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], a.c, nm));
-                if (need_mask && a.c == 0.f) {  // c > 0: exp2(-inf) is already 0
+                if (CZ && need_mask) {  // c > 0: exp2(-inf) is already 0
                     p0 = s[kb][r] == neg_inf() ? 0.f : p0;
                     p1 = s[kb][r + 1] == neg_inf() ? 0.f : p1;
                 }
@@ -412,12 +415,22 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     constexpr int PER_TILE = 2 * C::NI;  // vector-memory operations per tile and wave
     wait_vmcnt<PER_TILE * (S - 2)>();
     __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
+    auto step = [&](int t, auto stage) __attribute__((always_inline)) {
         issue(t + S - 1);
         const int key0 = t * BN;
-        if (key0 < kv_end_w) tile(lds + (t % S) * C::STAGE_B, key0, key0 + BN > nomask_end);
+        if (key0 < kv_end_w)
+            tile(lds + decltype(stage)::value * C::STAGE_B, key0, key0 + BN > nomask_end);
         wait_vmcnt<PER_TILE * (S - 2)>();
         __syncthreads();
+    };
+    // unrolled by S so that each stage's LDS offsets are compile-time constants
+    for (int t = 0; t < n_tiles; t += S) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1 % S>{});
+        if constexpr (S > 2) {
+            if (t + 2 < n_tiles) step(t + 2, std::integral_constant<int, 2 % S>{});
+            if (t + 3 < n_tiles) step(t + 3, std::integral_constant<int, 3 % S>{});
+        }
     }
 
     // epilogue: O = O^T / l written as bf16, LSE = ln2 * (m + log2 l)
@@ -446,9 +459,20 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     }
 }
 
+template <int D, int BN, int S, bool CZ>
+hipError_t launch_dz(const PrefillKArgs& a, int64_t n_wg, hipStream_t s) {
+    using C = PCfg<D, BN, S>;
+    // more than 64 KiB of dynamic LDS must be requested per kernel
+    hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, BN, S, CZ>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, BN, S, CZ>), dim3((unsigned)n_wg), dim3(kThreads),
+                       (size_t)C::LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+
 template <int D, int BN, int S>
 hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
-    using C = PCfg<D, BN, S>;
     PrefillKArgs a;
     a.q = static_cast<const bf16_t*>(pa.q);
     a.q_st = pa.q_st;
@@ -480,13 +504,7 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     const int64_t n_wg = (int64_t)a.n_qtiles * a.n_hg * a.batch;
     if (n_wg == 0) return hipSuccess;
     if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-    // more than 64 KiB of dynamic LDS must be requested per kernel
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, BN, S>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, BN, S>), dim3((unsigned)n_wg), dim3(kThreads),
-                       (size_t)C::LDS_BYTES, s, a);
-    return hipGetLastError();
+    return a.c == 0.f ? launch_dz<D, BN, S, true>(a, n_wg, s) : launch_dz<D, BN, S, false>(a, n_wg, s);
 }
 
 }  // namespace
