@@ -40,6 +40,7 @@
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace sdpa {
@@ -62,9 +63,19 @@ struct PrefillKArgs {
     int32_t causal;
     float* lse;
     int32_t lse_layout, lse_s_max;
+    int32_t n_work;  // work items (levels x batch x head groups)
+    int32_t slot;    // work-queue counter pair used by this launch
 };
 
-constexpr int kThreads = 256;
+// Work queue of the persistent prefill grid.  A launch with G work-groups
+// takes items 0..G-1 by work-group index and the rest by tickets from
+// counter [slot][0] (item = G + ticket); counter [slot][1] counts
+// work-groups that ran out of items, and the last one returns both counters
+// to 0 for the next launch that uses the slot.  Launches take slots round
+// robin, so up to kQueueSlots prefill calls may overlap on one device.
+constexpr int kQueueSlots = 64;
+__device__ __align__(256) uint32_t g_prefill_queue[kQueueSlots][32];
+
 constexpr float kLazyRescale = 8.f;  // log2 units the running max may lag behind
 constexpr int kWin = 4;              // LDS operand fragments read ahead of the MFMAs
 // Fourth word of a raw buffer resource on gfx9-family parts (CDNA): the
@@ -77,18 +88,19 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, int BN, int S>
+template <int D, int BN, int S, int NW>
 struct PCfg {
+    static constexpr int THREADS = 64 * NW;
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row
     static constexpr int ROW_B = 2 * D;                // bytes per row
     static constexpr int TILE_B = BN * ROW_B;          // bytes of a K (or V) tile
     static constexpr int STAGE_B = 2 * TILE_B;         // K tile then V tile
     static constexpr int LDS_BYTES = S * STAGE_B;
-    static constexpr int NI = TILE_B / 1024 / 4;       // LDS DMA instructions per wave per tile
+    static constexpr int NI = TILE_B / 1024 / NW;      // LDS DMA instructions per wave per tile
     static constexpr int NKB = BN / 32;                // 32-key blocks of a tile
     static constexpr int NB = D / 32;                  // 32-row blocks of O^T
     static constexpr int KK = D / 16;                  // k-steps of S^T = K Q^T
-    static_assert(NI >= 1 && TILE_B % 4096 == 0, "tile must fill whole DMA instructions");
+    static_assert(NI >= 1 && TILE_B % (1024 * NW) == 0, "tile must fill whole DMA instructions");
     static_assert(BN % 32 == 0 && D % 32 == 0 && CPR >= 8, "tile shape");
 };
 
@@ -161,6 +173,17 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff) {
 }
 #pragma clang diagnostic pop
 
+// Ticket from a work-queue counter: returns the value before adding 1.  The
+// result is NOT waited for: read it only after wait_vmcnt<0>.  (Written as
+// inline asm so that the compiler does not wait for the return right away,
+// as it does after its own wave-level atomic expansion.)  Same encoding as
+// the compiler's device-scope atomicAdd with return.
+__device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) {
+    uint32_t old;
+    asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=&v"(old) : "v"(ctr), "v"(1u) : "memory");
+    return old;
+}
+
 // Wait until at most N vector-memory operations of this wave are pending.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -170,21 +193,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // D <= 128: two work-groups per CU (<= 256 registers per lane, 2-stage ring).
 // D = 256: one, with a 4-stage ring and the O^T accumulators in AGPRs.
+// NW waves = 32 NW query rows per work-group, each wave 32 rows.
 // CZ: the scale is 0 (every logit is 0; masked keys need explicit zeros)
-template <int D, int BN, int S, bool CZ>
-__global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_kernel(PrefillKArgs a) {
-    using C = PCfg<D, BN, S>;
-    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-    char* const lds = reinterpret_cast<char*>(smem);
-    const uint32_t lds_base = lds_addr(smem);
-
+// PP: ping-pong schedule (NW = 8, two waves per SIMD); otherwise sequential.
+// One work item: NH heads x NW / NH blocks of 32 query rows of one sequence,
+// all keys it sees.  Uniform across the work-group (every exit is taken by
+// all waves).  On return every LDS DMA of the item has landed.
+template <int D, int BN, int S, int NW, bool PP, bool CZ>
+__device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& a, const int bid,
+                                                            char* const lds, const uint32_t lds_base) {
+    static_assert(!PP || (NW == 8 && S >= 4), "ping-pong needs two wave groups and S >= 4");
+    using C = PCfg<D, BN, S, NW>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Work items: levels of equal causal row block qt, longest first; inside a
-    // level the batch x head-group items are rotated by the level so that no
-    // sequence stays on fixed XCDs (the dispatcher sends work-group g to XCD
-    // g % 8) and ragged batches spread over the chip.
-    const int bid = blockIdx.x;
+    // Items: levels of equal causal row block qt, longest first; inside a
+    // level the batch x head-group items are rotated by the level so that
+    // neighbouring items belong to different sequences.
     const int n_items = a.batch * a.n_hg;
     const int level = bid / n_items;
     const int item = (bid % n_items + level) % n_items;
@@ -194,7 +218,7 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
 
     const int q_beg = a.cu_q[b], lq = a.cu_q[b + 1] - q_beg;
     const int kv_beg = a.cu_kv[b], lk = a.cu_kv[b + 1] - kv_beg;
-    const int nt = 4 / a.nh;
+    const int nt = NW / a.nh;
     const int q0 = qt * 32 * nt;
     if (q0 >= lq) return;  // uniform across the work-group
 
@@ -248,9 +272,10 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
 #pragma unroll
         for (int j = 0; j < C::NI; ++j) dma16(vr, st + C::TILE_B + j * 1024, v_src[j]);
     };
-    // start the first S - 1 tiles before the Q load so they overlap it
+    // start the first tiles before the Q load so they overlap it (S - 1 ahead
+    // in the sequential ring, S - 2 in the ping-pong one)
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t) issue(t);
+    for (int t = 0; t < (PP ? S - 2 : S - 1); ++t) issue(t);
 
     // Q^T operand: lane (col, half) holds d = 16 kk + 8 half .. +8 of row i
     bf16x8 qf[C::KK];
@@ -302,18 +327,18 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     float m = neg_inf();  // running max (log2 units) of this lane's query
     float l = 0.f;        // this lane half's running sum
 
-    // one KV tile for this wave; st: the tile's stage in LDS
-    auto tile = [&](const char* st, int key0, bool need_mask) __attribute__((always_inline)) {
-        // S^T = K Q^T.  MFMA o works on key block o % NKB (consecutive MFMAs
-        // use independent accumulators) and reads its K fragment kWin steps
-        // ahead.
-        constexpr int NQK = C::NKB * C::KK;
+    // ---- the three parts of a tile for this wave ------------------------------
+    // QK: s = S^T = K Q^T of the tile in stage st.  MFMA o works on key block
+    // o % NKB (consecutive MFMAs use independent accumulators) and reads its
+    // K fragment kWin steps ahead.
+    constexpr int NQK = C::NKB * C::KK;
+    constexpr int NPV = C::NB * (BN / 16);
+    auto qk = [&](const char* st, f32x16(&s)[C::NKB]) __attribute__((always_inline)) {
         auto kfrag = [&](int o) __attribute__((always_inline)) {
             const int kb = o % C::NKB, kk = o / C::NKB;
             return *reinterpret_cast<const bf16x8*>(st + k_rd[kk % KKW] + kb * 32 * C::ROW_B +
                                                     (kk / KKW) * 256);
         };
-        f32x16 s[C::NKB];
         const f32x16 zero = {};
         bf16x8 fk[kWin];
 #pragma unroll
@@ -331,19 +356,11 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (o + kWin < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        // V^T fragments: two transpose reads each; the first kWin load while
-        // the softmax runs
-        constexpr int NPV = C::NB * (BN / 16);
-        auto vfrag = [&](int o) __attribute__((always_inline)) {
-            const int nb = o % C::NB, kst = o / C::NB;
-            const char* vp = st + v_rd[nb % NBW] + (nb / NBW) * 256 + kst * 16 * C::ROW_B;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::ROW_B));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        bf16x8 fv[kWin];
-#pragma unroll
-        for (int w = 0; w < kWin; ++w) fv[w] = vfrag(w);
+    };
+    // softmax: scores s of the tile whose first key is key0 -> P^T operands pb
+    // (bf16), running max / sums, lazy rescale of the O^T accumulators.
+    auto softmax = [&](f32x16(&s)[C::NKB], bf16x8(&pb)[BN / 16], int key0,
+                       bool need_mask) __attribute__((always_inline)) {
         // raw tile max of this lane's query (masked scores -> -inf)
         float mx = neg_inf();
 #pragma unroll
@@ -378,7 +395,6 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
         // gives p = exp2(-inf) = 0 (c > 0) instead of exp2(-inf + inf) = NaN
         const float nm = m == neg_inf() ? 0.f : -m;
         float lsum = 0.f;
-        bf16x8 pb[BN / 16];
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
@@ -396,42 +412,102 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
             }
         }
         l += lsum;
-        // O^T += V^T P^T: MFMA o works on output block o % NB, 16-key step o / NB
+    };
+    // PV: O^T += V^T P^T for the tile in stage st.  MFMA o works on output
+    // block o % NB, 16-key step o / NB; V^T fragments are two transpose reads.
+    auto pv = [&](const char* st, const bf16x8(&pb)[BN / 16]) __attribute__((always_inline)) {
+        auto vfrag = [&](int o) __attribute__((always_inline)) {
+            const int nb = o % C::NB, kst = o / C::NB;
+            const char* vp = st + v_rd[nb % NBW] + (nb / NBW) * 256 + kst * 16 * C::ROW_B;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::ROW_B));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 fv[kWin];
+#pragma unroll
+        for (int w = 0; w < kWin; ++w) fv[w] = vfrag(w);
 #pragma unroll
         for (int o = 0; o < NPV; ++o) {
             acc[o % C::NB] = mfma_32x32x16(fv[o % kWin], pb[o / C::NB], acc[o % C::NB]);
             if (o + kWin < NPV) fv[o % kWin] = vfrag(o + kWin);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kWin, 1);
 #pragma unroll
         for (int o = 0; o < NPV; ++o) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
             if (o + kWin < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
     };
-
-    // Ring: at iteration t tile t is complete in stage t % S, tiles up to
-    // t + S - 2 are in flight; the DMA of tile t + S - 1 reuses the stage
-    // that tile t - 1 occupied (every wave passed the barrier after it).
+    auto stage_ptr = [&](int t) __attribute__((always_inline)) {
+        return lds + (t % S) * C::STAGE_B;
+    };
     constexpr int PER_TILE = 2 * C::NI;  // vector-memory operations per tile and wave
-    wait_vmcnt<PER_TILE * (S - 2)>();
-    __syncthreads();
-    auto step = [&](int t, auto stage) __attribute__((always_inline)) {
-        issue(t + S - 1);
-        const int key0 = t * BN;
-        if (key0 < kv_end_w)
-            tile(lds + decltype(stage)::value * C::STAGE_B, key0, key0 + BN > nomask_end);
+    f32x16 s[C::NKB];
+    bf16x8 pb[BN / 16];
+
+    if constexpr (!PP) {
+        // Sequential ring: at iteration t tile t is complete in stage t % S,
+        // tiles up to t + S - 2 are in flight; the DMA of tile t + S - 1
+        // reuses the stage tile t - 1 occupied (every wave passed the barrier
+        // after it).
         wait_vmcnt<PER_TILE * (S - 2)>();
         __syncthreads();
-    };
-    // unrolled by S so that each stage's LDS offsets are compile-time constants
-    for (int t = 0; t < n_tiles; t += S) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1 % S>{});
-        if constexpr (S > 2) {
-            if (t + 2 < n_tiles) step(t + 2, std::integral_constant<int, 2 % S>{});
-            if (t + 3 < n_tiles) step(t + 3, std::integral_constant<int, 3 % S>{});
+        auto step = [&](int t, auto stage) __attribute__((always_inline)) {
+            issue(t + S - 1);
+            const int key0 = t * BN;
+            if (key0 < kv_end_w) {
+                const char* st = lds + decltype(stage)::value * C::STAGE_B;
+                qk(st, s);
+                softmax(s, pb, key0, key0 + BN > nomask_end);
+                pv(st, pb);
+            }
+            wait_vmcnt<PER_TILE * (S - 2)>();
+            __syncthreads();
+        };
+        // unrolled by S so that each stage's LDS offsets are compile-time constants
+        for (int t = 0; t < n_tiles; t += S) {
+            step(t, std::integral_constant<int, 0>{});
+            if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1 % S>{});
+            if constexpr (S > 2) {
+                if (t + 2 < n_tiles) step(t + 2, std::integral_constant<int, 2 % S>{});
+                if (t + 3 < n_tiles) step(t + 3, std::integral_constant<int, 3 % S>{});
+            }
         }
+    } else {
+        // Ping-pong: waves w and w + 4 share a SIMD.  Each wave alternates an
+        // MFMA phase M(t) = [PV of tile t - 1, QK of tile t] and a VALU phase
+        // V(t) = [softmax of tile t], with a barrier after every phase; group
+        // 1 (waves 4..7) takes one extra barrier first, so between any two
+        // barriers one group runs MFMAs while the other runs the softmax.
+        // DMA: M(t) issues tile t + S - 2 into the stage tile t - 2 used
+        // (its last reader, PV(t - 2) of the late group, ended a window
+        // earlier).  Tile t is read first in window 2t; each wave has waited
+        // for its own part of it before the barrier that opens that window
+        // (group 0 after V(t - 1), group 1 after M(t - 1)).
+        const bool late = wave >= NW / 2;
+        wait_vmcnt<PER_TILE * (S - 3)>();
+        __syncthreads();
+        if (late) __syncthreads();
+        for (int t = 0; t <= n_tiles; ++t) {
+            __builtin_amdgcn_s_setprio(1);
+            issue(t + S - 2);
+            if (t >= 1 && (t - 1) * BN < kv_end_w) pv(stage_ptr(t - 1), pb);
+            if (t < n_tiles && t * BN < kv_end_w) qk(stage_ptr(t), s);
+            __builtin_amdgcn_s_setprio(0);
+            if (late) wait_vmcnt<PER_TILE>();
+            __syncthreads();
+            if (t == n_tiles) break;
+            const int key0 = t * BN;
+            if (key0 < kv_end_w) softmax(s, pb, key0, key0 + BN > nomask_end);
+            if (!late) wait_vmcnt<PER_TILE>();
+            __syncthreads();
+        }
+        if (!late) __syncthreads();
     }
+
+    // The DMA of tiles past the end writes zeros into LDS: let all of it land
+    // before this work-group can finish and its LDS be handed to another.
+    wait_vmcnt<0>();
 
     // epilogue: O = O^T / l written as bf16, LSE = ln2 * (m + log2 l)
     const float l_tot = half_sum(l);
@@ -459,19 +535,72 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void prefill_bf16_ker
     }
 }
 
-template <int D, int BN, int S, bool CZ>
-hipError_t launch_dz(const PrefillKArgs& a, int64_t n_wg, hipStream_t s) {
-    using C = PCfg<D, BN, S>;
+// Persistent grid: each work-group runs items until the queue is empty.  The
+// ticket of the next item is fetched (one atomic of wave 0) while the
+// current item runs and handed to the other waves through LDS.
+template <int D, int BN, int S, int NW, bool PP, bool CZ>
+__global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kernel(PrefillKArgs a) {
+    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    __shared__ int next_item;
+    char* const lds = reinterpret_cast<char*>(smem);
+    const uint32_t lds_base = lds_addr(smem);
+    uint32_t* const ctr = g_prefill_queue[a.slot];
+    const int grid = (int)gridDim.x;
+    int item = blockIdx.x;
+    for (;;) {
+        uint32_t ticket = 0;
+        if (threadIdx.x == 0) ticket = ticket_async(&ctr[0]);
+        prefill_item<D, BN, S, NW, PP, CZ>(a, item, lds, lds_base);
+        wait_vmcnt<0>();  // the ticket (and the last stores)
+        __syncthreads();  // every wave has read next_item of the last round
+        if (threadIdx.x == 0) next_item = grid + (int)ticket;
+        __syncthreads();
+        item = next_item;
+        if (item >= a.n_work) break;
+    }
+    if (threadIdx.x == 0 && atomicAdd(&ctr[1], 1u) == (uint32_t)grid - 1) {
+        // every work-group has taken its last ticket
+        atomicExch(&ctr[0], 0u);
+        atomicExch(&ctr[1], 0u);
+    }
+}
+
+// Resident work-groups per CU of a kernel (computed once) x CUs of the device.
+template <typename K>
+int resident_slots(K kernel, int threads, int lds_bytes) {
+    static std::atomic<int> per_cu{0};
+    int occ = per_cu.load(std::memory_order_relaxed);
+    if (occ == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void*)kernel, threads, lds_bytes) != hipSuccess ||
+            occ < 1)
+            occ = 1;
+        per_cu.store(occ, std::memory_order_relaxed);
+    }
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+        n_cu = 1;
+    return occ * n_cu;
+}
+
+std::atomic<uint32_t> g_slot_seq{0};
+
+template <int D, int BN, int S, int NW, bool PP, bool CZ>
+hipError_t launch_dz(PrefillKArgs a, int64_t n_wg, hipStream_t s) {
+    using C = PCfg<D, BN, S, NW>;
+    auto kernel = prefill_bf16_kernel<D, BN, S, NW, PP, CZ>;
     // more than 64 KiB of dynamic LDS must be requested per kernel
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, BN, S, CZ>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, BN, S, CZ>), dim3((unsigned)n_wg), dim3(kThreads),
+    const int64_t slots = resident_slots(kernel, C::THREADS, C::LDS_BYTES);
+    a.n_work = (int32_t)n_wg;
+    a.slot = (int32_t)(g_slot_seq.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(n_wg < slots ? n_wg : slots)), dim3(C::THREADS),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
-template <int D, int BN, int S>
+template <int D, int BN, int S, int NW, bool PP>
 hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     PrefillKArgs a;
     a.q = static_cast<const bf16_t*>(pa.q);
@@ -493,7 +622,7 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     a.group = pa.hq / pa.hkv;
     a.nh = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
     a.n_hg = pa.hq / a.nh;
-    const int tile_rows = 32 * (4 / a.nh);
+    const int tile_rows = 32 * (NW / a.nh);
     a.n_qtiles = (pa.max_q + tile_rows - 1) / tile_rows;
     a.c = (pa.scale < 0.f ? -pa.scale : pa.scale) * kLog2e;
     a.q_sign = pa.scale < 0.f ? 0x80008000u : 0u;
@@ -504,16 +633,17 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     const int64_t n_wg = (int64_t)a.n_qtiles * a.n_hg * a.batch;
     if (n_wg == 0) return hipSuccess;
     if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-    return a.c == 0.f ? launch_dz<D, BN, S, true>(a, n_wg, s) : launch_dz<D, BN, S, false>(a, n_wg, s);
+    return a.c == 0.f ? launch_dz<D, BN, S, NW, PP, true>(a, n_wg, s)
+                      : launch_dz<D, BN, S, NW, PP, false>(a, n_wg, s);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     switch (a.dqk) {
-        case 64: return launch_d<64, 128, 2>(a, s);
-        case 128: return launch_d<128, 64, 2>(a, s);
-        case 256: return launch_d<256, 32, 4>(a, s);
+        case 64: return launch_d<64, 128, 4, 8, true>(a, s);
+        case 128: return launch_d<128, 64, 4, 8, true>(a, s);
+        case 256: return launch_d<256, 32, 4, 4, false>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
