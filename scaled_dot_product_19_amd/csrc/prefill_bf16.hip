@@ -63,17 +63,21 @@ struct PrefillKArgs {
     int32_t causal;
     float* lse;
     int32_t lse_layout, lse_s_max;
-    int32_t n_work;  // work items (levels x batch x head groups)
-    int32_t slot;    // work-queue counter pair used by this launch
+    int32_t slot;    // work-queue counters used by this launch
 };
 
-// Work queue of the persistent prefill grid.  A launch with G work-groups
-// takes items 0..G-1 by work-group index and the rest by tickets from
-// counter [slot][0] (item = G + ticket); counter [slot][1] counts
-// work-groups that ran out of items, and the last one returns both counters
-// to 0 for the next launch that uses the slot.  Launches take slots round
-// robin, so up to kQueueSlots prefill calls may overlap on one device.
+// Work queues of the persistent prefill grid, one per XCD.  Pair p = (b, hg)
+// lives on XCD p % 8, so the K/V of a head group stays in one XCD's L2; the
+// queue of XCD x hands out its items level by level (longest causal row
+// blocks first): ticket t -> level t / m, pair x + 8 (t % m), with m the
+// number of pairs of XCD x.  A work-group takes tickets from the queue of
+// the XCD it runs on and, once that is empty, from the other seven in turn.
+// Counter [slot][8] counts work-groups that are done; the last one returns
+// all counters to 0 for the next launch that uses the slot.  Launches take
+// slots round robin, so up to kQueueSlots prefill calls may overlap on one
+// device.
 constexpr int kQueueSlots = 64;
+constexpr int kXcds = 8;
 __device__ __align__(256) uint32_t g_prefill_queue[kQueueSlots][32];
 
 constexpr float kLazyRescale = 8.f;  // log2 units the running max may lag behind
@@ -206,14 +210,13 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     using C = PCfg<D, BN, S, NW>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Items: levels of equal causal row block qt, longest first; inside a
-    // level the batch x head-group items are rotated by the level so that
-    // neighbouring items belong to different sequences.
-    const int n_items = a.batch * a.n_hg;
-    const int level = bid / n_items;
-    const int item = (bid % n_items + level) % n_items;
-    const int b = item / a.n_hg;
-    const int hg = item % a.n_hg;
+    // item = level * (batch * n_hg) + pair: level = causal row block counted
+    // from the last (longest first), pair = b * n_hg + hg
+    const int n_pairs = a.batch * a.n_hg;
+    const int level = bid / n_pairs;
+    const int pair = bid - level * n_pairs;
+    const int b = pair / a.n_hg;
+    const int hg = pair - b * a.n_hg;
     const int qt = a.n_qtiles - 1 - level;
 
     const int q_beg = a.cu_q[b], lq = a.cu_q[b + 1] - q_beg;
@@ -333,12 +336,22 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // K fragment kWin steps ahead.
     constexpr int NQK = C::NKB * C::KK;
     constexpr int NPV = C::NB * (BN / 16);
+    // K fragment of QK MFMA o (key block o % NKB, k-step o / NKB) in stage st
+    auto kfrag_at = [&](const char* st, int o) __attribute__((always_inline)) {
+        const int kb = o % C::NKB, kk = o / C::NKB;
+        return *reinterpret_cast<const bf16x8*>(st + k_rd[kk % KKW] + kb * 32 * C::ROW_B + (kk / KKW) * 256);
+    };
+    // V^T fragment of PV MFMA o (output block o % NB, 16-key step o / NB):
+    // two transpose reads
+    auto vfrag_at = [&](const char* st, int o) __attribute__((always_inline)) {
+        const int nb = o % C::NB, kst = o / C::NB;
+        const char* vp = st + v_rd[nb % NBW] + (nb / NBW) * 256 + kst * 16 * C::ROW_B;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::ROW_B));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     auto qk = [&](const char* st, f32x16(&s)[C::NKB]) __attribute__((always_inline)) {
-        auto kfrag = [&](int o) __attribute__((always_inline)) {
-            const int kb = o % C::NKB, kk = o / C::NKB;
-            return *reinterpret_cast<const bf16x8*>(st + k_rd[kk % KKW] + kb * 32 * C::ROW_B +
-                                                    (kk / KKW) * 256);
-        };
+        auto kfrag = [&](int o) __attribute__((always_inline)) { return kfrag_at(st, o); };
         const f32x16 zero = {};
         bf16x8 fk[kWin];
 #pragma unroll
@@ -416,13 +429,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // PV: O^T += V^T P^T for the tile in stage st.  MFMA o works on output
     // block o % NB, 16-key step o / NB; V^T fragments are two transpose reads.
     auto pv = [&](const char* st, const bf16x8(&pb)[BN / 16]) __attribute__((always_inline)) {
-        auto vfrag = [&](int o) __attribute__((always_inline)) {
-            const int nb = o % C::NB, kst = o / C::NB;
-            const char* vp = st + v_rd[nb % NBW] + (nb / NBW) * 256 + kst * 16 * C::ROW_B;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::ROW_B));
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
+        auto vfrag = [&](int o) __attribute__((always_inline)) { return vfrag_at(st, o); };
         bf16x8 fv[kWin];
 #pragma unroll
         for (int w = 0; w < kWin; ++w) fv[w] = vfrag(w);
@@ -436,6 +443,43 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         for (int o = 0; o < NPV; ++o) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
             if (o + kWin < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+    };
+    // PV of the tile in stage sv, then QK of the tile in stage sk, as one MFMA
+    // stream whose operand read-ahead window runs across the boundary; hook()
+    // (the DMA issue) comes after the first window of reads so that its
+    // scalar work overlaps their latency instead of delaying the first MFMA.
+    auto pv_qk = [&](const char* sv, const bf16x8(&pb)[BN / 16], const char* sk, f32x16(&s)[C::NKB],
+                     auto&& hook) __attribute__((always_inline)) {
+        constexpr int NM = NPV + NQK;
+        static_assert(NPV >= kWin, "read-ahead window within PV");
+        auto frag = [&](int o) __attribute__((always_inline)) {
+            return o < NPV ? vfrag_at(sv, o) : kfrag_at(sk, o - NPV);
+        };
+        const f32x16 zero = {};
+        bf16x8 fr[kWin];
+#pragma unroll
+        for (int w = 0; w < kWin; ++w) fr[w] = frag(w);
+        hook();
+#pragma unroll
+        for (int o = 0; o < NM; ++o) {
+            if (o < NPV) {
+                acc[o % C::NB] = mfma_32x32x16(fr[o % kWin], pb[o / C::NB], acc[o % C::NB]);
+            } else {
+                const int k = o - NPV;
+                s[k % C::NKB] = mfma_32x32x16(fr[o % kWin], qf[k / C::NKB], k < C::NKB ? zero : s[k % C::NKB]);
+            }
+            if (o + kWin < NM) fr[o % kWin] = frag(o + kWin);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kWin, 2);
+#pragma unroll
+        for (int o = 0; o < NM; ++o) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            if (o + kWin < NPV) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            } else if (o + kWin < NM) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+            }
         }
     };
     auto stage_ptr = [&](int t) __attribute__((always_inline)) {
@@ -488,19 +532,44 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         wait_vmcnt<PER_TILE * (S - 3)>();
         __syncthreads();
         if (late) __syncthreads();
-        for (int t = 0; t <= n_tiles; ++t) {
-            __builtin_amdgcn_s_setprio(1);
-            issue(t + S - 2);
-            if (t >= 1 && (t - 1) * BN < kv_end_w) pv(stage_ptr(t - 1), pb);
-            if (t < n_tiles && t * BN < kv_end_w) qk(stage_ptr(t), s);
+        // end of an MFMA phase / of a VALU phase
+        auto m_end = [&]() __attribute__((always_inline)) {
             __builtin_amdgcn_s_setprio(0);
             if (late) wait_vmcnt<PER_TILE>();
             __syncthreads();
-            if (t == n_tiles) break;
+        };
+        // V(t): softmax of tile t, or P = 0 for a wave that sees none of its keys
+        auto v_phase = [&](int t) __attribute__((always_inline)) {
             const int key0 = t * BN;
-            if (key0 < kv_end_w) softmax(s, pb, key0, key0 + BN > nomask_end);
+            if (key0 < kv_end_w) {
+                softmax(s, pb, key0, key0 + BN > nomask_end);
+            } else {
+#pragma unroll
+                for (int j = 0; j < BN / 16; ++j) pb[j] = bf16x8{};
+            }
             if (!late) wait_vmcnt<PER_TILE>();
             __syncthreads();
+        };
+        if (n_tiles > 0) {
+            // M(0): QK of tile 0
+            __builtin_amdgcn_s_setprio(1);
+            issue(S - 2);
+            qk(stage_ptr(0), s);
+            m_end();
+            v_phase(0);
+            // M(t) = PV(t - 1) and QK(t) as one MFMA stream (one code path:
+            // a wave whose keys end before tile t computes QK(t) and drops it)
+            for (int t = 1; t < n_tiles; ++t) {
+                __builtin_amdgcn_s_setprio(1);
+                pv_qk(stage_ptr(t - 1), pb, stage_ptr(t), s,
+                      [&]() __attribute__((always_inline)) { issue(t + S - 2); });
+                m_end();
+                v_phase(t);
+            }
+            // M(n_tiles): PV of the last tile
+            __builtin_amdgcn_s_setprio(1);
+            pv(stage_ptr(n_tiles - 1), pb);
+            m_end();
         }
         if (!late) __syncthreads();
     }
@@ -535,8 +604,8 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     }
 }
 
-// Persistent grid: each work-group runs items until the queue is empty.  The
-// ticket of the next item is fetched (one atomic of wave 0) while the
+// Persistent grid: each work-group runs items until every queue is empty.
+// The ticket of the next item is fetched (one atomic of wave 0) while the
 // current item runs and handed to the other waves through LDS.
 template <int D, int BN, int S, int NW, bool PP, bool CZ>
 __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kernel(PrefillKArgs a) {
@@ -545,23 +614,47 @@ __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kern
     char* const lds = reinterpret_cast<char*>(smem);
     const uint32_t lds_base = lds_addr(smem);
     uint32_t* const ctr = g_prefill_queue[a.slot];
-    const int grid = (int)gridDim.x;
-    int item = blockIdx.x;
-    for (;;) {
+    const int n_pairs = a.batch * a.n_hg;
+    // Only lane 0 of wave 0 talks to the queues: q is the queue it draws
+    // from, tries the number of queues it has found empty.
+    int q = 0, tries = 0;
+    // item of ticket t of queue x, or -1 when the queue is exhausted
+    auto item_of = [&](int x, uint32_t t) -> int {
+        const int m = n_pairs > x ? (n_pairs - x + kXcds - 1) / kXcds : 0;
+        if (m == 0 || t >= (uint32_t)(m * a.n_qtiles)) return -1;
+        const int level = (int)t / m;
+        return level * n_pairs + x + kXcds * ((int)t - level * m);
+    };
+    // next item after ticket t of queue q, moving on to the other queues
+    auto next_of = [&](uint32_t t) -> int {
+        int it = item_of(q, t);
+        while (it < 0 && ++tries < kXcds) {
+            q = (q + 1) % kXcds;
+            it = item_of(q, atomicAdd(&ctr[q], 1u));
+        }
+        return it;
+    };
+    if (threadIdx.x == 0) {
+        unsigned xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        q = (int)(xcc % kXcds);
+        next_item = next_of(atomicAdd(&ctr[q], 1u));
+    }
+    __syncthreads();
+    int item = next_item;
+    while (item >= 0) {
         uint32_t ticket = 0;
-        if (threadIdx.x == 0) ticket = ticket_async(&ctr[0]);
+        if (threadIdx.x == 0) ticket = ticket_async(&ctr[q]);
         prefill_item<D, BN, S, NW, PP, CZ>(a, item, lds, lds_base);
         wait_vmcnt<0>();  // the ticket (and the last stores)
         __syncthreads();  // every wave has read next_item of the last round
-        if (threadIdx.x == 0) next_item = grid + (int)ticket;
+        if (threadIdx.x == 0) next_item = next_of(ticket);
         __syncthreads();
         item = next_item;
-        if (item >= a.n_work) break;
     }
-    if (threadIdx.x == 0 && atomicAdd(&ctr[1], 1u) == (uint32_t)grid - 1) {
+    if (threadIdx.x == 0 && atomicAdd(&ctr[kXcds], 1u) == gridDim.x - 1) {
         // every work-group has taken its last ticket
-        atomicExch(&ctr[0], 0u);
-        atomicExch(&ctr[1], 0u);
+        for (int x = 0; x <= kXcds; ++x) atomicExch(&ctr[x], 0u);
     }
 }
 
@@ -593,7 +686,6 @@ hipError_t launch_dz(PrefillKArgs a, int64_t n_wg, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     const int64_t slots = resident_slots(kernel, C::THREADS, C::LDS_BYTES);
-    a.n_work = (int32_t)n_wg;
     a.slot = (int32_t)(g_slot_seq.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
     hipLaunchKernelGGL(kernel, dim3((unsigned)(n_wg < slots ? n_wg : slots)), dim3(C::THREADS),
                        (size_t)C::LDS_BYTES, s, a);
