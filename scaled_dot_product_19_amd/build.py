@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libsdpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["sdpa_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip",
-           "decode_small.hip", "combine.hip"]
+           "decode_small.hip", "decode_wide.hip", "combine.hip"]
 
 
 def hipcc() -> str:
@@ -36,8 +36,15 @@ def common_flags():
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source extra flags.  decode_wide.hip keeps 256 fp32 O^T accumulators
+# plus its Q^T operands live: MFMA destinations selected as VGPR-form (the
+# register allocator may still place them in AGPRs) let the score
+# accumulators sit in VGPRs instead of pushing O^T into scratch.
+EXTRA_FLAGS = {"decode_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(cc, src, obj):
-    cmd = [cc] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [cc] + common_flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature; that warning is harmless
     noise = [l for l in r.stderr.splitlines() if "is not a recognized feature" not in l]

@@ -1,0 +1,429 @@
+// decode_wide.hip -- paged-KV decode with many query rows per KV head, bf16.
+//
+// Serves s_q * G > 16 query rows per KV head with d_qk = 576, d_v = 512: the
+// absorbed-MLA decode shape with independent K/V page tables (cuDNN Frontend
+// v1.32.0 Release Notes, "SDPA: wider native forward support"; paged K/V and
+// split-KV: v1.31.0 "SDPA: paged KV, split-KV, and engine selection").  With
+// hundreds of rows sharing one KV head every key costs rows x 1088 MACs, so
+// the work is a dense contraction per K/V tile and runs on MFMA:
+//
+// Work-group = 4 waves = 128 query rows (row r of a KV head is query token
+// r / G, head kvh G + r % G) x one split-KV chunk of one sequence.  Per tile
+// of 32 keys (a tile never straddles a page: page_size % 32 == 0):
+//   K tile (32 x 576) and V tile (32 x 512) gathered from their pages into
+//   LDS by buffer_load_dwordx4 ... lds (lane L's 16 bytes land at M0 + 16 L),
+//   one 1 KB row per instruction, in a 2-stage ring.  Bank conflicts are
+//   avoided by a 16-byte pad after dims 0..511 of each K row, an XOR swizzle
+//   of the 8 chunks of dims 512..575 (kept in a region of their own) and an
+//   XOR swizzle of the V chunks;
+//   S^T = K Q^T: 36 v_mfma_f32_32x32x16_bf16 per wave, A = K rows
+//   (ds_read_b128), B = the wave's Q^T held in registers, so each lane holds
+//   the scores of one query;
+//   online softmax in registers (row max: 3-input max + one lane-half
+//   exchange), running max moved lazily (only when a tile's max exceeds it
+//   by more than 8 in log2 units);
+//   O^T += V^T P^T: 32 MFMAs, B = P^T straight from the score accumulators,
+//   A = V^T via ds_read_b64_tr_b16 from the row-major V tile.
+// The chunk's normalized partial (O_c, LSE_c) goes to the split workspace,
+// or O / LSE directly when num_splits == 1.
+#include "sdpa_device.h"
+#include "sdpa_launch.h"
+#include "tile_ops.h"
+
+namespace sdpa {
+namespace {
+
+struct WideArgs {
+    const bf16_t* q;
+    const bf16_t* k_pool;
+    int64_t k_sp, k_st, k_sh;
+    const bf16_t* v_pool;
+    int64_t v_sp, v_st, v_sh;
+    const int32_t* pt_k;
+    const int32_t* pt_v;
+    int32_t table_stride;
+    const int32_t* seq_lens;
+    int32_t batch, sq, hq, hkv, group, page, splits;
+    int32_t rows;     // s_q * group query rows per KV head
+    int32_t n_rb;     // 128-row blocks per KV head
+    int32_t n_g;      // batch * hkv * splits chunks
+    float c;          // |scale| * log2(e)
+    uint32_t q_sign;  // 0x80008000 when scale < 0 (Q negated on load), else 0
+    int32_t causal;
+    float* o_part;    // [splits, batch*sq*hq, 512] when splits > 1
+    float* lse_part;  // [splits, batch*sq*hq]
+    bf16_t* o;        // [batch, sq, hq, 512] when splits == 1
+    float* lse;       // [batch, sq, hq] or null
+};
+
+// LDS stage: K region A (dims 0..511 of 32 rows, pitch 1040 B: 1 KB + a
+// 16-byte pad), K region B (dims 512..575, 32 rows x 128 B, chunk XOR row
+// mod 8), V (32 rows x 1 KB, chunk XOR 4 (row mod 4)).
+template <int DQK, int DV>
+struct WCfg {
+    static constexpr int NW = 4;                    // waves, 32 query rows each
+    static constexpr int BN = 32;                   // keys per tile
+    static constexpr int KA_PITCH = 1040;
+    static constexpr int KA_B = BN * KA_PITCH;      // region A bytes
+    static constexpr int KB_OFF = KA_B;             // region B
+    static constexpr int KB_B = BN * 128;
+    static constexpr int V_OFF = KB_OFF + KB_B;     // V tile
+    static constexpr int VROW_B = 2 * DV;
+    static constexpr int STAGE_B = V_OFF + BN * VROW_B;
+    static constexpr int LDS_BYTES = 2 * STAGE_B;   // 2-stage ring
+    static constexpr int RPW = BN / NW;             // tile rows per wave (one DMA each)
+    static constexpr int KK = DQK / 16;             // k-steps of S^T = K Q^T
+    static constexpr int KKA = 32;                  // k-steps in region A
+    static constexpr int NB = DV / 32;              // 32-row blocks of O^T
+    static constexpr int NQK = KK;                  // QK MFMAs per tile
+    static constexpr int NPV = NB * (BN / 16);      // PV MFMAs per tile
+    static_assert(DQK == 576 && DV == 512, "geometry below is written for the 576/512 shape");
+    static_assert(BN * 8 == 64 * NW, "region B: one DMA instruction per wave");
+};
+
+constexpr int kWinW = 2;  // LDS operand fragments read ahead of the MFMAs
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
+    using C = WCfg<DQK, DV>;
+    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    char* const lds = reinterpret_cast<char*>(smem);
+    const uint32_t lds_base = lds_addr(smem);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // chunk g = (b, kvh, split); the n_rb row blocks of a chunk are 8 work-
+    // groups apart, i.e. on the same XCD (work-group i runs on XCD i % 8)
+    const int bid = blockIdx.x;
+    const int g = (bid / (8 * a.n_rb)) * 8 + bid % 8;
+    const int rb = (bid / 8) % a.n_rb;
+    if (g >= a.n_g) return;
+    const int split = g % a.splits;
+    const int bk = g / a.splits;
+    const int kvh = bk % a.hkv;
+    const int b = bk / a.hkv;
+
+    // keys of this chunk: [lo, hi)
+    const int L = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
+    int lo = 0, hi = L;
+    if (a.splits > 1) {
+        const int per = (L + a.splits - 1) / a.splits;
+        const int chunk = ((per + a.page - 1) / a.page) * a.page;
+        lo = min(L, split * chunk);
+        hi = min(L, lo + chunk);
+    }
+
+    // rows of this lane / wave / work-group
+    const int col = lane & 31, half = lane >> 5;
+    const int r = rb * 128 + wave * 32 + col;
+    const bool row_ok = r < a.rows;
+    const int tq = (row_ok ? r : a.rows - 1) / a.group;  // query token
+    const int h = kvh * a.group + (row_ok ? r : a.rows - 1) % a.group;
+    const int r_w0 = min(rb * 128 + wave * 32, a.rows - 1);        // first row of the wave
+    const int r_w1 = min(rb * 128 + wave * 32 + 31, a.rows - 1);   // last
+    const int r_g1 = min(rb * 128 + 127, a.rows - 1);
+    // key j is visible to token t iff j <= L - sq + t (causal) / j < L
+    auto end_of = [&](int row) { return a.causal ? min(hi, L - a.sq + row / a.group + 1) : hi; };
+    const int kv_end = max(lo, end_of(r_g1));
+    const bool wave_rows = rb * 128 + wave * 32 < a.rows;
+    const int kv_end_w = wave_rows ? max(lo, end_of(r_w1)) : lo;
+    const int nomask_end = wave_rows ? max(lo, end_of(r_w0)) : lo;
+    const int lim = a.causal ? L - a.sq + tq : L - 1;  // last visible key of this lane
+    const int n_tiles = (kv_end - lo + C::BN - 1) / C::BN;
+
+    // ---- LDS DMA of the K/V tiles -------------------------------------------
+    // Wave w moves rows 8 w .. 8 w + 7 of each tile: per row one instruction
+    // for K dims 0..511 (lane L: chunk L) and one for V (lane L: chunk
+    // L ^ 4 (row mod 4)); one more instruction covers its 8 rows of K dims
+    // 512..575 (lane L: row 8 w + L / 8, chunk (L mod 8) ^ (row mod 8)).
+    const uint32_t k_st2 = 2u * (uint32_t)a.k_st, v_st2 = 2u * (uint32_t)a.v_st;
+    const uint32_t l16 = 16u * (uint32_t)lane;
+    const int rb_row = wave * C::RPW + lane / 8;
+    const uint32_t kb_src = (uint32_t)rb_row * k_st2 + 1024u + 16u * (uint32_t)((lane & 7) ^ (rb_row & 7));
+    // Physical pages of the chunk's first 64 pages (lane i: page lo/page + i);
+    // a chunk of more pages reloads the window when it gets there.
+    const int pg0 = lo / a.page;
+    const int64_t pt_row = (int64_t)b * a.table_stride;
+    const int n_pages = (kv_end - lo + a.page - 1) / a.page;
+    int pwin = 0;  // first page (relative to pg0) of the loaded window
+    int pk = 0, pv = 0;
+    auto load_window = [&](int first) __attribute__((always_inline)) {
+        const int i = min(first + lane, max(n_pages - 1, 0));
+        pk = a.pt_k[pt_row + pg0 + i];
+        pv = a.pt_v[pt_row + pg0 + i];
+        pwin = first;
+    };
+    if (n_pages > 0) load_window(0);
+    const bf16_t* const kbase = a.k_pool + (int64_t)kvh * a.k_sh;
+    const bf16_t* const vbase = a.v_pool + (int64_t)kvh * a.v_sh;
+    auto issue = [&](int t, int stage) __attribute__((always_inline)) {
+        const int key0 = lo + t * C::BN;
+        const int nvalid = min(C::BN, kv_end - key0);
+        const int rel = key0 / a.page - pg0;
+        if (rel - pwin >= 64) {  // uniform; no DMA of this wave is pending here
+            load_window(rel);
+            wait_vmcnt<0>();
+        }
+        const int pkp = __builtin_amdgcn_readlane(pk, rel - pwin);
+        const int pvp = __builtin_amdgcn_readlane(pv, rel - pwin);
+        const int slot = key0 % a.page;
+        // rows at or past nvalid fall outside the buffer range and arrive as zeros
+        const uint32_t kn = nvalid > 0 ? (uint32_t)(nvalid - 1) * k_st2 + 2u * DQK : 0u;
+        const uint32_t vn = nvalid > 0 ? (uint32_t)(nvalid - 1) * v_st2 + 2u * DV : 0u;
+        const u32x4 kr = make_rsrc(kbase + (int64_t)pkp * a.k_sp + (int64_t)slot * a.k_st, kn);
+        const u32x4 vr = make_rsrc(vbase + (int64_t)pvp * a.v_sp + (int64_t)slot * a.v_st, vn);
+        const uint32_t st = lds_base + stage * C::STAGE_B;
+#pragma unroll
+        for (int j = 0; j < C::RPW; ++j) {
+            const int row = wave * C::RPW + j;
+            dma16(kr, st + row * C::KA_PITCH, l16 + (uint32_t)row * k_st2);
+        }
+        dma16(kr, st + C::KB_OFF + wave * 1024, kb_src);
+#pragma unroll
+        for (int j = 0; j < C::RPW; ++j) {
+            const int row = wave * C::RPW + j;
+            dma16(vr, st + C::V_OFF + row * C::VROW_B, (l16 ^ (64u * (uint32_t)(row & 3))) + (uint32_t)row * v_st2);
+        }
+    };
+    if (n_tiles > 0) issue(0, 0);
+
+    // Q^T operand: lane (col, half) holds d = 16 kk + 8 half .. +8 of row r
+    // (rows past the end read the last row and are zeroed)
+    bf16x8 qf[C::KK];
+    {
+        const bf16_t* qrow = a.q + ((int64_t)(b * a.sq + tq) * a.hq + h) * DQK + 8 * half;
+        const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) {
+            uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
+            w.x = (w.x & keep) ^ a.q_sign;
+            w.y = (w.y & keep) ^ a.q_sign;
+            w.z = (w.z & keep) ^ a.q_sign;
+            w.w = (w.w & keep) ^ a.q_sign;
+            qf[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    // ---- per-lane LDS read offsets (bytes within a stage) -------------------
+    // K fragment of k-step kk: lane (key = col, half) reads chunk 2 kk + half
+    // of row col: in region A at col * pitch + 32 kk + 16 half, in region B
+    // at chunk (2 (kk - 32) + half) ^ (col mod 8).
+    const int k_ra = col * C::KA_PITCH + 16 * half;
+    int k_rb[C::KK - C::KKA];
+#pragma unroll
+    for (int kk = C::KKA; kk < C::KK; ++kk)
+        k_rb[kk - C::KKA] = C::KB_OFF + col * 128 + 16 * ((2 * (kk - C::KKA) + half) ^ (col & 7));
+    // V^T fragment (A of O^T), two transpose reads per 16-key step: lane l of
+    // 16-lane group G = l / 16 supplies row 16 kst + 4 half + (l % 16) / 4
+    // (+8 for the second read) and 4 columns starting at 32 nb + 16 (G % 2) +
+    // 4 (l % 4); it receives 4 consecutive keys of column 32 nb + l % 32.
+    int v_rd[4];
+    {
+        const int r0 = 4 * half + (lane & 15) / 4;
+        const int cg = 2 * ((lane >> 4) & 1) + (lane & 3) / 2;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            v_rd[nb] = C::V_OFF + r0 * C::VROW_B + 16 * swz_v<64>(r0, 4 * nb + cg) + 8 * (lane & 1);
+    }
+    auto kfrag = [&](const char* st, int kk) __attribute__((always_inline)) {
+        const int off = kk < C::KKA ? k_ra + 32 * kk : k_rb[kk - C::KKA];
+        return *reinterpret_cast<const bf16x8*>(st + off);
+    };
+    auto vfrag = [&](const char* st, int o) __attribute__((always_inline)) {
+        const int nb = o % C::NB, kst = o / C::NB;
+        const char* vp = st + v_rd[nb % 4] + (nb / 4) * 256 + kst * 16 * C::VROW_B;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VROW_B));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    f32x16 acc[C::NB];
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
+    float m = neg_inf();  // running max (log2 units) of this lane's query
+    float l = 0.f;        // this lane half's running sum
+
+    auto tile = [&](const char* st, int key0, bool need_mask) __attribute__((always_inline)) {
+        // S^T = K Q^T
+        f32x16 s;
+        {
+            const f32x16 zero = {};
+            bf16x8 fk[kWinW];
+#pragma unroll
+            for (int w = 0; w < kWinW; ++w) fk[w] = kfrag(st, w);
+#pragma unroll
+            for (int o = 0; o < C::NQK; ++o) {
+                s = mfma_32x32x16(fk[o % kWinW], qf[o], o == 0 ? zero : s);
+                if (o + kWinW < C::NQK) fk[o % kWinW] = kfrag(st, o + kWinW);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, kWinW, 0);
+#pragma unroll
+            for (int o = 0; o < C::NQK; ++o) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (o + kWinW < C::NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
+        // online softmax; lane (col, half) holds keys key0 + 8 (i / 4) + 4 half + i % 4
+        float mx = neg_inf();
+        if (need_mask) {
+            const int dl = lim - key0 - 4 * half;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = (8 * (i >> 2) + (i & 3)) > dl ? neg_inf() : s[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = max3(mx, s[i], s[i + 1]);
+        mx = half_max(mx);
+        const float mt = mx == neg_inf() ? neg_inf() : mx * a.c;
+        const bool grow = mt > m + 8.f;
+        // a lane whose max is still -inf has nothing accumulated: no rescale
+        if (__builtin_amdgcn_ballot_w64(grow && m != neg_inf()) != 0) {
+            const float alpha = grow ? fast_exp2(m - mt) : 1.f;
+            l *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
+        }
+        m = grow ? mt : m;
+        const float nm = m == neg_inf() ? 0.f : -m;
+        bf16x8 pb[2];
+        float lsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            float p0 = fast_exp2(__builtin_fmaf(s[i], a.c, nm));
+            float p1 = fast_exp2(__builtin_fmaf(s[i + 1], a.c, nm));
+            if (need_mask) {  // exact zeros also when c = 0 (-inf * 0 = NaN)
+                p0 = s[i] == neg_inf() ? 0.f : p0;
+                p1 = s[i + 1] == neg_inf() ? 0.f : p1;
+            }
+            lsum += p0 + p1;
+            const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+            pb[i >> 3][i & 7] = pp[0];
+            pb[i >> 3][(i & 7) + 1] = pp[1];
+        }
+        l += lsum;
+        // O^T += V^T P^T
+        {
+            bf16x8 fv[kWinW];
+#pragma unroll
+            for (int w = 0; w < kWinW; ++w) fv[w] = vfrag(st, w);
+#pragma unroll
+            for (int o = 0; o < C::NPV; ++o) {
+                acc[o % C::NB] = mfma_32x32x16(fv[o % kWinW], pb[o / C::NB], acc[o % C::NB]);
+                if (o + kWinW < C::NPV) fv[o % kWinW] = vfrag(st, o + kWinW);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kWinW, 1);
+#pragma unroll
+            for (int o = 0; o < C::NPV; ++o) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                if (o + kWinW < C::NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            }
+        }
+    };
+
+    // 2-stage ring: tile t + 1 streams in while tile t is computed
+    wait_vmcnt<0>();
+    __syncthreads();
+    auto step = [&](int t, auto stage) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        if (t + 1 < n_tiles) issue(t + 1, ST ^ 1);
+        const int key0 = lo + t * C::BN;
+        if (key0 < kv_end_w) tile(lds + ST * C::STAGE_B, key0, key0 + C::BN > nomask_end);
+        wait_vmcnt<0>();
+        __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+    }
+
+    // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
+    const float l_tot = half_sum(l);
+    if (!row_ok) return;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? kLn2 * (m + fast_log2(l_tot)) : neg_inf();
+    const int64_t row_g = (int64_t)(b * a.sq + tq) * a.hq + h;
+    if (a.splits > 1) {
+        const int64_t rows_all = (int64_t)a.batch * a.sq * a.hq;
+        float* orow = a.o_part + ((int64_t)split * rows_all + row_g) * DV;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int n = nb * 32 + 8 * gq + 4 * half;
+                f32x4 w = {acc[nb][4 * gq] * inv, acc[nb][4 * gq + 1] * inv, acc[nb][4 * gq + 2] * inv,
+                           acc[nb][4 * gq + 3] * inv};
+                *reinterpret_cast<f32x4*>(orow + n) = w;
+            }
+        if (half == 0) a.lse_part[(int64_t)split * rows_all + row_g] = lse;
+    } else {
+        bf16_t* orow = a.o + row_g * DV;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int n = nb * 32 + 8 * gq + 4 * half;
+                uint2 w;
+                w.x = pack_bf16x2(acc[nb][4 * gq] * inv, acc[nb][4 * gq + 1] * inv);
+                w.y = pack_bf16x2(acc[nb][4 * gq + 2] * inv, acc[nb][4 * gq + 3] * inv);
+                *reinterpret_cast<uint2*>(orow + n) = w;
+            }
+        if (a.lse != nullptr && half == 0) a.lse[row_g] = lse;
+    }
+}
+
+}  // namespace
+
+bool decode_wide_supported(const DecodeArgs& a) {
+    const int rows = a.sq * (a.hq / a.hkv);
+    return a.dqk == 576 && a.dv == 512 && rows > 16 && a.page % 32 == 0;
+}
+
+hipError_t launch_decode_wide(const DecodeArgs& d, hipStream_t s) {
+    using C = WCfg<576, 512>;
+    WideArgs a;
+    a.q = static_cast<const bf16_t*>(d.q);
+    a.k_pool = static_cast<const bf16_t*>(d.k_pool);
+    a.k_sp = d.k_sp;
+    a.k_st = d.k_st;
+    a.k_sh = d.k_sh;
+    a.v_pool = static_cast<const bf16_t*>(d.v_pool);
+    a.v_sp = d.v_sp;
+    a.v_st = d.v_st;
+    a.v_sh = d.v_sh;
+    a.pt_k = d.pt_k;
+    a.pt_v = d.pt_v;
+    a.table_stride = d.table_stride;
+    a.seq_lens = d.seq_lens;
+    a.batch = d.batch;
+    a.sq = d.sq;
+    a.hq = d.hq;
+    a.hkv = d.hkv;
+    a.group = d.hq / d.hkv;
+    a.page = d.page;
+    a.splits = d.splits;
+    a.rows = d.sq * a.group;
+    a.n_rb = (a.rows + 127) / 128;
+    const int64_t n_g = (int64_t)d.batch * d.hkv * d.splits;
+    a.n_g = (int32_t)n_g;
+    a.c = (d.scale < 0.f ? -d.scale : d.scale) * kLog2e;
+    a.q_sign = d.scale < 0.f ? 0x80008000u : 0u;
+    a.causal = d.causal;
+    a.o_part = d.o_part;
+    a.lse_part = d.lse_part;
+    a.o = static_cast<bf16_t*>(d.o);
+    a.lse = d.lse;
+    const int64_t n_wg = (n_g + 7) / 8 * 8 * a.n_rb;
+    if (n_g == 0) return hipSuccess;
+    if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute((const void*)decode_wide_kernel<576, 512>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_wide_kernel<576, 512>), dim3((unsigned)n_wg), dim3(256), (size_t)C::LDS_BYTES, s,
+                       a);
+    return hipGetLastError();
+}
+
+}  // namespace sdpa

@@ -39,6 +39,7 @@
 //                           four consecutive keys of one column.
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
+#include "tile_ops.h"
 
 #include <atomic>
 #include <type_traits>
@@ -82,16 +83,6 @@ __device__ __align__(256) uint32_t g_prefill_queue[kQueueSlots][32];
 
 constexpr float kLazyRescale = 8.f;  // log2 units the running max may lag behind
 constexpr int kWin = 4;              // LDS operand fragments read ahead of the MFMAs
-// Fourth word of a raw buffer resource on gfx9-family parts (CDNA): the
-// range check returns zeros past num_records (also for loads into LDS).
-constexpr int kRsrcWord3 = 0x00020000;
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 template <int D, int BN, int S, int NW>
 struct PCfg {
     static constexpr int THREADS = 64 * NW;
@@ -108,75 +99,6 @@ struct PCfg {
     static_assert(BN % 32 == 0 && D % 32 == 0 && CPR >= 8, "tile shape");
 };
 
-// Swizzled position of 16-byte chunk lc of a K row: 16 lanes reading the
-// same chunk of 16 consecutive rows hit 16 different 16-byte bank groups.
-template <int CPR>
-__device__ __forceinline__ int swz_k(int row, int lc) {
-    return CPR >= 16 ? (lc ^ (row & 15)) : (lc ^ ((row >> 1) & 7));
-}
-// Swizzled chunk of a V row: the transpose reads of 32 lanes touch 4
-// consecutive rows x 4 consecutive chunks, which then cover all banks.
-template <int CPR>
-__device__ __forceinline__ int swz_v(int row, int lc) {
-    return CPR >= 16 ? (lc ^ (4 * (row & 3))) : (lc ^ (4 * ((row >> 1) & 1)));
-}
-
-// Lane-half exchange with v_permlane32_swap: on two copies a = b = v the
-// swap leaves a = v of lanes 0..31 and b = v of lanes 32..63 in every lane,
-// so a reduction of a and b is the reduction over the lane pair (l, l ^ 32).
-// Written as inline asm because the compiler folds the two results of the
-// builtin into one when both of its inputs are the same value.  The s_nop
-// covers the VALU-write -> permlane-read hazard on the copies.
-__device__ __forceinline__ void half_swap(float& a, float& b) {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-// 3-input max without the NaN-quieting copies the compiler adds around fmaxf
-__device__ __forceinline__ float max3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-__device__ __forceinline__ float half_max(float v) {
-    float a = v, b = v;
-    half_swap(a, b);
-    return fmaxf(a, b);
-}
-__device__ __forceinline__ float half_sum(float v) {
-    float a = v, b = v;
-    half_swap(a, b);
-    return a + b;
-}
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource (no stride) over [base, base + nbytes).
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, int nbytes) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, (uint32_t)nbytes, (uint32_t)kRsrcWord3};
-}
-
-// LDS byte address of a pointer into this work-group's LDS.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p);
-}
-
-// 16-byte LDS DMA: lane L's 16 bytes at rsrc + voff land at LDS address
-// lds + 16 L.  Issued as inline asm so the compiler does not hold LDS reads
-// back behind every pending DMA (its alias model cannot tell the ring stages
-// apart); completion is awaited explicitly with wait_vmcnt + a barrier.  The
-// s_nop covers the M0-write -> LDS-DMA hazard.  M0 is declared clobbered;
-// nothing else in these kernels keeps a value in M0 (the compiler only uses
-// it for LDS DMA, interpolation and indexed moves, none of which occur).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 // Ticket from a work-queue counter: returns the value before adding 1.  The
 // result is NOT waited for: read it only after wait_vmcnt<0>.  (Written as
 // inline asm so that the compiler does not wait for the return right away,
@@ -188,13 +110,6 @@ __device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) {
     return old;
 }
 
-// Wait until at most N vector-memory operations of this wave are pending.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // D <= 128: two work-groups per CU (<= 256 registers per lane, 2-stage ring).
 // D = 256: one, with a 4-stage ring and the O^T accumulators in AGPRs.
 // NW waves = 32 NW query rows per work-group, each wave 32 rows.
@@ -204,14 +119,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // all keys it sees.  Uniform across the work-group (every exit is taken by
 // all waves).  On return every LDS DMA of the item has landed.
 template <int D, int BN, int S, int NW, bool PP, bool CZ>
-__device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& a, const int bid,
-                                                            char* const lds, const uint32_t lds_base) {
+__device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& a, const int item,
+                                                            char* const lds, const uint32_t lds_base,
+                                                            uint32_t* const tctr, uint32_t& ticket) {
     static_assert(!PP || (NW == 8 && S >= 4), "ping-pong needs two wave groups and S >= 4");
     using C = PCfg<D, BN, S, NW>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // item = level * (batch * n_hg) + pair: level = causal row block counted
     // from the last (longest first), pair = b * n_hg + hg
+    const int bid = __builtin_amdgcn_readfirstlane(item);
     const int n_pairs = a.batch * a.n_hg;
     const int level = bid / n_pairs;
     const int pair = bid - level * n_pairs;
@@ -219,11 +136,15 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     const int hg = pair - b * a.n_hg;
     const int qt = a.n_qtiles - 1 - level;
 
-    const int q_beg = a.cu_q[b], lq = a.cu_q[b + 1] - q_beg;
-    const int kv_beg = a.cu_kv[b], lk = a.cu_kv[b + 1] - kv_beg;
+    const int q_beg = load_uniform(a.cu_q, b), lq = load_uniform(a.cu_q, b + 1) - q_beg;
+    const int kv_beg = load_uniform(a.cu_kv, b), lk = load_uniform(a.cu_kv, b + 1) - kv_beg;
     const int nt = NW / a.nh;
     const int q0 = qt * 32 * nt;
-    if (q0 >= lq) return;  // uniform across the work-group
+    if (q0 >= lq) {  // uniform across the work-group
+        if (tid == 0) ticket = ticket_async(tctr);
+        wait_vmcnt<0>();
+        return;
+    }
 
     const int hw = wave % a.nh, tb = wave / a.nh;
     const int h = hg * a.nh + hw;
@@ -489,6 +410,13 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     f32x16 s[C::NKB];
     bf16x8 pb[BN / 16];
 
+    // The next item's ticket: it returns while this item runs (the wait
+    // before the epilogue covers it).  Q is needed first, so that the wait
+    // for it does not include the atomic's round trip.
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) asm volatile("" ::"v"(qf[kk]));
+    if (tid == 0) ticket = ticket_async(tctr);
+
     if constexpr (!PP) {
         // Sequential ring: at iteration t tile t is complete in stage t % S,
         // tiles up to t + S - 2 are in flight; the DMA of tile t + S - 1
@@ -644,9 +572,7 @@ __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kern
     int item = next_item;
     while (item >= 0) {
         uint32_t ticket = 0;
-        if (threadIdx.x == 0) ticket = ticket_async(&ctr[q]);
-        prefill_item<D, BN, S, NW, PP, CZ>(a, item, lds, lds_base);
-        wait_vmcnt<0>();  // the ticket (and the last stores)
+        prefill_item<D, BN, S, NW, PP, CZ>(a, item, lds, lds_base, &ctr[q], ticket);
         __syncthreads();  // every wave has read next_item of the last round
         if (threadIdx.x == 0) next_item = next_of(ticket);
         __syncthreads();

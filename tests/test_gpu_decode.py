@@ -136,3 +136,26 @@ def test_full_size_mla_decode_sampled():
     check_o(o.reshape(rows, -1)[torch.from_numpy(sel).cuda()], o_ref)
     check_lse(l.reshape(rows)[torch.from_numpy(sel).cuda()], l_ref)
     assert torch.isfinite(o).all() and torch.isfinite(l).all()
+
+
+@pytest.mark.parametrize("case", [
+    # page 32, 3 tokens x 16 heads = 48 rows per KV head (two waves without rows)
+    dict(seed=2008, sq=3, hq=16, hkv=1, page=32, lengths=[33, 2100], splits=2, causal=True),
+    # page 128, 64 rows per KV head, 2 KV heads, one chunk of 71 pages (page-window reload)
+    dict(seed=2009, sq=1, hq=128, hkv=2, page=128, lengths=[9000, 40], splits=1, causal=False),
+    # 3 row blocks (2 x 160 = 320 rows), lengths not multiples of a tile
+    dict(seed=2010, sq=2, hq=160, hkv=1, page=64, lengths=[97, 1301], splits=3, causal=True),
+])
+def test_mla_wide_row_edges(case):
+    pc = inputs.paged_case(case["seed"], len(case["lengths"]), case["sq"], case["hq"], case["hkv"],
+                           576, 512, case["page"], lengths=case["lengths"],
+                           num_splits=case["splits"], causal=case["causal"], poison=True,
+                           name="mla_edges")
+    parity(pc)
+
+
+@pytest.mark.parametrize("scale", [-0.05, 0.0])
+def test_mla_negative_and_zero_scale(scale):
+    pc = inputs.paged_case(2011, 2, 2, 128, 1, 576, 512, 64, lengths=[70, 500], num_splits=2,
+                           causal=True, poison=True, scale=scale, name="mla_scale")
+    parity(pc)
