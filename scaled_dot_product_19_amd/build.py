@@ -36,11 +36,8 @@ def common_flags():
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-# Per-source extra flags.  decode_wide.hip keeps 256 fp32 O^T accumulators
-# plus its Q^T operands live: MFMA destinations selected as VGPR-form (the
-# register allocator may still place them in AGPRs) let the score
-# accumulators sit in VGPRs instead of pushing O^T into scratch.
-EXTRA_FLAGS = {"decode_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.
+EXTRA_FLAGS = {}
 
 
 def _compile(cc, src, obj):

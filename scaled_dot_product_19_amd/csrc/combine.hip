@@ -25,7 +25,7 @@ template <bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       int splits, int64_t rows, int dv, void* o,
-                                                      float* lse) {
+                                                      float* lse, int vec) {
     __shared__ float w_s[4][kMaxSplits];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -52,16 +52,53 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     __syncthreads();
     if (!valid) return;
-    for (int n = lane; n < dv; n += 64) {
-        float acc = 0.f;
-        for (int c = 0; c < splits; ++c) {
-            const float wc = w[c];
-            if (wc != 0.f) acc = fmaf(wc, o_part[((int64_t)c * rows + row) * dv + n], acc);
+    if (vec) {  // d_v % 4 == 0, o_part 16-byte and o 8/16-byte aligned
+        // 4 columns per lane and step; the loads of 8 splits are issued
+        // together (unconditionally: a split of weight 0 is dropped by a
+        // select, so its partial -- possibly never written -- cannot leak in)
+        const f32x4* src = reinterpret_cast<const f32x4*>(o_part) + row * (dv / 4);
+        const int64_t cstride = rows * (dv / 4);
+        for (int n4 = lane; n4 < dv / 4; n4 += 64) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            int c = 0;
+            for (; c + 8 <= splits; c += 8) {
+                f32x4 x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(c + j) * cstride + n4];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float wc = w[c + j];
+                    const f32x4 t = acc + wc * x[j];
+                    acc = wc != 0.f ? t : acc;
+                }
+            }
+            for (; c < splits; ++c) {
+                const float wc = w[c];
+                const f32x4 x = src[(int64_t)c * cstride + n4];
+                const f32x4 t = acc + wc * x;
+                acc = wc != 0.f ? t : acc;
+            }
+            if (OUT_F32) {
+                reinterpret_cast<f32x4*>(o)[row * (dv / 4) + n4] = acc;
+            } else {
+                uint2 u;
+                u.x = pack_bf16x2(acc[0], acc[1]);
+                u.y = pack_bf16x2(acc[2], acc[3]);
+                reinterpret_cast<uint2*>(o)[row * (dv / 4) + n4] = u;
+            }
         }
-        if (OUT_F32)
-            static_cast<float*>(o)[row * dv + n] = acc;
-        else
-            static_cast<bf16_t*>(o)[row * dv + n] = (bf16_t)f32_to_bf16_bits(acc);
+    } else {
+        for (int n = lane; n < dv; n += 64) {
+            float acc = 0.f;
+            for (int c = 0; c < splits; ++c) {
+                const float wc = w[c];
+                if (wc != 0.f) acc = fmaf(wc, o_part[((int64_t)c * rows + row) * dv + n], acc);
+            }
+            if (OUT_F32)
+                static_cast<float*>(o)[row * dv + n] = acc;
+            else
+                static_cast<bf16_t*>(o)[row * dv + n] = (bf16_t)f32_to_bf16_bits(acc);
+        }
     }
     if (lse != nullptr && lane == 0) lse[row] = lse_row;
 }
@@ -79,12 +116,14 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t sp
                           hipStream_t s) {
     if (rows == 0) return hipSuccess;
     const int64_t blocks = (rows + 3) / 4;
+    const int vec = (dv % 4 == 0) && reinterpret_cast<uintptr_t>(o_part) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(o) % (out_f32 ? 16 : 8) == 0;
     if (out_f32)
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, o_part,
-                           lse_part, (int)splits, rows, (int)dv, o, lse);
+                           lse_part, (int)splits, rows, (int)dv, o, lse, vec);
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, o_part,
-                           lse_part, (int)splits, rows, (int)dv, o, lse);
+                           lse_part, (int)splits, rows, (int)dv, o, lse, vec);
     return hipGetLastError();
 }
 

@@ -81,7 +81,35 @@ struct WCfg {
     static_assert(BN * 8 == 64 * NW, "region B: one DMA instruction per wave");
 };
 
-constexpr int kWinW = 2;  // LDS operand fragments read ahead of the MFMAs
+constexpr int kWinW = 4;  // LDS operand fragments read ahead of the MFMAs
+
+// S^T MFMAs are written as inline asm with VGPR operands: the 256 O^T
+// accumulators then take the whole AGPR file (compiler-selected MFMAs) while
+// the score accumulator and Q^T stay in VGPRs.  The compiler's hazard model
+// does not see MFMAs inside asm, so the chain carries its own wait states:
+// consecutive MFMAs accumulate into exactly the same registers (no wait
+// needed), each one first covers a VALU write of its A/B operands (s_nop 1),
+// and qk_fence() puts 24 wait states between the last MFMA and any VALU read
+// of the scores (an 8-pass MFMA result needs fewer).
+__device__ __forceinline__ void qk_first(f32x16& d, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_next(f32x16& d, bf16x8 a, bf16x8 b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_fence(f32x16& d) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+}
+
+// Softmax frame.  O^T is never rescaled inside the tile loop (any VALU work
+// on the 256 accumulators there makes the compiler move them out of the
+// AGPRs): each lane fixes its reference max m at its first visible tile and
+// adds p = exp2(s c - m) of later tiles in that frame.  Those p stay below
+// 2^kMaxExcess unless a tile's max exceeds m by more than kMaxExcess; the
+// work-group then runs the chunk once more with every lane's reference set to
+// the largest tile max it saw, so p <= 1 throughout.  Either way O = O^T / l
+// and LSE = ln2 (m + log2 l) are the softmax of the chunk.
+constexpr float kMaxExcess = 32.f;
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
@@ -242,28 +270,27 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
-    float m = neg_inf();  // running max (log2 units) of this lane's query
-    float l = 0.f;        // this lane half's running sum
+    float m = neg_inf();      // reference max (log2 units) of this lane's query
+    float l = 0.f;            // this lane half's sum of p
+    float mx_all = neg_inf(); // largest tile max seen (log2 units)
 
     auto tile = [&](const char* st, int key0, bool need_mask) __attribute__((always_inline)) {
         // S^T = K Q^T
         f32x16 s;
         {
-            const f32x16 zero = {};
             bf16x8 fk[kWinW];
 #pragma unroll
             for (int w = 0; w < kWinW; ++w) fk[w] = kfrag(st, w);
 #pragma unroll
             for (int o = 0; o < C::NQK; ++o) {
-                s = mfma_32x32x16(fk[o % kWinW], qf[o], o == 0 ? zero : s);
+                if (o == 0) {
+                    qk_first(s, fk[0], qf[0]);
+                } else {
+                    qk_next(s, fk[o % kWinW], qf[o]);
+                }
                 if (o + kWinW < C::NQK) fk[o % kWinW] = kfrag(st, o + kWinW);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, kWinW, 0);
-#pragma unroll
-            for (int o = 0; o < C::NQK; ++o) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (o + kWinW < C::NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
+            qk_fence(s);
         }
         // online softmax; lane (col, half) holds keys key0 + 8 (i / 4) + 4 half + i % 4
         float mx = neg_inf();
@@ -276,17 +303,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         for (int i = 0; i < 16; i += 2) mx = max3(mx, s[i], s[i + 1]);
         mx = half_max(mx);
         const float mt = mx == neg_inf() ? neg_inf() : mx * a.c;
-        const bool grow = mt > m + 8.f;
-        // a lane whose max is still -inf has nothing accumulated: no rescale
-        if (__builtin_amdgcn_ballot_w64(grow && m != neg_inf()) != 0) {
-            const float alpha = grow ? fast_exp2(m - mt) : 1.f;
-            l *= alpha;
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
-        }
-        m = grow ? mt : m;
+        mx_all = fmaxf(mx_all, mt);
+        m = m == neg_inf() ? mt : m;  // first visible tile fixes the frame
         const float nm = m == neg_inf() ? 0.f : -m;
         bf16x8 pb[2];
         float lsum = 0.f;
@@ -324,8 +342,6 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     };
 
     // 2-stage ring: tile t + 1 streams in while tile t is computed
-    wait_vmcnt<0>();
-    __syncthreads();
     auto step = [&](int t, auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
         if (t + 1 < n_tiles) issue(t + 1, ST ^ 1);
@@ -334,9 +350,29 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         wait_vmcnt<0>();
         __syncthreads();
     };
-    for (int t = 0; t < n_tiles; t += 2) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+    __shared__ int rerun;
+    for (int pass = 0;; ++pass) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        for (int t = 0; t < n_tiles; t += 2) {
+            step(t, std::integral_constant<int, 0>{});
+            if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+        }
+        if (pass == 1) break;
+        // another pass if any lane of the work-group saw a tile max beyond
+        // its reference by more than kMaxExcess
+        if (tid == 0) rerun = 0;
+        __syncthreads();
+        if (__builtin_amdgcn_ballot_w64(mx_all > m + kMaxExcess) != 0 && lane == 0) rerun = 1;
+        __syncthreads();
+        if (rerun == 0) break;
+        m = mx_all;
+        l = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
+        if (n_tiles > 0) issue(0, 0);
     }
 
     // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)

@@ -98,9 +98,10 @@ def test_split_partials_match_oracle_partials():
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_combine_matches_oracle_definition(dtype):
+@pytest.mark.parametrize("S,dv", [(7, 512), (19, 512), (16, 100)])
+def test_combine_matches_oracle_definition(dtype, S, dv):
     g = torch.Generator().manual_seed(2007)
-    S, rows, dv = 7, 100, 512
+    rows = 100
     o_part = torch.randn(S, rows, dv, generator=g)
     lse_part = torch.randn(S, rows, generator=g) * 4
     lse_part[2, :50] = -math.inf                      # some empty splits
@@ -159,3 +160,16 @@ def test_mla_negative_and_zero_scale(scale):
     pc = inputs.paged_case(2011, 2, 2, 128, 1, 576, 512, 64, lengths=[70, 500], num_splits=2,
                            causal=True, poison=True, scale=scale, name="mla_scale")
     parity(pc)
+
+
+def test_mla_late_large_logit_takes_second_pass():
+    # key 40 of sequence 0 is 1.5 x the query of (token 1, head 3): its logit
+    # (~36 nats) exceeds the first tile's maxima by far more than 2^32, so the
+    # work-group reruns its chunk with the exact max as reference
+    pc = inputs.paged_case(2012, 2, 2, 128, 1, 576, 512, 64, lengths=[300, 90], num_splits=2,
+                           causal=True, poison=True, name="mla_big_logit")
+    key = 40
+    page = int(pc.pt_k[0, key // pc.page_size])
+    pc.k_pool[page, key % pc.page_size, 0] = (1.5 * pc.q[0, 1, 3].float()).to(pc.k_pool.dtype)
+    o, l, o_ref, l_ref = parity(pc)
+    assert float(l[0, 1, 3]) > 30.0
