@@ -79,6 +79,7 @@ struct WCfg {
     static constexpr int NPV = NB * (BN / 16);      // PV MFMAs per tile
     static_assert(DQK == 576 && DV == 512, "geometry below is written for the 576/512 shape");
     static_assert(BN * 8 == 64 * NW, "region B: one DMA instruction per wave");
+    static_assert(KK / 4 + (NB * (BN / 16)) / 4 == 2 * RPW + 1, "one DMA piece per four MFMAs");
 };
 
 constexpr int kWinW = 4;  // LDS operand fragments read ahead of the MFMAs
@@ -87,18 +88,20 @@ constexpr int kWinW = 4;  // LDS operand fragments read ahead of the MFMAs
 // accumulators then take the whole AGPR file (compiler-selected MFMAs) while
 // the score accumulator and Q^T stay in VGPRs.  The compiler's hazard model
 // does not see MFMAs inside asm, so the chain carries its own wait states:
-// consecutive MFMAs accumulate into exactly the same registers (no wait
-// needed), each one first covers a VALU write of its A/B operands (s_nop 1),
-// and qk_fence() puts 24 wait states between the last MFMA and any VALU read
-// of the scores (an 8-pass MFMA result needs fewer).
+// the even and odd k-steps accumulate into two register sets (so adjacent
+// MFMAs are independent; each set is only read back as the srcC of an MFMA
+// into exactly the same registers, which needs no wait), each MFMA first
+// covers a VALU write of its A/B operands (s_nop 1), and qk_fence() puts 24
+// wait states between the last MFMAs and any VALU read of the scores (an
+// 8-pass MFMA result needs fewer).
 __device__ __forceinline__ void qk_first(f32x16& d, bf16x8 a, bf16x8 b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void qk_next(f32x16& d, bf16x8 a, bf16x8 b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void qk_fence(f32x16& d) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+__device__ __forceinline__ void qk_fence(f32x16& d0, f32x16& d1) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d0), "+v"(d1));
 }
 
 // Softmax frame.  O^T is never rescaled inside the tile loop (any VALU work
@@ -110,6 +113,20 @@ __device__ __forceinline__ void qk_fence(f32x16& d) {
 // the largest tile max it saw, so p <= 1 throughout.  Either way O = O^T / l
 // and LSE = ln2 (m + log2 l) are the softmax of the chunk.
 constexpr float kMaxExcess = 32.f;
+
+// DMA source offsets v + s and (v ^ x) + s, computed where they are used: as
+// volatile asm the compiler cannot hoist them out of the tile loop (and then
+// spill them for lack of VGPRs).
+__device__ __forceinline__ uint32_t add_here(uint32_t v, uint32_t s) {
+    uint32_t r;
+    asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(s), "v"(v));
+    return r;
+}
+__device__ __forceinline__ uint32_t xor_add_here(uint32_t v, uint32_t x, uint32_t s) {
+    uint32_t r;
+    asm volatile("v_xor_b32 %0, %1, %2\n\tv_add_u32 %0, %3, %0" : "=&v"(r) : "s"(x), "v"(v), "s"(s));
+    return r;
+}
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
@@ -184,10 +201,19 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     if (n_pages > 0) load_window(0);
     const bf16_t* const kbase = a.k_pool + (int64_t)kvh * a.k_sh;
     const bf16_t* const vbase = a.v_pool + (int64_t)kvh * a.v_sh;
-    auto issue = [&](int t, int stage) __attribute__((always_inline)) {
+    // The 17 DMA instructions of a tile (per wave: 8 rows of K dims 0..511,
+    // its rows of K dims 512..575, 8 rows of V) are issued one at a time
+    // between the MFMAs of the tile before (issued back to back they stall
+    // the wave while the memory pipeline takes 68 KB).  A tile at or past the
+    // end gets an empty buffer range: its DMA writes zeros and reads nothing.
+    struct DmaPlan {
+        u32x4 kr, vr;
+        uint32_t st;
+    };
+    auto plan = [&](int t, int stage) __attribute__((always_inline)) {
         const int key0 = lo + t * C::BN;
         const int nvalid = min(C::BN, kv_end - key0);
-        const int rel = key0 / a.page - pg0;
+        const int rel = min(key0 / a.page - pg0, n_pages - 1);
         if (rel - pwin >= 64) {  // uniform; no DMA of this wave is pending here
             load_window(rel);
             wait_vmcnt<0>();
@@ -198,20 +224,29 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         // rows at or past nvalid fall outside the buffer range and arrive as zeros
         const uint32_t kn = nvalid > 0 ? (uint32_t)(nvalid - 1) * k_st2 + 2u * DQK : 0u;
         const uint32_t vn = nvalid > 0 ? (uint32_t)(nvalid - 1) * v_st2 + 2u * DV : 0u;
-        const u32x4 kr = make_rsrc(kbase + (int64_t)pkp * a.k_sp + (int64_t)slot * a.k_st, kn);
-        const u32x4 vr = make_rsrc(vbase + (int64_t)pvp * a.v_sp + (int64_t)slot * a.v_st, vn);
-        const uint32_t st = lds_base + stage * C::STAGE_B;
-#pragma unroll
-        for (int j = 0; j < C::RPW; ++j) {
+        DmaPlan d;
+        d.kr = make_rsrc(kbase + (int64_t)pkp * a.k_sp + (int64_t)slot * a.k_st, kn);
+        d.vr = make_rsrc(vbase + (int64_t)pvp * a.v_sp + (int64_t)slot * a.v_st, vn);
+        d.st = lds_base + stage * C::STAGE_B;
+        return d;
+    };
+    constexpr int NPIECE = 2 * C::RPW + 1;
+    auto piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
+        if (j < C::RPW) {
             const int row = wave * C::RPW + j;
-            dma16(kr, st + row * C::KA_PITCH, l16 + (uint32_t)row * k_st2);
+            dma16(d.kr, d.st + row * C::KA_PITCH, add_here(l16, (uint32_t)row * k_st2));
+        } else if (j == C::RPW) {
+            dma16(d.kr, d.st + C::KB_OFF + wave * 1024, kb_src);
+        } else {
+            const int row = wave * C::RPW + j - C::RPW - 1;
+            dma16(d.vr, d.st + C::V_OFF + row * C::VROW_B,
+                  xor_add_here(l16, 64u * (uint32_t)(row & 3), (uint32_t)row * v_st2));
         }
-        dma16(kr, st + C::KB_OFF + wave * 1024, kb_src);
+    };
+    auto issue = [&](int t, int stage) __attribute__((always_inline)) {
+        const DmaPlan d = plan(t, stage);
 #pragma unroll
-        for (int j = 0; j < C::RPW; ++j) {
-            const int row = wave * C::RPW + j;
-            dma16(vr, st + C::V_OFF + row * C::VROW_B, (l16 ^ (64u * (uint32_t)(row & 3))) + (uint32_t)row * v_st2);
-        }
+        for (int j = 0; j < NPIECE; ++j) piece(d, j);
     };
     if (n_tiles > 0) issue(0, 0);
 
@@ -274,23 +309,28 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     float l = 0.f;            // this lane half's sum of p
     float mx_all = neg_inf(); // largest tile max seen (log2 units)
 
-    auto tile = [&](const char* st, int key0, bool need_mask) __attribute__((always_inline)) {
+    // hook(j), j = 0..16, is called after every fourth MFMA (9 in S^T, 8 in O^T)
+    auto tile = [&](const char* st, int key0, bool need_mask, auto&& hook) __attribute__((always_inline)) {
         // S^T = K Q^T
         f32x16 s;
         {
+            f32x16 s0, s1;
             bf16x8 fk[kWinW];
 #pragma unroll
             for (int w = 0; w < kWinW; ++w) fk[w] = kfrag(st, w);
 #pragma unroll
             for (int o = 0; o < C::NQK; ++o) {
-                if (o == 0) {
-                    qk_first(s, fk[0], qf[0]);
+                f32x16& d = (o & 1) ? s1 : s0;
+                if (o < 2) {
+                    qk_first(d, fk[o % kWinW], qf[o]);
                 } else {
-                    qk_next(s, fk[o % kWinW], qf[o]);
+                    qk_next(d, fk[o % kWinW], qf[o]);
                 }
                 if (o + kWinW < C::NQK) fk[o % kWinW] = kfrag(st, o + kWinW);
+                if (o % 4 == 3) hook(o / 4);
             }
-            qk_fence(s);
+            qk_fence(s0, s1);
+            s = s0 + s1;
         }
         // online softmax; lane (col, half) holds keys key0 + 8 (i / 4) + 4 half + i % 4
         float mx = neg_inf();
@@ -331,6 +371,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
             for (int o = 0; o < C::NPV; ++o) {
                 acc[o % C::NB] = mfma_32x32x16(fv[o % kWinW], pb[o / C::NB], acc[o % C::NB]);
                 if (o + kWinW < C::NPV) fv[o % kWinW] = vfrag(st, o + kWinW);
+                if (o % 4 == 3) hook(C::NQK / 4 + o / 4);
             }
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kWinW, 1);
 #pragma unroll
@@ -344,9 +385,15 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     // 2-stage ring: tile t + 1 streams in while tile t is computed
     auto step = [&](int t, auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
-        if (t + 1 < n_tiles) issue(t + 1, ST ^ 1);
+        const DmaPlan d = plan(t + 1, ST ^ 1);
         const int key0 = lo + t * C::BN;
-        if (key0 < kv_end_w) tile(lds + ST * C::STAGE_B, key0, key0 + C::BN > nomask_end);
+        if (key0 < kv_end_w) {
+            tile(lds + ST * C::STAGE_B, key0, key0 + C::BN > nomask_end,
+                 [&](int j) __attribute__((always_inline)) { piece(d, j); });
+        } else {
+#pragma unroll
+            for (int j = 0; j < NPIECE; ++j) piece(d, j);
+        }
         wait_vmcnt<0>();
         __syncthreads();
     };
