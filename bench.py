@@ -18,6 +18,14 @@ sample of the same workloads (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 Prints ONE JSON line on stdout.
+
+``roofline.traffic`` (HBM bytes per launch of the kernel) comes from the
+committed counter summary profiles/prefill_thd_d128_traffic.md (decode:
+profiles/paged_decode_d128_traffic.md): rocprofv3
+FETCH_SIZE and WRITE_SIZE of the kernel, each scaled by what the same counter
+reads for a plain device copy of known size (``--calibrate-copy`` runs that
+copy).  It is null when the kernel sources differ from the ones the counters
+were taken on (SHA-1 of the sources recorded in the summary).
 """
 from __future__ import annotations
 
@@ -66,6 +74,61 @@ def decode_bytes(pc):
     pages = sum((L + pc.page_size - 1) // pc.page_size for L in lens)
     tables = 2 * pages * 4 + pc.batch * 4
     return kv, kv + q + o + lse + tables
+
+
+PREFILL_SOURCES = ["scaled_dot_product_19_amd/csrc/prefill_bf16.hip",
+                   "scaled_dot_product_19_amd/csrc/tile_ops.h",
+                   "scaled_dot_product_19_amd/csrc/sdpa_device.h"]
+DECODE_SOURCES = ["scaled_dot_product_19_amd/csrc/decode_small.hip",
+                  "scaled_dot_product_19_amd/csrc/combine.hip",
+                  "scaled_dot_product_19_amd/csrc/decode_paged.hip",
+                  "scaled_dot_product_19_amd/csrc/sdpa_device.h"]
+PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_thd_d128_traffic.md")
+DECODE_TRAFFIC = os.path.join(ROOT, "profiles", "paged_decode_d128_traffic.md")
+
+
+def sources_sha1(paths):
+    import hashlib
+    h = hashlib.sha1()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(summary, sources):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    summary is missing or was taken on other kernel sources."""
+    try:
+        with open(summary) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        line = line.strip().strip("`")
+        if ":" in line and line.split(":", 1)[0] in ("sources_sha1", "traffic_bytes_per_launch"):
+            k, v = line.split(":", 1)
+            vals[k] = v.strip().split()[0].strip("`")
+    if vals.get("sources_sha1") != sources_sha1(sources):
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(nbytes):
+    """One plain device-to-device copy of nbytes (the FETCH_SIZE / WRITE_SIZE
+    reference under rocprofv3 --pmc)."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes}), flush=True)
 
 
 def host_threads():
@@ -149,6 +212,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU seconds of each oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one device copy of BYTES (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -162,6 +227,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     sdpa.load()  # raises if the HIP library is missing; there is no fallback
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
@@ -280,22 +348,22 @@ def main():
             "what": "K/V bytes of live tokens / (split kernel + combine kernel) time",
         },
         "roofline": {
-            "kernel": "prefill_bf16_kernel<128, 64>",
+            "kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false>",
             "bound": "mfma",
             "achieved": round(pre_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(PREFILL_TRAFFIC, PREFILL_SOURCES),
         },
         "roofline_decode": {
-            "kernel": "decode_kernel<128, 128, 1, true> + combine_kernel<false>",
+            "kernel": "decode_small_kernel<128> + combine_kernel<false>",
             "bound": "hbm",
             "achieved": round(dec_comp_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(dec_comp_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(DECODE_TRAFFIC, DECODE_SOURCES),
         },
         "cpu_baseline": cpu_pre,
         "cpu_baseline_decode": cpu_dec,
