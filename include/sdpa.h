@@ -43,8 +43,12 @@
  *     sequence with Lq queries and Lk keys sees key j iff j <= i + Lk - Lq
  *     (v1.28.0 "New: FROST SDPA ...", per-sequence THD bottom-right
  *     diagonals).
- *   - Thread-safe: no mutable global state besides the thread-local error
- *     detail.
+ *   - Thread-safe.  Mutable global state: the thread-local error detail, and
+ *     the work-queue counters of the persistent prefill grid (a small
+ *     static device array per GPU, 64 slots taken round robin by successive
+ *     prefill calls; each launch returns its slot to zero when it ends).  Up
+ *     to 64 prefill calls may therefore be in flight on one GPU at once
+ *     (different streams); a 65th overlapping call would share a slot.
  */
 #ifndef SDPA_MI355X_H
 #define SDPA_MI355X_H
