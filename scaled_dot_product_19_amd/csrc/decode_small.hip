@@ -26,6 +26,8 @@
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 
+#include <atomic>
+
 namespace sdpa {
 namespace {
 
@@ -48,7 +50,8 @@ struct SmallKArgs {
     const int32_t* pt_v;
     int32_t table_stride;
     const int32_t* seq_lens;
-    int32_t sq, hq, hkv, group, page, page_shift, splits, rows, n_units;
+    int32_t batch, sq, hq, hkv, group, page, page_shift, splits, rows, n_units;
+    int32_t slot;  // work-queue counters used by this launch
     int64_t total_rows;
     float scale_log2;
     int32_t causal;
@@ -59,6 +62,26 @@ struct SmallKArgs {
 };
 
 constexpr int kWaves = 4;
+
+// Work queue of the persistent decode grid: counter [slot][0] hands out
+// units (ticket t: the t-th (sequence, KV head, split) in order of
+// decreasing sequence length), counter [slot][1] counts work-groups that
+// are done; the last one returns both to 0 for the next launch that uses
+// the slot.  Launches take slots round robin (kQueueSlots calls may overlap
+// on one device).
+constexpr int kQueueSlots = 64;
+constexpr int kRankMax = 256;  // longest-first order for batches up to this size
+__device__ __align__(256) uint32_t g_decode_queue[kQueueSlots][32];
+
+// Ticket from a work-queue counter: returns the value before adding 1.  The
+// result is not waited for: read it only after a wait for every vector-memory
+// operation of the wave (same encoding as a device-scope atomicAdd with
+// return).
+__device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) {
+    uint32_t old;
+    asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=&v"(old) : "v"(ctr), "v"(1u) : "memory");
+    return old;
+}
 
 // Fourth word of a raw buffer resource on gfx9-family parts (CDNA): no
 // swizzle, 32-bit data format; the range check returns zeros past num_records.
@@ -92,19 +115,19 @@ struct TileRegs {
     uint4 v[SmallCfg<D>::VU][4];
 };
 
-template <int D>
-__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(SmallKArgs a) {
+// One unit: the keys of split `split` of sequence b for KV head kvh.  The
+// next unit's ticket (lane 0 of wave 0) is requested at the start and turned
+// into next_unit during the merge; returns that unit (-1: none left).
+template <int D, class NextOf>
+__device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, bf16_t* smem, const int b,
+                                                          const int kvh, const int split, uint32_t* ctr,
+                                                          int* next_unit, NextOf&& next_of) {
     using C = SmallCfg<D>;
-    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4;
-
-    const int unit = blockIdx.x;
-    const int split = unit % a.splits;
-    const int bh = unit / a.splits;
-    const int kvh = bh % a.hkv, b = bh / a.hkv;
+    uint32_t ticket = 0;
+    if (threadIdx.x == 0) ticket = ticket_async(ctr);
 
     // a length past the table's reach is clamped: the table is never read out of bounds
     const int L = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
@@ -325,7 +348,14 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
         red_m[wave * 16 + c] = m;
         red_l[wave * 16 + c] = l;
     }
+    // lane 0 of wave 0: the unit after this one (its ticket has returned:
+    // every vector-memory operation of the wave is done by now)
+    if (threadIdx.x == 0) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        *next_unit = next_of(ticket);
+    }
     __syncthreads();
+    const int nxt = *next_unit;
     const int items = a.rows * (D / 4);
     for (int it = threadIdx.x; it < items; it += 256) {
         const int q = it / (D / 4), n = 4 * (it % (D / 4));
@@ -362,17 +392,72 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
             if (n == 0 && a.lse != nullptr) a.lse[row] = lse;
         }
     }
+    return nxt;
+}
+
+// Persistent grid: each work-group runs units until the queue is empty,
+// longest sequences first (every unit of a sequence has the same number of
+// keys but the last split).
+template <int D>
+__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(SmallKArgs a) {
+    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    __shared__ int next_unit;
+    __shared__ int by_len[kRankMax];  // by_len[r] = sequence with the r-th largest length
+    uint32_t* const ctr = g_decode_queue[a.slot];
+    const int per_seq = a.hkv * a.splits;
+    const bool ranked = a.batch <= kRankMax;
+    if (ranked && (int)threadIdx.x < a.batch) {
+        const int me = threadIdx.x;
+        const int lm = a.seq_lens[me];
+        int r = 0;
+        for (int j = 0; j < a.batch; ++j) {
+            const int lj = a.seq_lens[j];
+            r += (lj > lm) || (lj == lm && j < me);
+        }
+        by_len[r] = me;
+    }
+    auto next_of = [&](uint32_t t) -> int { return t < (uint32_t)a.n_units ? (int)t : -1; };
+    if (threadIdx.x == 0) next_unit = next_of(atomicAdd(&ctr[0], 1u));
+    __syncthreads();
+    int unit = next_unit;
+    while (unit >= 0) {
+        const int r = unit / per_seq, rem = unit - r * per_seq;
+        const int b = ranked ? by_len[r] : r;
+        const int kvh = rem / a.splits, split = rem - (rem / a.splits) * a.splits;
+        const int nxt = decode_unit<D>(a, smem, b, kvh, split, &ctr[0], &next_unit, next_of);
+        __syncthreads();  // the merge's LDS reads are done before the next unit's V^T stores
+        unit = nxt;
+    }
+    if (threadIdx.x == 0 && atomicAdd(&ctr[1], 1u) == gridDim.x - 1) {
+        // every work-group has taken its last ticket
+        atomicExch(&ctr[0], 0u);
+        atomicExch(&ctr[1], 0u);
+    }
 }
 
 template <int D>
-hipError_t launch_small_d(const SmallKArgs& a, hipStream_t s) {
+hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
     using C = SmallCfg<D>;
     if (a.n_units == 0) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void*)decode_small_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       C::LDS_BYTES);
+    const void* kernel = (const void*)decode_small_kernel<D>;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_small_kernel<D>, dim3((unsigned)a.n_units), dim3(256),
+    // resident work-groups: per CU (computed once) x CUs of the device
+    static std::atomic<int> per_cu{0};
+    int occ = per_cu.load(std::memory_order_relaxed);
+    if (occ == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, C::LDS_BYTES) != hipSuccess || occ < 1)
+            occ = 1;
+        per_cu.store(occ, std::memory_order_relaxed);
+    }
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+        n_cu = 1;
+    const int64_t slots = (int64_t)occ * n_cu;
+    static std::atomic<uint32_t> slot_seq{0};
+    a.slot = (int32_t)(slot_seq.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
+    hipLaunchKernelGGL(decode_small_kernel<D>, dim3((unsigned)(a.n_units < slots ? a.n_units : slots)), dim3(256),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
@@ -398,6 +483,7 @@ hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
     a.pt_v = da.pt_v;
     a.table_stride = da.table_stride;
     a.seq_lens = da.seq_lens;
+    a.batch = da.batch;
     a.sq = da.sq;
     a.hq = da.hq;
     a.hkv = da.hkv;
