@@ -36,8 +36,11 @@ def common_flags():
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-# Per-source extra flags.
-EXTRA_FLAGS = {}
+# Per-source extra flags.  The persistent kernels fetch their next work item
+# with a one-lane atomicAdd while the current one runs; the wave-level atomic
+# optimizer would turn it into a scan that waits for the result on the spot.
+_NO_ATOMIC_OPT = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+EXTRA_FLAGS = {"prefill_bf16.hip": _NO_ATOMIC_OPT, "decode_small.hip": _NO_ATOMIC_OPT}
 
 
 def _compile(cc, src, obj):

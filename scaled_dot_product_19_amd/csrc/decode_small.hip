@@ -73,15 +73,13 @@ constexpr int kQueueSlots = 64;
 constexpr int kRankMax = 256;  // longest-first order for batches up to this size
 __device__ __align__(256) uint32_t g_decode_queue[kQueueSlots][32];
 
-// Ticket from a work-queue counter: returns the value before adding 1.  The
-// result is not waited for: read it only after a wait for every vector-memory
-// operation of the wave (same encoding as a device-scope atomicAdd with
-// return).
-__device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) {
-    uint32_t old;
-    asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=&v"(old) : "v"(ctr), "v"(1u) : "memory");
-    return old;
-}
+// Ticket from a work-queue counter: the value before adding 1.  A plain
+// one-lane atomicAdd: this file is compiled without the wave-level atomic
+// optimizer, so the compiler waits for the returned value only where it is
+// used and keeps its register reserved until then.  (An asm atomic would hide
+// the pending write from the register allocator, which could hand the
+// register to another value before the atomic returns.)
+__device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) { return atomicAdd(ctr, 1u); }
 
 // Fourth word of a raw buffer resource on gfx9-family parts (CDNA): no
 // swizzle, 32-bit data format; the range check returns zeros past num_records.

@@ -99,16 +99,13 @@ struct PCfg {
     static_assert(BN % 32 == 0 && D % 32 == 0 && CPR >= 8, "tile shape");
 };
 
-// Ticket from a work-queue counter: returns the value before adding 1.  The
-// result is NOT waited for: read it only after wait_vmcnt<0>.  (Written as
-// inline asm so that the compiler does not wait for the return right away,
-// as it does after its own wave-level atomic expansion.)  Same encoding as
-// the compiler's device-scope atomicAdd with return.
-__device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) {
-    uint32_t old;
-    asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=&v"(old) : "v"(ctr), "v"(1u) : "memory");
-    return old;
-}
+// Ticket from a work-queue counter: the value before adding 1.  A plain
+// one-lane atomicAdd: this file is compiled without the wave-level atomic
+// optimizer, so the compiler waits for the returned value only where it is
+// used and keeps its register reserved until then.  (An asm atomic would hide
+// the pending write from the register allocator, which could hand the
+// register to another value before the atomic returns.)
+__device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) { return atomicAdd(ctr, 1u); }
 
 // D <= 128: two work-groups per CU (<= 256 registers per lane, 2-stage ring).
 // D = 256: one, with a 4-stage ring and the O^T accumulators in AGPRs.
