@@ -204,6 +204,62 @@ def cpu_baseline_decode(pc, target_s, threads):
                       "workload, 8-way split + LSE merge, fp64, %.1f s" % (n, nrows, dt)}
 
 
+def chunked_prefill_flops(pc):
+    """Visible (row, key) pairs x 2 (D_qk + D_v): token i of a chunk of s_q tokens at the end of
+    a cache of L tokens sees keys 0 .. L - s_q + i."""
+    pairs = 0
+    for L in pc.seq_lens.tolist():
+        first = L - pc.sq + 1  # keys seen by token 0
+        for i in range(pc.sq):
+            pairs += max(0, min(L, first + i))
+    return 2.0 * (128 + 128) * pairs * pc.hq
+
+
+def run_chunked_prefill(args, torch, inputs, sdpa, dev):
+    """Chunked prefill over the paged cache: one sdpa_decode_paged call per step (the
+    prefill kernel over the page tables, plus the LSE combine when splits > 1)."""
+    pc = inputs.chunked_prefill_paged(num_splits=args.splits)
+    q, kp, vp = pc.q.to(dev), pc.k_pool.to(dev), pc.v_pool.to(dev)
+    ptk, ptv, sl = pc.pt_k.to(dev), pc.pt_v.to(dev), pc.seq_lens.to(dev)
+    o = torch.empty((pc.batch, pc.sq, pc.hq, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((pc.batch, pc.sq, pc.hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, sdpa.decode_workspace_bytes(pc.batch, pc.sq, pc.hq, 128,
+                                                        pc.num_splits)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sdpa.decode_paged(q, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, pc.causal,
+                          num_splits=pc.num_splits, workspace=ws, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = chunked_prefill_flops(pc)
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {"metric": "chunked prefill attn TFLOP/s (% MFMA peak)", "value": round(tflops, 2),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) bf16; cache lengths, page permutations per seed)",
+            "config": {"workload": pc.name, "chunk": pc.sq, "cache_lengths": pc.seq_lens.tolist(),
+                       "splits": pc.num_splits, "flop": flops},
+            "roofline": {"kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false, true>"
+                                   + (" + combine_kernel<false>" if pc.num_splits > 1 else ""),
+                         "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +270,10 @@ def main():
                     help="target CPU seconds of each oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one device copy of BYTES (counter calibration)")
+    ap.add_argument("--chunked-prefill", action="store_true",
+                    help="time only chunked prefill over the paged cache (2 x 1024-token chunks, "
+                         "caches U[32768, 65536], 32/8 heads, D=128, page 64) and print its line")
+    ap.add_argument("--splits", type=int, default=4, help="num_splits of --chunked-prefill")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -233,6 +293,9 @@ def main():
     sdpa.load()  # raises if the HIP library is missing; there is no fallback
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.chunked_prefill:
+        run_chunked_prefill(args, torch, inputs, sdpa, dev)
+        return
 
     t0 = time.time()
     case = inputs.thd_prefill_d128()
@@ -348,7 +411,7 @@ def main():
             "what": "K/V bytes of live tokens / (split kernel + combine kernel) time",
         },
         "roofline": {
-            "kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false>",
+            "kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false, false>",
             "bound": "mfma",
             "achieved": round(pre_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,

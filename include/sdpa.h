@@ -164,7 +164,18 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  * o       [batch, s_q, h_q, d_v] dense bf16; lse [batch, s_q, h_q] fp32 or NULL.
  * Supported: dtype SDPA_BF16; (d_qk, d_v) in {(64,64), (128,128), (256,256),
  * (576,512)}; page_size a multiple of 16; 1 <= num_splits <= 256;
- * s_q * (h_q/h_kv) <= 512 query rows per KV head.
+ * s_q * (h_q/h_kv) <= 512 query rows per KV head, or any larger s_q when
+ * d_qk = d_v = 128, page_size is a multiple of 64 and k_st, v_st < 2^22.
+ *
+ * Chunked prefill over the paged cache is this same call with s_q = the
+ * chunk's tokens (the last s_q of each cache; v1.31.0 "SDPA: paged KV,
+ * split-KV, and engine selection", paged D128 prefill and chunked-prefill
+ * selection; the context phase of v1.28.0 "Samples, Benchmarks, and Tests",
+ * 512/1024-token chunks against 64k/128k caches).  With d_qk = d_v = 128,
+ * page_size % 64 == 0 and s_q of at least one prefill work item (64 tokens
+ * when h_q/h_kv is a multiple of 4, 128 when it is 2 mod 4, 256 when odd) it
+ * runs on the prefill kernel, which reads its 64-key K/V tiles through the
+ * page tables; num_splits > 1 then writes the same partials as decode.
  */
 int sdpa_decode_paged(const void* q,
                       const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,

@@ -239,6 +239,7 @@ bool decode_supported(int32_t dqk, int32_t dv) {
 hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
     if (decode_small_supported(da.dqk, da.dv, da.sq * (da.hq / da.hkv)))
         return launch_decode_small(da, s);
+    if (prefill_paged_supported(da)) return launch_prefill_paged(da, s);
     if (decode_wide_supported(da)) return launch_decode_wide(da, s);
     DecodeKArgs a;
     a.q = static_cast<const bf16_t*>(da.q);

@@ -9,11 +9,12 @@
 // offsets, bottom-right THD diagonals, pack_gqa: v1.28.0 release notes,
 // "New: FROST SDPA on Ampere, Ada/Blackwell-consumer, and Rubin".
 //
-// Work-group = 4 waves = 128 query rows sharing one KV head: NH query heads
-// of one GQA group x (4 / NH) blocks of 32 consecutive tokens, NH = largest
-// of {4, 2, 1} dividing G, so every K/V tile staged in LDS serves NH heads
-// (partial GQA packing: v1.30.0 "New: decode tiles", Partial PackGQA bullet).
-// Work-groups are issued longest causal row block first.
+// Work-group = NW waves of 32 query rows sharing one KV head (NW = 8 for
+// D <= 128, 4 for D = 256): NH query heads of one GQA group x (NW / NH)
+// blocks of 32 consecutive tokens, NH = largest of {4, 2, 1} dividing G, so
+// every K/V tile staged in LDS serves NH heads (partial GQA packing: v1.30.0
+// "New: decode tiles", Partial PackGQA bullet).  Items are handed out
+// longest causal row block first.
 //
 // K/V staging (gfx950 LDS DMA).  Tiles of BN keys go from HBM straight into
 // LDS with buffer_load_dwordx4 ... lds: each lane's 16 bytes land at
@@ -65,6 +66,17 @@ struct PrefillKArgs {
     float* lse;
     int32_t lse_layout, lse_s_max;
     int32_t slot;    // work-queue counters used by this launch
+    // paged mode (chunked prefill over a paged cache; see launch_prefill_paged):
+    // Q [batch, sq, hq, D] dense, K/V rows through independent page tables,
+    // key range split in `splits` chunks, fp32 partials when splits > 1
+    const int32_t* pt_k;
+    const int32_t* pt_v;
+    const int32_t* seq_lens;
+    int64_t k_sp, v_sp;      // page strides (elements)
+    int32_t table_stride, page, sq, splits;
+    int64_t total_rows;      // batch * sq * hq
+    float* o_part;           // [splits, total_rows, D]
+    float* lse_part;         // [splits, total_rows]
 };
 
 // Work queues of the persistent prefill grid, one per XCD.  Pair p = (b, hg)
@@ -115,7 +127,7 @@ __device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) { return atomicA
 // One work item: NH heads x NW / NH blocks of 32 query rows of one sequence,
 // all keys it sees.  Uniform across the work-group (every exit is taken by
 // all waves).  On return every LDS DMA of the item has landed.
-template <int D, int BN, int S, int NW, bool PP, bool CZ>
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED>
 __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& a, const int item,
                                                             char* const lds, const uint32_t lds_base,
                                                             uint32_t* const tctr, uint32_t& ticket) {
@@ -123,18 +135,42 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     using C = PCfg<D, BN, S, NW>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // item = level * (batch * n_hg) + pair: level = causal row block counted
-    // from the last (longest first), pair = b * n_hg + hg
+    // item = level * n_pairs + pair: level = causal row block counted from
+    // the last (longest first), pair = b * n_hg + hg (paged: (b * n_hg + hg)
+    // * splits + split)
     const int bid = __builtin_amdgcn_readfirstlane(item);
-    const int n_pairs = a.batch * a.n_hg;
+    const int n_pairs = a.batch * a.n_hg * (PAGED ? a.splits : 1);
     const int level = bid / n_pairs;
     const int pair = bid - level * n_pairs;
-    const int b = pair / a.n_hg;
-    const int hg = pair - b * a.n_hg;
+    const int bh = PAGED ? pair / a.splits : pair;
+    const int split = PAGED ? pair - bh * a.splits : 0;
+    const int b = bh / a.n_hg;
+    const int hg = bh - b * a.n_hg;
     const int qt = a.n_qtiles - 1 - level;
 
-    const int q_beg = load_uniform(a.cu_q, b), lq = load_uniform(a.cu_q, b + 1) - q_beg;
-    const int kv_beg = load_uniform(a.cu_kv, b), lk = load_uniform(a.cu_kv, b + 1) - kv_beg;
+    // rows [q_beg, q_beg + lq) and keys [kv_beg, kv_beg + lk) of the sequence;
+    // this item sees keys [lo, hi) of it (the split's chunk when paged)
+    int q_beg, lq, kv_beg, lk, lo = 0, hi;
+    if constexpr (PAGED) {
+        q_beg = b * a.sq;
+        lq = a.sq;
+        kv_beg = 0;
+        // a length past the table's reach is clamped: the table is never read out of bounds
+        lk = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
+        hi = lk;
+        if (a.splits > 1) {
+            const int per = (lk + a.splits - 1) / a.splits;
+            const int chunk = ((per + a.page - 1) / a.page) * a.page;
+            lo = min(lk, split * chunk);
+            hi = min(lk, lo + chunk);
+        }
+    } else {
+        q_beg = load_uniform(a.cu_q, b);
+        lq = load_uniform(a.cu_q, b + 1) - q_beg;
+        kv_beg = load_uniform(a.cu_kv, b);
+        lk = load_uniform(a.cu_kv, b + 1) - kv_beg;
+        hi = lk;
+    }
     const int nt = NW / a.nh;
     const int q0 = qt * 32 * nt;
     if (q0 >= lq) {  // uniform across the work-group
@@ -152,17 +188,17 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     const bool row_ok = i < lq;
     const int shift = lk - lq;  // bottom-right diagonal offset
 
-    // key extents: the work-group's, this wave's, and this lane's
+    // key extents within [lo, hi): the work-group's, this wave's, and this lane's
     const int last_wg = min(q0 + 32 * nt, lq) - 1;
-    const int kv_end = a.causal ? max(0, min(lk, last_wg + shift + 1)) : lk;
-    int kv_end_w = 0, nomask_end = 0;
+    const int kv_end = a.causal ? max(lo, min(hi, last_wg + shift + 1)) : hi;
+    int kv_end_w = lo, nomask_end = lo;
     if (i0 < lq) {
         const int last_w = min(i0 + 32, lq) - 1;
-        kv_end_w = a.causal ? max(0, min(lk, last_w + shift + 1)) : lk;
-        nomask_end = a.causal ? max(0, min(lk, i0 + shift + 1)) : lk;
+        kv_end_w = a.causal ? max(lo, min(hi, last_w + shift + 1)) : hi;
+        nomask_end = a.causal ? max(lo, min(hi, i0 + shift + 1)) : hi;
     }
-    const int lim = a.causal ? min(lk - 1, i + shift) : lk - 1;
-    const int n_tiles = (kv_end + BN - 1) / BN;
+    const int lim = a.causal ? min(hi - 1, i + shift) : hi - 1;
+    const int n_tiles = (kv_end - lo + BN - 1) / BN;  // tile t: keys lo + t BN ..
 
     // ---- LDS DMA of the K/V tiles -------------------------------------------
     // Wave w's instruction j fills bytes [(w NI + j) KiB, +1 KiB) of a tile;
@@ -180,13 +216,43 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         k_src[j] = row * k_st2 + 16 * swz_k<C::CPR>(row, pc);
         v_src[j] = row * v_st2 + 16 * swz_v<C::CPR>(row, pc);
     }
+    // Paged: the K and V page ids of the next tile to be issued (scalar
+    // loads).  An outstanding scalar load makes every later LDS wait a full
+    // lgkmcnt(0), so in the ping-pong schedule the loads are started at the
+    // beginning of a VALU phase (which reads no LDS) and waited for at its end.
+    int pk_nx = 0, pv_nx = 0;
+    const int32_t* const ptk_b = PAGED ? a.pt_k + (int64_t)b * a.table_stride : nullptr;
+    const int32_t* const ptv_b = PAGED ? a.pt_v + (int64_t)b * a.table_stride : nullptr;
+    auto page_ids = [&](int t) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            const int k0 = lo + t * BN;
+            const int e = k0 < kv_end ? k0 / a.page : 0;  // a tile past the end reads no page
+            pk_nx = load_uniform(ptk_b, e);
+            pv_nx = load_uniform(ptv_b, e);
+        }
+    };
+    auto page_ids_ready = [&]() __attribute__((always_inline)) {
+        if constexpr (PAGED) asm volatile("" ::"s"(pk_nx), "s"(pv_nx));
+    };
     auto issue = [&](int t) __attribute__((always_inline)) {
         // a tile at or past kv_end gets an empty range: its DMA writes zeros
         // and reads nothing
-        const int k0 = t * BN;
+        const int k0 = lo + t * BN;
         const int nvalid = min(BN, kv_end - k0);
-        const u32x4 kr = make_rsrc(kb0 + (int64_t)k0 * a.k_st, nvalid > 0 ? (nvalid - 1) * k_st2 + 2 * D : 0);
-        const u32x4 vr = make_rsrc(vb0 + (int64_t)k0 * a.v_st, nvalid > 0 ? (nvalid - 1) * v_st2 + 2 * D : 0);
+        const bf16_t* kt;
+        const bf16_t* vt;
+        if constexpr (PAGED) {
+            // BN divides the page size and lo is a multiple of it: the tile
+            // lies in one page (K and V pages looked up independently)
+            const int64_t in_page = nvalid > 0 ? k0 % a.page : 0;
+            kt = a.k + (int64_t)pk_nx * a.k_sp + in_page * a.k_st + (int64_t)kvh * a.k_sh;
+            vt = a.v + (int64_t)pv_nx * a.v_sp + in_page * a.v_st + (int64_t)kvh * a.v_sh;
+        } else {
+            kt = kb0 + (int64_t)k0 * a.k_st;
+            vt = vb0 + (int64_t)k0 * a.v_st;
+        }
+        const u32x4 kr = make_rsrc(kt, nvalid > 0 ? (nvalid - 1) * k_st2 + 2 * D : 0);
+        const u32x4 vr = make_rsrc(vt, nvalid > 0 ? (nvalid - 1) * v_st2 + 2 * D : 0);
         const uint32_t st = lds_base + (t % S) * C::STAGE_B + wave * C::NI * 1024;
 #pragma unroll
         for (int j = 0; j < C::NI; ++j) dma16(kr, st + j * 1024, k_src[j]);
@@ -196,7 +262,12 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // start the first tiles before the Q load so they overlap it (S - 1 ahead
     // in the sequential ring, S - 2 in the ping-pong one)
 #pragma unroll
-    for (int t = 0; t < (PP ? S - 2 : S - 1); ++t) issue(t);
+    for (int t = 0; t < (PP ? S - 2 : S - 1); ++t) {
+        page_ids(t);
+        page_ids_ready();
+        issue(t);
+    }
+    if constexpr (PP) page_ids(S - 2);  // for M(0)
 
     // Q^T operand: lane (col, half) holds d = 16 kk + 8 half .. +8 of row i
     bf16x8 qf[C::KK];
@@ -422,8 +493,10 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         wait_vmcnt<PER_TILE * (S - 2)>();
         __syncthreads();
         auto step = [&](int t, auto stage) __attribute__((always_inline)) {
+            page_ids(t + S - 1);
+            page_ids_ready();
             issue(t + S - 1);
-            const int key0 = t * BN;
+            const int key0 = lo + t * BN;
             if (key0 < kv_end_w) {
                 const char* st = lds + decltype(stage)::value * C::STAGE_B;
                 qk(st, s);
@@ -465,19 +538,22 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         };
         // V(t): softmax of tile t, or P = 0 for a wave that sees none of its keys
         auto v_phase = [&](int t) __attribute__((always_inline)) {
-            const int key0 = t * BN;
+            page_ids(t + S - 1);  // issued by M(t + 1)
+            const int key0 = lo + t * BN;
             if (key0 < kv_end_w) {
                 softmax(s, pb, key0, key0 + BN > nomask_end);
             } else {
 #pragma unroll
                 for (int j = 0; j < BN / 16; ++j) pb[j] = bf16x8{};
             }
+            page_ids_ready();
             if (!late) wait_vmcnt<PER_TILE>();
             __syncthreads();
         };
         if (n_tiles > 0) {
             // M(0): QK of tile 0
             __builtin_amdgcn_s_setprio(1);
+            page_ids_ready();
             issue(S - 2);
             qk(stage_ptr(0), s);
             m_end();
@@ -503,10 +579,31 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // before this work-group can finish and its LDS be handed to another.
     wait_vmcnt<0>();
 
-    // epilogue: O = O^T / l written as bf16, LSE = ln2 * (m + log2 l)
+    // epilogue: O = O^T / l written as bf16, LSE = ln2 * (m + log2 l); a
+    // split of a paged call writes its normalized fp32 partial and LSE_c
+    // (-inf and zeros when it sees no key of the row)
     const float l_tot = half_sum(l);
     if (!row_ok) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if constexpr (PAGED) {
+        if (a.splits > 1) {
+            const int64_t grow = (int64_t)(q_beg + i) * a.hq + h;
+            float* prow = a.o_part + ((int64_t)split * a.total_rows + grow) * D;
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = nb * 32 + 8 * g + 4 * half;
+                    *reinterpret_cast<f32x4*>(prow + n) = f32x4{acc[nb][4 * g] * inv, acc[nb][4 * g + 1] * inv,
+                                                               acc[nb][4 * g + 2] * inv, acc[nb][4 * g + 3] * inv};
+                }
+            }
+            if (half == 0)
+                a.lse_part[(int64_t)split * a.total_rows + grow] =
+                    l_tot > 0.f ? kLn2 * (m + fast_log2(l_tot)) : neg_inf();
+            return;
+        }
+    }
     bf16_t* orow = a.o + (int64_t)(q_beg + i) * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
@@ -532,14 +629,14 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
 // Persistent grid: each work-group runs items until every queue is empty.
 // The ticket of the next item is fetched (one atomic of wave 0) while the
 // current item runs and handed to the other waves through LDS.
-template <int D, int BN, int S, int NW, bool PP, bool CZ>
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED>
 __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kernel(PrefillKArgs a) {
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     __shared__ int next_item;
     char* const lds = reinterpret_cast<char*>(smem);
     const uint32_t lds_base = lds_addr(smem);
     uint32_t* const ctr = g_prefill_queue[a.slot];
-    const int n_pairs = a.batch * a.n_hg;
+    const int n_pairs = a.batch * a.n_hg * (PAGED ? a.splits : 1);
     // Only lane 0 of wave 0 talks to the queues: q is the queue it draws
     // from, tries the number of queues it has found empty.
     int q = 0, tries = 0;
@@ -569,7 +666,7 @@ __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kern
     int item = next_item;
     while (item >= 0) {
         uint32_t ticket = 0;
-        prefill_item<D, BN, S, NW, PP, CZ>(a, item, lds, lds_base, &ctr[q], ticket);
+        prefill_item<D, BN, S, NW, PP, CZ, PAGED>(a, item, lds, lds_base, &ctr[q], ticket);
         __syncthreads();  // every wave has read next_item of the last round
         if (threadIdx.x == 0) next_item = next_of(ticket);
         __syncthreads();
@@ -581,8 +678,9 @@ __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kern
     }
 }
 
-// Resident work-groups per CU of a kernel (computed once) x CUs of the device.
-template <typename K>
+// Resident work-groups per CU of a kernel (computed once per kernel: the Tag
+// is the kernel's own template) x CUs of the device.
+template <typename Tag, typename K>
 int resident_slots(K kernel, int threads, int lds_bytes) {
     static std::atomic<int> per_cu{0};
     int occ = per_cu.load(std::memory_order_relaxed);
@@ -601,14 +699,18 @@ int resident_slots(K kernel, int threads, int lds_bytes) {
 
 std::atomic<uint32_t> g_slot_seq{0};
 
-template <int D, int BN, int S, int NW, bool PP, bool CZ>
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED>
+struct KernelTag {};
+
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED>
 hipError_t launch_dz(PrefillKArgs a, int64_t n_wg, hipStream_t s) {
     using C = PCfg<D, BN, S, NW>;
-    auto kernel = prefill_bf16_kernel<D, BN, S, NW, PP, CZ>;
+    auto kernel = prefill_bf16_kernel<D, BN, S, NW, PP, CZ, PAGED>;
     // more than 64 KiB of dynamic LDS must be requested per kernel
     hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    const int64_t slots = resident_slots(kernel, C::THREADS, C::LDS_BYTES);
+    const int64_t slots =
+        resident_slots<KernelTag<D, BN, S, NW, PP, CZ, PAGED>>(kernel, C::THREADS, C::LDS_BYTES);
     a.slot = (int32_t)(g_slot_seq.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
     hipLaunchKernelGGL(kernel, dim3((unsigned)(n_wg < slots ? n_wg : slots)), dim3(C::THREADS),
                        (size_t)C::LDS_BYTES, s, a);
@@ -645,14 +747,81 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     a.lse = pa.lse;
     a.lse_layout = pa.lse_layout;
     a.lse_s_max = pa.lse_s_max;
+    a.pt_k = a.pt_v = a.seq_lens = nullptr;
+    a.k_sp = a.v_sp = 0;
+    a.table_stride = a.page = a.sq = 0;
+    a.splits = 1;
+    a.total_rows = 0;
+    a.o_part = a.lse_part = nullptr;
     const int64_t n_wg = (int64_t)a.n_qtiles * a.n_hg * a.batch;
     if (n_wg == 0) return hipSuccess;
     if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-    return a.c == 0.f ? launch_dz<D, BN, S, NW, PP, true>(a, n_wg, s)
-                      : launch_dz<D, BN, S, NW, PP, false>(a, n_wg, s);
+    return a.c == 0.f ? launch_dz<D, BN, S, NW, PP, true, false>(a, n_wg, s)
+                      : launch_dz<D, BN, S, NW, PP, false, false>(a, n_wg, s);
+}
+
+// Query tokens per work item of the D = 128 kernel (8 waves of 32 rows over
+// NH heads of a GQA group).
+int paged_item_tokens(int group) {
+    const int nh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
+    return 32 * (8 / nh);
 }
 
 }  // namespace
+
+bool prefill_paged_supported(const DecodeArgs& d) {
+    if (d.dqk != 128 || d.dv != 128 || d.page % 64 != 0) return false;
+    if (d.k_st >= (1 << 22) || d.v_st >= (1 << 22)) return false;
+    return d.sq >= paged_item_tokens(d.hq / d.hkv);
+}
+
+hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
+    constexpr int D = 128, BN = 64, S = 4, NW = 8;
+    PrefillKArgs a;
+    a.q = static_cast<const bf16_t*>(d.q);
+    a.q_st = (int64_t)d.hq * D;
+    a.q_sh = D;
+    a.k = static_cast<const bf16_t*>(d.k_pool);
+    a.k_st = d.k_st;
+    a.k_sh = d.k_sh;
+    a.v = static_cast<const bf16_t*>(d.v_pool);
+    a.v_st = d.v_st;
+    a.v_sh = d.v_sh;
+    a.o = static_cast<bf16_t*>(d.o);
+    a.o_st = (int64_t)d.hq * D;
+    a.o_sh = D;
+    a.cu_q = a.cu_kv = nullptr;
+    a.batch = d.batch;
+    a.hq = d.hq;
+    a.group = d.hq / d.hkv;
+    a.nh = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
+    a.n_hg = d.hq / a.nh;
+    const int tokens = paged_item_tokens(a.group);
+    a.n_qtiles = (d.sq + tokens - 1) / tokens;
+    a.c = (d.scale < 0.f ? -d.scale : d.scale) * kLog2e;
+    a.q_sign = d.scale < 0.f ? 0x80008000u : 0u;
+    a.causal = d.causal;
+    a.lse = d.lse;
+    a.lse_layout = d.lse != nullptr ? 1 : 0;  // [B, s_q, Hq] = token-major
+    a.lse_s_max = 0;
+    a.pt_k = d.pt_k;
+    a.pt_v = d.pt_v;
+    a.seq_lens = d.seq_lens;
+    a.k_sp = d.k_sp;
+    a.v_sp = d.v_sp;
+    a.table_stride = d.table_stride;
+    a.page = d.page;
+    a.sq = d.sq;
+    a.splits = d.splits;
+    a.total_rows = (int64_t)d.batch * d.sq * d.hq;
+    a.o_part = d.o_part;
+    a.lse_part = d.lse_part;
+    const int64_t n_wg = (int64_t)a.n_qtiles * a.n_hg * a.batch * a.splits;
+    if (n_wg == 0) return hipSuccess;
+    if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+    return a.c == 0.f ? launch_dz<D, BN, S, NW, true, true, true>(a, n_wg, s)
+                      : launch_dz<D, BN, S, NW, true, false, true>(a, n_wg, s);
+}
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
     switch (a.dqk) {

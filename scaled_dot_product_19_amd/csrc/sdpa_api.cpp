@@ -186,9 +186,24 @@ int sdpa_decode_paged(const void* q, const void* k_pool, int64_t k_sp, int64_t k
                     page_size);
     if (num_splits < 1 || num_splits > 256)
         return fail(SDPA_ERR_SHAPE, "num_splits=%d outside [1, 256]", num_splits);
-    if ((int64_t)s_q * (h_q / h_kv) > 512)
-        return fail(SDPA_ERR_UNSUPPORTED, "s_q * (h_q / h_kv) = %lld query rows per KV head > 512",
-                    (long long)s_q * (h_q / h_kv));
+    {
+        // more than 512 query rows per KV head: only the chunked-prefill path
+        // (prefill kernel over the page tables) serves them
+        sdpa::DecodeArgs probe{};
+        probe.dqk = d_qk;
+        probe.dv = d_v;
+        probe.page = page_size;
+        probe.k_st = k_st;
+        probe.v_st = v_st;
+        probe.sq = s_q;
+        probe.hq = h_q;
+        probe.hkv = h_kv;
+        if ((int64_t)s_q * (h_q / h_kv) > 512 && !sdpa::prefill_paged_supported(probe))
+            return fail(SDPA_ERR_UNSUPPORTED,
+                        "s_q * (h_q / h_kv) = %lld query rows per KV head > 512 (more need "
+                        "d_qk = d_v = 128 and page_size %% 64 == 0)",
+                        (long long)s_q * (h_q / h_kv));
+    }
     if (causal != 0 && causal != 1) return fail(SDPA_ERR_SHAPE, "causal must be 0 or 1");
     if (table_stride <= 0) return fail(SDPA_ERR_SHAPE, "table_stride must be positive");
     if (max_seqlen_kv < 0 || (int64_t)max_seqlen_kv > (int64_t)table_stride * page_size)

@@ -63,6 +63,12 @@ bool decode_supported(int32_t dqk, int32_t dv);
 bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows);
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t s);
 
+// Chunked prefill over the paged cache (d_qk = d_v = 128, page_size % 64 ==
+// 0, s_q at least one work item of query tokens): the ping-pong prefill
+// kernel of prefill_bf16.hip with K/V tiles addressed through the page tables.
+bool prefill_paged_supported(const DecodeArgs& a);
+hipError_t launch_prefill_paged(const DecodeArgs& a, hipStream_t s);
+
 // Many-row decode (s_q * G > 16 query rows per KV head, d_qk = 576,
 // d_v = 512, page_size % 32 == 0): the MFMA kernel of decode_wide.hip.
 bool decode_wide_supported(const DecodeArgs& a);

@@ -229,6 +229,18 @@ def mla_decode(seed: int = SEED_BASE + 5, batch: int = 32, lo: int = 4096, hi: i
                       % (batch, lo, hi))
 
 
+def chunked_prefill_paged(seed: int = SEED_BASE + 6, batch: int = 2, chunk: int = 1024,
+                          lo: int = 32768, hi: int = 65536, num_splits: int = 4,
+                          poison: bool = False) -> PagedCase:
+    """Chunked prefill over the paged cache bf16: 1024-token query chunks against caches of
+    U[32768, 65536] tokens (the chunk is the cache's last tokens), 32/8 heads, D=128, page 64,
+    bottom-right causal, 4 splits."""
+    return paged_case(seed, batch=batch, sq=chunk, hq=32, hkv=8, d_qk=128, d_v=128, page_size=64,
+                      lo=lo, hi=hi, num_splits=num_splits, causal=True, poison=poison,
+                      name="chunked_prefill_paged_bf16_b%d_c%d_h32x8_d128_p64_%d-%d_s%d"
+                      % (batch, chunk, lo, hi, num_splits))
+
+
 def thd_with_capacity(case: ThdCase, extra_rows: int, fill: float = float("nan")):
     """Copies of Q/K/V with ``extra_rows`` unwritten capacity rows appended (NaN by default)."""
     def pad(t):

@@ -122,6 +122,10 @@ def _decode(**over):
     (dict(ws=ctypes.c_void_p(0x100040)), sdpa.SDPA_ERR_WORKSPACE),
     (dict(ptv=None), sdpa.SDPA_ERR_NULL),
     (dict(hq=1024, hkv=1, sq=1), sdpa.SDPA_ERR_UNSUPPORTED),
+    # > 512 query rows per KV head: only the chunked-prefill path (D 128, page % 64) takes them
+    (dict(sq=1024, page=32), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(sq=1024, dqk=64, dv=64, k_st=8 * 64, v_st=8 * 64, k_sh=64, v_sh=64),
+     sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(k_st=8 * 128 + 1), sdpa.SDPA_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects(over, code):

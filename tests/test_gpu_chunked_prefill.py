@@ -1,0 +1,103 @@
+"""GPU parity of chunked prefill over the paged cache (sdpa_decode_paged with many query
+tokens per sequence) against the fp64 oracle.
+
+A query chunk of s_q tokens is the last s_q tokens of a cache of L tokens (bottom-right
+causal: token i sees keys 0 .. L - s_q + i).  For d_qk = d_v = 128 and page sizes that are
+multiples of 64, once s_q covers a work item of the prefill kernel, the library runs the
+ping-pong prefill kernel with K/V tiles addressed through the two page tables (and fp32
+split partials merged by the LSE combine); these cases pin that path, including shapes the
+few-row decode kernels refuse (more than 512 query rows per KV head).
+"""
+import numpy as np
+import pytest
+import torch
+
+from scaled_dot_product_19_amd import inputs, sdpa
+from tests.helpers import check_lse, check_o, log, oracle_decode, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sdpa.load()
+
+
+def run(pc, splits=None):
+    S = pc.num_splits if splits is None else splits
+    o, l = sdpa.decode_paged(to_dev(pc.q), to_dev(pc.k_pool), to_dev(pc.v_pool),
+                             to_dev(pc.pt_k), to_dev(pc.pt_v), to_dev(pc.seq_lens), pc.max_kv,
+                             pc.scale, pc.causal, num_splits=S)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def parity(pc, sel_rows=None):
+    log("chunked prefill parity: %s lens=%s sq=%d hq=%d hkv=%d page=%d splits=%d causal=%s "
+        "scale=%g" % (pc.name, pc.seq_lens.tolist()[:8], pc.sq, pc.hq, pc.hkv, pc.page_size,
+                      pc.num_splits, pc.causal, pc.scale))
+    o, l = run(pc)
+    rows = pc.batch * pc.sq * pc.hq
+    o_ref, l_ref = oracle_decode(pc, sel_rows=sel_rows)
+    if sel_rows is None:
+        e_o = check_o(o, o_ref)
+        e_l = check_lse(l, l_ref)
+    else:
+        idx = torch.from_numpy(sel_rows).cuda()
+        e_o = check_o(o.reshape(rows, -1)[idx], o_ref)
+        e_l = check_lse(l.reshape(rows)[idx], l_ref)
+    log("  max|dO|=%.3g max|dLSE|=%.3g" % (e_o, e_l))
+    return o, l
+
+
+CASES = [
+    # G = 4, one 64-token item per (sequence, head group); L < s_q leaves early tokens keyless
+    dict(seed=2101, sq=64, hq=8, hkv=2, page=64, lengths=[40, 300, 1000], splits=1, causal=True),
+    # ragged last item (200 = 3 x 64 + 8), page 128, three splits
+    dict(seed=2102, sq=200, hq=8, hkv=2, page=128, lengths=[700, 2100], splits=3, causal=True),
+    # G = 8 (two head groups of 4 per KV head), non-causal, two splits
+    dict(seed=2103, sq=96, hq=16, hkv=2, page=64, lengths=[96, 1500], splits=2, causal=False),
+    # G = 1: items of 256 tokens of one head
+    dict(seed=2104, sq=256, hq=4, hkv=4, page=64, lengths=[900], splits=1, causal=True),
+    # 1200 query rows per KV head (refused by the few-row kernels); more splits than pages
+    # for the short sequence
+    dict(seed=2105, sq=300, hq=8, hkv=2, page=64, lengths=[320, 5000], splits=8, causal=True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c["seed"]) for c in CASES])
+def test_chunked_prefill_paged(case):
+    pc = inputs.paged_case(case["seed"], len(case["lengths"]), case["sq"], case["hq"],
+                           case["hkv"], 128, 128, case["page"], lengths=case["lengths"],
+                           num_splits=case["splits"], causal=case["causal"], poison=True,
+                           name="chunked_%d" % case["seed"])
+    o, l = parity(pc)
+    assert torch.isfinite(o).all()
+
+
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_chunked_prefill_scale_edges(scale):
+    pc = inputs.paged_case(2106, 2, 128, 8, 2, 128, 128, 64, lengths=[128, 700], num_splits=2,
+                           scale=scale, poison=True, name="chunked_scale")
+    parity(pc)
+
+
+def test_chunked_prefill_rows_without_keys_are_empty():
+    # L = 30 < s_q = 64: tokens 0..33 of the chunk see no key (O = 0, LSE = -inf)
+    pc = inputs.paged_case(2107, 1, 64, 8, 2, 128, 128, 64, lengths=[30], num_splits=3,
+                           poison=True, name="chunked_short")
+    o, l = parity(pc)
+    assert torch.all(o[0, :34] == 0)
+    assert torch.all(l[0, :34] == float("-inf"))
+    assert torch.all(torch.isfinite(l[0, 34:]))
+
+
+def test_full_size_chunked_prefill_sampled():
+    pc = inputs.chunked_prefill_paged()
+    log("full-size %s pages=%d" % (pc.name, pc.k_pool.shape[0]))
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 96, 7, must=[0, rows - 1])
+    o, l = parity(pc, sel_rows=sel)
+    assert torch.isfinite(o).all() and torch.isfinite(l).all()
