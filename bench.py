@@ -260,6 +260,76 @@ def run_chunked_prefill(args, torch, inputs, sdpa, dev):
     print(json.dumps(line), flush=True)
 
 
+def time_decode(torch, sdpa, pc, dev, steps, warmup, q=None, kp=None, vp=None):
+    """Average ms of one sdpa_decode_paged call (split kernel + combine) over `steps`."""
+    q = pc.q.to(dev) if q is None else q
+    kp = pc.k_pool.to(dev) if kp is None else kp
+    vp = pc.v_pool.to(dev) if vp is None else vp
+    ptk, ptv, sl = pc.pt_k.to(dev), pc.pt_v.to(dev), pc.seq_lens.to(dev)
+    dv = int(vp.shape[3])
+    o = torch.empty((pc.batch, int(q.shape[1]), pc.hq, dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((pc.batch, int(q.shape[1]), pc.hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, sdpa.decode_workspace_bytes(pc.batch, int(q.shape[1]), pc.hq, dv,
+                                                        pc.num_splits)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sdpa.decode_paged(q, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, pc.causal,
+                          num_splits=pc.num_splits, workspace=ws, out=o, lse=lse, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def run_decode_variant(args, torch, inputs, sdpa, dev):
+    """--mtp-sweep: q_tokens 1..4 over the same 128k caches; --mla-aliased: the MLA-shaped
+    decode with V aliased into the K rows.  K/V bytes count each live cache row once (for the
+    aliased cache: the 576-wide K row, which holds V)."""
+    peak = PEAK_HBM_GBS
+    if args.mtp_sweep:
+        pc = inputs.mtp_decode_d128()
+        kp, vp, q4 = pc.k_pool.to(dev), pc.v_pool.to(dev), pc.q.to(dev)
+        kv, _ = decode_bytes(pc)
+        res = []
+        for qt in (1, 2, 3, 4):
+            ms = time_decode(torch, sdpa, pc, dev, args.steps, args.warmup,
+                             q=q4[:, :qt].contiguous(), kp=kp, vp=vp)
+            res.append({"q_tokens": qt, "ms": round(ms, 4), "kv_gbs": round(kv / ms / 1e6, 1),
+                        "frac_hbm": round(kv / ms / 1e6 / peak, 4)})
+        line = {"metric": "multi-token decode KV GB/s (% HBM peak), q_tokens 1..4",
+                "value": res[0]["kv_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16)",
+                "config": {"workload": pc.name.replace("_q4_", "_q1-4_"), "kv_bytes": kv,
+                           "splits": pc.num_splits},
+                "sweep": res}
+    else:
+        pc = inputs.mla_decode_aliased()
+        kp = pc.k_pool.to(dev)
+        lens = [int(x) for x in pc.seq_lens.tolist()]
+        kv = sum(lens) * pc.hkv * 576 * 2  # one 576-wide row per live token holds K and V
+        ms = time_decode(torch, sdpa, pc, dev, args.steps, args.warmup, kp=kp, vp=kp[..., :512])
+        gbs = kv / ms / 1e6
+        line = {"metric": "aliased-MLA decode KV GB/s (% HBM peak)", "value": round(gbs, 1),
+                "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16)",
+                "config": {"workload": pc.name, "kv_bytes": kv, "splits": pc.num_splits},
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": peak,
+                             "unit": "GB/s", "frac": round(gbs / peak, 4), "traffic": None}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +344,12 @@ def main():
                     help="time only chunked prefill over the paged cache (2 x 1024-token chunks, "
                          "caches U[32768, 65536], 32/8 heads, D=128, page 64) and print its line")
     ap.add_argument("--splits", type=int, default=4, help="num_splits of --chunked-prefill")
+    ap.add_argument("--mtp-sweep", action="store_true",
+                    help="time only multi-token decode, q_tokens 1..4 against 128k caches "
+                         "(batch 4, 32/8 heads, D=128, page 64, 32 splits)")
+    ap.add_argument("--mla-aliased", action="store_true",
+                    help="time only the MLA-shaped decode over an absorbed-MLA cache (V = the "
+                         "first 512 columns of the 576-wide K rows, one page table)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -295,6 +371,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.chunked_prefill:
         run_chunked_prefill(args, torch, inputs, sdpa, dev)
+        return
+    if args.mtp_sweep or args.mla_aliased:
+        run_decode_variant(args, torch, inputs, sdpa, dev)
         return
 
     t0 = time.time()

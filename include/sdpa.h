@@ -163,7 +163,7 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  *         <= table_stride*page_size).
  * o       [batch, s_q, h_q, d_v] dense bf16; lse [batch, s_q, h_q] fp32 or NULL.
  * Supported: dtype SDPA_BF16; (d_qk, d_v) in {(64,64), (128,128), (256,256),
- * (576,512)}; page_size a multiple of 16; 1 <= num_splits <= 256;
+ * (192,128), (576,512)}; page_size a multiple of 16; 1 <= num_splits <= 256;
  * s_q * (h_q/h_kv) <= 512 query rows per KV head, or any larger s_q when
  * d_qk = d_v = 128, page_size is a multiple of 64 and k_st, v_st < 2^22.
  *

@@ -4,7 +4,9 @@
 // chunk's keys through the K and V page tables (independent tables and
 // pools: cuDNN Frontend v1.31.0 Release Notes, "SDPA: paged KV, split-KV, and
 // engine selection"; v1.32.0 Release Notes, "SDPA: wider native forward
-// support", Q/K 576 with V 512) and computes, for the s_q * G query rows that
+// support", Q/K 576 with V 512; the non-absorbed MLA pools d_qk 192 / d_v 128:
+// v1.28.0 release notes, "New: FROST SDPA on Ampere, Ada/Blackwell-consumer,
+// and Rubin", SM120 bullet) and computes, for the s_q * G query rows that
 // share the KV head, the normalized partial O_c and its natural-log LSE_c.
 // With one split the result is final and goes straight to O / LSE.
 //
@@ -233,7 +235,7 @@ hipError_t launch_dims(DecodeKArgs& a, hipStream_t s) {
 
 bool decode_supported(int32_t dqk, int32_t dv) {
     return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 256 && dv == 256) ||
-           (dqk == 576 && dv == 512);
+           (dqk == 192 && dv == 128) || (dqk == 576 && dv == 512);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
@@ -275,6 +277,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
     if (da.dqk == 64) return launch_dims<64, 64>(a, s);
     if (da.dqk == 128) return launch_dims<128, 128>(a, s);
     if (da.dqk == 256) return launch_dims<256, 256>(a, s);
+    if (da.dqk == 192) return launch_dims<192, 128>(a, s);
     if (da.dqk == 576) return launch_dims<576, 512>(a, s);
     return hipErrorInvalidValue;
 }

@@ -179,7 +179,7 @@ int sdpa_decode_paged(const void* q, const void* k_pool, int64_t k_sp, int64_t k
     if (!sdpa::decode_supported(d_qk, d_v))
         return fail(SDPA_ERR_UNSUPPORTED,
                     "paged decode serves (d_qk, d_v) in {(64,64), (128,128), (256,256), "
-                    "(576,512)}; got (%d, %d)",
+                    "(192,128), (576,512)}; got (%d, %d)",
                     d_qk, d_v);
     if (page_size <= 0 || page_size % 16 != 0)
         return fail(SDPA_ERR_UNSUPPORTED, "page_size=%d must be a positive multiple of 16",

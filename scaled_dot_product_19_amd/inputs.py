@@ -17,6 +17,7 @@ split-KV, and engine selection").
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from dataclasses import dataclass, field
 from typing import List, Optional
@@ -239,6 +240,27 @@ def chunked_prefill_paged(seed: int = SEED_BASE + 6, batch: int = 2, chunk: int 
                       lo=lo, hi=hi, num_splits=num_splits, causal=True, poison=poison,
                       name="chunked_prefill_paged_bf16_b%d_c%d_h32x8_d128_p64_%d-%d_s%d"
                       % (batch, chunk, lo, hi, num_splits))
+
+
+def mtp_decode_d128(seed: int = SEED_BASE + 7, batch: int = 4, cache: int = 131072,
+                    q_tokens: int = 4, num_splits: int = 32) -> PagedCase:
+    """Multi-token decode bf16 against 128k caches: batch 4, q_tokens (1 + MTP) query tokens
+    at the end of each cache, 32/8 heads, D=128, page 64, 32 splits."""
+    return paged_case(seed, batch=batch, sq=q_tokens, hq=32, hkv=8, d_qk=128, d_v=128,
+                      page_size=64, lengths=[cache] * batch, num_splits=num_splits, causal=True,
+                      name="mtp_decode_bf16_b%d_q%d_h32x8_d128_p64_%d_s%d"
+                      % (batch, q_tokens, cache, num_splits))
+
+
+def mla_decode_aliased(seed: int = SEED_BASE + 8, batch: int = 32, lo: int = 4096,
+                       hi: int = 16384) -> PagedCase:
+    """The MLA-shaped decode over an absorbed-MLA cache: one 576-wide pool and one page table,
+    V = the first 512 columns of each K row (a strided view of the K pool)."""
+    pc = paged_case(seed, batch=batch, sq=2, hq=128, hkv=1, d_qk=576, d_v=576, page_size=64,
+                    lo=lo, hi=hi, num_splits=16, causal=True,
+                    name="mla_decode_aliased_bf16_b%d_sq2_h128x1_d576-512_p64_%d-%d_s16"
+                    % (batch, lo, hi))
+    return dataclasses.replace(pc, v_pool=pc.k_pool[..., :512], pt_v=pc.pt_k)
 
 
 def thd_with_capacity(case: ThdCase, extra_rows: int, fill: float = float("nan")):

@@ -110,7 +110,8 @@ def _decode(**over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(dtype=1), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(dqk=192, dv=128), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dqk=192, dv=192), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dqk=96, dv=96), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(page=24), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(splits=0), sdpa.SDPA_ERR_SHAPE),
     (dict(splits=257), sdpa.SDPA_ERR_SHAPE),
