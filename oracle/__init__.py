@@ -56,7 +56,7 @@ def _load(path: str | None = None):
     lib.oracle_prefill_thd.restype = ctypes.c_int
     lib.oracle_prefill_thd.argtypes = [
         ctypes.c_int, P, I64, I64, P, I64, I64, P, I64, I64, P, P, I32, I32, I32, I32, I32,
-        D, I32, I64, P, P, P, P, P, I32]
+        D, I32, I32, P, I64, P, P, P, P, P, I32]
     lib.oracle_decode_paged.restype = ctypes.c_int
     lib.oracle_decode_paged.argtypes = [
         ctypes.c_int, P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P, I32, I32, I32,
@@ -114,8 +114,12 @@ def _strides(a: np.ndarray):
 
 
 def prefill_thd(q, k, v, cu_q, cu_kv, scale, causal, hq=None, hkv=None, sel_tok=None,
-                sel_head=None, want_probs=False, nthreads=0):
+                sel_head=None, want_probs=False, nthreads=0, window=0, sinks=None):
     """Packed THD prefill by definition.
+
+    window > 0: left sliding window W (a row sees keys diag - W + 1 .. diag of its
+    bottom-right diagonal position diag); sinks: Hq per-head sink logits (same units as
+    scale * q.k) that join the softmax denominator and carry no value.
 
     q [Tq, Hq, Dqk], k [Tk, Hkv, Dqk], v [Tk, Hkv, Dv]; last axis contiguous,
     any token/head strides.  cu_q/cu_kv int32 [B+1].
@@ -149,10 +153,15 @@ def prefill_thd(q, k, v, cu_q, cu_kv, scale, causal, hq=None, hkv=None, sel_tok=
     if want_probs:
         probs = np.zeros((o.shape[0], max_lk), np.float64)
     qs, ks, vs = _strides(q), _strides(k), _strides(v)
+    sk = None
+    if sinks is not None:
+        sk = np.ascontiguousarray(sinks, dtype=np.float64)
+        assert sk.shape == (hq_,)
     rc = lib.oracle_prefill_thd(dt, _ptr(q), qs[0], qs[1], _ptr(k), ks[0], ks[1], _ptr(v),
                                 vs[0], vs[1], _ptr(cu_q), _ptr(cu_kv), batch, hq_, hkv_, dqk,
-                                dv, float(scale), int(bool(causal)), n_sel, _ptr(st),
-                                _ptr(sh), _ptr(o), _ptr(lse), _ptr(probs), int(nthreads))
+                                dv, float(scale), int(bool(causal)), int(window), _ptr(sk),
+                                n_sel, _ptr(st), _ptr(sh), _ptr(o), _ptr(lse), _ptr(probs),
+                                int(nthreads))
     if rc != 0:
         raise ValueError("oracle_prefill_thd rejected its arguments (rc=%d)" % rc)
     if sel_tok is None:

@@ -13,12 +13,17 @@
  *   For a query row q_i (head h) and the keys k_j / values v_j of KV head
  *   kvh = h / G, G = Hq / Hkv:
  *     s_ij   = scale * <q_i, k_j>                         (fp64)
- *     V_i    = { j : j < Lk  and (not causal or j <= i + Lk - Lq) }
- *     m      = max_{j in V_i} s_ij
- *     l      = sum_{j in V_i} exp(s_ij - m)
+ *     V_i    = { j : j < Lk  and (not causal or j <= i + Lk - Lq)
+ *                     and (W <= 0 or j >= i + Lk - Lq - W + 1) }
+ *     m      = max of { s_ij : j in V_i } and, with a sink, sink_h
+ *     l      = sum_{j in V_i} exp(s_ij - m)  [+ exp(sink_h - m)]
  *     O_i    = sum_{j in V_i} exp(s_ij - m) * v_j / l
  *     LSE_i  = m + ln(l)                                   (natural log)
- *     V_i empty  ->  O_i = 0, LSE_i = -inf.
+ *     V_i empty and no sink  ->  O_i = 0, LSE_i = -inf.
+ *   W is the left sliding window (prefill only): a row sees at most the W
+ *   keys that end at its bottom-right diagonal position.  sink_h is a
+ *   per-head logit in the units of s_ij that joins the softmax denominator
+ *   and carries no value.
  *
  * Passages followed:
  *   - natural-log FP32 Stats "max + ln(sum_exp)": cuDNN Frontend v1.30.0
@@ -43,6 +48,13 @@
  *   - split-KV partials merged by LSE: v1.31.0 "SDPA: paged KV, split-KV, and
  *     engine selection"; the merge formula is not printed on the pages, the
  *     textbook log-sum-exp merge is taken (oracle_combine below).
+ *   - left sliding windows: v1.32.0 Release Notes, "SDPA: backward and
+ *     numerical fixes" (left sliding windows for dense D64/D128); attention
+ *     sinks: v1.32.0 "SDPA: wider native forward support" (masks, sinks) and
+ *     v1.30.0 Release Notes (sinks at S_q == 1 with paged KV and sliding
+ *     window).  The pages print no formula for either; the readings taken
+ *     are the ones stated above (window counted from the diagonal key
+ *     inclusive; sink = an extra logit in the denominator only).
  *
  * Inputs are read as bf16 (raw 16-bit patterns, widened exactly: a bf16 is
  * the top half of an IEEE binary32) or as fp32, then widened to double.
@@ -75,20 +87,22 @@ static double load_elem(const void* base, int dtype, int64_t idx) {
  */
 static void attend_row(const double* q, int dqk, int dv, const void* k, const void* v,
                        const int64_t* koff, const int64_t* voff, int64_t n, int dtype,
-                       double scale, double* s, double* o, double* lse, double* p_out) {
-    if (n == 0) {
+                       double scale, double sink, double* s, double* o, double* lse,
+                       double* p_out) {
+    /* sink = -inf: no sink */
+    if (n == 0 && sink == -INFINITY) {
         for (int d = 0; d < dv; ++d) o[d] = 0.0;
         *lse = -INFINITY;
         return;
     }
-    double m = -INFINITY;
+    double m = sink;
     for (int64_t j = 0; j < n; ++j) {
         double dot = 0.0;
         for (int d = 0; d < dqk; ++d) dot += q[d] * load_elem(k, dtype, koff[j] + d);
         s[j] = scale * dot;
         if (s[j] > m) m = s[j];
     }
-    double l = 0.0;
+    double l = sink == -INFINITY ? 0.0 : exp(sink - m);
     for (int64_t j = 0; j < n; ++j) {
         s[j] = exp(s[j] - m);
         l += s[j];
@@ -166,6 +180,8 @@ typedef struct {
     const int32_t* sel_head;
     double *o, *lse, *p_out;
     int64_t max_lk;
+    int32_t window;        /* left window W (<= 0: none) */
+    const double* sinks;   /* [hq] sink logits, or NULL */
 } prefill_ctx;
 
 /* Sequence b that owns packed query row t: cu_q[b] <= t < cu_q[b+1]. */
@@ -198,13 +214,14 @@ static void prefill_unit(void* vctx, int64_t unit, double* scratch) {
     int64_t lq = c->cu_q[b + 1] - c->cu_q[b];
     int64_t lk = c->cu_kv[b + 1] - c->cu_kv[b];
     int32_t kvh = h / (c->hq / c->hkv);
-    /* visible keys: j < lk, and j <= i + lk - lq when causal */
-    int64_t n = lk;
-    if (c->causal) {
-        int64_t last = i + lk - lq;  /* last visible key index */
-        n = last + 1 < lk ? last + 1 : lk;
-        if (n < 0) n = 0;
-    }
+    /* visible keys j0 <= j < j1: j < lk; j <= i + lk - lq when causal;
+       j >= i + lk - lq - W + 1 with a left window W */
+    const int64_t diag = i + lk - lq;  /* the row's bottom-right diagonal key */
+    int64_t j1 = lk;
+    if (c->causal && diag + 1 < j1) j1 = diag + 1;
+    int64_t j0 = 0;
+    if (c->window > 0 && diag - c->window + 1 > j0) j0 = diag - c->window + 1;
+    int64_t n = j1 > j0 ? j1 - j0 : 0;
     double* qrow = scratch;
     int64_t* koff = (int64_t*)(scratch + c->dqk);
     int64_t* voff = koff + c->max_lk;
@@ -212,16 +229,19 @@ static void prefill_unit(void* vctx, int64_t unit, double* scratch) {
     for (int d = 0; d < c->dqk; ++d)
         qrow[d] = load_elem(c->q, c->dtype, t * c->q_st + (int64_t)h * c->q_sh + d);
     for (int64_t j = 0; j < n; ++j) {
-        koff[j] = (c->cu_kv[b] + j) * c->k_st + (int64_t)kvh * c->k_sh;
-        voff[j] = (c->cu_kv[b] + j) * c->v_st + (int64_t)kvh * c->v_sh;
+        koff[j] = (c->cu_kv[b] + j0 + j) * c->k_st + (int64_t)kvh * c->k_sh;
+        voff[j] = (c->cu_kv[b] + j0 + j) * c->v_st + (int64_t)kvh * c->v_sh;
     }
     double* p_out = NULL;
+    double* p_row = NULL;
     if (c->p_out) { /* probabilities for every key of the sequence, 0 when masked */
         p_out = c->p_out + unit * c->max_lk;
         for (int64_t j = 0; j < c->max_lk; ++j) p_out[j] = 0.0;
+        p_row = p_out + j0;
     }
-    attend_row(qrow, c->dqk, c->dv, c->k, c->v, koff, voff, n, c->dtype, c->scale, s, o, lse,
-               p_out);
+    const double sink = c->sinks ? c->sinks[h] : -INFINITY;
+    attend_row(qrow, c->dqk, c->dv, c->k, c->v, koff, voff, n, c->dtype, c->scale, sink, s, o,
+               lse, p_row);
 }
 
 /*
@@ -234,14 +254,16 @@ static void prefill_unit(void* vctx, int64_t unit, double* scratch) {
  * [Tq*Hq].  n_sel >= 0: only the listed rows (sel_tok[r], sel_head[r]); o is
  * [n_sel, Dv], lse [n_sel].  p_out (optional, may be NULL) receives, per
  * computed row, max_lk softmax weights (key index j of the row's sequence).
- * Returns 0, or -1 on a bad argument / failed allocation.
+ * window > 0 is the left sliding window W; sinks (optional) holds Hq sink
+ * logits.  Returns 0, or -1 on a bad argument / failed allocation.
  */
 int oracle_prefill_thd(int dtype, const void* q, int64_t q_st, int64_t q_sh, const void* k,
                        int64_t k_st, int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh,
                        const int32_t* cu_q, const int32_t* cu_kv, int32_t batch, int32_t hq,
                        int32_t hkv, int32_t dqk, int32_t dv, double scale, int32_t causal,
-                       int64_t n_sel, const int64_t* sel_tok, const int32_t* sel_head,
-                       double* o, double* lse, double* p_out, int32_t nthreads) {
+                       int32_t window, const double* sinks, int64_t n_sel,
+                       const int64_t* sel_tok, const int32_t* sel_head, double* o, double* lse,
+                       double* p_out, int32_t nthreads) {
     if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || dqk <= 0 || dv <= 0) return -1;
     int64_t max_lk = 1;
     for (int32_t b = 0; b < batch; ++b) {
@@ -251,7 +273,7 @@ int oracle_prefill_thd(int dtype, const void* q, int64_t q_st, int64_t q_sh, con
     }
     prefill_ctx c = {dtype, q, k, v, q_st, q_sh, k_st, k_sh, v_st, v_sh, cu_q, cu_kv, batch,
                      hq, hkv, dqk, dv, causal, scale, n_sel, sel_tok, sel_head, o, lse, p_out,
-                     max_lk};
+                     max_lk, window, sinks};
     int64_t tq = batch > 0 ? cu_q[batch] : 0;
     int64_t n_units = n_sel < 0 ? tq * hq : n_sel;
     size_t scratch = (size_t)dqk + 3 * (size_t)max_lk;
@@ -325,7 +347,7 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
             koff[n] = kpage * c->k_sp + slot * c->k_st + (int64_t)kvh * c->k_sh;
             voff[n] = vpage * c->v_sp + slot * c->v_st + (int64_t)kvh * c->v_sh;
         }
-        attend_row(qrow, c->dqk, c->dv, c->kp, c->vp, koff, voff, n, c->dtype, c->scale, s,
+        attend_row(qrow, c->dqk, c->dv, c->kp, c->vp, koff, voff, n, c->dtype, c->scale, -INFINITY, s,
                    ol + (size_t)sp * c->dv, ll + sp, NULL);
         if (ll[sp] > m_all) m_all = ll[sp];
         if (c->o_part) {

@@ -20,14 +20,24 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "sdpa_oracle.c")
 MUTATIONS = [
     ("gqa_head_mapping_mod", "int32_t kvh = h / (c->hq / c->hkv);\n    /* visible",
      "int32_t kvh = h % c->hkv;\n    /* visible"),
-    ("causal_top_left", "int64_t last = i + lk - lq;", "int64_t last = i;"),
-    ("causal_off_by_one", "n = last + 1 < lk ? last + 1 : lk;", "n = last < lk ? last : lk;"),
+    ("causal_top_left", "const int64_t diag = i + lk - lq;", "const int64_t diag = i;"),
+    ("causal_off_by_one", "if (c->causal && diag + 1 < j1) j1 = diag + 1;",
+     "if (c->causal && diag < j1) j1 = diag;"),
     ("lse_base_two", "*lse = m + log(l);", "*lse = m + log2(l);"),
     ("scale_dropped", "s[j] = scale * dot;", "s[j] = dot;"),
     ("exp_sign", "s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
     ("normalizer_dropped", "for (int d = 0; d < dv; ++d) o[d] /= l;", ""),
-    ("k_strides_swapped", "koff[j] = (c->cu_kv[b] + j) * c->k_st + (int64_t)kvh * c->k_sh;",
-     "koff[j] = (c->cu_kv[b] + j) * c->k_sh + (int64_t)kvh * c->k_st;"),
+    ("k_strides_swapped", "koff[j] = (c->cu_kv[b] + j0 + j) * c->k_st + (int64_t)kvh * c->k_sh;",
+     "koff[j] = (c->cu_kv[b] + j0 + j) * c->k_sh + (int64_t)kvh * c->k_st;"),
+    ("window_one_too_wide", "if (c->window > 0 && diag - c->window + 1 > j0) j0 = diag - c->window + 1;",
+     "if (c->window > 0 && diag - c->window > j0) j0 = diag - c->window;"),
+    ("window_ignored", "if (c->window > 0 && diag - c->window + 1 > j0) j0 = diag - c->window + 1;",
+     ""),
+    ("window_keys_not_shifted", "koff[j] = (c->cu_kv[b] + j0 + j) * c->k_st",
+     "koff[j] = (c->cu_kv[b] + j) * c->k_st"),
+    ("sink_dropped_from_denominator", "double l = sink == -INFINITY ? 0.0 : exp(sink - m);",
+     "double l = 0.0;"),
+    ("sink_row_without_keys_empty", "if (n == 0 && sink == -INFINITY) {", "if (n == 0) {"),
     ("v_uses_k_table", "int64_t vpage = c->pt_v[", "int64_t vpage = c->pt_k["),
     ("merge_weight_uses_max", "double w = exp(ll[sp] - L_all);",
      "double w = exp(ll[sp] - m_all);"),
@@ -56,6 +66,11 @@ def _pin_suite():
         ("split_merge", lambda: pins.test_split_merge_equals_unsplit(3)),
         ("combine_closed", pins.test_combine_closed_forms),
         ("decode_causal", pins.test_decode_causal_two_tokens),
+        ("window_brute", lambda: pins.test_window_and_sinks_brute_force_vs_torch(3, True, False)),
+        ("window_one", pins.test_window_one_sees_only_the_diagonal_key),
+        ("sink_brute", lambda: pins.test_window_and_sinks_brute_force_vs_torch(40, False, True)),
+        ("sink_closed", pins.test_sink_closed_form_single_key),
+        ("sink_empty_rows", pins.test_rows_without_keys_take_the_sink_as_lse),
     ]
     failed = []
     for name, fn in checks:

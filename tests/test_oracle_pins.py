@@ -32,8 +32,11 @@ def _torch64(t):
     return t.to(torch.float64)
 
 
-def _brute(case: inputs.ThdCase):
-    """Independent per-sequence reference: torch fp64 SDPA + explicit mask."""
+def _brute(case: inputs.ThdCase, window: int = 0, sinks=None):
+    """Independent per-sequence reference: torch fp64 SDPA + explicit mask.
+
+    window > 0 adds the left bound j >= diag - window + 1 to the mask; sinks (per-head
+    logits) are an extra logit column that joins the softmax and multiplies a zero value."""
     G = case.hq // case.hkv
     outs, lses = [], []
     for b in range(case.batch):
@@ -48,7 +51,19 @@ def _brute(case: inputs.ThdCase):
         mask = torch.ones(lq, lk, dtype=torch.bool)
         if case.causal:
             mask = j <= i + (lk - lq)                                      # bottom-right
+        if window > 0:
+            mask = mask & (j >= i + (lk - lq) - window + 1)
         logits = case.scale * torch.matmul(q, k.transpose(1, 2))
+        if sinks is not None:
+            aug = torch.cat([logits.masked_fill(~mask, float("-inf")),
+                             torch.as_tensor(sinks, dtype=torch.float64).view(-1, 1, 1)
+                             .expand(-1, lq, 1)], dim=-1)                  # [Hq, Lq, Lk + 1]
+            lse = torch.logsumexp(aug, dim=-1)
+            p = torch.softmax(aug, dim=-1)[..., :lk]                       # sink's weight dropped
+            o = torch.matmul(p, v)
+            outs.append(o.permute(1, 0, 2))
+            lses.append(lse.permute(1, 0))
+            continue
         lse = torch.logsumexp(logits.masked_fill(~mask, float("-inf")), dim=-1)  # [Hq, Lq]
         if lk > 0 and lq > 0:
             o = torch.nn.functional.scaled_dot_product_attention(
@@ -283,3 +298,68 @@ def test_decode_causal_two_tokens():
     # L=1 < sq=2: token 0 sees nothing, token 1 sees key 0 only
     assert np.all(lse[1, 0] == -np.inf) and np.all(o[1, 0] == 0.0)
     assert np.array_equal(o[1, 1, 0], v[20, 0].double().numpy())
+
+
+# ---- left sliding window and attention sinks ---------------------------------
+
+@pytest.mark.parametrize("window", [1, 3, 40])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("with_sinks", [False, True])
+def test_window_and_sinks_brute_force_vs_torch(window, causal, with_sinks):
+    case = inputs.thd_case(7, hq=4, hkv=2, d_qk=64, lengths=[9, 70, 33],
+                           lengths_kv=[12, 70, 100], causal=causal, dtype=torch.float32)
+    sinks = np.array([0.3, -2.0, 5.0, 1.1]) if with_sinks else None
+    o, lse = _run_oracle(case, window=window, sinks=sinks)
+    o_b, l_b = _brute(case, window=window, sinks=sinks)
+    np.testing.assert_allclose(o, o_b, rtol=1e-10, atol=1e-12)
+    fin = np.isfinite(l_b)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], l_b[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_window_one_sees_only_the_diagonal_key():
+    case = inputs.thd_case(8, hq=2, hkv=1, d_qk=64, lengths=[6], lengths_kv=[10],
+                           dtype=torch.float32)
+    o, lse = _run_oracle(case, window=1)
+    q, k, v = (t.double().numpy() for t in (case.q, case.k, case.v))
+    for i in range(6):
+        diag = i + 4
+        for h in range(2):
+            np.testing.assert_array_equal(o[i, h], v[diag, 0])
+            assert lse[i, h] == pytest.approx(case.scale * float(q[i, h] @ k[diag, 0]), abs=1e-12)
+
+
+def test_window_covering_every_key_is_no_window_bitwise():
+    case = inputs.thd_case(9, hq=4, hkv=2, d_qk=64, lengths=[33, 5], lengths_kv=[40, 5])
+    o0, l0 = _run_oracle(case)
+    o1, l1 = _run_oracle(case, window=41)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_sink_minus_inf_is_no_sink_bitwise():
+    case = inputs.thd_case(10, hq=4, hkv=1, d_qk=64, lengths=[20, 3])
+    o0, l0 = _run_oracle(case)
+    o1, l1 = _run_oracle(case, sinks=np.full(4, -np.inf))
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_sink_closed_form_single_key():
+    # one query, one key: p = e^s / (e^s + e^sink), O = p v, LSE = ln(e^s + e^sink)
+    case = inputs.thd_case(11, hq=1, hkv=1, d_qk=64, lengths=[1], dtype=torch.float32)
+    sink = 0.7
+    o, lse = _run_oracle(case, sinks=np.array([sink]))
+    q, k, v = (t.double().numpy()[0, 0] for t in (case.q, case.k, case.v))
+    s_ = case.scale * float(q @ k)
+    p = math.exp(s_) / (math.exp(s_) + math.exp(sink))
+    np.testing.assert_allclose(o[0, 0], p * v, rtol=1e-13, atol=1e-15)
+    assert lse[0, 0] == pytest.approx(math.log(math.exp(s_) + math.exp(sink)), abs=1e-13)
+
+
+def test_rows_without_keys_take_the_sink_as_lse():
+    # lk = 2 < lq = 5 (causal): rows 0..2 see no key -> O = 0, LSE = sink_h
+    case = inputs.thd_case(12, hq=2, hkv=1, d_qk=64, lengths=[5], lengths_kv=[2])
+    sinks = np.array([-1.5, 2.25])
+    o, lse = _run_oracle(case, sinks=sinks)
+    assert np.all(o[:3] == 0.0)
+    assert np.array_equal(lse[:3], np.tile(sinks, (3, 1)))
+    assert np.all(np.isfinite(lse[3:]))
