@@ -78,9 +78,13 @@ typedef enum {
 typedef enum {
     SDPA_LSE_NONE = 0,    /* no Stats written (lse may be NULL)                         */
     SDPA_LSE_PACKED = 1,  /* token-major packed rows: lse[(cu_seqlens_q[b] + i) * h_q + h] */
-    SDPA_LSE_PADDED = 2   /* per-batch padded rows: lse[(b * lse_s_max + i) * h_q + h];
+    SDPA_LSE_PADDED = 2,  /* per-batch padded rows: lse[(b * lse_s_max + i) * h_q + h];
                              the library first fills all batch*lse_s_max*h_q entries with
                              -inf on `stream`, so rows i >= Lq_b read -inf           */
+    SDPA_LSE_HEAD_MAJOR = 3 /* head-major rows [h_q, total]: lse[h * lse_s_max +
+                             cu_seqlens_q[b] + i]; lse_s_max is the per-head stride,
+                             at least cu_seqlens_q[batch] (bf16 prefill only; v1.28.0
+                             release notes, Bug Fixes, head-major stats)             */
 } sdpa_lse_layout_t;
 
 /*
@@ -104,7 +108,8 @@ typedef enum {
  * max_seqlen_q / max_seqlen_kv: host-known upper bounds of Lq_b / Lk_b (they
  *   size the grid; a sequence longer than its bound is only partly computed).
  * causal: 0 or 1 (bottom-right).  lse_layout: sdpa_lse_layout_t; lse_s_max:
- *   padded row capacity (>= max_seqlen_q) for SDPA_LSE_PADDED, else ignored.
+ *   padded row capacity (>= max_seqlen_q) for SDPA_LSE_PADDED, the per-head
+ *   stride for SDPA_LSE_HEAD_MAJOR, else ignored.
  * dtype: SDPA_BF16 (d_qk == d_v in {64, 128, 256}; rows 16-byte aligned: base
  *   pointers 16-byte aligned and strides multiples of 8) or SDPA_FP32
  *   (d_qk, d_v <= 256; 4-byte aligned).
@@ -121,6 +126,36 @@ int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh,
                      float scale, int32_t causal,
                      float* lse, int32_t lse_layout, int32_t lse_s_max,
                      int32_t dtype, void* stream);
+
+/*
+ * Packed THD ragged prefill with the mask and Stats variants (bf16 only).
+ * Same arguments and layouts as sdpa_prefill_thd, plus:
+ * window_left: 0 = none; W > 0 = left sliding window: row i of sequence b
+ *   sees only keys j >= i + Lk_b - Lq_b - W + 1 (the W keys ending at its
+ *   bottom-right diagonal position when causal).  Left sliding windows:
+ *   v1.32.0 Release Notes, "SDPA: backward and numerical fixes".  Negative
+ *   values are rejected (SDPA_ERR_SHAPE).
+ * sinks: NULL, or device fp32 [h_q] attention-sink logits, in the units of
+ *   scale*<q,k>: head h's sink joins the softmax denominator of every row
+ *   and carries no value, so O = sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{sink_h})
+ *   and LSE = ln(sum_j e^{s_j} + e^{sink_h}); a row with no visible key gets
+ *   O = 0, LSE = sink_h (sinks: v1.32.0 "SDPA: wider native forward support",
+ *   v1.30.0 Release Notes, sinks with paged KV and sliding window; the pages
+ *   print no formula, the denominator-only reading is taken).
+ * stats_log2: 0 = natural-log LSE; 1 = base 2, LSE2 = max + log2(sum_exp) =
+ *   LSE * log2(e) (v1.30.0 Release Notes, "New: stats_use_log2 -- LSE in
+ *   base 2").
+ */
+int sdpa_prefill_thd_ex(const void* q, int64_t q_st, int64_t q_sh,
+                        const void* k, int64_t k_st, int64_t k_sh,
+                        const void* v, int64_t v_st, int64_t v_sh,
+                        void* o, int64_t o_st, int64_t o_sh,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                        int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                        int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v,
+                        float scale, int32_t causal, int32_t window_left, const float* sinks,
+                        float* lse, int32_t lse_layout, int32_t lse_s_max, int32_t stats_log2,
+                        int32_t dtype, void* stream);
 
 /*
  * Bytes of caller workspace sdpa_decode_paged needs for these extents

@@ -64,7 +64,10 @@ struct PrefillKArgs {
     uint32_t q_sign;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
     int32_t causal;
     float* lse;
-    int32_t lse_layout, lse_s_max;
+    int32_t lse_layout, lse_s_max;  // layout 3 (head-major): lse_s_max = per-head stride
+    int32_t window;                 // left sliding window (0: none)
+    const float* sinks;             // [hq] sink logits (natural-log units) or nullptr
+    int32_t stats_log2;             // LSE in base 2
     int32_t slot;    // work-queue counters used by this launch
     // paged mode (chunked prefill over a paged cache; see launch_prefill_paged):
     // Q [batch, sq, hq, D] dense, K/V rows through independent page tables,
@@ -188,16 +191,32 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     const bool row_ok = i < lq;
     const int shift = lk - lq;  // bottom-right diagonal offset
 
+    // left sliding window: row i sees keys >= i + shift - W + 1, so the item
+    // starts at the first tile holding a key of its first row's window
+    if (a.window > 0) lo = max(lo, ((max(0, q0 + shift - a.window + 1)) / BN) * BN);
     // key extents within [lo, hi): the work-group's, this wave's, and this lane's
     const int last_wg = min(q0 + 32 * nt, lq) - 1;
     const int kv_end = a.causal ? max(lo, min(hi, last_wg + shift + 1)) : hi;
-    int kv_end_w = lo, nomask_end = lo;
+    int kv_end_w = lo, nomask_end = lo, kv_beg_w = lo;
     if (i0 < lq) {
+        // with a window, tiles that end before the wave's first visible key are skipped
+        if (a.window > 0) kv_beg_w = max(lo, i0 + shift - a.window + 1);
         const int last_w = min(i0 + 32, lq) - 1;
         kv_end_w = a.causal ? max(lo, min(hi, last_w + shift + 1)) : hi;
         nomask_end = a.causal ? max(lo, min(hi, i0 + shift + 1)) : hi;
     }
     const int lim = a.causal ? min(hi - 1, i + shift) : hi - 1;
+    // first visible key of this lane's row, and the largest of the wave's rows:
+    // tiles starting below it need the lower mask
+    const int first = i + shift - a.window + 1;  // used only with a window
+    const int first_w_max = a.window > 0 ? min(i0 + 31, lq - 1) + shift - a.window + 1 : INT32_MIN;
+    // the tile starting at key0 holds keys of this wave, and needs the mask
+    auto sees = [&](int key0) __attribute__((always_inline)) {
+        return key0 < kv_end_w && key0 + BN > kv_beg_w;
+    };
+    auto masked = [&](int key0) __attribute__((always_inline)) {
+        return key0 + BN > nomask_end || key0 < first_w_max;
+    };
     const int n_tiles = (kv_end - lo + BN - 1) / BN;  // tile t: keys lo + t BN ..
 
     // ---- LDS DMA of the K/V tiles -------------------------------------------
@@ -368,12 +387,14 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
             if (need_mask) {
-                // key = key0 + 4 half + (compile-time offset); masked iff offset > dl
+                // key = key0 + 4 half + (compile-time offset); masked iff the
+                // offset is above dl (causal / end) or below dl_lo (window)
                 const int dl = lim - key0 - 4 * half;
+                const int dl_lo = a.window > 0 ? first - key0 - 4 * half : -1;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-                    s[kb][r] = off > dl ? neg_inf() : s[kb][r];
+                    s[kb][r] = (off > dl || off < dl_lo) ? neg_inf() : s[kb][r];
                 }
             }
 #pragma unroll
@@ -497,10 +518,10 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             page_ids_ready();
             issue(t + S - 1);
             const int key0 = lo + t * BN;
-            if (key0 < kv_end_w) {
+            if (sees(key0)) {
                 const char* st = lds + decltype(stage)::value * C::STAGE_B;
                 qk(st, s);
-                softmax(s, pb, key0, key0 + BN > nomask_end);
+                softmax(s, pb, key0, masked(key0));
                 pv(st, pb);
             }
             wait_vmcnt<PER_TILE * (S - 2)>();
@@ -540,8 +561,8 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         auto v_phase = [&](int t) __attribute__((always_inline)) {
             page_ids(t + S - 1);  // issued by M(t + 1)
             const int key0 = lo + t * BN;
-            if (key0 < kv_end_w) {
-                softmax(s, pb, key0, key0 + BN > nomask_end);
+            if (sees(key0)) {
+                softmax(s, pb, key0, masked(key0));
             } else {
 #pragma unroll
                 for (int j = 0; j < BN / 16; ++j) pb[j] = bf16x8{};
@@ -582,9 +603,9 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // epilogue: O = O^T / l written as bf16, LSE = ln2 * (m + log2 l); a
     // split of a paged call writes its normalized fp32 partial and LSE_c
     // (-inf and zeros when it sees no key of the row)
-    const float l_tot = half_sum(l);
+    float l_tot = half_sum(l);
     if (!row_ok) return;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if constexpr (PAGED) {
         if (a.splits > 1) {
             const int64_t grow = (int64_t)(q_beg + i) * a.hq + h;
@@ -604,6 +625,19 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             return;
         }
     }
+    if (a.sinks != nullptr) {
+        // head h's sink: one more logit (log2 units below) in the denominator
+        // only.  m2 = max(m, sink); O^T stays relative to m and is scaled by
+        // alpha / l_tot; a row without keys (l = 0) keeps O = 0, LSE = sink.
+        const float sk = a.sinks[h] * kLog2e;
+        const float m2 = max(m, sk);
+        if (m2 != neg_inf()) {
+            const float alpha = fast_exp2(m - m2);  // 0 when m = -inf
+            l_tot = l_tot * alpha + fast_exp2(sk - m2);
+            inv = alpha / l_tot;
+            m = m2;
+        }
+    }
     bf16_t* orow = a.o + (int64_t)(q_beg + i) * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
@@ -617,11 +651,15 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         }
     }
     if (a.lse != nullptr && half == 0) {
-        const float lse = l_tot > 0.f ? kLn2 * (m + fast_log2(l_tot)) : neg_inf();
+        // natural log, or base 2 (the running statistics are already log2)
+        const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
+        const float lse = a.stats_log2 ? lse2 : kLn2 * lse2;
         if (a.lse_layout == 1) {
             a.lse[(int64_t)(q_beg + i) * a.hq + h] = lse;
         } else if (a.lse_layout == 2 && i < a.lse_s_max) {
             a.lse[((int64_t)b * a.lse_s_max + i) * a.hq + h] = lse;
+        } else if (a.lse_layout == 3) {
+            a.lse[(int64_t)h * a.lse_s_max + q_beg + i] = lse;
         }
     }
 }
@@ -747,6 +785,11 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     a.lse = pa.lse;
     a.lse_layout = pa.lse_layout;
     a.lse_s_max = pa.lse_s_max;
+    // a window of 2^30 keys covers every key of any sequence the int32
+    // offsets can describe; the clamp keeps i + shift - W + 1 in range
+    a.window = pa.window > 0 ? min(pa.window, 1 << 30) : 0;
+    a.sinks = pa.sinks;
+    a.stats_log2 = pa.stats_log2;
     a.pt_k = a.pt_v = a.seq_lens = nullptr;
     a.k_sp = a.v_sp = 0;
     a.table_stride = a.page = a.sq = 0;
@@ -804,6 +847,9 @@ hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
     a.lse = d.lse;
     a.lse_layout = d.lse != nullptr ? 1 : 0;  // [B, s_q, Hq] = token-major
     a.lse_s_max = 0;
+    a.window = 0;
+    a.sinks = nullptr;
+    a.stats_log2 = 0;
     a.pt_k = d.pt_k;
     a.pt_v = d.pt_v;
     a.seq_lens = d.seq_lens;

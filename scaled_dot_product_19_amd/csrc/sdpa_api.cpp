@@ -61,13 +61,14 @@ const char* sdpa_status_string(int status) {
 
 const char* sdpa_last_error_detail(void) { return g_detail; }
 
-int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
-                     int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, void* o,
-                     int64_t o_st, int64_t o_sh, const int32_t* cu_seqlens_q,
-                     const int32_t* cu_seqlens_kv, int32_t batch, int32_t max_seqlen_q,
-                     int32_t max_seqlen_kv, int32_t h_q, int32_t h_kv, int32_t d_qk,
-                     int32_t d_v, float scale, int32_t causal, float* lse, int32_t lse_layout,
-                     int32_t lse_s_max, int32_t dtype, void* stream) {
+static int prefill_impl(const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                        int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, void* o,
+                        int64_t o_st, int64_t o_sh, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_kv, int32_t batch, int32_t max_seqlen_q,
+                        int32_t max_seqlen_kv, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                        int32_t d_v, float scale, int32_t causal, float* lse, int32_t lse_layout,
+                        int32_t lse_s_max, int32_t window, const float* sinks, int32_t stats_log2,
+                        int32_t dtype, void* stream) {
     if (batch < 0 || batch > 65535) return fail(SDPA_ERR_SHAPE, "batch=%d outside [0, 65535]", batch);
     if (h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0)
         return fail(SDPA_ERR_SHAPE, "h_q=%d must be a positive multiple of h_kv=%d", h_q, h_kv);
@@ -77,8 +78,16 @@ int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh, const void* k, i
         return fail(SDPA_ERR_SHAPE, "max_seqlen_q/kv must be >= 0");
     if (causal != 0 && causal != 1) return fail(SDPA_ERR_SHAPE, "causal must be 0 or 1");
     if (lse_layout != SDPA_LSE_NONE && lse_layout != SDPA_LSE_PACKED &&
-        lse_layout != SDPA_LSE_PADDED)
+        lse_layout != SDPA_LSE_PADDED && lse_layout != SDPA_LSE_HEAD_MAJOR)
         return fail(SDPA_ERR_LSE_LAYOUT, "unknown lse_layout %d", lse_layout);
+    if (lse_layout == SDPA_LSE_HEAD_MAJOR && lse_s_max <= 0)
+        return fail(SDPA_ERR_LSE_LAYOUT, "head-major LSE needs its per-head stride in lse_s_max");
+    if (stats_log2 != 0 && stats_log2 != 1) return fail(SDPA_ERR_SHAPE, "stats_log2 must be 0 or 1");
+    const bool variant = window > 0 || sinks != nullptr || stats_log2 != 0 ||
+                         lse_layout == SDPA_LSE_HEAD_MAJOR;
+    if (variant && dtype != SDPA_BF16)
+        return fail(SDPA_ERR_UNSUPPORTED,
+                    "windows, sinks, base-2 and head-major LSE are served for bf16 only");
     if (lse_layout != SDPA_LSE_NONE && lse == nullptr)
         return fail(SDPA_ERR_NULL, "lse is NULL but lse_layout=%d requests Stats", lse_layout);
     if (lse_layout == SDPA_LSE_PADDED && lse_s_max < max_seqlen_q)
@@ -113,7 +122,8 @@ int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh, const void* k, i
         return fail(SDPA_ERR_NULL, "q/k/v/o/cu_seqlens_q/cu_seqlens_kv must be non-NULL");
     const size_t align = dtype == SDPA_BF16 ? 16 : 4;
     if (!aligned(q, align) || !aligned(k, align) || !aligned(v, align) || !aligned(o, align) ||
-        (lse && !aligned(lse, 4)) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
+        (lse && !aligned(lse, 4)) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4) ||
+        (sinks && !aligned(sinks, 4)))
         return fail(SDPA_ERR_UNSUPPORTED, "pointer alignment: need %zu bytes for q/k/v/o", align);
 
     sdpa::PrefillArgs a;
@@ -143,6 +153,9 @@ int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh, const void* k, i
     a.lse = lse_layout == SDPA_LSE_NONE ? nullptr : lse;
     a.lse_layout = lse_layout;
     a.lse_s_max = lse_s_max;
+    a.window = window > 0 ? window : 0;
+    a.sinks = sinks;
+    a.stats_log2 = stats_log2;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (lse_layout == SDPA_LSE_PADDED) {
         hipError_t e = sdpa::launch_fill_neg_inf(lse, (int64_t)batch * lse_s_max * h_q, s);
@@ -152,6 +165,33 @@ int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh, const void* k, i
                                       : sdpa::launch_prefill_f32(a, s);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return ok();
+}
+
+int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                     int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, void* o,
+                     int64_t o_st, int64_t o_sh, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_kv, int32_t batch, int32_t max_seqlen_q,
+                     int32_t max_seqlen_kv, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                     int32_t d_v, float scale, int32_t causal, float* lse, int32_t lse_layout,
+                     int32_t lse_s_max, int32_t dtype, void* stream) {
+    return prefill_impl(q, q_st, q_sh, k, k_st, k_sh, v, v_st, v_sh, o, o_st, o_sh, cu_seqlens_q,
+                        cu_seqlens_kv, batch, max_seqlen_q, max_seqlen_kv, h_q, h_kv, d_qk, d_v,
+                        scale, causal, lse, lse_layout, lse_s_max, 0, nullptr, 0, dtype, stream);
+}
+
+int sdpa_prefill_thd_ex(const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                        int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, void* o,
+                        int64_t o_st, int64_t o_sh, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_kv, int32_t batch, int32_t max_seqlen_q,
+                        int32_t max_seqlen_kv, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                        int32_t d_v, float scale, int32_t causal, int32_t window_left,
+                        const float* sinks, float* lse, int32_t lse_layout, int32_t lse_s_max,
+                        int32_t stats_log2, int32_t dtype, void* stream) {
+    if (window_left < 0) return fail(SDPA_ERR_SHAPE, "window_left=%d < 0", window_left);
+    return prefill_impl(q, q_st, q_sh, k, k_st, k_sh, v, v_st, v_sh, o, o_st, o_sh, cu_seqlens_q,
+                        cu_seqlens_kv, batch, max_seqlen_q, max_seqlen_kv, h_q, h_kv, d_qk, d_v,
+                        scale, causal, lse, lse_layout, lse_s_max, window_left, sinks, stats_log2,
+                        dtype, stream);
 }
 
 size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t d_v,

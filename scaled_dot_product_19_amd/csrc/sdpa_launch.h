@@ -24,7 +24,10 @@ struct PrefillArgs {
     float scale;
     int32_t causal;
     float* lse;
-    int32_t lse_layout, lse_s_max;
+    int32_t lse_layout, lse_s_max;  // layout 3 (head-major): lse_s_max = per-head stride
+    int32_t window;                 // left sliding window (<= 0: none)
+    const float* sinks;             // [hq] sink logits or nullptr
+    int32_t stats_log2;             // LSE in base 2
 };
 
 struct DecodeArgs {

@@ -182,6 +182,19 @@ def paged_case(seed: int, batch: int, sq: int, hq: int, hkv: int, d_qk: int, d_v
                      num_splits, name)
 
 
+
+def sink_logits(seed: int, hq: int, special: bool = True) -> torch.Tensor:
+    """fp32 [hq] attention-sink logits, N(0.5, 2^2) (the range of learned per-head
+    sinks).  special=True makes head 0 -inf (no sink) and head 1 +12 (a sink that
+    outweighs most rows' keys)."""
+    g = torch.Generator().manual_seed(seed)
+    s = torch.randn(hq, generator=g, dtype=torch.float32) * 2.0 + 0.5
+    if special and hq > 0:
+        s[0] = float("-inf")
+    if special and hq > 1:
+        s[1] = 12.0
+    return s
+
 # ---- the five workloads -----------------------------------------------------
 
 SEED_BASE = 1000      # seed 1000 + k for workload k

@@ -35,9 +35,10 @@ SDPA_FP32 = 1
 LSE_NONE = 0
 LSE_PACKED = 1
 LSE_PADDED = 2
+LSE_HEAD_MAJOR = 3
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_prefill_thd", "sdpa_decode_workspace_bytes", "sdpa_decode_paged",
+EXPORTS = ("sdpa_prefill_thd", "sdpa_prefill_thd_ex", "sdpa_decode_workspace_bytes", "sdpa_decode_paged",
            "sdpa_splitkv_combine", "sdpa_status_string", "sdpa_last_error_detail",
            "sdpa_version")
 
@@ -71,6 +72,10 @@ def load():
     lib.sdpa_prefill_thd.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, I64, I64, P, P,
                                      I32, I32, I32, I32, I32, I32, I32, F, I32, P, I32, I32,
                                      I32, P]
+    lib.sdpa_prefill_thd_ex.restype = ctypes.c_int
+    lib.sdpa_prefill_thd_ex.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, I64, I64, P, P,
+                                        I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P, P, I32,
+                                        I32, I32, I32, P]
     lib.sdpa_decode_workspace_bytes.restype = SZ
     lib.sdpa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.sdpa_decode_paged.restype = ctypes.c_int
@@ -153,6 +158,41 @@ def prefill_thd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q:
         _ptr(cu_seqlens_kv), batch, int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, dqk, dv,
         float(scale), int(bool(causal)), _ptr(lse) if lse_layout != LSE_NONE else None,
         int(lse_layout), int(lse_s_max), _dtype_code(q), _stream(stream))
+    _check(rc)
+    return out, (lse if lse_layout != LSE_NONE else None)
+
+
+def prefill_thd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                   cu_seqlens_kv: torch.Tensor, max_seqlen_q: int, max_seqlen_kv: int,
+                   scale: float, causal: bool = True, window_left: int = 0,
+                   sinks: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, lse_layout: int = LSE_PACKED,
+                   lse_s_max: int = 0, stats_log2: bool = False, stream=None):
+    """sdpa_prefill_thd_ex: sdpa_prefill_thd plus a left sliding window, per-head
+    sinks (fp32 [Hq]) and base-2 Stats.  lse is [Tq, Hq] (packed), [B, lse_s_max, Hq]
+    (padded), [Hq, lse_s_max] (head-major; lse_s_max defaults to Tq) or None.
+    """
+    lib = load()
+    batch = int(cu_seqlens_q.numel()) - 1
+    hq, dqk = int(q.shape[1]), int(q.shape[2])
+    hkv, dv = int(k.shape[1]), int(v.shape[2])
+    if out is None:
+        out = torch.empty((q.shape[0], hq, dv), dtype=q.dtype, device=q.device)
+    if lse_layout == LSE_HEAD_MAJOR and lse_s_max == 0:
+        lse_s_max = int(q.shape[0])
+    if lse is None and lse_layout == LSE_PACKED:
+        lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    elif lse is None and lse_layout == LSE_PADDED:
+        lse = torch.empty((batch, lse_s_max, hq), dtype=torch.float32, device=q.device)
+    elif lse is None and lse_layout == LSE_HEAD_MAJOR:
+        lse = torch.empty((hq, lse_s_max), dtype=torch.float32, device=q.device)
+    rc = lib.sdpa_prefill_thd_ex(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1), _ptr(v),
+        v.stride(0), v.stride(1), _ptr(out), out.stride(0), out.stride(1), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_kv), batch, int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, dqk, dv,
+        float(scale), int(bool(causal)), int(window_left), _ptr(sinks),
+        _ptr(lse) if lse_layout != LSE_NONE else None, int(lse_layout), int(lse_s_max),
+        int(bool(stats_log2)), _dtype_code(q), _stream(stream))
     _check(rc)
     return out, (lse if lse_layout != LSE_NONE else None)
 

@@ -76,7 +76,9 @@ def _prefill(**over):
     (dict(dtype=1, dqk=320, dv=320), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(q_st=32 * 128 + 4), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(q_sh=0), sdpa.SDPA_ERR_SHAPE),
-    (dict(lse_layout=3), sdpa.SDPA_ERR_LSE_LAYOUT),
+    (dict(lse_layout=3), sdpa.SDPA_ERR_LSE_LAYOUT),  # head-major without its stride
+    (dict(lse_layout=4, lse_s_max=64), sdpa.SDPA_ERR_LSE_LAYOUT),
+    (dict(lse_layout=3, lse_s_max=64, dtype=1), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(lse_layout=2, lse_s_max=8), sdpa.SDPA_ERR_LSE_LAYOUT),
     (dict(lse=None), sdpa.SDPA_ERR_NULL),
     (dict(q=None), sdpa.SDPA_ERR_NULL),
@@ -88,6 +90,42 @@ def test_prefill_rejects(over, code):
     rc, detail = _prefill(**over)
     assert rc == code, (rc, detail)
     assert detail
+
+
+def _prefill_ex(**over):
+    lib = sdpa.load()
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation
+    args = dict(q=fake, q_st=32 * 128, q_sh=128, k=fake, k_st=8 * 128, k_sh=128, v=fake,
+                v_st=8 * 128, v_sh=128, o=fake, o_st=32 * 128, o_sh=128, cu_q=fake, cu_kv=fake,
+                batch=2, max_q=16, max_kv=16, hq=32, hkv=8, dqk=128, dv=128, scale=0.1,
+                causal=1, window=0, sinks=None, lse=fake, lse_layout=1, lse_s_max=0,
+                stats_log2=0, dtype=0, stream=None)
+    args.update(over)
+    rc = lib.sdpa_prefill_thd_ex(*args.values())
+    return rc, lib.sdpa_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(window=-1), sdpa.SDPA_ERR_SHAPE),
+    (dict(stats_log2=2), sdpa.SDPA_ERR_SHAPE),
+    (dict(dtype=1, window=16), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=1, sinks=ctypes.c_void_p(0x100000)), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=1, stats_log2=1), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(sinks=ctypes.c_void_p(0x100002)), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(lse_layout=3), sdpa.SDPA_ERR_LSE_LAYOUT),
+    (dict(window=8, q=None), sdpa.SDPA_ERR_NULL),
+    (dict(dqk=96, dv=96, window=8), sdpa.SDPA_ERR_UNSUPPORTED),
+])
+def test_prefill_ex_rejects(over, code):
+    rc, detail = _prefill_ex(**over)
+    assert rc == code, (rc, detail)
+    assert detail
+
+
+def test_prefill_ex_empty_batch_is_ok_without_pointers():
+    rc, detail = _prefill_ex(batch=0, window=4, stats_log2=1, q=None, k=None, v=None, o=None,
+                             cu_q=None, cu_kv=None)
+    assert rc == sdpa.SDPA_OK and detail == ""
 
 
 def test_prefill_empty_batch_is_ok_without_pointers():
