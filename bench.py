@@ -204,6 +204,69 @@ def cpu_baseline_decode(pc, target_s, threads):
                       "workload, 8-way split + LSE merge, fp64, %.1f s" % (n, nrows, dt)}
 
 
+def window_prefill_flops(lengths_q, lengths_kv, hq, dqk, dv, causal, window):
+    """Visible (row, key) pairs x 2 (Dqk + Dv) x Hq with a left window W: row i of a
+    sequence (Lq, Lk) sees keys max(0, d - W + 1) .. min(Lk, d + 1) - 1 (causal) or
+    .. Lk - 1, d = i + Lk - Lq."""
+    import numpy as np
+    pairs = 0
+    for lq, lk in zip(lengths_q, lengths_kv):
+        d = np.arange(lq, dtype=np.int64) + (lk - lq)
+        j1 = np.minimum(lk, d + 1) if causal else np.full(lq, lk, dtype=np.int64)
+        j0 = np.maximum(0, d - window + 1) if window > 0 else np.zeros(lq, dtype=np.int64)
+        pairs += int(np.maximum(0, j1 - j0).sum())
+    return pairs * hq * 2 * (dqk + dv)
+
+
+def run_window_prefill(args, torch, inputs, sdpa, dev):
+    """Sliding-window prefill with sinks, base-2 head-major Stats: one sdpa_prefill_thd_ex
+    call per step, on the D=128 prefill workload (W = 1024) and on a 64/8-head D=64 one
+    (W = 128).  One JSON line each."""
+    for case, window, dk in ((inputs.thd_prefill_d128(), 1024, 128),
+                             (inputs.window_prefill_d64(), 128, 64)):
+        q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+        cu_q, cu_kv = case.cu_q.to(dev), case.cu_kv.to(dev)
+        sinks = inputs.sink_logits(inputs.SEED_BASE + 9, case.hq, special=False).to(dev)
+        T = int(case.cu_q[-1])
+        o = torch.empty((T, case.hq, dk), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((case.hq, T), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream()
+
+        def step():
+            sdpa.prefill_thd_ex(q, k, v, cu_q, cu_kv, case.max_q, case.max_kv, case.scale, True,
+                                window_left=window, sinks=sinks, out=o, lse=lse,
+                                lse_layout=sdpa.LSE_HEAD_MAJOR, lse_s_max=T, stats_log2=True,
+                                stream=stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        flops = window_prefill_flops(case.lengths_q, case.lengths_kv, case.hq, dk, dk, True,
+                                     window)
+        tflops = flops / (ms * 1e-3) / 1e12
+        kern = "prefill_bf16_kernel<%d, %d, 4, 8, true, false, false>" % (dk, 64 if dk == 128
+                                                                           else 128)
+        line = {"metric": "sliding-window prefill attn TFLOP/s (% MFMA peak)",
+                "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic (seeded N(0,1) bf16; lengths and sinks per seed)",
+                "config": {"workload": case.name + "_w%d_sinks_log2_headmajor" % window,
+                           "window": window, "lengths": case.lengths_q, "flop": flops},
+                "roofline": {"kernel": kern, "bound": "mfma", "achieved": round(tflops, 2),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+        print(json.dumps(line), flush=True)
+
+
 def chunked_prefill_flops(pc):
     """Visible (row, key) pairs x 2 (D_qk + D_v): token i of a chunk of s_q tokens at the end of
     a cache of L tokens sees keys 0 .. L - s_q + i."""
@@ -347,6 +410,9 @@ def main():
     ap.add_argument("--mtp-sweep", action="store_true",
                     help="time only multi-token decode, q_tokens 1..4 against 128k caches "
                          "(batch 4, 32/8 heads, D=128, page 64, 32 splits)")
+    ap.add_argument("--window-prefill", action="store_true",
+                    help="time only sliding-window prefill with sinks and base-2 head-major "
+                         "Stats (D=128 workload with W=1024; 64/8 heads D=64 with W=128)")
     ap.add_argument("--mla-aliased", action="store_true",
                     help="time only the MLA-shaped decode over an absorbed-MLA cache (V = the "
                          "first 512 columns of the 576-wide K rows, one page table)")
@@ -371,6 +437,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.chunked_prefill:
         run_chunked_prefill(args, torch, inputs, sdpa, dev)
+        return
+    if args.window_prefill:
+        run_window_prefill(args, torch, inputs, sdpa, dev)
         return
     if args.mtp_sweep or args.mla_aliased:
         run_decode_variant(args, torch, inputs, sdpa, dev)

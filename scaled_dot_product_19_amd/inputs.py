@@ -243,6 +243,14 @@ def mla_decode(seed: int = SEED_BASE + 5, batch: int = 32, lo: int = 4096, hi: i
                       % (batch, lo, hi))
 
 
+def window_prefill_d64(seed: int = SEED_BASE + 9, batch: int = 8, lo: int = 128,
+                      hi: int = 4096) -> ThdCase:
+    """THD ragged causal prefill bf16 with the shape of sliding-window layers that carry
+    sinks: 8 sequences U[128, 4096], 64/8 heads, D=64 (run with a 128-key window)."""
+    return thd_case(seed, hq=64, hkv=8, d_qk=64, batch=batch, lo=lo, hi=hi,
+                    name="thd_prefill_bf16_b%d_%d-%d_h64x8_d64" % (batch, lo, hi))
+
+
 def chunked_prefill_paged(seed: int = SEED_BASE + 6, batch: int = 2, chunk: int = 1024,
                           lo: int = 32768, hi: int = 65536, num_splits: int = 4,
                           poison: bool = False) -> PagedCase:

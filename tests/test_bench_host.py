@@ -1,5 +1,7 @@
-"""Host-side helpers of bench.py (no GPU): work counting of the chunked-prefill line."""
+"""Host-side helpers of bench.py (no GPU): work counting of the chunked and windowed prefill lines."""
 import types
+
+import pytest
 
 import torch
 
@@ -15,3 +17,18 @@ def test_chunked_prefill_flops_counts_visible_pairs():
             brute += sum(1 for j in range(L) if j <= L - 4 + i)
     assert brute == (2 + 3 + 4 + 5) + (0 + 1 + 2 + 3) + (1 + 2 + 3 + 4)
     assert bench.chunked_prefill_flops(pc) == 2.0 * 256 * brute * 3
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_prefill_flops_counts_visible_pairs(causal):
+    lq, lk = [5, 9, 3, 0], [7, 4, 3, 2]
+    for w in (0, 1, 3, 100):
+        brute = 0
+        for a, b in zip(lq, lk):
+            for i in range(a):
+                d = i + b - a
+                brute += sum(1 for j in range(b)
+                             if (not causal or j <= d) and (w <= 0 or j >= d - w + 1))
+        assert bench.window_prefill_flops(lq, lk, 2, 64, 32, causal, w) == brute * 2 * 2 * 96
+    assert (bench.window_prefill_flops(lq, lk, 2, 64, 64, causal, 0)
+            == bench.prefill_flops(lq, lk, 2, 64, 64, causal))

@@ -165,3 +165,16 @@ def test_full_size_window_sinks_sampled():
     check_o(o[ti, hi], o_ref)
     check_lse(l[hi, ti] * LN2, l_ref)
     assert torch.isfinite(l).all()
+
+
+def test_full_size_d64_window128_sampled():
+    case = inputs.window_prefill_d64()
+    sinks = inputs.sink_logits(inputs.SEED_BASE + 9, case.hq, special=False)
+    log("full-size %s T=%d W=128 sinks" % (case.name, int(case.cu_q[-1])))
+    o, l = run_ex(case, 128, sinks, lse_layout=sdpa.LSE_HEAD_MAJOR, stats_log2=True)
+    toks, heads = thd_sample(case, 384, 2010)
+    o_ref, l_ref = oracle_ex(case, 128, sinks, sel_tok=toks, sel_head=heads)
+    ti, hi = torch.from_numpy(toks).cuda(), torch.from_numpy(heads).long().cuda()
+    check_o(o[ti, hi], o_ref)
+    check_lse(l[hi, ti] * LN2, l_ref)
+    assert torch.isfinite(l).all()
