@@ -5,8 +5,9 @@ CPU-baseline leg use this module; the HIP library and its Python binding never
 import it.  It shares no code with the GPU path.
 
 Arrays are numpy.  bf16 inputs are passed as their raw ``uint16`` bit
-patterns, fp32 inputs as ``float32``; the C side widens them exactly to
-double.  Outputs are float64.
+patterns, fp32 inputs as ``float32``, FP8 E4M3 inputs as their ``uint8``
+codes (with per-tensor descales); the C side widens them exactly to double.
+Outputs are float64.
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 BF16 = 0
 F32 = 1
+E4M3 = 2
 
 _lib = None
 
@@ -61,6 +63,12 @@ def _load(path: str | None = None):
     lib.oracle_decode_paged.argtypes = [
         ctypes.c_int, P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P, I32, I32, I32,
         I32, I32, I32, I32, D, I32, I32, I64, P, P, P, P, P, I32]
+    lib.oracle_decode_paged_scaled.restype = ctypes.c_int
+    lib.oracle_decode_paged_scaled.argtypes = [
+        ctypes.c_int, P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P, I32, I32, I32,
+        I32, I32, I32, I32, D, I32, I32, D, D, D, I64, P, P, P, P, P, I32]
+    lib.oracle_e4m3_value.restype = D
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_combine.restype = None
     lib.oracle_combine.argtypes = [P, P, I32, I64, I32, P, P]
     lib.oracle_nproc.restype = ctypes.c_int
@@ -106,7 +114,15 @@ def _dtype_code(a: np.ndarray) -> int:
         return BF16
     if a.dtype == np.float32:
         return F32
-    raise TypeError("oracle inputs are uint16 (bf16 bits) or float32, got %s" % a.dtype)
+    if a.dtype == np.uint8:
+        return E4M3
+    raise TypeError("oracle inputs are uint16 (bf16 bits), float32 or uint8 (E4M3 codes), "
+                    "got %s" % a.dtype)
+
+
+def e4m3_value(code: int) -> float:
+    """The value of one OCP E4M3 code (0..255), by the format's definition."""
+    return float(_load().oracle_e4m3_value(int(code)))
 
 
 def _strides(a: np.ndarray):
@@ -173,8 +189,11 @@ def prefill_thd(q, k, v, cu_q, cu_kv, scale, causal, hq=None, hkv=None, sel_tok=
 
 
 def decode_paged(q, k_pool, v_pool, pt_k, pt_v, seq_lens, page_size, scale, causal,
-                 num_splits=1, sel_rows=None, want_partials=False, nthreads=0):
+                 num_splits=1, sel_rows=None, want_partials=False, nthreads=0, descale=None):
     """Paged decode by definition (num_splits > 1: per-chunk partials + LSE merge).
+
+    E4M3 inputs (uint8 codes) need descale = (descale_q, descale_k, descale_v): each
+    code stands for its descale times its E4M3 value (per-tensor FP8).
 
     q [B, sq, Hq, Dqk] contiguous; pools [P, page, Hkv, D] with contiguous last
     axis; page tables int32 [B, table_stride]; seq_lens int32 [B].
@@ -212,12 +231,18 @@ def decode_paged(q, k_pool, v_pool, pt_k, pt_v, seq_lens, page_size, scale, caus
         o_part = np.zeros((S, rows, dv), np.float64)
         lse_part = np.zeros((S, rows), np.float64)
     ks, vs = _strides(k_pool), _strides(v_pool)
-    rc = lib.oracle_decode_paged(dt, _ptr(q), _ptr(k_pool), ks[0], ks[1], ks[2], _ptr(v_pool),
-                                 vs[0], vs[1], vs[2], _ptr(pt_k), _ptr(pt_v), pt_k.shape[1],
-                                 _ptr(seq_lens), B, sq, hq, hkv, dqk, dv, int(page_size),
-                                 float(scale), int(bool(causal)), int(num_splits), n_sel,
-                                 _ptr(sr), _ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part),
-                                 int(nthreads))
+    if dt == E4M3:
+        assert descale is not None and len(descale) == 3, "E4M3 inputs need their descales"
+        dsc = [float(x) for x in descale]
+    else:
+        assert descale is None, "descales apply to E4M3 inputs only"
+        dsc = [1.0, 1.0, 1.0]
+    rc = lib.oracle_decode_paged_scaled(
+        dt, _ptr(q), _ptr(k_pool), ks[0], ks[1], ks[2], _ptr(v_pool), vs[0], vs[1], vs[2],
+        _ptr(pt_k), _ptr(pt_v), pt_k.shape[1], _ptr(seq_lens), B, sq, hq, hkv, dqk, dv,
+        int(page_size), float(scale), int(bool(causal)), int(num_splits), dsc[0], dsc[1],
+        dsc[2], n_sel, _ptr(sr), _ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part),
+        int(nthreads))
     if rc != 0:
         raise ValueError("oracle_decode_paged rejected its arguments (rc=%d)" % rc)
     if sel_rows is None:

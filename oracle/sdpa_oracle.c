@@ -56,8 +56,21 @@
  *     are the ones stated above (window counted from the diagonal key
  *     inclusive; sink = an extra logit in the denominator only).
  *
+ *   - per-tensor FP8 (E4M3) forward and paged KV: v1.31.0 Release Notes,
+ *     paged KV (per-tensor FP8 D128 paged KV); v1.32.0 "SDPA: wider native
+ *     forward support" (paged per-tensor FP8 D256); the SM120 per-tensor FP8
+ *     (E4M3) forward engine; v1.32.0 Known issues (descale_q * descale_k).
+ *     The pages print no scale formula; the reading taken is the per-tensor
+ *     one: each stored code x8 stands for descale_x * E4M3(x8), so
+ *     s_ij = scale * descale_q * descale_k * <q8_i, k8_j> and the values are
+ *     descale_v * v8_j.  E4M3 is the OCP 8-bit format (sign, 4 exponent bits
+ *     with bias 7, 3 mantissa bits, subnormals at exponent 0, S.1111.111 the
+ *     only NaN, no infinities).
+ *
  * Inputs are read as bf16 (raw 16-bit patterns, widened exactly: a bf16 is
- * the top half of an IEEE binary32) or as fp32, then widened to double.
+ * the top half of an IEEE binary32), as fp32, or as E4M3 codes, then
+ * widened to double (every E4M3 value is exact in double, and so is its
+ * product with an fp32 descale).
  * Nothing is ever rounded on the oracle side.
  */
 #include <math.h>
@@ -69,11 +82,22 @@
 
 #define ORACLE_BF16 0
 #define ORACLE_F32 1
+#define ORACLE_E4M3 2
 
 /* ---- element access ---------------------------------------------------- */
 
+/* OCP E4M3 code -> value: (-1)^s * 2^(e-7) * (1 + m/8) for e = 1..15,
+   (-1)^s * 2^-6 * (m/8) for e = 0; e = 15 with m = 7 is NaN. */
+double oracle_e4m3_value(uint8_t code) {
+    int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
 static double load_elem(const void* base, int dtype, int64_t idx) {
     if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+    if (dtype == ORACLE_E4M3) return oracle_e4m3_value(((const uint8_t*)base)[idx]);
     uint32_t bits = (uint32_t)((const uint16_t*)base)[idx] << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -84,11 +108,13 @@ static double load_elem(const void* base, int dtype, int64_t idx) {
  * q: the query row (already widened), dqk long.
  * koff/voff: element offsets of the n visible key / value rows.
  * s: scratch of n doubles.  p_out (optional): the n softmax weights.
+ * kscale / vscale: per-tensor descales of the stored K and V codes (1 for
+ * bf16 and fp32 inputs).
  */
 static void attend_row(const double* q, int dqk, int dv, const void* k, const void* v,
                        const int64_t* koff, const int64_t* voff, int64_t n, int dtype,
-                       double scale, double sink, double* s, double* o, double* lse,
-                       double* p_out) {
+                       double kscale, double vscale, double scale, double sink, double* s,
+                       double* o, double* lse, double* p_out) {
     /* sink = -inf: no sink */
     if (n == 0 && sink == -INFINITY) {
         for (int d = 0; d < dv; ++d) o[d] = 0.0;
@@ -98,7 +124,7 @@ static void attend_row(const double* q, int dqk, int dv, const void* k, const vo
     double m = sink;
     for (int64_t j = 0; j < n; ++j) {
         double dot = 0.0;
-        for (int d = 0; d < dqk; ++d) dot += q[d] * load_elem(k, dtype, koff[j] + d);
+        for (int d = 0; d < dqk; ++d) dot += q[d] * (kscale * load_elem(k, dtype, koff[j] + d));
         s[j] = scale * dot;
         if (s[j] > m) m = s[j];
     }
@@ -109,7 +135,7 @@ static void attend_row(const double* q, int dqk, int dv, const void* k, const vo
     }
     for (int d = 0; d < dv; ++d) o[d] = 0.0;
     for (int64_t j = 0; j < n; ++j)
-        for (int d = 0; d < dv; ++d) o[d] += s[j] * load_elem(v, dtype, voff[j] + d);
+        for (int d = 0; d < dv; ++d) o[d] += s[j] * (vscale * load_elem(v, dtype, voff[j] + d));
     for (int d = 0; d < dv; ++d) o[d] /= l;
     *lse = m + log(l);
     if (p_out)
@@ -240,7 +266,7 @@ static void prefill_unit(void* vctx, int64_t unit, double* scratch) {
         p_row = p_out + j0;
     }
     const double sink = c->sinks ? c->sinks[h] : -INFINITY;
-    attend_row(qrow, c->dqk, c->dv, c->k, c->v, koff, voff, n, c->dtype, c->scale, sink, s, o,
+    attend_row(qrow, c->dqk, c->dv, c->k, c->v, koff, voff, n, c->dtype, 1.0, 1.0, c->scale, sink, s, o,
                lse, p_row);
 }
 
@@ -265,6 +291,7 @@ int oracle_prefill_thd(int dtype, const void* q, int64_t q_st, int64_t q_sh, con
                        const int64_t* sel_tok, const int32_t* sel_head, double* o, double* lse,
                        double* p_out, int32_t nthreads) {
     if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || dqk <= 0 || dv <= 0) return -1;
+    if (dtype == ORACLE_E4M3) return -1;  /* FP8 prefill is not defined here */
     int64_t max_lk = 1;
     for (int32_t b = 0; b < batch; ++b) {
         int64_t lk = cu_kv[b + 1] - cu_kv[b];
@@ -289,6 +316,7 @@ typedef struct {
     const int32_t *pt_k, *pt_v, *seq_lens;
     int32_t table_stride, batch, sq, hq, hkv, dqk, dv, page, causal, num_splits;
     double scale;
+    double dq, dk, dv_scale;   /* per-tensor descales of Q, K, V (1 unless E4M3) */
     int64_t n_sel;
     const int64_t* sel_row;
     double *o, *lse;       /* merged output (or unsplit) */
@@ -322,7 +350,7 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
     int64_t* voff = koff + c->max_lk;
     double* s = (double*)(voff + c->max_lk);
     for (int d = 0; d < c->dqk; ++d)
-        qrow[d] = load_elem(c->q, c->dtype, row * c->dqk + d);
+        qrow[d] = c->dq * load_elem(c->q, c->dtype, row * c->dqk + d);
 
     int32_t S = c->num_splits < 1 ? 1 : c->num_splits;
     int64_t chunk = split_chunk(L, S, c->page);
@@ -347,7 +375,8 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
             koff[n] = kpage * c->k_sp + slot * c->k_st + (int64_t)kvh * c->k_sh;
             voff[n] = vpage * c->v_sp + slot * c->v_st + (int64_t)kvh * c->v_sh;
         }
-        attend_row(qrow, c->dqk, c->dv, c->kp, c->vp, koff, voff, n, c->dtype, c->scale, -INFINITY, s,
+        attend_row(qrow, c->dqk, c->dv, c->kp, c->vp, koff, voff, n, c->dtype, c->dk, c->dv_scale,
+                   c->scale, -INFINITY, s,
                    ol + (size_t)sp * c->dv, ll + sp, NULL);
         if (ll[sp] > m_all) m_all = ll[sp];
         if (c->o_part) {
@@ -393,15 +422,19 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
  *   o_part/lse_part (optional) receive the partials, [S, rows, Dv]/[S, rows],
  *   row = (b*sq + t)*Hq + h.
  * n_sel < 0: all rows; else only rows sel_row[r] (same row numbering).
+ * dtype ORACLE_E4M3: Q, K and V are E4M3 codes standing for descale_q/k/v
+ * times their values (per-tensor FP8); other dtypes take descales of 1.
  */
-int oracle_decode_paged(int dtype, const void* q, const void* kpool, int64_t k_sp, int64_t k_st,
-                        int64_t k_sh, const void* vpool, int64_t v_sp, int64_t v_st,
-                        int64_t v_sh, const int32_t* pt_k, const int32_t* pt_v,
-                        int32_t table_stride, const int32_t* seq_lens, int32_t batch,
-                        int32_t sq, int32_t hq, int32_t hkv, int32_t dqk, int32_t dv,
-                        int32_t page, double scale, int32_t causal, int32_t num_splits,
-                        int64_t n_sel, const int64_t* sel_row, double* o, double* lse,
-                        double* o_part, double* lse_part, int32_t nthreads) {
+int oracle_decode_paged_scaled(int dtype, const void* q, const void* kpool, int64_t k_sp,
+                               int64_t k_st, int64_t k_sh, const void* vpool, int64_t v_sp,
+                               int64_t v_st, int64_t v_sh, const int32_t* pt_k,
+                               const int32_t* pt_v, int32_t table_stride,
+                               const int32_t* seq_lens, int32_t batch, int32_t sq, int32_t hq,
+                               int32_t hkv, int32_t dqk, int32_t dv, int32_t page, double scale,
+                               int32_t causal, int32_t num_splits, double descale_q,
+                               double descale_k, double descale_v, int64_t n_sel,
+                               const int64_t* sel_row, double* o, double* lse, double* o_part,
+                               double* lse_part, int32_t nthreads) {
     if (batch < 0 || sq <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || page <= 0) return -1;
     if (o_part && n_sel >= 0) return -1;
     int64_t max_lk = 1;
@@ -411,11 +444,28 @@ int oracle_decode_paged(int dtype, const void* q, const void* kpool, int64_t k_s
     }
     decode_ctx c = {dtype, q, kpool, vpool, k_sp, k_st, k_sh, v_sp, v_st, v_sh, pt_k, pt_v,
                     seq_lens, table_stride, batch, sq, hq, hkv, dqk, dv, page, causal,
-                    num_splits, scale, n_sel, sel_row, o, lse, o_part, lse_part, max_lk};
+                    num_splits, scale, descale_q, descale_k, descale_v, n_sel, sel_row, o, lse,
+                    o_part, lse_part, max_lk};
     int64_t rows = (int64_t)batch * sq * hq;
     int64_t n_units = n_sel < 0 ? rows : n_sel;
     size_t scratch = (size_t)dqk + 3 * (size_t)max_lk;
     return run_pool(decode_unit, &c, n_units, scratch, nthreads);
+}
+
+/* bf16 / fp32 paged decode: the same definition with descales of 1. */
+int oracle_decode_paged(int dtype, const void* q, const void* kpool, int64_t k_sp, int64_t k_st,
+                        int64_t k_sh, const void* vpool, int64_t v_sp, int64_t v_st,
+                        int64_t v_sh, const int32_t* pt_k, const int32_t* pt_v,
+                        int32_t table_stride, const int32_t* seq_lens, int32_t batch,
+                        int32_t sq, int32_t hq, int32_t hkv, int32_t dqk, int32_t dv,
+                        int32_t page, double scale, int32_t causal, int32_t num_splits,
+                        int64_t n_sel, const int64_t* sel_row, double* o, double* lse,
+                        double* o_part, double* lse_part, int32_t nthreads) {
+    if (dtype == ORACLE_E4M3) return -1;  /* E4M3 needs its descales */
+    return oracle_decode_paged_scaled(dtype, q, kpool, k_sp, k_st, k_sh, vpool, v_sp, v_st, v_sh,
+                                      pt_k, pt_v, table_stride, seq_lens, batch, sq, hq, hkv,
+                                      dqk, dv, page, scale, causal, num_splits, 1.0, 1.0, 1.0,
+                                      n_sel, sel_row, o, lse, o_part, lse_part, nthreads);
 }
 
 /*

@@ -20,7 +20,7 @@ from __future__ import annotations
 import dataclasses
 import math
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import torch
 
@@ -86,6 +86,9 @@ class PagedCase:
     causal: bool
     num_splits: int
     name: str = ""
+    # per-tensor FP8: q / k_pool / v_pool hold uint8 E4M3 codes standing for
+    # descale * value; (descale_q, descale_k, descale_v), fp32-representable
+    descale: Optional[Tuple[float, float, float]] = None
 
     @property
     def batch(self) -> int:
@@ -194,6 +197,36 @@ def sink_logits(seed: int, hq: int, special: bool = True) -> torch.Tensor:
     if special and hq > 1:
         s[1] = 12.0
     return s
+
+
+E4M3_MAX = 448.0  # largest finite OCP E4M3 value
+
+
+def quantize_e4m3(x: torch.Tensor) -> Tuple[torch.Tensor, float]:
+    """Per-tensor FP8 of an fp32 tensor: descale = amax / 448 (rounded to fp32; NaNs
+    ignored), codes = x / descale rounded to E4M3 (torch's float8_e4m3fn cast, RNE), as
+    uint8.  NaN entries become the NaN code."""
+    finite = x[torch.isfinite(x)]
+    amax = float(finite.abs().max()) if finite.numel() else 1.0
+    descale = float(torch.tensor(max(amax, 1e-30) / E4M3_MAX, dtype=torch.float32))
+    codes = (x / descale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, descale
+
+
+def fp8_paged_case(seed: int, batch: int, sq: int, hq: int, hkv: int, d: int, page_size: int,
+                   lo: int = 0, hi: int = 0, lengths: Optional[List[int]] = None,
+                   num_splits: int = 1, causal: bool = True, scale: Optional[float] = None,
+                   poison: bool = False, name: str = "") -> PagedCase:
+    """Paged decode problem in per-tensor FP8 E4M3: the fp32 problem paged_case draws for
+    the same arguments, each of Q, the K pool and the V pool quantized on its own
+    (quantize_e4m3).  Poisoned slots hold the NaN code."""
+    pc = paged_case(seed, batch, sq, hq, hkv, d, d, page_size, lo=lo, hi=hi, lengths=lengths,
+                    num_splits=num_splits, causal=causal, scale=scale, dtype=torch.float32,
+                    poison=poison, name=name)
+    q8, dq = quantize_e4m3(pc.q)
+    k8, dk = quantize_e4m3(pc.k_pool)
+    v8, dv = quantize_e4m3(pc.v_pool)
+    return dataclasses.replace(pc, q=q8, k_pool=k8, v_pool=v8, descale=(dq, dk, dv))
 
 # ---- the five workloads -----------------------------------------------------
 
@@ -304,4 +337,4 @@ def host_array(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         import numpy as np
         return t.view(torch.int16).numpy().view(np.uint16)
-    return t.numpy()
+    return t.numpy()  # float32, or uint8 E4M3 codes

@@ -44,6 +44,13 @@ MUTATIONS = [
     ("decode_causal_position", "int64_t last = c->causal ? (L - c->sq + tq) : (L - 1);",
      "int64_t last = c->causal ? (L - 1 - tq) : (L - 1);"),
     ("combine_lse_dropped_log", "double L = m + log(w_sum);", "double L = m + w_sum;"),
+    ("e4m3_bias_off_by_one", "ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    ("e4m3_subnormal_as_normal", "e == 0 ? ldexp((double)m / 8.0, -6)",
+     "e == 0 ? ldexp(1.0 + (double)m / 8.0, -7)"),
+    ("e4m3_nan_code_wrong", "if (e == 15 && m == 7) return NAN;", "if (e == 15) return NAN;"),
+    ("descale_v_dropped", "o[d] += s[j] * (vscale * load_elem", "o[d] += s[j] * (1.0 * load_elem"),
+    ("descales_k_v_swapped", "c->dk, c->dv_scale,", "c->dv_scale, c->dk,"),
+    ("descale_q_dropped", "qrow[d] = c->dq * load_elem", "qrow[d] = load_elem"),
 ]
 
 
@@ -71,6 +78,9 @@ def _pin_suite():
         ("sink_brute", lambda: pins.test_window_and_sinks_brute_force_vs_torch(40, False, True)),
         ("sink_closed", pins.test_sink_closed_form_single_key),
         ("sink_empty_rows", pins.test_rows_without_keys_take_the_sink_as_lse),
+        ("e4m3_codes", pins.test_e4m3_values_match_torch_float8_e4m3fn),
+        ("fp8_brute", lambda: pins.test_fp8_decode_brute_force_vs_torch(3, 2)),
+        ("fp8_single_key", pins.test_fp8_single_key_closed_form),
     ]
     failed = []
     for name, fn in checks:

@@ -363,3 +363,68 @@ def test_rows_without_keys_take_the_sink_as_lse():
     assert np.all(o[:3] == 0.0)
     assert np.array_equal(lse[:3], np.tile(sinks, (3, 1)))
     assert np.all(np.isfinite(lse[3:]))
+
+
+# ---- per-tensor FP8 (E4M3) ----------------------------------------------------
+
+def _e4m3_torch(codes: torch.Tensor) -> torch.Tensor:
+    """E4M3 codes -> float64 through torch's float8_e4m3fn dtype (an independent decoder)."""
+    return codes.view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def test_e4m3_values_match_torch_float8_e4m3fn():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = _e4m3_torch(codes).numpy()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(got, ref, equal_nan=True)
+    assert np.isnan(got).sum() == 2 and got[0x7E] == 448.0 and got[1] == 2.0 ** -9
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("sq", [1, 2])
+def test_fp8_decode_brute_force_vs_torch(splits, sq):
+    # the codes dequantized by torch (float8_e4m3fn x descale) and attended in float64
+    pc = inputs.fp8_paged_case(51, 3, sq, 4, 2, 64, 16, lengths=[1, 37, 80],
+                               num_splits=splits, poison=True)
+    dq, dk, dv = pc.descale
+    o, lse = oracle.decode_paged(_np(pc.q), _np(pc.k_pool), _np(pc.v_pool), pc.pt_k.numpy(),
+                                 pc.pt_v.numpy(), pc.seq_lens.numpy(), 16, pc.scale, True,
+                                 num_splits=splits, descale=pc.descale)
+    assert not np.isnan(lse).any() and not np.isnan(o).any()  # NaN codes of unused slots unread
+    P = pc.page_size
+    for b in range(pc.batch):
+        L = int(pc.seq_lens[b])
+        j = torch.arange(L)
+        k = _e4m3_torch(pc.k_pool[pc.pt_k[b, j // P].long(), j % P]) * dk    # [L, Hkv, D]
+        v = _e4m3_torch(pc.v_pool[pc.pt_v[b, j // P].long(), j % P]) * dv
+        for t in range(sq):
+            n = max(0, L - sq + t + 1)
+            q = _e4m3_torch(pc.q[b, t]) * dq                                  # [Hq, D]
+            kk = k[:n].repeat_interleave(2, dim=1).permute(1, 0, 2)          # [Hq, n, D]
+            vv = v[:n].repeat_interleave(2, dim=1).permute(1, 0, 2)
+            logits = pc.scale * torch.einsum("hd,hnd->hn", q, kk)
+            if n == 0:
+                assert np.all(lse[b, t] == -np.inf) and np.all(o[b, t] == 0.0)
+                continue
+            ref_l = torch.logsumexp(logits, -1)
+            ref_o = torch.einsum("hn,hnd->hd", torch.softmax(logits, -1), vv)
+            np.testing.assert_allclose(lse[b, t], ref_l.numpy(), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(o[b, t], ref_o.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_fp8_single_key_closed_form():
+    # one key: O = descale_v * E4M3(v codes) exactly (every code in one 256-wide V row),
+    # LSE = scale * descale_q * descale_k * <q, k> of the decoded codes
+    g = torch.Generator().manual_seed(53)
+    d = 256
+    q8 = torch.randint(0, 0x7E, (1, 1, 1, d), generator=g).to(torch.uint8)
+    k8 = torch.randint(0, 0x7E, (1, 16, 1, d), generator=g).to(torch.uint8)
+    v8 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(1, 1, 1, d).repeat(1, 16, 1, 1)
+    dsc = (0.5, 0.125, 3.0)
+    o, lse = oracle.decode_paged(q8.numpy(), k8.numpy(), v8.numpy(), np.zeros((1, 1), np.int32),
+                                 np.zeros((1, 1), np.int32), np.array([1], np.int32), 16, 0.25,
+                                 True, descale=dsc)
+    ref_o = (3.0 * _e4m3_torch(v8[0, 0, 0])).numpy()
+    assert np.array_equal(o[0, 0, 0], ref_o, equal_nan=True)
+    dot = float((_e4m3_torch(q8[0, 0, 0]) * _e4m3_torch(k8[0, 0, 0])).sum())
+    assert abs(lse[0, 0, 0] - 0.25 * 0.5 * 0.125 * dot) <= 1e-12 * max(1.0, abs(dot))
