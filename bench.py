@@ -63,12 +63,14 @@ def prefill_flops(lengths_q, lengths_kv, hq, dqk, dv, causal=True):
 
 
 def decode_bytes(pc):
-    """Compulsory HBM bytes of one paged decode call and its K/V share."""
+    """Compulsory HBM bytes of one paged decode call and its K/V share (FP8 cases: one
+    byte per Q/K/V element, O still bf16)."""
+    eb = 1 if pc.descale is not None else 2
     lens = [int(x) for x in pc.seq_lens.tolist()]
     dqk, dv = int(pc.q.shape[3]), int(pc.v_pool.shape[3])
-    kv = sum(lens) * pc.hkv * (dqk + dv) * 2
+    kv = sum(lens) * pc.hkv * (dqk + dv) * eb
     rows = pc.batch * pc.sq * pc.hq
-    q = rows * dqk * 2
+    q = rows * dqk * eb
     o = rows * dv * 2
     lse = rows * 4
     pages = sum((L + pc.page_size - 1) // pc.page_size for L in lens)
@@ -354,12 +356,66 @@ def time_decode(torch, sdpa, pc, dev, steps, warmup, q=None, kp=None, vp=None):
     return start.elapsed_time(end) / steps
 
 
+def time_decode_fp8(torch, sdpa, pc, dev, steps, warmup):
+    """Average ms of one sdpa_decode_paged_fp8 call (split kernel + combine) over `steps`."""
+    q, kp, vp = pc.q.to(dev), pc.k_pool.to(dev), pc.v_pool.to(dev)
+    ptk, ptv, sl = pc.pt_k.to(dev), pc.pt_v.to(dev), pc.seq_lens.to(dev)
+    dq, dk, dv = (torch.tensor([x], dtype=torch.float32, device=dev) for x in pc.descale)
+    d = int(vp.shape[3])
+    o = torch.empty((pc.batch, pc.sq, pc.hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((pc.batch, pc.sq, pc.hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, sdpa.decode_workspace_bytes(pc.batch, pc.sq, pc.hq, d,
+                                                        pc.num_splits)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sdpa.decode_paged_fp8(q, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, dq, dk, dv,
+                              causal=pc.causal, num_splits=pc.num_splits, workspace=ws, out=o,
+                              lse=lse, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
 def run_decode_variant(args, torch, inputs, sdpa, dev):
     """--mtp-sweep: q_tokens 1..4 over the same 128k caches; --mla-aliased: the MLA-shaped
     decode with V aliased into the K rows.  K/V bytes count each live cache row once (for the
     aliased cache: the 576-wide K row, which holds V)."""
     peak = PEAK_HBM_GBS
-    if args.mtp_sweep:
+    if args.fp8_decode:
+        # the paged decode workload in per-tensor FP8, and in bf16 on the same GPU
+        pc = inputs.paged_decode_d128_fp8()
+        ms = time_decode_fp8(torch, sdpa, pc, dev, args.steps, args.warmup)
+        kv, _ = decode_bytes(pc)
+        name = pc.name
+        del pc
+        pcb = inputs.paged_decode_d128()
+        ms_bf16 = time_decode(torch, sdpa, pcb, dev, args.steps, args.warmup)
+        gbs = kv / ms / 1e6
+        tokens = int(pcb.seq_lens.sum())
+        line = {"metric": "FP8 paged decode KV GB/s (% HBM peak)", "value": round(gbs, 1),
+                "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "fp8_e4m3",
+                "data": "synthetic (seeded N(0,1) fp32 quantized per tensor to E4M3)",
+                "config": {"workload": name, "kv_bytes": kv, "splits": 8,
+                           "cached_tokens": tokens,
+                           "bf16_ms_same_gpu": round(ms_bf16, 4),
+                           "speedup_vs_bf16": round(ms_bf16 / ms, 3)},
+                "roofline": {"kernel": "decode_small_kernel<128, true> + combine_kernel<false>",
+                             "bound": "hbm", "achieved": round(gbs, 1), "peak": peak,
+                             "unit": "GB/s", "frac": round(gbs / peak, 4), "traffic": None}}
+    elif args.mtp_sweep:
         pc = inputs.mtp_decode_d128()
         kp, vp, q4 = pc.k_pool.to(dev), pc.v_pool.to(dev), pc.q.to(dev)
         kv, _ = decode_bytes(pc)
@@ -413,6 +469,9 @@ def main():
     ap.add_argument("--window-prefill", action="store_true",
                     help="time only sliding-window prefill with sinks and base-2 head-major "
                          "Stats (D=128 workload with W=1024; 64/8 heads D=64 with W=128)")
+    ap.add_argument("--fp8-decode", action="store_true",
+                    help="time only the paged decode workload in per-tensor FP8 E4M3 (and in "
+                         "bf16 on the same GPU for the ratio)")
     ap.add_argument("--mla-aliased", action="store_true",
                     help="time only the MLA-shaped decode over an absorbed-MLA cache (V = the "
                          "first 512 columns of the 576-wide K rows, one page table)")
@@ -441,7 +500,7 @@ def main():
     if args.window_prefill:
         run_window_prefill(args, torch, inputs, sdpa, dev)
         return
-    if args.mtp_sweep or args.mla_aliased:
+    if args.mtp_sweep or args.mla_aliased or args.fp8_decode:
         run_decode_variant(args, torch, inputs, sdpa, dev)
         return
 

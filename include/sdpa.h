@@ -71,8 +71,10 @@ typedef enum {
 } sdpa_status_t;
 
 typedef enum {
-    SDPA_BF16 = 0,  /* Q/K/V/O bfloat16, FP32 accumulation (MFMA) */
-    SDPA_FP32 = 1   /* Q/K/V/O float32, FP32 arithmetic (VALU)    */
+    SDPA_BF16 = 0,     /* Q/K/V/O bfloat16, FP32 accumulation (MFMA)              */
+    SDPA_FP32 = 1,     /* Q/K/V/O float32, FP32 arithmetic (VALU)                 */
+    SDPA_FP8_E4M3 = 2  /* Q/K/V OCP E4M3 codes with per-tensor descales, O bf16;
+                          sdpa_decode_paged_fp8 only                              */
 } sdpa_dtype_t;
 
 typedef enum {
@@ -222,6 +224,36 @@ int sdpa_decode_paged(const void* q,
                       float scale, int32_t causal, int32_t num_splits,
                       void* workspace, size_t workspace_bytes,
                       void* o, float* lse, int32_t dtype, void* stream);
+
+/*
+ * Per-tensor FP8 (E4M3) paged decode: sdpa_decode_paged with Q, the K pool and
+ * the V pool holding one-byte OCP E4M3 codes (sign, 4 exponent bits biased by
+ * 7, 3 mantissa bits, S.1111.111 the only NaN), each standing for its tensor's
+ * descale times its value.  Per-tensor FP8 paged KV: v1.31.0 Release Notes,
+ * paged KV (SM100 per-tensor FP8 D128); v1.32.0 "SDPA: wider native forward
+ * support" (paged per-tensor FP8 D256); the pages print no scale formula, the
+ * per-tensor reading is taken:
+ *   s_tj = scale * descale_q * descale_k * <q8_t, k8_j>,
+ *   O_t  = descale_v * sum_j softmax_j(s_t) v8_j   (bf16),  LSE natural log.
+ * descale_q / descale_k / descale_v: device pointers to one fp32 each, read by
+ * the kernel (so a captured launch picks up new values).  Strides count
+ * elements (= bytes).  Other arguments, the split workspace and its layout
+ * are those of sdpa_decode_paged.
+ * Supported: d_qk == d_v in {128, 256}; s_q * (h_q/h_kv) <= 16; page_size a
+ * multiple of 16; K pool strides multiples of 16, V pool strides multiples of
+ * 8; q and the pools 16-byte aligned.  Else SDPA_ERR_UNSUPPORTED.
+ */
+int sdpa_decode_paged_fp8(const void* q,
+                          const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,
+                          const void* v_pool, int64_t v_sp, int64_t v_st, int64_t v_sh,
+                          const int32_t* page_table_k, const int32_t* page_table_v,
+                          int32_t table_stride, const int32_t* seq_lens, int32_t max_seqlen_kv,
+                          int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv,
+                          int32_t d_qk, int32_t d_v, int32_t page_size,
+                          float scale, int32_t causal, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes,
+                          const float* descale_q, const float* descale_k,
+                          const float* descale_v, void* o, float* lse, void* stream);
 
 /*
  * LSE merge of split-KV partials (the merge the notes use but never print;

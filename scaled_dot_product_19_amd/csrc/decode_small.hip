@@ -23,15 +23,27 @@
 //   - the next tile's loads are issued before the current tile is computed
 //     (register double buffer) and page ids are fetched two tiles ahead with
 //     scalar loads, so a wave keeps 16 KB in flight.
+//
+// Per-tensor FP8 (E4M3) instantiation (F8): Q, K and V are E4M3 codes that
+// stand for descale_{q,k,v} times their values (cuDNN Frontend v1.31.0
+// Release Notes, per-tensor FP8 D128 paged KV; v1.32.0 "SDPA: wider native
+// forward support", paged per-tensor FP8 D256).  A tile holds twice the keys
+// (the same 16 KB in flight); S^T = K Q^T runs on the FP8 MFMA
+// (v_mfma_f32_16x16x32_fp8_fp8, exact products, FP32 accumulate) with
+// scale * descale_q * descale_k folded into the exponent; V codes are widened
+// exactly to bf16 on their way into the V^T tile, so P V stays on the bf16
+// MFMA with P in bf16, and descale_v multiplies the normalized output.
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 
 #include <atomic>
+#include <type_traits>
 
 namespace sdpa {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -39,12 +51,29 @@ __device__ __forceinline__ f32x4 mfma16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16_k16(s16x4 a, s16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// 16x16x32 on E4M3 codes: lane (row l % 16, k-group l / 16) holds 8 codes
+__device__ __forceinline__ f32x4 mfma16_fp8(uint64_t a, uint64_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
+}
+// 8 E4M3 codes -> 8 bf16.  Every E4M3 value has at most 4 significant bits,
+// so the top half of its fp32 conversion is the same value in bf16.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    auto hi2 = [](float lo, float hi) {
+        return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                                     0x07060302u);
+    };
+    return uint4{hi2(a[0], a[1]), hi2(b[0], b[1]), hi2(c[0], c[1]), hi2(d[0], d[1])};
+}
 
 struct SmallKArgs {
-    const bf16_t* q;
-    const bf16_t* kp;
+    const void* q;   // bf16, or E4M3 codes (F8)
+    const void* kp;
     int64_t k_sp, k_st, k_sh;
-    const bf16_t* vp;
+    const void* vp;
     int64_t v_sp, v_st, v_sh;
     const int32_t* pt_k;
     const int32_t* pt_v;
@@ -59,6 +88,9 @@ struct SmallKArgs {
     float* lse_part;
     bf16_t* o;
     float* lse;
+    const float* descale_q;  // F8 only: one fp32 each
+    const float* descale_k;
+    const float* descale_v;
 };
 
 constexpr int kWaves = 4;
@@ -91,11 +123,13 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t i) {
     return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
-template <int D>
+template <int D, bool F8>
 struct SmallCfg {
-    static constexpr int TK = 4096 / D;      // keys per wave tile
+    static constexpr int EB = F8 ? 1 : 2;    // bytes per stored element
+    static constexpr int TK = 8192 / (EB * D);  // keys per wave tile (8 KB of K)
     static constexpr int SB = TK / 16;       // 16-key sub-blocks per tile
     static constexpr int KK = D / 32;        // k-steps of S^T = K Q^T
+    static constexpr int KL = EB * D / 64;   // 16-byte K loads per lane and sub-block
     static constexpr int NB = D / 16;        // 16-row blocks of O^T
     static constexpr int VP = TK + 4;        // V^T LDS pitch in elements
     static constexpr int VU = TK * D / 32 / 64;  // V units (4 keys x 8 columns) per lane
@@ -106,21 +140,23 @@ struct SmallCfg {
     static_assert(SB >= 1 && VU >= 1, "tile shape");
 };
 
-// One wave's registers for one tile: K operands and raw V rows.
-template <int D>
+// One wave's registers for one tile: K operands and raw V rows (8 columns of
+// 4 keys per unit: 16 bytes a row in bf16, 8 in E4M3).
+template <int D, bool F8>
 struct TileRegs {
-    bf16x8 k[SmallCfg<D>::SB][SmallCfg<D>::KK];
-    uint4 v[SmallCfg<D>::VU][4];
+    uint4 k[SmallCfg<D, F8>::SB][SmallCfg<D, F8>::KL];
+    typename std::conditional<F8, uint2, uint4>::type v[SmallCfg<D, F8>::VU][4];
 };
 
 // One unit: the keys of split `split` of sequence b for KV head kvh.  The
 // next unit's ticket (lane 0 of wave 0) is requested at the start and turned
 // into next_unit during the merge; returns that unit (-1: none left).
-template <int D, class NextOf>
+template <int D, bool F8, class NextOf>
 __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, bf16_t* smem, const int b,
                                                           const int kvh, const int split, uint32_t* ctr,
                                                           int* next_unit, NextOf&& next_of) {
-    using C = SmallCfg<D>;
+    using C = SmallCfg<D, F8>;
+    constexpr int EB = C::EB;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4;
@@ -145,16 +181,27 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     // keys every live row sees (the first token has the earliest causal limit)
     const int nomask_end = max(lo, min(hi, a.causal ? L - a.sq + 1 : hi));
 
-    // Q^T operand: lane (q = c, d-group g) holds d = 32 kk + 8 g .. +8 of its row
-    bf16x8 qf[C::KK];
+    // Q^T operand, 16 bytes per load.  bf16: lane (q = c, d-group g) holds
+    // d = 32 kl + 8 g .. +8 of its row for k-step kl.  E4M3: load kl holds
+    // d = 64 kl + 16 g .. +16, its low / high 8 codes feed k-steps 2 kl and
+    // 2 kl + 1 (K fragments are split the same way, so the dot product sums
+    // every d once).
+    uint4 qf[C::KL];
     {
-        const bf16_t* qrow = a.q + grow * D + 8 * g;
+        const char* qrow = reinterpret_cast<const char*>(a.q) + (grow * D) * EB + 16 * g;
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) {
+        for (int kl = 0; kl < C::KL; ++kl) {
             uint4 w = {0u, 0u, 0u, 0u};
-            if (row_ok) w = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-            qf[kk] = __builtin_bit_cast(bf16x8, w);
+            if (row_ok) w = *reinterpret_cast<const uint4*>(qrow + 64 * kl);
+            qf[kl] = w;
         }
+    }
+    // log2-domain logit scale: scale (x descale_q x descale_k for E4M3)
+    float scale_log2 = a.scale_log2;
+    float o_mul = 1.f;  // descale_v
+    if constexpr (F8) {
+        scale_log2 *= a.descale_q[0] * a.descale_k[0];
+        o_mul = a.descale_v[0];
     }
 
     f32x4 acc[C::NB];
@@ -165,16 +212,17 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     const int n_tiles = (hi - lo + C::TK - 1) / C::TK;
     const int32_t* ptk = a.pt_k + (int64_t)b * a.table_stride;
     const int32_t* ptv = a.pt_v + (int64_t)b * a.table_stride;
-    const char* kbase = reinterpret_cast<const char*>(a.kp + (int64_t)kvh * a.k_sh);
-    const char* vbase = reinterpret_cast<const char*>(a.vp + (int64_t)kvh * a.v_sh);
-    const int64_t k_sp2 = 2 * a.k_sp, v_sp2 = 2 * a.v_sp;
-    const int k_st2 = 2 * (int)a.k_st, v_st2 = 2 * (int)a.v_st;
+    const char* kbase = reinterpret_cast<const char*>(a.kp) + (int64_t)kvh * a.k_sh * EB;
+    const char* vbase = reinterpret_cast<const char*>(a.vp) + (int64_t)kvh * a.v_sh * EB;
+    // byte strides
+    const int64_t k_sp2 = EB * a.k_sp, v_sp2 = EB * a.v_sp;
+    const int k_st2 = EB * (int)a.k_st, v_st2 = EB * (int)a.v_st;
     bf16_t* vt = smem + wave * C::WAVE_LDS;
     // the last key index whose page may be looked up (the table is never read past it)
     const int last_key = max(hi - 1, 0);
 
     // Per-lane byte offsets inside a 16-key sub-block; all loop-invariant.
-    //   K (A operand of S^T = K Q^T): lane (key c, d-group g) -> row c, bytes 16 g + 64 kk.
+    //   K (A operand of S^T = K Q^T): lane (key c, d-group g) -> row c, bytes 16 g + 64 kl.
     //   V (row-coalesced 4 keys x 8 columns units): unit lane + 64 u.
     const int k_off = c * k_st2 + 16 * g;
     int v_off[C::VU], v_kt[C::VU], v_n8[C::VU];
@@ -183,7 +231,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
         const int unitv = lane + 64 * u;
         v_n8[u] = unitv % (D / 8);
         v_kt[u] = 4 * (unitv / (D / 8));           // first key of the unit in the tile
-        v_off[u] = (v_kt[u] & 15) * v_st2 + 16 * v_n8[u];
+        v_off[u] = (v_kt[u] & 15) * v_st2 + 8 * EB * v_n8[u];
     }
 
     // Buffer resources of one tile's 16-key sub-blocks.  The range of a
@@ -202,8 +250,8 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             const int slot = ks - pidx * a.page;    // in [0, page) whenever nvalid > 0
             const int32_t pk = load_uniform(ptk, pidx);
             const int32_t pv = load_uniform(ptv, pidx);
-            const int k_bytes = nvalid > 0 ? (nvalid - 1) * k_st2 + 2 * D : 0;
-            const int v_bytes = nvalid > 0 ? (nvalid - 1) * v_st2 + 2 * D : 0;
+            const int k_bytes = nvalid > 0 ? (nvalid - 1) * k_st2 + EB * D : 0;
+            const int v_bytes = nvalid > 0 ? (nvalid - 1) * v_st2 + EB * D : 0;
             rs.k[sb] = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(kbase + (int64_t)pk * k_sp2 + (int64_t)slot * k_st2), (short)0, k_bytes,
                 kRsrcWord3);
@@ -212,33 +260,46 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
                 kRsrcWord3);
         }
     };
-    auto issue = [&](const Rsrc& rs, TileRegs<D>& r) {
+    auto issue = [&](const Rsrc& rs, TileRegs<D, F8>& r) {
 #pragma unroll
         for (int sb = 0; sb < C::SB; ++sb) {
 #pragma unroll
-            for (int kk = 0; kk < C::KK; ++kk)
-                r.k[sb][kk] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs.k[sb], k_off + 64 * kk, 0, 0));
+            for (int kl = 0; kl < C::KL; ++kl)
+                r.k[sb][kl] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.k[sb], k_off + 64 * kl, 0, 0));
         }
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
             const int sb = (64 * u) / (D / 2);   // uniform: every lane's unit is in this sub-block
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                r.v[u][e] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v[sb], v_off[u], e * v_st2, 0));
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (F8)
+                    r.v[u][e] = __builtin_bit_cast(
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.v[sb], v_off[u], e * v_st2, 0));
+                else
+                    r.v[u][e] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v[sb], v_off[u], e * v_st2, 0));
+            }
         }
     };
-    auto compute = [&](int t, const TileRegs<D>& r) {
+    auto compute = [&](int t, const TileRegs<D, F8>& r) {
         const int key0 = lo + t * C::TK;
-        // V rows -> V^T[n][key] in this wave's LDS tile
+        // V rows -> V^T[n][key] in this wave's LDS tile (E4M3 rows widened to bf16 first)
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
             const int kt = v_kt[u];
-            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[u][0]);
-            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[u][1]);
-            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[u][2]);
-            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[u][3]);
+            uint4 vr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (F8)
+                    vr[e] = e4m3x8_to_bf16(r.v[u][e]);
+                else
+                    vr[e] = r.v[u][e];
+            }
+            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[0]);
+            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[1]);
+            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[2]);
+            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[3]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 uint2 even, odd;
@@ -257,7 +318,16 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
         for (int sb = 0; sb < C::SB; ++sb) {
             s[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < C::KK; ++kk) s[sb] = mfma16_k32(r.k[sb][kk], qf[kk], s[sb]);
+            for (int kl = 0; kl < C::KL; ++kl) {
+                if constexpr (F8) {
+                    const uint4 kw = r.k[sb][kl], qw = qf[kl];
+                    s[sb] = mfma16_fp8((uint64_t)kw.y << 32 | kw.x, (uint64_t)qw.y << 32 | qw.x, s[sb]);
+                    s[sb] = mfma16_fp8((uint64_t)kw.w << 32 | kw.z, (uint64_t)qw.w << 32 | qw.z, s[sb]);
+                } else {
+                    s[sb] = mfma16_k32(__builtin_bit_cast(bf16x8, r.k[sb][kl]),
+                                       __builtin_bit_cast(bf16x8, qf[kl]), s[sb]);
+                }
+            }
         }
         const bool need_mask = key0 + C::TK > nomask_end;
         float mt = neg_inf();
@@ -265,7 +335,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
         for (int sb = 0; sb < C::SB; ++sb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float x = s[sb][i] * a.scale_log2;
+                float x = s[sb][i] * scale_log2;
                 if (need_mask) x = key0 + 16 * sb + 4 * g + i > lim ? neg_inf() : x;
                 s[sb][i] = x;
                 mt = fmaxf(mt, x);
@@ -312,7 +382,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     // the top: r0 holds (or is loading) tile t, ra is the resource set of
     // tile t + 4.
     {
-        TileRegs<D> r0, r1;
+        TileRegs<D, F8> r0, r1;
         Rsrc ra, rb;
         int t = wave;
         make_rsrc(t, rb);
@@ -374,7 +444,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
                 tot += sc * red_l[w * 16 + q];
                 o += sc * *reinterpret_cast<const f32x4*>(red_o + (w * 16 + q) * D + n);
             }
-            o *= 1.f / tot;
+            o *= o_mul / tot;
             lse = kLn2 * (M + fast_log2(tot));
         }
         const int t2 = q / a.group;
@@ -396,7 +466,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
 // Persistent grid: each work-group runs units until the queue is empty,
 // longest sequences first (every unit of a sequence has the same number of
 // keys but the last split).
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(SmallKArgs a) {
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     __shared__ int next_unit;
@@ -422,7 +492,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
         const int r = unit / per_seq, rem = unit - r * per_seq;
         const int b = ranked ? by_len[r] : r;
         const int kvh = rem / a.splits, split = rem - (rem / a.splits) * a.splits;
-        const int nxt = decode_unit<D>(a, smem, b, kvh, split, &ctr[0], &next_unit, next_of);
+        const int nxt = decode_unit<D, F8>(a, smem, b, kvh, split, &ctr[0], &next_unit, next_of);
         __syncthreads();  // the merge's LDS reads are done before the next unit's V^T stores
         unit = nxt;
     }
@@ -433,11 +503,11 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
     }
 }
 
-template <int D>
+template <int D, bool F8>
 hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
-    using C = SmallCfg<D>;
+    using C = SmallCfg<D, F8>;
     if (a.n_units == 0) return hipSuccess;
-    const void* kernel = (const void*)decode_small_kernel<D>;
+    const void* kernel = (const void*)decode_small_kernel<D, F8>;
     hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     // resident work-groups: per CU (computed once) x CUs of the device
@@ -455,7 +525,7 @@ hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
     const int64_t slots = (int64_t)occ * n_cu;
     static std::atomic<uint32_t> slot_seq{0};
     a.slot = (int32_t)(slot_seq.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
-    hipLaunchKernelGGL(decode_small_kernel<D>, dim3((unsigned)(a.n_units < slots ? a.n_units : slots)), dim3(256),
+    hipLaunchKernelGGL((decode_small_kernel<D, F8>), dim3((unsigned)(a.n_units < slots ? a.n_units : slots)), dim3(256),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
@@ -468,12 +538,12 @@ bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows) {
 
 hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
     SmallKArgs a;
-    a.q = static_cast<const bf16_t*>(da.q);
-    a.kp = static_cast<const bf16_t*>(da.k_pool);
+    a.q = da.q;
+    a.kp = da.k_pool;
     a.k_sp = da.k_sp;
     a.k_st = da.k_st;
     a.k_sh = da.k_sh;
-    a.vp = static_cast<const bf16_t*>(da.v_pool);
+    a.vp = da.v_pool;
     a.v_sp = da.v_sp;
     a.v_st = da.v_st;
     a.v_sh = da.v_sh;
@@ -500,9 +570,19 @@ hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
     a.lse_part = da.lse_part;
     a.o = static_cast<bf16_t*>(da.o);
     a.lse = da.lse;
+    a.descale_q = da.descale_q;
+    a.descale_k = da.descale_k;
+    a.descale_v = da.descale_v;
+    if (da.fp8) {
+        switch (da.dqk) {
+            case 128: return launch_small_d<128, true>(a, s);
+            case 256: return launch_small_d<256, true>(a, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (da.dqk) {
-        case 128: return launch_small_d<128>(a, s);
-        case 256: return launch_small_d<256>(a, s);
+        case 128: return launch_small_d<128, false>(a, s);
+        case 256: return launch_small_d<256, false>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -203,15 +203,16 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
     return o_bytes + (size_t)num_splits * rows * sizeof(float);
 }
 
-int sdpa_decode_paged(const void* q, const void* k_pool, int64_t k_sp, int64_t k_st,
-                      int64_t k_sh, const void* v_pool, int64_t v_sp, int64_t v_st, int64_t v_sh,
-                      const int32_t* page_table_k, const int32_t* page_table_v,
-                      int32_t table_stride, const int32_t* seq_lens, int32_t max_seqlen_kv,
-                      int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
-                      int32_t d_v, int32_t page_size, float scale, int32_t causal,
-                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
-                      float* lse, int32_t dtype, void* stream) {
-    if (dtype != SDPA_BF16) return fail(SDPA_ERR_UNSUPPORTED, "paged decode serves bf16 only");
+static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t k_st,
+                       int64_t k_sh, const void* v_pool, int64_t v_sp, int64_t v_st, int64_t v_sh,
+                       const int32_t* page_table_k, const int32_t* page_table_v,
+                       int32_t table_stride, const int32_t* seq_lens, int32_t max_seqlen_kv,
+                       int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                       int32_t d_v, int32_t page_size, float scale, int32_t causal,
+                       int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
+                       float* lse, int32_t dtype, const float* descale_q,
+                       const float* descale_k, const float* descale_v, void* stream) {
+    const bool fp8 = dtype == SDPA_FP8_E4M3;
     if (batch < 0) return fail(SDPA_ERR_SHAPE, "batch=%d < 0", batch);
     if (s_q <= 0) return fail(SDPA_ERR_SHAPE, "s_q=%d must be >= 1", s_q);
     if (h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0)
@@ -226,7 +227,19 @@ int sdpa_decode_paged(const void* q, const void* k_pool, int64_t k_sp, int64_t k
                     page_size);
     if (num_splits < 1 || num_splits > 256)
         return fail(SDPA_ERR_SHAPE, "num_splits=%d outside [1, 256]", num_splits);
-    {
+    if (fp8) {
+        // per-tensor FP8: the few-row decode kernel only (HBM-streaming decode)
+        if (!sdpa::decode_small_supported(d_qk, d_v, s_q * (h_q / h_kv)))
+            return fail(SDPA_ERR_UNSUPPORTED,
+                        "FP8 paged decode serves d_qk == d_v in {128, 256} with s_q * (h_q / h_kv) "
+                        "<= 16 query rows per KV head; got (%d, %d), %lld rows",
+                        d_qk, d_v, (long long)s_q * (h_q / h_kv));
+        const int64_t kst[3] = {k_sp, k_st, k_sh};
+        for (int64_t x : kst)
+            if (x % 16 != 0)
+                return fail(SDPA_ERR_UNSUPPORTED, "FP8 K pool strides must be multiples of 16");
+    }
+    if (!fp8) {
         // more than 512 query rows per KV head: only the chunked-prefill path
         // (prefill kernel over the page tables) serves them
         sdpa::DecodeArgs probe{};
@@ -265,6 +278,10 @@ int sdpa_decode_paged(const void* q, const void* k_pool, int64_t k_sp, int64_t k
     if (batch == 0) return ok();
     if (!q || !k_pool || !v_pool || !page_table_k || !page_table_v || !seq_lens || !o)
         return fail(SDPA_ERR_NULL, "q/k_pool/v_pool/page tables/seq_lens/o must be non-NULL");
+    if (fp8 && (!descale_q || !descale_k || !descale_v))
+        return fail(SDPA_ERR_NULL, "FP8 decode needs descale_q, descale_k and descale_v");
+    if (fp8 && (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
+        return fail(SDPA_ERR_UNSUPPORTED, "descale pointers must be 4-byte aligned");
     if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
         (lse && !aligned(lse, 4)))
         return fail(SDPA_ERR_UNSUPPORTED, "q/pools/o must be 16-byte aligned");
@@ -314,14 +331,51 @@ int sdpa_decode_paged(const void* q, const void* k_pool, int64_t k_sp, int64_t k
     }
     a.o = o;
     a.lse = lse;
+    a.fp8 = fp8 ? 1 : 0;
+    a.descale_q = fp8 ? descale_q : nullptr;
+    a.descale_k = fp8 ? descale_k : nullptr;
+    a.descale_v = fp8 ? descale_v : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = sdpa::launch_decode_bf16(a, s);
+    hipError_t e = fp8 ? sdpa::launch_decode_small(a, s) : sdpa::launch_decode_bf16(a, s);
     if (e != hipSuccess) return hip_fail(e, "paged decode launch");
     if (num_splits > 1) {
         e = sdpa::launch_combine(a.o_part, a.lse_part, num_splits, rows, d_v, o, lse, 0, s);
         if (e != hipSuccess) return hip_fail(e, "split-KV combine launch");
     }
     return ok();
+}
+
+int sdpa_decode_paged(const void* q, const void* k_pool, int64_t k_sp, int64_t k_st,
+                      int64_t k_sh, const void* v_pool, int64_t v_sp, int64_t v_st, int64_t v_sh,
+                      const int32_t* page_table_k, const int32_t* page_table_v,
+                      int32_t table_stride, const int32_t* seq_lens, int32_t max_seqlen_kv,
+                      int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                      int32_t d_v, int32_t page_size, float scale, int32_t causal,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
+                      float* lse, int32_t dtype, void* stream) {
+    if (dtype == SDPA_FP8_E4M3)
+        return fail(SDPA_ERR_UNSUPPORTED, "per-tensor FP8 needs its descales: sdpa_decode_paged_fp8");
+    if (dtype != SDPA_BF16) return fail(SDPA_ERR_UNSUPPORTED, "paged decode serves bf16 only");
+    return decode_impl(q, k_pool, k_sp, k_st, k_sh, v_pool, v_sp, v_st, v_sh, page_table_k,
+                       page_table_v, table_stride, seq_lens, max_seqlen_kv, batch, s_q, h_q, h_kv,
+                       d_qk, d_v, page_size, scale, causal, num_splits, workspace,
+                       workspace_bytes, o, lse, SDPA_BF16, nullptr, nullptr, nullptr, stream);
+}
+
+int sdpa_decode_paged_fp8(const void* q, const void* k_pool, int64_t k_sp, int64_t k_st,
+                          int64_t k_sh, const void* v_pool, int64_t v_sp, int64_t v_st,
+                          int64_t v_sh, const int32_t* page_table_k, const int32_t* page_table_v,
+                          int32_t table_stride, const int32_t* seq_lens, int32_t max_seqlen_kv,
+                          int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                          int32_t d_v, int32_t page_size, float scale, int32_t causal,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          const float* descale_q, const float* descale_k,
+                          const float* descale_v, void* o, float* lse, void* stream) {
+    return decode_impl(q, k_pool, k_sp, k_st, k_sh, v_pool, v_sp, v_st, v_sh, page_table_k,
+                       page_table_v, table_stride, seq_lens, max_seqlen_kv, batch, s_q, h_q, h_kv,
+                       d_qk, d_v, page_size, scale, causal, num_splits, workspace,
+                       workspace_bytes, o, lse, SDPA_FP8_E4M3, descale_q, descale_k, descale_v,
+                       stream);
 }
 
 int sdpa_splitkv_combine(const float* o_part, const float* lse_part, int32_t num_splits,

@@ -47,6 +47,10 @@ struct DecodeArgs {
     float* lse_part;  // [splits, rows]
     void* o;          // final output when splits == 1
     float* lse;
+    int32_t fp8;      // Q/K/V are E4M3 codes (per-tensor descales below)
+    const float* descale_q;
+    const float* descale_k;
+    const float* descale_v;
 };
 
 // Each returns hipSuccess or the launch error.

@@ -255,6 +255,15 @@ def paged_decode_d128(seed: int = SEED_BASE + 3, batch: int = 64, lo: int = 512,
                       name="paged_decode_bf16_b%d_h32x8_d128_p64_%d-%d_s8" % (batch, lo, hi))
 
 
+def paged_decode_d128_fp8(seed: int = SEED_BASE + 3, batch: int = 64, lo: int = 512,
+                          hi: int = 32768, poison: bool = False) -> PagedCase:
+    """The paged decode workload in per-tensor FP8 E4M3: the same draws as paged_decode_d128
+    (before bf16 rounding), Q / K pool / V pool each quantized with its own descale."""
+    return fp8_paged_case(seed, batch=batch, sq=1, hq=32, hkv=8, d=128, page_size=64, lo=lo,
+                          hi=hi, num_splits=8, causal=True, poison=poison,
+                          name="paged_decode_fp8_b%d_h32x8_d128_p64_%d-%d_s8" % (batch, lo, hi))
+
+
 def dense_prefill_d256(seed: int = SEED_BASE + 4, seqlen: int = 8192) -> ThdCase:
     """Dense causal prefill bf16 D=256: batch 2 x 8192, 24 Q / 2 KV heads (GQA 12)."""
     return thd_case(seed, hq=24, hkv=2, d_qk=256, lengths=[seqlen, seqlen],

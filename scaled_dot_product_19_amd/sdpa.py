@@ -31,6 +31,7 @@ SDPA_ERR_HIP = 6
 
 SDPA_BF16 = 0
 SDPA_FP32 = 1
+SDPA_FP8_E4M3 = 2
 
 LSE_NONE = 0
 LSE_PACKED = 1
@@ -39,6 +40,7 @@ LSE_HEAD_MAJOR = 3
 
 # every symbol include/sdpa.h declares
 EXPORTS = ("sdpa_prefill_thd", "sdpa_prefill_thd_ex", "sdpa_decode_workspace_bytes", "sdpa_decode_paged",
+           "sdpa_decode_paged_fp8",
            "sdpa_splitkv_combine", "sdpa_status_string", "sdpa_last_error_detail",
            "sdpa_version")
 
@@ -82,6 +84,10 @@ def load():
     lib.sdpa_decode_paged.argtypes = [P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P, I32,
                                       I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P, SZ, P,
                                       P, I32, P]
+    lib.sdpa_decode_paged_fp8.restype = ctypes.c_int
+    lib.sdpa_decode_paged_fp8.argtypes = [P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P,
+                                          I32, I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P,
+                                          SZ, P, P, P, P, P, P]
     lib.sdpa_splitkv_combine.restype = ctypes.c_int
     lib.sdpa_splitkv_combine.argtypes = [P, P, I32, I64, I32, P, P, I32, P]
     lib.sdpa_status_string.restype = ctypes.c_char_p
@@ -225,6 +231,46 @@ def decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
         _ptr(page_table_v), int(page_table_k.shape[1]), _ptr(seq_lens), int(max_seqlen_kv), B,
         s_q, hq, hkv, dqk, dv, page, float(scale), int(bool(causal)), int(num_splits),
         _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _dtype_code(q), _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def decode_paged_fp8(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                     page_table_k: torch.Tensor, page_table_v: torch.Tensor,
+                     seq_lens: torch.Tensor, max_seqlen_kv: int, scale: float,
+                     descale_q: torch.Tensor, descale_k: torch.Tensor, descale_v: torch.Tensor,
+                     causal: bool = True, num_splits: int = 1,
+                     workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
+    """sdpa_decode_paged_fp8.  q [B, s_q, Hq, D] and pools [P, page, Hkv, D] hold uint8 E4M3
+    codes; descale_q/k/v are one-element fp32 device tensors.
+
+    Returns (out [B, s_q, Hq, D] bf16, lse [B, s_q, Hq] or None).
+    """
+    lib = load()
+    for t in (q, k_pool, v_pool):
+        if t.dtype != torch.uint8:
+            raise TypeError("FP8 decode takes uint8 E4M3 codes, got %s" % t.dtype)
+    for t in (descale_q, descale_k, descale_v):
+        if t.dtype != torch.float32 or t.numel() != 1:
+            raise TypeError("descales are one-element float32 tensors")
+    B, s_q, hq, dqk = (int(x) for x in q.shape)
+    page, hkv, dv = int(k_pool.shape[1]), int(k_pool.shape[2]), int(v_pool.shape[3])
+    if out is None:
+        out = torch.empty((B, s_q, hq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, s_q, hq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, s_q, hq, dv, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.sdpa_decode_paged_fp8(
+        _ptr(q), _ptr(k_pool), k_pool.stride(0), k_pool.stride(1), k_pool.stride(2),
+        _ptr(v_pool), v_pool.stride(0), v_pool.stride(1), v_pool.stride(2), _ptr(page_table_k),
+        _ptr(page_table_v), int(page_table_k.shape[1]), _ptr(seq_lens), int(max_seqlen_kv), B,
+        s_q, hq, hkv, dqk, dv, page, float(scale), int(bool(causal)), int(num_splits),
+        _ptr(workspace), ws_bytes, _ptr(descale_q), _ptr(descale_k), _ptr(descale_v), _ptr(out),
+        _ptr(lse), _stream(stream))
     _check(rc)
     return out, lse
 

@@ -173,6 +173,42 @@ def test_decode_rejects(over, code):
     assert detail
 
 
+def _decode_fp8(**over):
+    lib = sdpa.load()
+    fake = ctypes.c_void_p(0x100000)
+    args = dict(q=fake, kp=fake, k_sp=64 * 8 * 128, k_st=8 * 128, k_sh=128, vp=fake,
+                v_sp=64 * 8 * 128, v_st=8 * 128, v_sh=128, ptk=fake, ptv=fake, ts=512,
+                seq_lens=fake, max_kv=32768, batch=64, sq=1, hq=32, hkv=8, dqk=128, dv=128,
+                page=64, scale=0.1, causal=1, splits=8, ws=fake, ws_bytes=1 << 40, dq=fake,
+                dk=fake, dv_=fake, o=fake, lse=fake, stream=None)
+    args.update(over)
+    rc = lib.sdpa_decode_paged_fp8(*args.values())
+    return rc, lib.sdpa_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dqk=64, dv=64, k_st=8 * 64, v_st=8 * 64, k_sh=64, v_sh=64), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dqk=576, dv=512), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(sq=4, hq=64, hkv=8), sdpa.SDPA_ERR_UNSUPPORTED),      # 32 rows per KV head
+    (dict(k_st=8 * 128 + 8), sdpa.SDPA_ERR_UNSUPPORTED),         # K rows need 16-byte strides
+    (dict(v_st=8 * 128 + 4), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dq=None), sdpa.SDPA_ERR_NULL),
+    (dict(dv_=None), sdpa.SDPA_ERR_NULL),
+    (dict(dk=ctypes.c_void_p(0x100002)), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(ws=None), sdpa.SDPA_ERR_WORKSPACE),
+    (dict(splits=0), sdpa.SDPA_ERR_SHAPE),
+])
+def test_decode_fp8_rejects(over, code):
+    rc, detail = _decode_fp8(**over)
+    assert rc == code, (rc, detail)
+    assert detail
+
+
+def test_decode_bf16_entry_refuses_fp8_codes():
+    rc, detail = _decode(dtype=sdpa.SDPA_FP8_E4M3)
+    assert rc == sdpa.SDPA_ERR_UNSUPPORTED and "descale" in detail
+
+
 def test_decode_one_split_needs_no_workspace_but_other_checks_still_run():
     rc, _ = _decode(splits=1, ws=None, ws_bytes=0, o=None)
     assert rc == sdpa.SDPA_ERR_NULL
