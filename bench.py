@@ -627,7 +627,7 @@ def main():
             "traffic": recorded_traffic(PREFILL_TRAFFIC, PREFILL_SOURCES),
         },
         "roofline_decode": {
-            "kernel": "decode_small_kernel<128> + combine_kernel<false>",
+            "kernel": "decode_small_kernel<128, false> + combine_kernel<false>",
             "bound": "hbm",
             "achieved": round(dec_comp_gbs, 1),
             "peak": PEAK_HBM_GBS,
