@@ -59,6 +59,10 @@ def _load(path: str | None = None):
     lib.oracle_prefill_thd.argtypes = [
         ctypes.c_int, P, I64, I64, P, I64, I64, P, I64, I64, P, P, I32, I32, I32, I32, I32,
         D, I32, I32, P, I64, P, P, P, P, P, I32]
+    lib.oracle_prefill_thd_scaled.restype = ctypes.c_int
+    lib.oracle_prefill_thd_scaled.argtypes = [
+        ctypes.c_int, P, I64, I64, P, I64, I64, P, I64, I64, P, P, I32, I32, I32, I32, I32,
+        D, I32, I32, P, D, D, D, I64, P, P, P, P, P, I32]
     lib.oracle_decode_paged.restype = ctypes.c_int
     lib.oracle_decode_paged.argtypes = [
         ctypes.c_int, P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P, I32, I32, I32,
@@ -130,8 +134,11 @@ def _strides(a: np.ndarray):
 
 
 def prefill_thd(q, k, v, cu_q, cu_kv, scale, causal, hq=None, hkv=None, sel_tok=None,
-                sel_head=None, want_probs=False, nthreads=0, window=0, sinks=None):
+                sel_head=None, want_probs=False, nthreads=0, window=0, sinks=None, descale=None):
     """Packed THD prefill by definition.
+
+    E4M3 inputs (uint8 codes) need descale = (descale_q, descale_k, descale_v): each
+    code stands for its descale times its E4M3 value (per-tensor FP8).
 
     window > 0: left sliding window W (a row sees keys diag - W + 1 .. diag of its
     bottom-right diagonal position diag); sinks: Hq per-head sink logits (same units as
@@ -173,11 +180,18 @@ def prefill_thd(q, k, v, cu_q, cu_kv, scale, causal, hq=None, hkv=None, sel_tok=
     if sinks is not None:
         sk = np.ascontiguousarray(sinks, dtype=np.float64)
         assert sk.shape == (hq_,)
-    rc = lib.oracle_prefill_thd(dt, _ptr(q), qs[0], qs[1], _ptr(k), ks[0], ks[1], _ptr(v),
-                                vs[0], vs[1], _ptr(cu_q), _ptr(cu_kv), batch, hq_, hkv_, dqk,
-                                dv, float(scale), int(bool(causal)), int(window), _ptr(sk),
-                                n_sel, _ptr(st), _ptr(sh), _ptr(o), _ptr(lse), _ptr(probs),
-                                int(nthreads))
+    if dt == E4M3:
+        assert descale is not None and len(descale) == 3, "E4M3 inputs need their descales"
+        dsc = [float(x) for x in descale]
+    else:
+        assert descale is None, "descales apply to E4M3 inputs only"
+        dsc = [1.0, 1.0, 1.0]
+    rc = lib.oracle_prefill_thd_scaled(dt, _ptr(q), qs[0], qs[1], _ptr(k), ks[0], ks[1],
+                                       _ptr(v), vs[0], vs[1], _ptr(cu_q), _ptr(cu_kv), batch,
+                                       hq_, hkv_, dqk, dv, float(scale), int(bool(causal)),
+                                       int(window), _ptr(sk), dsc[0], dsc[1], dsc[2], n_sel,
+                                       _ptr(st), _ptr(sh), _ptr(o), _ptr(lse), _ptr(probs),
+                                       int(nthreads))
     if rc != 0:
         raise ValueError("oracle_prefill_thd rejected its arguments (rc=%d)" % rc)
     if sel_tok is None:

@@ -208,6 +208,7 @@ typedef struct {
     int64_t max_lk;
     int32_t window;        /* left window W (<= 0: none) */
     const double* sinks;   /* [hq] sink logits, or NULL */
+    double q_descale, k_descale, v_descale;  /* per-tensor descales (1 unless E4M3) */
 } prefill_ctx;
 
 /* Sequence b that owns packed query row t: cu_q[b] <= t < cu_q[b+1]. */
@@ -253,7 +254,7 @@ static void prefill_unit(void* vctx, int64_t unit, double* scratch) {
     int64_t* voff = koff + c->max_lk;
     double* s = (double*)(voff + c->max_lk);
     for (int d = 0; d < c->dqk; ++d)
-        qrow[d] = load_elem(c->q, c->dtype, t * c->q_st + (int64_t)h * c->q_sh + d);
+        qrow[d] = c->q_descale * load_elem(c->q, c->dtype, t * c->q_st + (int64_t)h * c->q_sh + d);
     for (int64_t j = 0; j < n; ++j) {
         koff[j] = (c->cu_kv[b] + j0 + j) * c->k_st + (int64_t)kvh * c->k_sh;
         voff[j] = (c->cu_kv[b] + j0 + j) * c->v_st + (int64_t)kvh * c->v_sh;
@@ -266,8 +267,8 @@ static void prefill_unit(void* vctx, int64_t unit, double* scratch) {
         p_row = p_out + j0;
     }
     const double sink = c->sinks ? c->sinks[h] : -INFINITY;
-    attend_row(qrow, c->dqk, c->dv, c->k, c->v, koff, voff, n, c->dtype, 1.0, 1.0, c->scale, sink, s, o,
-               lse, p_row);
+    attend_row(qrow, c->dqk, c->dv, c->k, c->v, koff, voff, n, c->dtype, c->k_descale,
+               c->v_descale, c->scale, sink, s, o, lse, p_row);
 }
 
 /*
@@ -281,17 +282,20 @@ static void prefill_unit(void* vctx, int64_t unit, double* scratch) {
  * [n_sel, Dv], lse [n_sel].  p_out (optional, may be NULL) receives, per
  * computed row, max_lk softmax weights (key index j of the row's sequence).
  * window > 0 is the left sliding window W; sinks (optional) holds Hq sink
- * logits.  Returns 0, or -1 on a bad argument / failed allocation.
+ * logits.  dtype ORACLE_E4M3: Q, K and V are E4M3 codes standing for
+ * descale_q/k/v times their values (per-tensor FP8); other dtypes take
+ * descales of 1.  Returns 0, or -1 on a bad argument / failed allocation.
  */
-int oracle_prefill_thd(int dtype, const void* q, int64_t q_st, int64_t q_sh, const void* k,
-                       int64_t k_st, int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh,
-                       const int32_t* cu_q, const int32_t* cu_kv, int32_t batch, int32_t hq,
-                       int32_t hkv, int32_t dqk, int32_t dv, double scale, int32_t causal,
-                       int32_t window, const double* sinks, int64_t n_sel,
-                       const int64_t* sel_tok, const int32_t* sel_head, double* o, double* lse,
-                       double* p_out, int32_t nthreads) {
+int oracle_prefill_thd_scaled(int dtype, const void* q, int64_t q_st, int64_t q_sh,
+                              const void* k, int64_t k_st, int64_t k_sh, const void* v,
+                              int64_t v_st, int64_t v_sh, const int32_t* cu_q,
+                              const int32_t* cu_kv, int32_t batch, int32_t hq, int32_t hkv,
+                              int32_t dqk, int32_t dv, double scale, int32_t causal,
+                              int32_t window, const double* sinks, double descale_q,
+                              double descale_k, double descale_v, int64_t n_sel,
+                              const int64_t* sel_tok, const int32_t* sel_head, double* o,
+                              double* lse, double* p_out, int32_t nthreads) {
     if (batch < 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || dqk <= 0 || dv <= 0) return -1;
-    if (dtype == ORACLE_E4M3) return -1;  /* FP8 prefill is not defined here */
     int64_t max_lk = 1;
     for (int32_t b = 0; b < batch; ++b) {
         int64_t lk = cu_kv[b + 1] - cu_kv[b];
@@ -300,11 +304,26 @@ int oracle_prefill_thd(int dtype, const void* q, int64_t q_st, int64_t q_sh, con
     }
     prefill_ctx c = {dtype, q, k, v, q_st, q_sh, k_st, k_sh, v_st, v_sh, cu_q, cu_kv, batch,
                      hq, hkv, dqk, dv, causal, scale, n_sel, sel_tok, sel_head, o, lse, p_out,
-                     max_lk, window, sinks};
+                     max_lk, window, sinks, descale_q, descale_k, descale_v};
     int64_t tq = batch > 0 ? cu_q[batch] : 0;
     int64_t n_units = n_sel < 0 ? tq * hq : n_sel;
     size_t scratch = (size_t)dqk + 3 * (size_t)max_lk;
     return run_pool(prefill_unit, &c, n_units, scratch, nthreads);
+}
+
+/* bf16 / fp32 prefill: the same definition with descales of 1. */
+int oracle_prefill_thd(int dtype, const void* q, int64_t q_st, int64_t q_sh, const void* k,
+                       int64_t k_st, int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh,
+                       const int32_t* cu_q, const int32_t* cu_kv, int32_t batch, int32_t hq,
+                       int32_t hkv, int32_t dqk, int32_t dv, double scale, int32_t causal,
+                       int32_t window, const double* sinks, int64_t n_sel,
+                       const int64_t* sel_tok, const int32_t* sel_head, double* o, double* lse,
+                       double* p_out, int32_t nthreads) {
+    if (dtype == ORACLE_E4M3) return -1;  /* E4M3 needs its descales */
+    return oracle_prefill_thd_scaled(dtype, q, q_st, q_sh, k, k_st, k_sh, v, v_st, v_sh, cu_q,
+                                     cu_kv, batch, hq, hkv, dqk, dv, scale, causal, window, sinks,
+                                     1.0, 1.0, 1.0, n_sel, sel_tok, sel_head, o, lse, p_out,
+                                     nthreads);
 }
 
 /* ---- paged-KV decode ------------------------------------------------------ */

@@ -56,6 +56,8 @@ class ThdCase:
     scale: float
     causal: bool = True
     name: str = ""
+    # per-tensor FP8: q / k / v hold uint8 E4M3 codes standing for descale * value
+    descale: Optional[Tuple[float, float, float]] = None
 
     @property
     def batch(self) -> int:
@@ -211,6 +213,21 @@ def quantize_e4m3(x: torch.Tensor) -> Tuple[torch.Tensor, float]:
     descale = float(torch.tensor(max(amax, 1e-30) / E4M3_MAX, dtype=torch.float32))
     codes = (x / descale).to(torch.float8_e4m3fn).view(torch.uint8)
     return codes, descale
+
+
+def fp8_thd_case(seed: int, hq: int, hkv: int, d: int, lengths: Optional[List[int]] = None,
+                 batch: int = 0, lo: int = 0, hi: int = 0,
+                 lengths_kv: Optional[List[int]] = None, causal: bool = True,
+                 scale: Optional[float] = None, name: str = "") -> ThdCase:
+    """THD prefill problem in per-tensor FP8 E4M3: the fp32 problem thd_case draws for the
+    same arguments, Q, K and V each quantized on its own (quantize_e4m3)."""
+    case = thd_case(seed, hq=hq, hkv=hkv, d_qk=d, lengths=lengths, batch=batch, lo=lo, hi=hi,
+                    lengths_kv=lengths_kv, dtype=torch.float32, causal=causal, scale=scale,
+                    name=name)
+    q8, dq = quantize_e4m3(case.q)
+    k8, dk = quantize_e4m3(case.k)
+    v8, dv = quantize_e4m3(case.v)
+    return dataclasses.replace(case, q=q8, k=k8, v=v8, descale=(dq, dk, dv))
 
 
 def fp8_paged_case(seed: int, batch: int, sq: int, hq: int, hkv: int, d: int, page_size: int,

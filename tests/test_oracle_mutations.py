@@ -51,6 +51,9 @@ MUTATIONS = [
     ("descale_v_dropped", "o[d] += s[j] * (vscale * load_elem", "o[d] += s[j] * (1.0 * load_elem"),
     ("descales_k_v_swapped", "c->dk, c->dv_scale,", "c->dv_scale, c->dk,"),
     ("descale_q_dropped", "qrow[d] = c->dq * load_elem", "qrow[d] = load_elem"),
+    ("prefill_descale_q_dropped", "qrow[d] = c->q_descale * load_elem", "qrow[d] = load_elem"),
+    ("prefill_descales_k_v_swapped", "c->k_descale,\n               c->v_descale,",
+     "c->v_descale,\n               c->k_descale,"),
 ]
 
 
@@ -81,6 +84,7 @@ def _pin_suite():
         ("e4m3_codes", pins.test_e4m3_values_match_torch_float8_e4m3fn),
         ("fp8_brute", lambda: pins.test_fp8_decode_brute_force_vs_torch(3, 2)),
         ("fp8_single_key", pins.test_fp8_single_key_closed_form),
+        ("fp8_prefill_brute", lambda: pins.test_fp8_prefill_brute_force_vs_torch(5, True, True)),
     ]
     failed = []
     for name, fn in checks:

@@ -428,3 +428,25 @@ def test_fp8_single_key_closed_form():
     assert np.array_equal(o[0, 0, 0], ref_o, equal_nan=True)
     dot = float((_e4m3_torch(q8[0, 0, 0]) * _e4m3_torch(k8[0, 0, 0])).sum())
     assert abs(lse[0, 0, 0] - 0.25 * 0.5 * 0.125 * dot) <= 1e-12 * max(1.0, abs(dot))
+
+
+def _dequantized(case: inputs.ThdCase) -> inputs.ThdCase:
+    """The FP8 case's real values (torch-decoded codes x descales) as a float64 case."""
+    import dataclasses
+    dq, dk, dv = case.descale
+    return dataclasses.replace(case, q=_e4m3_torch(case.q) * dq, k=_e4m3_torch(case.k) * dk,
+                               v=_e4m3_torch(case.v) * dv, descale=None)
+
+
+@pytest.mark.parametrize("window,with_sinks", [(0, False), (5, True)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_brute_force_vs_torch(window, causal, with_sinks):
+    case = inputs.fp8_thd_case(57, 4, 2, 64, lengths=[1, 9, 20], lengths_kv=[3, 9, 17],
+                               causal=causal)
+    sinks = np.array([0.5, -1.0, 2.0, 3.0]) if with_sinks else None
+    o, lse = _run_oracle(case, window=window, sinks=sinks, descale=case.descale)
+    ro, rl = _brute(_dequantized(case), window=window, sinks=sinks)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse), fin)
+    np.testing.assert_allclose(lse[fin], rl[fin], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(o, ro, rtol=1e-12, atol=1e-13)
