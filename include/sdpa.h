@@ -74,7 +74,7 @@ typedef enum {
     SDPA_BF16 = 0,     /* Q/K/V/O bfloat16, FP32 accumulation (MFMA)              */
     SDPA_FP32 = 1,     /* Q/K/V/O float32, FP32 arithmetic (VALU)                 */
     SDPA_FP8_E4M3 = 2  /* Q/K/V OCP E4M3 codes with per-tensor descales, O bf16;
-                          sdpa_decode_paged_fp8 only                              */
+                          sdpa_prefill_thd_fp8 / sdpa_decode_paged_fp8 only       */
 } sdpa_dtype_t;
 
 typedef enum {
@@ -158,6 +158,34 @@ int sdpa_prefill_thd_ex(const void* q, int64_t q_st, int64_t q_sh,
                         float scale, int32_t causal, int32_t window_left, const float* sinks,
                         float* lse, int32_t lse_layout, int32_t lse_s_max, int32_t stats_log2,
                         int32_t dtype, void* stream);
+
+/*
+ * Per-tensor FP8 (E4M3) packed THD ragged prefill: sdpa_prefill_thd_ex with
+ * Q, K and V holding one-byte OCP E4M3 codes, each standing for its tensor's
+ * descale times its value (per-tensor FP8 forward: v1.31.0 Release Notes,
+ * SM100 per-tensor FP8 D128; the SM120 per-tensor FP8 (E4M3) forward engine;
+ * v1.32.0 Known issues on negative descale_q * descale_k, which is served
+ * here).  The pages print no scale formula; the per-tensor reading is taken:
+ *   s_ij = scale * descale_q * descale_k * <q8_i, k8_j>,
+ *   O_i  = descale_v * sum_j softmax_j(s_i) v8_j   (bf16),  LSE natural log
+ *   (or base 2), with the window, sinks and Stats layouts of _ex.
+ * descale_q / descale_k / descale_v: device pointers to one fp32 each, read by
+ * the kernel.  Q/K/V strides count elements (= bytes); o is bf16 as in
+ * sdpa_prefill_thd.
+ * Supported: d_qk == d_v == 128; Q/K/V strides multiples of 16, O strides
+ * multiples of 8; q/k/v/o 16-byte aligned.  Else SDPA_ERR_UNSUPPORTED.
+ */
+int sdpa_prefill_thd_fp8(const void* q, int64_t q_st, int64_t q_sh,
+                         const void* k, int64_t k_st, int64_t k_sh,
+                         const void* v, int64_t v_st, int64_t v_sh,
+                         void* o, int64_t o_st, int64_t o_sh,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                         int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                         int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v,
+                         float scale, int32_t causal, int32_t window_left, const float* sinks,
+                         float* lse, int32_t lse_layout, int32_t lse_s_max, int32_t stats_log2,
+                         const float* descale_q, const float* descale_k,
+                         const float* descale_v, void* stream);
 
 /*
  * Bytes of caller workspace sdpa_decode_paged needs for these extents

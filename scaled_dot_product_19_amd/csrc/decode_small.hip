@@ -43,7 +43,6 @@ namespace sdpa {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -55,20 +54,6 @@ __device__ __forceinline__ f32x4 mfma16_k16(s16x4 a, s16x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma16_fp8(uint64_t a, uint64_t b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)b, c, 0, 0, 0);
 }
-// 8 E4M3 codes -> 8 bf16.  Every E4M3 value has at most 4 significant bits,
-// so the top half of its fp32 conversion is the same value in bf16.
-__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-    const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-    auto hi2 = [](float lo, float hi) {
-        return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
-                                     0x07060302u);
-    };
-    return uint4{hi2(a[0], a[1]), hi2(b[0], b[1]), hi2(c[0], c[1]), hi2(d[0], d[1])};
-}
-
 struct SmallKArgs {
     const void* q;   // bf16, or E4M3 codes (F8)
     const void* kp;

@@ -38,6 +38,17 @@
 //                           (bf16); A = V^T read from the row-major V tile
 //                           with ds_read_b64_tr_b16, which hands each lane
 //                           four consecutive keys of one column.
+//
+// Per-tensor FP8 (E4M3) instantiation (F8, D = 128): Q, K and V are E4M3
+// codes standing for descale_{q,k,v} times their values (cuDNN Frontend
+// v1.31.0 Release Notes, per-tensor FP8 D128; the SM120 per-tensor E4M3
+// forward engine).  K and V tiles arrive as codes (half the DMA bytes);
+// S^T = K Q^T runs on the FP8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4 with
+// unit scales: four times the K depth of the bf16 MFMA per instruction),
+// scale * descale_q * descale_k folded into the exponent.  Each V tile is
+// widened exactly to a bf16 V tile in LDS, half by each wave group during
+// its softmax phase, so P V stays on the bf16 MFMA with P in bf16;
+// descale_v multiplies the normalized output.
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 #include "tile_ops.h"
@@ -61,7 +72,10 @@ struct PrefillKArgs {
     const int32_t* cu_kv;
     int32_t batch, hq, group, nh, n_hg, n_qtiles;
     float c;          // |scale| * log2(e)
-    uint32_t q_sign;  // 0x80008000 when scale < 0 (Q is negated on load), else 0
+    uint32_t q_sign;  // sign bits of every element when scale < 0 (Q is negated on load), else 0
+    const float* descale_q;  // F8 only: one fp32 each, read on the device
+    const float* descale_k;
+    const float* descale_v;
     int32_t causal;
     float* lse;
     int32_t lse_layout, lse_s_max;  // layout 3 (head-major): lse_s_max = per-head stride
@@ -97,15 +111,27 @@ constexpr int kXcds = 8;
 __device__ __align__(256) uint32_t g_prefill_queue[kQueueSlots][32];
 
 constexpr float kLazyRescale = 8.f;  // log2 units the running max may lag behind
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// 32x32x64 on E4M3 codes (format 0 for A and B), unit block scales (E8M0 127)
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+}
 constexpr int kWin = 4;              // LDS operand fragments read ahead of the MFMAs
-template <int D, int BN, int S, int NW>
+template <int D, int BN, int S, int NW, bool F8 = false>
 struct PCfg {
     static constexpr int THREADS = 64 * NW;
-    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-    static constexpr int ROW_B = 2 * D;                // bytes per row
-    static constexpr int TILE_B = BN * ROW_B;          // bytes of a K (or V) tile
-    static constexpr int STAGE_B = 2 * TILE_B;         // K tile then V tile
+    static constexpr int EB = F8 ? 1 : 2;              // bytes per stored element
+    static constexpr int CPR = EB * D / 16;            // 16-byte chunks per stored row
+    static constexpr int ROW_B = EB * D;               // bytes per stored row
+    static constexpr int TILE_B = BN * ROW_B;          // bytes of a stored K (or V) tile
+    static constexpr int VROW_B = 2 * D;               // bytes per bf16 V row
+    static constexpr int VCPR = D / 8;                 // 16-byte chunks per bf16 V row
+    // stage: K tile, V tile (as stored), then for F8 the V tile widened to bf16
+    static constexpr int VOFF = F8 ? 2 * TILE_B : TILE_B;  // bf16 V tile in a stage
+    static constexpr int STAGE_B = F8 ? 2 * TILE_B + BN * VROW_B : 2 * TILE_B;
     static constexpr int LDS_BYTES = S * STAGE_B;
+    static constexpr int KK8 = D / 64;                 // k-steps of the FP8 MFMA
     static constexpr int NI = TILE_B / 1024 / NW;      // LDS DMA instructions per wave per tile
     static constexpr int NKB = BN / 32;                // 32-key blocks of a tile
     static constexpr int NB = D / 32;                  // 32-row blocks of O^T
@@ -130,12 +156,13 @@ __device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) { return atomicA
 // One work item: NH heads x NW / NH blocks of 32 query rows of one sequence,
 // all keys it sees.  Uniform across the work-group (every exit is taken by
 // all waves).  On return every LDS DMA of the item has landed.
-template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED>
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED, bool F8>
 __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& a, const int item,
                                                             char* const lds, const uint32_t lds_base,
                                                             uint32_t* const tctr, uint32_t& ticket) {
     static_assert(!PP || (NW == 8 && S >= 4), "ping-pong needs two wave groups and S >= 4");
-    using C = PCfg<D, BN, S, NW>;
+    static_assert(!F8 || (PP && !PAGED && D == 128), "FP8: the D = 128 ping-pong THD kernel");
+    using C = PCfg<D, BN, S, NW, F8>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // item = level * n_pairs + pair: level = causal row block counted from
@@ -224,16 +251,17 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // lane L of it writes chunk position p = (w NI + j) * 64 + L, i.e. row
     // p / CPR, physical chunk p % CPR, and so fetches logical chunk
     // swz(row, p % CPR) of that row.  These byte offsets never change.
-    const bf16_t* kb0 = a.k + (int64_t)kv_beg * a.k_st + (int64_t)kvh * a.k_sh;
-    const bf16_t* vb0 = a.v + (int64_t)kv_beg * a.v_st + (int64_t)kvh * a.v_sh;
-    const int k_st2 = 2 * (int)a.k_st, v_st2 = 2 * (int)a.v_st;
+    const char* kb0 = reinterpret_cast<const char*>(a.k) + C::EB * ((int64_t)kv_beg * a.k_st + (int64_t)kvh * a.k_sh);
+    const char* vb0 = reinterpret_cast<const char*>(a.v) + C::EB * ((int64_t)kv_beg * a.v_st + (int64_t)kvh * a.v_sh);
+    const int k_st2 = C::EB * (int)a.k_st, v_st2 = C::EB * (int)a.v_st;  // byte strides
     int k_src[C::NI], v_src[C::NI];
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
         const int p = (wave * C::NI + j) * 64 + lane;
         const int row = p / C::CPR, pc = p % C::CPR;
         k_src[j] = row * k_st2 + 16 * swz_k<C::CPR>(row, pc);
-        v_src[j] = row * v_st2 + 16 * swz_v<C::CPR>(row, pc);
+        // an FP8 V tile stays unswizzled: it is only read row-contiguously, by the widening
+        v_src[j] = row * v_st2 + 16 * (F8 ? pc : swz_v<C::CPR>(row, pc));
     }
     // Paged: the K and V page ids of the next tile to be issued (scalar
     // loads).  An outstanding scalar load makes every later LDS wait a full
@@ -258,8 +286,8 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         // and reads nothing
         const int k0 = lo + t * BN;
         const int nvalid = min(BN, kv_end - k0);
-        const bf16_t* kt;
-        const bf16_t* vt;
+        const void* kt;
+        const void* vt;
         if constexpr (PAGED) {
             // BN divides the page size and lo is a multiple of it: the tile
             // lies in one page (K and V pages looked up independently)
@@ -267,11 +295,11 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             kt = a.k + (int64_t)pk_nx * a.k_sp + in_page * a.k_st + (int64_t)kvh * a.k_sh;
             vt = a.v + (int64_t)pv_nx * a.v_sp + in_page * a.v_st + (int64_t)kvh * a.v_sh;
         } else {
-            kt = kb0 + (int64_t)k0 * a.k_st;
-            vt = vb0 + (int64_t)k0 * a.v_st;
+            kt = kb0 + (int64_t)k0 * k_st2;
+            vt = vb0 + (int64_t)k0 * v_st2;
         }
-        const u32x4 kr = make_rsrc(kt, nvalid > 0 ? (nvalid - 1) * k_st2 + 2 * D : 0);
-        const u32x4 vr = make_rsrc(vt, nvalid > 0 ? (nvalid - 1) * v_st2 + 2 * D : 0);
+        const u32x4 kr = make_rsrc(kt, nvalid > 0 ? (nvalid - 1) * k_st2 + C::ROW_B : 0);
+        const u32x4 vr = make_rsrc(vt, nvalid > 0 ? (nvalid - 1) * v_st2 + C::ROW_B : 0);
         const uint32_t st = lds_base + (t % S) * C::STAGE_B + wave * C::NI * 1024;
 #pragma unroll
         for (int j = 0; j < C::NI; ++j) dma16(kr, st + j * 1024, k_src[j]);
@@ -288,19 +316,51 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     }
     if constexpr (PP) page_ids(S - 2);  // for M(0)
 
-    // Q^T operand: lane (col, half) holds d = 16 kk + 8 half .. +8 of row i
-    bf16x8 qf[C::KK];
+    // log2-domain logit scale and the sign flip of Q; FP8 folds in
+    // descale_q * descale_k (a negative product flips Q like a negative scale)
+    float c = a.c;
+    uint32_t q_sign = a.q_sign;
+    float o_mul = 1.f;  // descale_v
+    if constexpr (F8) {
+        const float dqk = a.descale_q[0] * a.descale_k[0];
+        c *= fabsf(dqk);
+        if (dqk < 0.f) q_sign ^= 0x80808080u;
+        o_mul = a.descale_v[0];
+    }
+    // Q^T operand.  bf16: lane (col, half) holds d = 16 kk + 8 half .. +8 of
+    // row i.  FP8: for k-step kk it holds the 32 codes d = 64 kk + 32 half ..
+    // +32; the K fragment of the same lane half covers the same d (the FP8
+    // MFMA pairs the bytes of A and B lanes of equal half one to one).
+    constexpr int NQF = F8 ? 1 : C::KK;
+    constexpr int NQF8 = F8 ? C::KK8 : 1;
+    bf16x8 qf[NQF];
+    i32x8 qf8[NQF8];
     {
-        const bf16_t* qrow = a.q + (int64_t)(q_beg + i) * a.q_st + (int64_t)h * a.q_sh + 8 * half;
+        const char* qrow = reinterpret_cast<const char*>(a.q) +
+                           C::EB * ((int64_t)(q_beg + i) * a.q_st + (int64_t)h * a.q_sh);
+        if constexpr (F8) {
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) {
-            uint4 w = {0u, 0u, 0u, 0u};
-            if (row_ok) w = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
-            w.x ^= a.q_sign;
-            w.y ^= a.q_sign;
-            w.z ^= a.q_sign;
-            w.w ^= a.q_sign;
-            qf[kk] = __builtin_bit_cast(bf16x8, w);
+            for (int kk = 0; kk < C::KK8; ++kk) {
+                uint4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+                if (row_ok) {
+                    w0 = *reinterpret_cast<const uint4*>(qrow + 64 * kk + 32 * half);
+                    w1 = *reinterpret_cast<const uint4*>(qrow + 64 * kk + 32 * half + 16);
+                }
+                qf8[kk] = i32x8{(int)(w0.x ^ q_sign), (int)(w0.y ^ q_sign), (int)(w0.z ^ q_sign),
+                                (int)(w0.w ^ q_sign), (int)(w1.x ^ q_sign), (int)(w1.y ^ q_sign),
+                                (int)(w1.z ^ q_sign), (int)(w1.w ^ q_sign)};
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk) {
+                uint4 w = {0u, 0u, 0u, 0u};
+                if (row_ok) w = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 16 * half);
+                w.x ^= q_sign;
+                w.y ^= q_sign;
+                w.z ^= q_sign;
+                w.w ^= q_sign;
+                qf[kk] = __builtin_bit_cast(bf16x8, w);
+            }
         }
     }
 
@@ -313,6 +373,14 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
 #pragma unroll
     for (int kk = 0; kk < KKW; ++kk)
         k_rd[kk] = col * C::ROW_B + 16 * swz_k<C::CPR>(col, 2 * kk + half);
+    // FP8 K fragment: lane (key = col, half) reads logical chunks 4 kk + 2 half
+    // and + 1 (32 codes) of row 32 kb + col; the swizzle depends on the row
+    // modulo 16 only, so block kb adds 32 rows exactly.
+    constexpr int NK8 = F8 ? 2 * C::KK8 : 1;
+    int k_rd8[NK8];
+#pragma unroll
+    for (int j = 0; j < NK8; ++j)
+        k_rd8[j] = col * C::ROW_B + 16 * swz_k<C::CPR>(col, 4 * (j / 2) + 2 * half + (j % 2));
     // V^T fragment (A of O^T), two transpose reads per 16-key step: lane l of
     // 16-lane group G = l / 16 supplies row 16 kst + 4 half + (l % 16) / 4
     // (+8 for the second read) and the 4 columns starting at
@@ -326,7 +394,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         const int cg = 2 * ((lane >> 4) & 1) + (lane & 3) / 2;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
-            v_rd[nb] = C::TILE_B + r0 * C::ROW_B + 16 * swz_v<C::CPR>(r0, 4 * nb + cg) +
+            v_rd[nb] = C::VOFF + r0 * C::VROW_B + 16 * swz_v<C::VCPR>(r0, 4 * nb + cg) +
                        8 * (lane & 1);
     }
 
@@ -353,9 +421,9 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // two transpose reads
     auto vfrag_at = [&](const char* st, int o) __attribute__((always_inline)) {
         const int nb = o % C::NB, kst = o / C::NB;
-        const char* vp = st + v_rd[nb % NBW] + (nb / NBW) * 256 + kst * 16 * C::ROW_B;
+        const char* vp = st + v_rd[nb % NBW] + (nb / NBW) * 256 + kst * 16 * C::VROW_B;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::ROW_B));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VROW_B));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto qk = [&](const char* st, f32x16(&s)[C::NKB]) __attribute__((always_inline)) {
@@ -376,6 +444,27 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         for (int o = 0; o < NQK; ++o) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (o + kWin < NQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+    // FP8 QK: NKB x KK8 MFMAs of 32x32x64, each with a 32-code K fragment
+    // (two 16-byte reads); all fragments are read first.
+    auto qk8 = [&](const char* st, f32x16(&s)[C::NKB]) __attribute__((always_inline)) {
+        if constexpr (F8) {
+            constexpr int N8 = C::NKB * C::KK8;
+            const f32x16 zero = {};
+            i32x8 fk[N8];
+#pragma unroll
+            for (int o = 0; o < N8; ++o) {
+                const int kb = o % C::NKB, kk = o / C::NKB;
+                const char* kp = st + kb * 32 * C::ROW_B;
+                const uint4 w0 = *reinterpret_cast<const uint4*>(kp + k_rd8[2 * kk]);
+                const uint4 w1 = *reinterpret_cast<const uint4*>(kp + k_rd8[2 * kk + 1]);
+                fk[o] = i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
+                              (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+            }
+#pragma unroll
+            for (int o = 0; o < N8; ++o)
+                s[o % C::NKB] = mfma_32x32x64_fp8(fk[o], qf8[o / C::NKB], o < C::NKB ? zero : s[o % C::NKB]);
         }
     };
     // softmax: scores s of the tile whose first key is key0 -> P^T operands pb
@@ -401,7 +490,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             for (int r = 0; r < 16; r += 2) mx = max3(mx, s[kb][r], s[kb][r + 1]);
         }
         mx = half_max(mx);
-        const float mt = mx == neg_inf() ? neg_inf() : mx * a.c;
+        const float mt = mx == neg_inf() ? neg_inf() : mx * c;
         // lazy rescale: move the running max only when the tile's exceeds it by > 8
         const bool grow = mt > m + kLazyRescale;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -422,9 +511,11 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                float p0 = fast_exp2(__builtin_fmaf(s[kb][r], a.c, nm));
-                float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], a.c, nm));
-                if (CZ && need_mask) {  // c > 0: exp2(-inf) is already 0
+                float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, nm));
+                float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, nm));
+                // c > 0: exp2(-inf) is already 0; FP8's c comes from device
+                // descales and may be 0
+                if ((CZ || F8) && need_mask) {
                     p0 = s[kb][r] == neg_inf() ? 0.f : p0;
                     p1 = s[kb][r + 1] == neg_inf() ? 0.f : p1;
                 }
@@ -547,10 +638,33 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         // earlier).  Tile t is read first in window 2t; each wave has waited
         // for its own part of it before the barrier that opens that window
         // (group 0 after V(t - 1), group 1 after M(t - 1)).
+        //
+        // FP8: the bf16 V tile of tile t is written by the early group in
+        // V(t) (window 2t + 1, rows 0..31) and by the late group in V(t - 1)
+        // (window 2t, rows 32..63; for tile 0 in window 0, where the late
+        // group otherwise waits).  Tile t has landed by window 2t and its
+        // first P V (early group) runs in window 2t + 2.
         const bool late = wave >= NW / 2;
+        // rows 32 part .. +32 of tile t: E4M3 codes -> the stage's bf16 V tile
+        // (one 16-code chunk per thread of the group)
+        auto convert_v = [&](int t, int part) __attribute__((always_inline)) {
+            if constexpr (F8) {
+                char* st = lds + (t % S) * C::STAGE_B;
+                const int tt = tid & (NW / 2 * 64 - 1);
+                const int row = 32 * part + tt / C::CPR, ch = tt % C::CPR;
+                const uint4 w = *reinterpret_cast<const uint4*>(st + C::TILE_B + row * C::ROW_B + 16 * ch);
+                char* vrow = st + C::VOFF + row * C::VROW_B;
+                *reinterpret_cast<uint4*>(vrow + 16 * swz_v<C::VCPR>(row, 2 * ch)) = e4m3x8_to_bf16(uint2{w.x, w.y});
+                *reinterpret_cast<uint4*>(vrow + 16 * swz_v<C::VCPR>(row, 2 * ch + 1)) = e4m3x8_to_bf16(uint2{w.z, w.w});
+            }
+        };
+        static_assert(!F8 || (BN == 64 && 32 * C::CPR == NW / 2 * 64), "one chunk per thread of a group");
         wait_vmcnt<PER_TILE * (S - 3)>();
         __syncthreads();
-        if (late) __syncthreads();
+        if (late) {
+            if (n_tiles > 0) convert_v(0, 1);
+            __syncthreads();
+        }
         // end of an MFMA phase / of a VALU phase
         auto m_end = [&]() __attribute__((always_inline)) {
             __builtin_amdgcn_s_setprio(0);
@@ -560,6 +674,13 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         // V(t): softmax of tile t, or P = 0 for a wave that sees none of its keys
         auto v_phase = [&](int t) __attribute__((always_inline)) {
             page_ids(t + S - 1);  // issued by M(t + 1)
+            if constexpr (F8) {
+                if (!late) {
+                    convert_v(t, 0);
+                } else if (t + 1 < n_tiles) {
+                    convert_v(t + 1, 1);
+                }
+            }
             const int key0 = lo + t * BN;
             if (sees(key0)) {
                 softmax(s, pb, key0, masked(key0));
@@ -576,15 +697,24 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             __builtin_amdgcn_s_setprio(1);
             page_ids_ready();
             issue(S - 2);
-            qk(stage_ptr(0), s);
+            if constexpr (F8)
+                qk8(stage_ptr(0), s);
+            else
+                qk(stage_ptr(0), s);
             m_end();
             v_phase(0);
             // M(t) = PV(t - 1) and QK(t) as one MFMA stream (one code path:
             // a wave whose keys end before tile t computes QK(t) and drops it)
             for (int t = 1; t < n_tiles; ++t) {
                 __builtin_amdgcn_s_setprio(1);
-                pv_qk(stage_ptr(t - 1), pb, stage_ptr(t), s,
-                      [&]() __attribute__((always_inline)) { issue(t + S - 2); });
+                if constexpr (F8) {
+                    issue(t + S - 2);
+                    pv(stage_ptr(t - 1), pb);
+                    qk8(stage_ptr(t), s);
+                } else {
+                    pv_qk(stage_ptr(t - 1), pb, stage_ptr(t), s,
+                          [&]() __attribute__((always_inline)) { issue(t + S - 2); });
+                }
                 m_end();
                 v_phase(t);
             }
@@ -638,6 +768,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             m = m2;
         }
     }
+    inv *= o_mul;  // descale_v (1 unless FP8)
     bf16_t* orow = a.o + (int64_t)(q_beg + i) * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) {
@@ -667,7 +798,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
 // Persistent grid: each work-group runs items until every queue is empty.
 // The ticket of the next item is fetched (one atomic of wave 0) while the
 // current item runs and handed to the other waves through LDS.
-template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED>
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED, bool F8>
 __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kernel(PrefillKArgs a) {
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     __shared__ int next_item;
@@ -704,7 +835,7 @@ __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kern
     int item = next_item;
     while (item >= 0) {
         uint32_t ticket = 0;
-        prefill_item<D, BN, S, NW, PP, CZ, PAGED>(a, item, lds, lds_base, &ctr[q], ticket);
+        prefill_item<D, BN, S, NW, PP, CZ, PAGED, F8>(a, item, lds, lds_base, &ctr[q], ticket);
         __syncthreads();  // every wave has read next_item of the last round
         if (threadIdx.x == 0) next_item = next_of(ticket);
         __syncthreads();
@@ -737,25 +868,25 @@ int resident_slots(K kernel, int threads, int lds_bytes) {
 
 std::atomic<uint32_t> g_slot_seq{0};
 
-template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED>
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED, bool F8>
 struct KernelTag {};
 
-template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED>
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED, bool F8 = false>
 hipError_t launch_dz(PrefillKArgs a, int64_t n_wg, hipStream_t s) {
-    using C = PCfg<D, BN, S, NW>;
-    auto kernel = prefill_bf16_kernel<D, BN, S, NW, PP, CZ, PAGED>;
+    using C = PCfg<D, BN, S, NW, F8>;
+    auto kernel = prefill_bf16_kernel<D, BN, S, NW, PP, CZ, PAGED, F8>;
     // more than 64 KiB of dynamic LDS must be requested per kernel
     hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     const int64_t slots =
-        resident_slots<KernelTag<D, BN, S, NW, PP, CZ, PAGED>>(kernel, C::THREADS, C::LDS_BYTES);
+        resident_slots<KernelTag<D, BN, S, NW, PP, CZ, PAGED, F8>>(kernel, C::THREADS, C::LDS_BYTES);
     a.slot = (int32_t)(g_slot_seq.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
     hipLaunchKernelGGL(kernel, dim3((unsigned)(n_wg < slots ? n_wg : slots)), dim3(C::THREADS),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 
-template <int D, int BN, int S, int NW, bool PP>
+template <int D, int BN, int S, int NW, bool PP, bool F8 = false>
 hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     PrefillKArgs a;
     a.q = static_cast<const bf16_t*>(pa.q);
@@ -780,7 +911,10 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     const int tile_rows = 32 * (NW / a.nh);
     a.n_qtiles = (pa.max_q + tile_rows - 1) / tile_rows;
     a.c = (pa.scale < 0.f ? -pa.scale : pa.scale) * kLog2e;
-    a.q_sign = pa.scale < 0.f ? 0x80008000u : 0u;
+    a.q_sign = pa.scale < 0.f ? (F8 ? 0x80808080u : 0x80008000u) : 0u;
+    a.descale_q = F8 ? pa.descale_q : nullptr;
+    a.descale_k = F8 ? pa.descale_k : nullptr;
+    a.descale_v = F8 ? pa.descale_v : nullptr;
     a.causal = pa.causal;
     a.lse = pa.lse;
     a.lse_layout = pa.lse_layout;
@@ -799,8 +933,8 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
     const int64_t n_wg = (int64_t)a.n_qtiles * a.n_hg * a.batch;
     if (n_wg == 0) return hipSuccess;
     if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-    return a.c == 0.f ? launch_dz<D, BN, S, NW, PP, true, false>(a, n_wg, s)
-                      : launch_dz<D, BN, S, NW, PP, false, false>(a, n_wg, s);
+    return a.c == 0.f ? launch_dz<D, BN, S, NW, PP, true, false, F8>(a, n_wg, s)
+                      : launch_dz<D, BN, S, NW, PP, false, false, F8>(a, n_wg, s);
 }
 
 // Query tokens per work item of the D = 128 kernel (8 waves of 32 rows over
@@ -843,6 +977,7 @@ hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
     a.n_qtiles = (d.sq + tokens - 1) / tokens;
     a.c = (d.scale < 0.f ? -d.scale : d.scale) * kLog2e;
     a.q_sign = d.scale < 0.f ? 0x80008000u : 0u;
+    a.descale_q = a.descale_k = a.descale_v = nullptr;
     a.causal = d.causal;
     a.lse = d.lse;
     a.lse_layout = d.lse != nullptr ? 1 : 0;  // [B, s_q, Hq] = token-major
@@ -870,6 +1005,7 @@ hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
+    if (a.fp8) return a.dqk == 128 ? launch_d<128, 64, 4, 8, true, true>(a, s) : hipErrorInvalidValue;
     switch (a.dqk) {
         case 64: return launch_d<64, 128, 4, 8, true>(a, s);
         case 128: return launch_d<128, 64, 4, 8, true>(a, s);

@@ -68,7 +68,9 @@ static int prefill_impl(const void* q, int64_t q_st, int64_t q_sh, const void* k
                         int32_t max_seqlen_kv, int32_t h_q, int32_t h_kv, int32_t d_qk,
                         int32_t d_v, float scale, int32_t causal, float* lse, int32_t lse_layout,
                         int32_t lse_s_max, int32_t window, const float* sinks, int32_t stats_log2,
-                        int32_t dtype, void* stream) {
+                        int32_t dtype, const float* descale_q, const float* descale_k,
+                        const float* descale_v, void* stream) {
+    const bool fp8 = dtype == SDPA_FP8_E4M3;
     if (batch < 0 || batch > 65535) return fail(SDPA_ERR_SHAPE, "batch=%d outside [0, 65535]", batch);
     if (h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0)
         return fail(SDPA_ERR_SHAPE, "h_q=%d must be a positive multiple of h_kv=%d", h_q, h_kv);
@@ -85,9 +87,9 @@ static int prefill_impl(const void* q, int64_t q_st, int64_t q_sh, const void* k
     if (stats_log2 != 0 && stats_log2 != 1) return fail(SDPA_ERR_SHAPE, "stats_log2 must be 0 or 1");
     const bool variant = window > 0 || sinks != nullptr || stats_log2 != 0 ||
                          lse_layout == SDPA_LSE_HEAD_MAJOR;
-    if (variant && dtype != SDPA_BF16)
+    if (variant && dtype != SDPA_BF16 && !fp8)
         return fail(SDPA_ERR_UNSUPPORTED,
-                    "windows, sinks, base-2 and head-major LSE are served for bf16 only");
+                    "windows, sinks, base-2 and head-major LSE are served for bf16 and FP8 only");
     if (lse_layout != SDPA_LSE_NONE && lse == nullptr)
         return fail(SDPA_ERR_NULL, "lse is NULL but lse_layout=%d requests Stats", lse_layout);
     if (lse_layout == SDPA_LSE_PADDED && lse_s_max < max_seqlen_q)
@@ -111,6 +113,22 @@ static int prefill_impl(const void* q, int64_t q_st, int64_t q_sh, const void* k
             if (s % 8 != 0)
                 return fail(SDPA_ERR_UNSUPPORTED,
                             "bf16 prefill needs strides that are multiples of 8 elements");
+    } else if (fp8) {
+        if (d_qk != 128 || d_v != 128)
+            return fail(SDPA_ERR_UNSUPPORTED, "FP8 prefill serves d_qk == d_v == 128; got (%d, %d)",
+                        d_qk, d_v);
+        if (k_st < d_qk || v_st < d_v)
+            return fail(SDPA_ERR_SHAPE, "K/V token rows overlap: k_st=%lld < d_qk or v_st=%lld < d_v",
+                        (long long)k_st, (long long)v_st);
+        if (k_st >= ((int64_t)1 << 22) || v_st >= ((int64_t)1 << 22))
+            return fail(SDPA_ERR_UNSUPPORTED, "FP8 prefill K/V token strides must be below 2^22");
+        const int64_t st8[6] = {q_st, q_sh, k_st, k_sh, v_st, v_sh};
+        for (int64_t x : st8)
+            if (x % 16 != 0)
+                return fail(SDPA_ERR_UNSUPPORTED,
+                            "FP8 prefill needs Q/K/V strides that are multiples of 16 elements");
+        if (o_st % 8 != 0 || o_sh % 8 != 0)
+            return fail(SDPA_ERR_UNSUPPORTED, "FP8 prefill writes bf16 O: strides multiples of 8");
     } else if (dtype == SDPA_FP32) {
         if (d_qk > 256 || d_v > 256)
             return fail(SDPA_ERR_UNSUPPORTED, "fp32 prefill serves head dims <= 256");
@@ -120,7 +138,11 @@ static int prefill_impl(const void* q, int64_t q_st, int64_t q_sh, const void* k
     if (batch == 0) return ok();
     if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_kv)
         return fail(SDPA_ERR_NULL, "q/k/v/o/cu_seqlens_q/cu_seqlens_kv must be non-NULL");
-    const size_t align = dtype == SDPA_BF16 ? 16 : 4;
+    if (fp8 && (!descale_q || !descale_k || !descale_v))
+        return fail(SDPA_ERR_NULL, "FP8 prefill needs descale_q, descale_k and descale_v");
+    if (fp8 && (!aligned(descale_q, 4) || !aligned(descale_k, 4) || !aligned(descale_v, 4)))
+        return fail(SDPA_ERR_UNSUPPORTED, "descale pointers must be 4-byte aligned");
+    const size_t align = dtype == SDPA_FP32 ? 4 : 16;
     if (!aligned(q, align) || !aligned(k, align) || !aligned(v, align) || !aligned(o, align) ||
         (lse && !aligned(lse, 4)) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4) ||
         (sinks && !aligned(sinks, 4)))
@@ -156,13 +178,17 @@ static int prefill_impl(const void* q, int64_t q_st, int64_t q_sh, const void* k
     a.window = window > 0 ? window : 0;
     a.sinks = sinks;
     a.stats_log2 = stats_log2;
+    a.fp8 = fp8 ? 1 : 0;
+    a.descale_q = fp8 ? descale_q : nullptr;
+    a.descale_k = fp8 ? descale_k : nullptr;
+    a.descale_v = fp8 ? descale_v : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (lse_layout == SDPA_LSE_PADDED) {
         hipError_t e = sdpa::launch_fill_neg_inf(lse, (int64_t)batch * lse_s_max * h_q, s);
         if (e != hipSuccess) return hip_fail(e, "padded LSE -inf fill");
     }
-    hipError_t e = dtype == SDPA_BF16 ? sdpa::launch_prefill_bf16(a, s)
-                                      : sdpa::launch_prefill_f32(a, s);
+    hipError_t e = dtype == SDPA_FP32 ? sdpa::launch_prefill_f32(a, s)
+                                      : sdpa::launch_prefill_bf16(a, s);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return ok();
 }
@@ -174,9 +200,12 @@ int sdpa_prefill_thd(const void* q, int64_t q_st, int64_t q_sh, const void* k, i
                      int32_t max_seqlen_kv, int32_t h_q, int32_t h_kv, int32_t d_qk,
                      int32_t d_v, float scale, int32_t causal, float* lse, int32_t lse_layout,
                      int32_t lse_s_max, int32_t dtype, void* stream) {
+    if (dtype == SDPA_FP8_E4M3)
+        return fail(SDPA_ERR_UNSUPPORTED, "per-tensor FP8 needs its descales: sdpa_prefill_thd_fp8");
     return prefill_impl(q, q_st, q_sh, k, k_st, k_sh, v, v_st, v_sh, o, o_st, o_sh, cu_seqlens_q,
                         cu_seqlens_kv, batch, max_seqlen_q, max_seqlen_kv, h_q, h_kv, d_qk, d_v,
-                        scale, causal, lse, lse_layout, lse_s_max, 0, nullptr, 0, dtype, stream);
+                        scale, causal, lse, lse_layout, lse_s_max, 0, nullptr, 0, dtype, nullptr,
+                        nullptr, nullptr, stream);
 }
 
 int sdpa_prefill_thd_ex(const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
@@ -187,11 +216,29 @@ int sdpa_prefill_thd_ex(const void* q, int64_t q_st, int64_t q_sh, const void* k
                         int32_t d_v, float scale, int32_t causal, int32_t window_left,
                         const float* sinks, float* lse, int32_t lse_layout, int32_t lse_s_max,
                         int32_t stats_log2, int32_t dtype, void* stream) {
+    if (dtype == SDPA_FP8_E4M3)
+        return fail(SDPA_ERR_UNSUPPORTED, "per-tensor FP8 needs its descales: sdpa_prefill_thd_fp8");
     if (window_left < 0) return fail(SDPA_ERR_SHAPE, "window_left=%d < 0", window_left);
     return prefill_impl(q, q_st, q_sh, k, k_st, k_sh, v, v_st, v_sh, o, o_st, o_sh, cu_seqlens_q,
                         cu_seqlens_kv, batch, max_seqlen_q, max_seqlen_kv, h_q, h_kv, d_qk, d_v,
                         scale, causal, lse, lse_layout, lse_s_max, window_left, sinks, stats_log2,
-                        dtype, stream);
+                        dtype, nullptr, nullptr, nullptr, stream);
+}
+
+int sdpa_prefill_thd_fp8(const void* q, int64_t q_st, int64_t q_sh, const void* k, int64_t k_st,
+                         int64_t k_sh, const void* v, int64_t v_st, int64_t v_sh, void* o,
+                         int64_t o_st, int64_t o_sh, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_kv, int32_t batch, int32_t max_seqlen_q,
+                         int32_t max_seqlen_kv, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                         int32_t d_v, float scale, int32_t causal, int32_t window_left,
+                         const float* sinks, float* lse, int32_t lse_layout, int32_t lse_s_max,
+                         int32_t stats_log2, const float* descale_q, const float* descale_k,
+                         const float* descale_v, void* stream) {
+    if (window_left < 0) return fail(SDPA_ERR_SHAPE, "window_left=%d < 0", window_left);
+    return prefill_impl(q, q_st, q_sh, k, k_st, k_sh, v, v_st, v_sh, o, o_st, o_sh, cu_seqlens_q,
+                        cu_seqlens_kv, batch, max_seqlen_q, max_seqlen_kv, h_q, h_kv, d_qk, d_v,
+                        scale, causal, lse, lse_layout, lse_s_max, window_left, sinks, stats_log2,
+                        SDPA_FP8_E4M3, descale_q, descale_k, descale_v, stream);
 }
 
 size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int32_t d_v,

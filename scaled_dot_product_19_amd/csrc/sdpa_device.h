@@ -39,6 +39,22 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// 8 OCP E4M3 codes -> 8 bf16 (gfx950's FP8 conversions read OCP E4M3).
+// Every E4M3 value has at most 4 significant bits, so the top half of its
+// fp32 conversion is the same value in bf16: the widening is exact.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 w) {
+    typedef float e4m3_f32x2 __attribute__((ext_vector_type(2)));
+    const e4m3_f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
+    const e4m3_f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
+    const e4m3_f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
+    const e4m3_f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
+    auto hi2 = [](float lo, float hi) {
+        return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                                     0x07060302u);
+    };
+    return uint4{hi2(a[0], a[1]), hi2(b[0], b[1]), hi2(c[0], c[1]), hi2(d[0], d[1])};
+}
+
 // Round-to-nearest-even float -> bf16 bits (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);

@@ -28,6 +28,10 @@ struct PrefillArgs {
     int32_t window;                 // left sliding window (<= 0: none)
     const float* sinks;             // [hq] sink logits or nullptr
     int32_t stats_log2;             // LSE in base 2
+    int32_t fp8;                    // Q/K/V are E4M3 codes (per-tensor descales below)
+    const float* descale_q;
+    const float* descale_k;
+    const float* descale_v;
 };
 
 struct DecodeArgs {

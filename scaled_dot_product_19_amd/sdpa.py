@@ -39,7 +39,7 @@ LSE_PADDED = 2
 LSE_HEAD_MAJOR = 3
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_prefill_thd", "sdpa_prefill_thd_ex", "sdpa_decode_workspace_bytes", "sdpa_decode_paged",
+EXPORTS = ("sdpa_prefill_thd", "sdpa_prefill_thd_ex", "sdpa_prefill_thd_fp8", "sdpa_decode_workspace_bytes", "sdpa_decode_paged",
            "sdpa_decode_paged_fp8",
            "sdpa_splitkv_combine", "sdpa_status_string", "sdpa_last_error_detail",
            "sdpa_version")
@@ -78,6 +78,10 @@ def load():
     lib.sdpa_prefill_thd_ex.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, I64, I64, P, P,
                                         I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P, P, I32,
                                         I32, I32, I32, P]
+    lib.sdpa_prefill_thd_fp8.restype = ctypes.c_int
+    lib.sdpa_prefill_thd_fp8.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, I64, I64, P,
+                                         P, I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P, P,
+                                         I32, I32, I32, P, P, P, P]
     lib.sdpa_decode_workspace_bytes.restype = SZ
     lib.sdpa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.sdpa_decode_paged.restype = ctypes.c_int
@@ -199,6 +203,47 @@ def prefill_thd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
         float(scale), int(bool(causal)), int(window_left), _ptr(sinks),
         _ptr(lse) if lse_layout != LSE_NONE else None, int(lse_layout), int(lse_s_max),
         int(bool(stats_log2)), _dtype_code(q), _stream(stream))
+    _check(rc)
+    return out, (lse if lse_layout != LSE_NONE else None)
+
+
+def prefill_thd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_kv: torch.Tensor, max_seqlen_q: int, max_seqlen_kv: int,
+                    scale: float, descale_q: torch.Tensor, descale_k: torch.Tensor,
+                    descale_v: torch.Tensor, causal: bool = True, window_left: int = 0,
+                    sinks: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, lse_layout: int = LSE_PACKED,
+                    lse_s_max: int = 0, stats_log2: bool = False, stream=None):
+    """sdpa_prefill_thd_fp8: q [Tq, Hq, D], k/v [Tk, Hkv, D] uint8 E4M3 codes; descales are
+    one-element fp32 device tensors.  Returns (out [Tq, Hq, D] bf16, lse as prefill_thd_ex)."""
+    lib = load()
+    for t in (q, k, v):
+        if t.dtype != torch.uint8:
+            raise TypeError("FP8 prefill takes uint8 E4M3 codes, got %s" % t.dtype)
+    for t in (descale_q, descale_k, descale_v):
+        if t.dtype != torch.float32 or t.numel() != 1:
+            raise TypeError("descales are one-element float32 tensors")
+    batch = int(cu_seqlens_q.numel()) - 1
+    hq, dqk = int(q.shape[1]), int(q.shape[2])
+    hkv, dv = int(k.shape[1]), int(v.shape[2])
+    if out is None:
+        out = torch.empty((q.shape[0], hq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse_layout == LSE_HEAD_MAJOR and lse_s_max == 0:
+        lse_s_max = int(q.shape[0])
+    if lse is None and lse_layout == LSE_PACKED:
+        lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    elif lse is None and lse_layout == LSE_PADDED:
+        lse = torch.empty((batch, lse_s_max, hq), dtype=torch.float32, device=q.device)
+    elif lse is None and lse_layout == LSE_HEAD_MAJOR:
+        lse = torch.empty((hq, lse_s_max), dtype=torch.float32, device=q.device)
+    rc = lib.sdpa_prefill_thd_fp8(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1), _ptr(v),
+        v.stride(0), v.stride(1), _ptr(out), out.stride(0), out.stride(1), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_kv), batch, int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, dqk, dv,
+        float(scale), int(bool(causal)), int(window_left), _ptr(sinks),
+        _ptr(lse) if lse_layout != LSE_NONE else None, int(lse_layout), int(lse_s_max),
+        int(bool(stats_log2)), _ptr(descale_q), _ptr(descale_k), _ptr(descale_v),
+        _stream(stream))
     _check(rc)
     return out, (lse if lse_layout != LSE_NONE else None)
 

@@ -128,6 +128,45 @@ def test_prefill_ex_empty_batch_is_ok_without_pointers():
     assert rc == sdpa.SDPA_OK and detail == ""
 
 
+def _prefill_fp8(**over):
+    lib = sdpa.load()
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation
+    args = dict(q=fake, q_st=32 * 128, q_sh=128, k=fake, k_st=8 * 128, k_sh=128, v=fake,
+                v_st=8 * 128, v_sh=128, o=fake, o_st=32 * 128, o_sh=128, cu_q=fake, cu_kv=fake,
+                batch=2, max_q=16, max_kv=16, hq=32, hkv=8, dqk=128, dv=128, scale=0.1,
+                causal=1, window=0, sinks=None, lse=fake, lse_layout=1, lse_s_max=0,
+                stats_log2=0, dq=fake, dk=fake, dv_=fake, stream=None)
+    args.update(over)
+    rc = lib.sdpa_prefill_thd_fp8(*args.values())
+    return rc, lib.sdpa_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dqk=64, dv=64), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dqk=256, dv=256), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(q_sh=136), sdpa.SDPA_ERR_UNSUPPORTED),             # Q rows need 16-byte strides
+    (dict(k_st=8 * 128 + 8), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(o_sh=132), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dq=None), sdpa.SDPA_ERR_NULL),
+    (dict(dv_=None), sdpa.SDPA_ERR_NULL),
+    (dict(dk=ctypes.c_void_p(0x100001)), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(window=-2), sdpa.SDPA_ERR_SHAPE),
+    (dict(lse_layout=3), sdpa.SDPA_ERR_LSE_LAYOUT),
+    (dict(k=ctypes.c_void_p(0x100008)), sdpa.SDPA_ERR_UNSUPPORTED),
+])
+def test_prefill_fp8_rejects(over, code):
+    rc, detail = _prefill_fp8(**over)
+    assert rc == code, (rc, detail)
+    assert detail
+
+
+def test_prefill_bf16_entries_refuse_fp8_codes():
+    rc, detail = _prefill(dtype=sdpa.SDPA_FP8_E4M3)
+    assert rc == sdpa.SDPA_ERR_UNSUPPORTED and "descale" in detail
+    rc, detail = _prefill_ex(dtype=sdpa.SDPA_FP8_E4M3)
+    assert rc == sdpa.SDPA_ERR_UNSUPPORTED and "descale" in detail
+
+
 def test_prefill_empty_batch_is_ok_without_pointers():
     rc, detail = _prefill(batch=0, q=None, k=None, v=None, o=None, cu_q=None, cu_kv=None)
     assert rc == sdpa.SDPA_OK and detail == ""
