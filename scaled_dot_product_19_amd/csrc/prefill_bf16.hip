@@ -734,10 +734,10 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // split of a paged call writes its normalized fp32 partial and LSE_c
     // (-inf and zeros when it sees no key of the row)
     float l_tot = half_sum(l);
-    if (!row_ok) return;
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if constexpr (PAGED) {
-        if (a.splits > 1) {
+        if (a.splits > 1) {  // uniform
+            if (!row_ok) return;
             const int64_t grow = (int64_t)(q_beg + i) * a.hq + h;
             float* prow = a.o_part + ((int64_t)split * a.total_rows + grow) * D;
 #pragma unroll
@@ -769,16 +769,56 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         }
     }
     inv *= o_mul;  // descale_v (1 unless FP8)
-    bf16_t* orow = a.o + (int64_t)(q_beg + i) * a.o_st + (int64_t)h * a.o_sh;
+    // Ping-pong kernels: O goes out through LDS, so that every store writes
+    // whole rows.  The wave's 32 x D bf16 block is written to its own part of
+    // the (now idle) ring as this lane's column of O^T, 16-byte chunks
+    // XOR-swizzled by the row so that neither side conflicts, and read back
+    // as 16-byte row chunks.  Each global store then covers 64 / (D / 8) full
+    // rows instead of 16 bytes of each of 32 rows.
+    if constexpr (PP) {
+        constexpr int OROW_B = 2 * D;      // bytes per O row
+        constexpr int OCPR = D / 8;        // 16-byte chunks per O row
+        constexpr int RPI = 64 / OCPR;     // rows per 64-lane read
+        static_assert((OCPR & (OCPR - 1)) == 0 && OCPR <= 64, "O row chunks");
+        static_assert(NW * 32 * OROW_B <= C::LDS_BYTES, "O staging fits the ring");
+        __syncthreads();  // every wave's DMAs have landed and its ring reads are done
+        char* const ow = lds + wave * 32 * OROW_B;
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
+        for (int nb = 0; nb < C::NB; ++nb) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = nb * 32 + 8 * g + 4 * half;
-            uint2 w;
-            w.x = pack_bf16x2(acc[nb][4 * g] * inv, acc[nb][4 * g + 1] * inv);
-            w.y = pack_bf16x2(acc[nb][4 * g + 2] * inv, acc[nb][4 * g + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + n) = w;
+            for (int g = 0; g < 4; ++g) {
+                // d = nb 32 + 8 g + 4 half .. +4: chunk 4 nb + g, bytes 8 half ..
+                const int pc = (4 * nb + g) ^ (col & (OCPR - 1));
+                uint2 w;
+                w.x = pack_bf16x2(acc[nb][4 * g] * inv, acc[nb][4 * g + 1] * inv);
+                w.y = pack_bf16x2(acc[nb][4 * g + 2] * inv, acc[nb][4 * g + 3] * inv);
+                *reinterpret_cast<uint2*>(ow + col * OROW_B + 16 * pc + 8 * half) = w;
+            }
+        }
+        const int rc = lane % OCPR;  // the chunk this lane moves
+#pragma unroll
+        for (int j = 0; j < 32 / RPI; ++j) {
+            const int r = j * RPI + lane / OCPR;
+            const uint4 w = *reinterpret_cast<const uint4*>(ow + r * OROW_B + 16 * (rc ^ (r & (OCPR - 1))));
+            if (i0 + r < lq) {
+                bf16_t* orow = a.o + (int64_t)(q_beg + i0 + r) * a.o_st + (int64_t)h * a.o_sh;
+                *reinterpret_cast<uint4*>(orow + 8 * rc) = w;
+            }
+        }
+    }
+    if (!row_ok) return;
+    if constexpr (!PP) {
+        bf16_t* orow = a.o + (int64_t)(q_beg + i) * a.o_st + (int64_t)h * a.o_sh;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = nb * 32 + 8 * g + 4 * half;
+                uint2 w;
+                w.x = pack_bf16x2(acc[nb][4 * g] * inv, acc[nb][4 * g + 1] * inv);
+                w.y = pack_bf16x2(acc[nb][4 * g + 2] * inv, acc[nb][4 * g + 3] * inv);
+                *reinterpret_cast<uint2*>(orow + n) = w;
+            }
         }
     }
     if (a.lse != nullptr && half == 0) {
