@@ -42,6 +42,10 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
+# FP8 prefill runs S = K Q^T (half the flops) on the FP8 MFMA and P V on the
+# bf16 MFMA: the time-weighted peak of that mix
+PEAK_FP8_PREFILL_TFLOPS = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
 
 
 def log(msg):
@@ -449,6 +453,62 @@ def run_decode_variant(args, torch, inputs, sdpa, dev):
     print(json.dumps(line), flush=True)
 
 
+def time_prefill(torch, steps, warmup, call):
+    """Average ms of `call` (one prefill launch) over `steps` back-to-back launches."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def run_fp8_prefill(args, torch, inputs, sdpa, dev):
+    """--fp8-prefill: the THD prefill workload (same seed, lengths and fp32 draws) in
+    per-tensor FP8 E4M3, and the bf16 workload on the same GPU."""
+    case = inputs.thd_prefill_d128()
+    c8 = inputs.fp8_thd_case(inputs.SEED_BASE + 2, hq=32, hkv=8, d=128, batch=8, lo=128,
+                             hi=4096, name=case.name.replace("bf16", "fp8"))
+    assert c8.lengths_q == case.lengths_q
+    stream = torch.cuda.current_stream()
+    T = int(case.cu_q[-1])
+    cu_q, cu_kv = case.cu_q.to(dev), case.cu_kv.to(dev)
+    o = torch.empty((T, case.hq, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, case.hq), dtype=torch.float32, device=dev)
+    q8, k8, v8 = c8.q.to(dev), c8.k.to(dev), c8.v.to(dev)
+    dq, dk, dv = (torch.tensor([x], dtype=torch.float32, device=dev) for x in c8.descale)
+    ms8 = time_prefill(torch, args.steps, args.warmup, lambda: sdpa.prefill_thd_fp8(
+        q8, k8, v8, cu_q, cu_kv, case.max_q, case.max_kv, case.scale, dq, dk, dv, True,
+        out=o, lse=lse, lse_layout=sdpa.LSE_PACKED, stream=stream))
+    del q8, k8, v8
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    ms16 = time_prefill(torch, args.steps, args.warmup, lambda: sdpa.prefill_thd(
+        q, k, v, cu_q, cu_kv, case.max_q, case.max_kv, case.scale, True, out=o, lse=lse,
+        lse_layout=sdpa.LSE_PACKED, stream=stream))
+    flops = prefill_flops(case.lengths_q, case.lengths_kv, case.hq, 128, 128)
+    tf = flops / (ms8 * 1e-3) / 1e12
+    line = {"metric": "FP8 prefill attn TFLOP/s (% of the FP8-QK / bf16-PV MFMA peak)",
+            "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms8, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+            "data": "synthetic (seeded N(0,1) fp32 quantized per tensor to E4M3)",
+            "config": {"workload": c8.name, "prefill_lengths": case.lengths_q, "flop": flops,
+                       "bf16_ms_same_gpu": round(ms16, 4),
+                       "speedup_vs_bf16": round(ms16 / ms8, 3)},
+            "roofline": {"kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false, false, true>",
+                         "bound": "mfma", "achieved": round(tf, 2),
+                         "peak": round(PEAK_FP8_PREFILL_TFLOPS, 1), "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP8_PREFILL_TFLOPS, 4),
+                         "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -472,6 +532,9 @@ def main():
     ap.add_argument("--fp8-decode", action="store_true",
                     help="time only the paged decode workload in per-tensor FP8 E4M3 (and in "
                          "bf16 on the same GPU for the ratio)")
+    ap.add_argument("--fp8-prefill", action="store_true",
+                    help="time only the THD prefill workload in per-tensor FP8 E4M3 (and in "
+                         "bf16 on the same GPU)")
     ap.add_argument("--mla-aliased", action="store_true",
                     help="time only the MLA-shaped decode over an absorbed-MLA cache (V = the "
                          "first 512 columns of the 576-wide K rows, one page table)")
@@ -499,6 +562,9 @@ def main():
         return
     if args.window_prefill:
         run_window_prefill(args, torch, inputs, sdpa, dev)
+        return
+    if args.fp8_prefill:
+        run_fp8_prefill(args, torch, inputs, sdpa, dev)
         return
     if args.mtp_sweep or args.mla_aliased or args.fp8_decode:
         run_decode_variant(args, torch, inputs, sdpa, dev)
