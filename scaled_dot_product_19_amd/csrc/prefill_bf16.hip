@@ -593,8 +593,13 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // The next item's ticket: it returns while this item runs (the wait
     // before the epilogue covers it).  Q is needed first, so that the wait
     // for it does not include the atomic's round trip.
+    if constexpr (F8) {
 #pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) asm volatile("" ::"v"(qf[kk]));
+        for (int kk = 0; kk < NQF8; ++kk) asm volatile("" ::"v"(qf8[kk]));
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < NQF; ++kk) asm volatile("" ::"v"(qf[kk]));
+    }
     if (tid == 0) ticket = ticket_async(tctr);
 
     if constexpr (!PP) {
