@@ -650,11 +650,11 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         // for its own part of it before the barrier that opens that window
         // (group 0 after V(t - 1), group 1 after M(t - 1)).
         //
-        // FP8: the bf16 V tile of tile t is written by the early group in
-        // V(t) (window 2t + 1, rows 0..31) and by the late group in V(t - 1)
-        // (window 2t, rows 32..63; for tile 0 in window 0, where the late
-        // group otherwise waits).  Tile t has landed by window 2t and its
-        // first P V (early group) runs in window 2t + 2.
+        // FP8: the bf16 V tile of tile t is written in the MFMA phases M(t),
+        // where the VALU is otherwise idle: rows 0..31 by the early group
+        // (window 2t), rows 32..63 by the late group (window 2t + 1), each
+        // after issuing its PV(t - 1) MFMAs.  Tile t has landed by window 2t
+        // and its first P V (early group) runs in window 2t + 2.
         const bool late = wave >= NW / 2;
         // rows 32 part .. +32 of tile t: E4M3 codes -> the stage's bf16 V tile
         // (one 16-code chunk per thread of the group)
@@ -672,10 +672,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         static_assert(!F8 || (BN == 64 && 32 * C::CPR == NW / 2 * 64), "one chunk per thread of a group");
         wait_vmcnt<PER_TILE * (S - 3)>();
         __syncthreads();
-        if (late) {
-            if (n_tiles > 0) convert_v(0, 1);
-            __syncthreads();
-        }
+        if (late) __syncthreads();
         // end of an MFMA phase / of a VALU phase
         auto m_end = [&]() __attribute__((always_inline)) {
             __builtin_amdgcn_s_setprio(0);
@@ -685,13 +682,6 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         // V(t): softmax of tile t, or P = 0 for a wave that sees none of its keys
         auto v_phase = [&](int t) __attribute__((always_inline)) {
             page_ids(t + S - 1);  // issued by M(t + 1)
-            if constexpr (F8) {
-                if (!late) {
-                    convert_v(t, 0);
-                } else if (t + 1 < n_tiles) {
-                    convert_v(t + 1, 1);
-                }
-            }
             const int key0 = lo + t * BN;
             if (sees(key0)) {
                 softmax(s, pb, key0, masked(key0));
@@ -708,10 +698,12 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             __builtin_amdgcn_s_setprio(1);
             page_ids_ready();
             issue(S - 2);
-            if constexpr (F8)
+            if constexpr (F8) {
                 qk8(stage_ptr(0), s);
-            else
+                convert_v(0, late ? 1 : 0);
+            } else {
                 qk(stage_ptr(0), s);
+            }
             m_end();
             v_phase(0);
             // M(t) = PV(t - 1) and QK(t) as one MFMA stream (one code path:
@@ -721,6 +713,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
                 if constexpr (F8) {
                     issue(t + S - 2);
                     pv(stage_ptr(t - 1), pb);
+                    convert_v(t, late ? 1 : 0);
                     qk8(stage_ptr(t), s);
                 } else {
                     pv_qk(stage_ptr(t - 1), pb, stage_ptr(t), s,
