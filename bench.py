@@ -171,8 +171,8 @@ def cpu_baseline_prefill(case, target_s, threads):
     n = int(max(8 * threads, min(200000, 8 * threads * target_s / max(dt, 1e-3))))
     f, dt = run(n)
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d random (token, head) rows of the THD prefill workload, fp64, %.1f s"
-                      % (n, dt)}
+            "sample": "%d random (token, head) rows of the %s workload, fp64, %.1f s"
+                      % (n, case.name, dt)}
 
 
 def cpu_baseline_decode(pc, target_s, threads):
@@ -206,8 +206,9 @@ def cpu_baseline_decode(pc, target_s, threads):
     n = int(max(2, min(pc.batch * pc.hkv * 4, max(2, threads // G) * target_s / max(dt, 1e-3))))
     by, dt, nrows = run(n)
     return {"value": by / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d random (sequence, KV head) units (%d query rows) of the paged decode "
-                      "workload, 8-way split + LSE merge, fp64, %.1f s" % (n, nrows, dt)}
+            "sample": "%d random (sequence, KV head) units (%d query rows) of the %s workload, "
+                      "%d-way split + LSE merge, fp64, %.1f s"
+                      % (n, nrows, pc.name, pc.num_splits, dt)}
 
 
 def window_prefill_flops(lengths_q, lengths_kv, hq, dqk, dv, causal, window):
@@ -327,6 +328,49 @@ def run_chunked_prefill(args, torch, inputs, sdpa, dev):
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                          "traffic": None}}
     print(json.dumps(line), flush=True)
+
+
+def per_call_ms(torch, stream, call, steps, warmup, between=None):
+    """Milliseconds of each of `steps` calls, from HIP events recorded on `stream` right
+    before and after the call (after `warmup` untimed calls).  `between()` runs before
+    every call, outside its events (e.g. a cache flush)."""
+    for _ in range(warmup):
+        if between is not None:
+            between()
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        if between is not None:
+            between()
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def ms_stats(ms):
+    """mean / median / min of per-call milliseconds."""
+    srt = sorted(ms)
+    n = len(srt)
+    med = srt[n // 2] if n % 2 else 0.5 * (srt[n // 2 - 1] + srt[n // 2])
+    return {"mean": round(sum(ms) / n, 4), "median": round(med, 4), "min": round(srt[0], 4)}
+
+
+MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MiB MALL
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def time_decode(torch, sdpa, pc, dev, steps, warmup, q=None, kp=None, vp=None):
@@ -509,6 +553,130 @@ def run_fp8_prefill(args, torch, inputs, sdpa, dev):
     print(json.dumps(line), flush=True)
 
 
+def decode_visible_pairs(lens, sq, causal):
+    """(token, key) pairs a paged decode computes per query head: token t of a sequence of
+    length L sits at key position L - sq + t and sees keys 0 .. L - sq + t (causal) or all
+    L keys."""
+    pairs = 0
+    for L in lens:
+        for t in range(sq):
+            pairs += max(0, min(L, L - sq + t + 1)) if causal else L
+    return pairs
+
+
+def d256_leg(args, torch, inputs, sdpa, dev, stream, threads, ragged):
+    """The D = 256 prefill workload (dense 2 x 8192 or ragged {8192, 3000}, 24/2 heads,
+    padded [2, 8192, 24] LSE seeded -inf by the call): per-call HIP events around
+    sdpa_prefill_thd (the -inf fill and the prefill kernel)."""
+    case = inputs.ragged_prefill_d256() if ragged else inputs.dense_prefill_d256()
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    cu_q, cu_kv = case.cu_q.to(dev), case.cu_kv.to(dev)
+    T = int(case.cu_q[-1])
+    o = torch.empty((T, case.hq, 256), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((2, 8192, case.hq), dtype=torch.float32, device=dev)
+
+    def call():
+        sdpa.prefill_thd(q, k, v, cu_q, cu_kv, case.max_q, case.max_kv, case.scale, True, out=o,
+                         lse=lse, lse_layout=sdpa.LSE_PADDED, lse_s_max=8192, stream=stream)
+
+    ms = per_call_ms(torch, stream, call, args.steps, args.warmup)
+    st = ms_stats(ms)
+    flops = prefill_flops(case.lengths_q, case.lengths_kv, case.hq, 256, 256)
+    tf = flops / (st["mean"] * 1e-3) / 1e12
+    log("%s: %.4f ms mean (median %.4f, min %.4f) -> %.1f TFLOP/s (%.1f%% of bf16 peak)"
+        % (case.name, st["mean"], st["median"], st["min"], tf, 100 * tf / PEAK_BF16_TFLOPS))
+    leg = {"workload": case.name, "lengths": case.lengths_q, "flop": flops, "ms": st,
+           "value": round(tf, 2), "unit": "TFLOP/s",
+           "roofline": {"kernel": "prefill_bf16_kernel<256, 32, 4, 4, false, false, false, false>",
+                        "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None}}
+    del q, k, v, o
+    if not args.no_cpu_baseline:
+        leg["cpu_baseline"] = cpu_baseline_prefill(case, args.cpu_seconds / 2, threads)
+        log("  oracle: %.3g TFLOP/s (%s)" % (leg["cpu_baseline"]["value"],
+                                            leg["cpu_baseline"]["sample"]))
+    return leg
+
+
+def mla_leg(args, torch, inputs, sdpa, dev, stream, threads):
+    """The absorbed-MLA-shaped decode (576/512, 128/1 heads, 2 tokens, B = 32, 16 splits):
+    per-call HIP events around sdpa_decode_paged (the wide split kernel and the combine)."""
+    pc = inputs.mla_decode()
+    q, kp, vp = pc.q.to(dev), pc.k_pool.to(dev), pc.v_pool.to(dev)
+    ptk, ptv, sl = pc.pt_k.to(dev), pc.pt_v.to(dev), pc.seq_lens.to(dev)
+    o = torch.empty((pc.batch, pc.sq, pc.hq, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((pc.batch, pc.sq, pc.hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(sdpa.decode_workspace_bytes(pc.batch, pc.sq, pc.hq, 512, pc.num_splits),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        sdpa.decode_paged(q, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, pc.causal,
+                          num_splits=pc.num_splits, workspace=ws, out=o, lse=lse, stream=stream)
+
+    ms = per_call_ms(torch, stream, call, args.steps, args.warmup)
+    st = ms_stats(ms)
+    kv, comp = decode_bytes(pc)
+    lens = [int(x) for x in pc.seq_lens.tolist()]
+    flops = decode_visible_pairs(lens, pc.sq, pc.causal) * pc.hq * 2 * (576 + 512)
+    gbs = comp / (st["mean"] * 1e-3) / 1e9
+    tf = flops / (st["mean"] * 1e-3) / 1e12
+    rows = pc.batch * pc.sq * pc.hq
+    part_bytes = 2 * pc.num_splits * rows * (512 + 1) * 4  # fp32 partials written + read back
+    log("%s: %.4f ms mean (median %.4f, min %.4f) -> %.1f GB/s compulsory (%.1f%% of HBM), "
+        "%.1f TFLOP/s (%.1f%% of bf16 MFMA)" % (pc.name, st["mean"], st["median"], st["min"], gbs,
+                                                 100 * gbs / PEAK_HBM_GBS, tf,
+                                                 100 * tf / PEAK_BF16_TFLOPS))
+    leg = {"workload": pc.name, "kv_bytes": kv, "compulsory_bytes": comp,
+           "split_partial_bytes": part_bytes, "flop": flops, "ms": st,
+           "value": round(kv / (st["mean"] * 1e-3) / 1e9, 1), "unit": "GB/s",
+           "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+           "roofline": {"kernel": "decode_wide_kernel<576, 512> + combine_kernel<false>",
+                        "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+    del q, kp, vp
+    if not args.no_cpu_baseline:
+        leg["cpu_baseline"] = cpu_baseline_decode(pc, args.cpu_seconds / 2, threads)
+        log("  oracle: %.3g GB/s (%s)" % (leg["cpu_baseline"]["value"],
+                                         leg["cpu_baseline"]["sample"]))
+    return leg
+
+
+def tiny_leg(args, torch, inputs, sdpa, dev, stream, threads):
+    """The tiny fp32 THD workload ({5, 17}, 2/1 heads, D = 64): the oracle's CPU seconds on
+    one thread and on `threads`, and the GPU call for context."""
+    import oracle
+    case = inputs.tiny_fp32()
+    qa, ka, va = (inputs.host_array(case.q), inputs.host_array(case.k),
+                  inputs.host_array(case.v))
+    res = {"workload": case.name, "flop": prefill_flops(case.lengths_q, case.lengths_kv,
+                                                        case.hq, 64, 64)}
+    for key, n in (("oracle_s_1_thread", 1), ("oracle_s_all_threads", threads)):
+        oracle.prefill_thd(qa, ka, va, case.cu_q.numpy(), case.cu_kv.numpy(), case.scale, True,
+                           nthreads=n)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 0.5:
+            oracle.prefill_thd(qa, ka, va, case.cu_q.numpy(), case.cu_kv.numpy(), case.scale,
+                               True, nthreads=n)
+            reps += 1
+        res[key] = (time.perf_counter() - t0) / reps
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    cu_q, cu_kv = case.cu_q.to(dev), case.cu_kv.to(dev)
+    o = torch.empty((22, 2, 64), dtype=torch.float32, device=dev)
+    lse = torch.empty((22, 2), dtype=torch.float32, device=dev)
+
+    def call():
+        sdpa.prefill_thd(q, k, v, cu_q, cu_kv, case.max_q, case.max_kv, case.scale, True, out=o,
+                         lse=lse, stream=stream)
+
+    res["gpu_ms"] = ms_stats(per_call_ms(torch, stream, call, args.steps, args.warmup))
+    res["cores"] = threads
+    log("%s: oracle %.3g s (1 thread), %.3g s (%d threads); GPU %.4f ms"
+        % (case.name, res["oracle_s_1_thread"], res["oracle_s_all_threads"], threads,
+           res["gpu_ms"]["median"]))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -535,6 +703,10 @@ def main():
     ap.add_argument("--fp8-prefill", action="store_true",
                     help="time only the THD prefill workload in per-tensor FP8 E4M3 (and in "
                          "bf16 on the same GPU)")
+    ap.add_argument("--legs", default="c4,c5,c1",
+                    help="extra workloads timed after the step, comma-separated from c4 (D=256 "
+                         "dense and ragged prefill), c5 (absorbed-MLA-shaped decode), c1 (tiny "
+                         "fp32: oracle CPU seconds); empty for none")
     ap.add_argument("--mla-aliased", action="store_true",
                     help="time only the MLA-shaped decode over an absorbed-MLA cache (V = the "
                          "first 512 columns of the 576-wide K rows, one page table)")
@@ -630,6 +802,16 @@ def main():
     dec_avg = sum(dec_ms) / len(dec_ms)
     ms_per_step = total_ms / args.steps
 
+    # the decode call alone, with a 512 MiB write between calls that evicts the MALL
+    flush = torch.empty(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    dec_flushed = ms_stats(per_call_ms(
+        torch, stream,
+        lambda: sdpa.decode_paged(dq, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, pc.causal,
+                                  num_splits=pc.num_splits, workspace=ws, out=o_d, lse=lse_d,
+                                  stream=stream),
+        args.steps, args.warmup, between=lambda: flush.fill_(1.0)))
+    del flush
+
     flops = prefill_flops(case.lengths_q, case.lengths_kv, case.hq, 128, 128)
     kv_bytes, comp_bytes = decode_bytes(pc)
     pre_tflops = flops / (pre_avg * 1e-3) / 1e12
@@ -640,6 +822,8 @@ def main():
     log("decode : %.4f ms avg (min %.4f) -> %.1f GB/s K/V, %.1f GB/s compulsory (%.1f%% of HBM)"
         % (dec_avg, min(dec_ms), dec_kv_gbs, dec_comp_gbs, 100 * dec_comp_gbs / PEAK_HBM_GBS))
     log("step   : %.4f ms (wall %.4f ms)" % (ms_per_step, 1e3 * wall / args.steps))
+    log("decode alone, MALL flushed before each call: %.4f ms median (min %.4f)"
+        % (dec_flushed["median"], dec_flushed["min"]))
 
     cpu_pre = cpu_dec = None
     if not args.no_cpu_baseline:
@@ -650,6 +834,21 @@ def main():
         log("  prefill oracle: %.3g TFLOP/s (%s)" % (cpu_pre["value"], cpu_pre["sample"]))
         cpu_dec = cpu_baseline_decode(pc, args.cpu_seconds, threads)
         log("  decode oracle: %.3g GB/s (%s)" % (cpu_dec["value"], cpu_dec["sample"]))
+
+    legs = [x for x in args.legs.split(",") if x]
+    extra = {}
+    threads = host_threads()
+    del q, k, v, dq, kp, vp
+    torch.cuda.empty_cache()
+    if "c4" in legs:
+        extra["c4_dense"] = d256_leg(args, torch, inputs, sdpa, dev, stream, threads, False)
+        extra["c4_ragged"] = d256_leg(args, torch, inputs, sdpa, dev, stream, threads, True)
+        torch.cuda.empty_cache()
+    if "c5" in legs:
+        extra["c5_mla_decode"] = mla_leg(args, torch, inputs, sdpa, dev, stream, threads)
+        torch.cuda.empty_cache()
+    if "c1" in legs:
+        extra["c1_tiny_fp32"] = tiny_leg(args, torch, inputs, sdpa, dev, stream, threads)
 
     line = {
         "metric": "prefill attn TFLOP/s (% MFMA peak); paged decode KV GB/s (% HBM peak)",
@@ -672,10 +871,13 @@ def main():
             "prefill_lengths": case.lengths_q,
             "prefill_flop": flops,
             "prefill_ms": round(pre_avg, 4),
+            "prefill_ms_stats": ms_stats(pre_ms),
             "decode_batch": pc.batch,
             "decode_kv_bytes": kv_bytes,
             "decode_compulsory_bytes": comp_bytes,
             "decode_ms": round(dec_avg, 4),
+            "decode_ms_stats": ms_stats(dec_ms),
+            "decode_ms_mall_flushed": dec_flushed,
             "seeds": [inputs.SEED_BASE + 2, inputs.SEED_BASE + 3],
         },
         "decode": {
@@ -684,7 +886,7 @@ def main():
             "what": "K/V bytes of live tokens / (split kernel + combine kernel) time",
         },
         "roofline": {
-            "kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false, false>",
+            "kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false, false, false>",
             "bound": "mfma",
             "achieved": round(pre_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -703,7 +905,9 @@ def main():
         },
         "cpu_baseline": cpu_pre,
         "cpu_baseline_decode": cpu_dec,
+        "host_cpu": {"model": host_cpu_model(), "threads_used": threads},
     }
+    line.update(extra)
     print(json.dumps(line), flush=True)
 
 

@@ -466,11 +466,14 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             for (int o = 0; o < N8; ++o)
                 s[o % C::NKB] = mfma_32x32x64_fp8(fk[o], qf8[o / C::NKB], o < C::NKB ? zero : s[o % C::NKB]);
             // Keep the scores' MFMAs in this (MFMA) phase: left alone, the
-            // compiler sank them into the next phase, just before the
-            // softmax reads their results, and repeated identical calls then
-            // gave scores differing in their last bits.
+            // compiler sinks them into the branch of the next phase that
+            // reads them (the softmax), where they no longer overlap the
+            // other wave group's softmax.  An empty asm that only USES the
+            // scores pins them here; it must not redefine them, or the
+            // compiler would lose track of the MFMA results its softmax reads
+            // and would not put the MFMA -> VALU wait states in front of them.
 #pragma unroll
-            for (int kb = 0; kb < C::NKB; ++kb) asm volatile("" : "+v"(s[kb]));
+            for (int kb = 0; kb < C::NKB; ++kb) asm volatile("" ::"v"(s[kb]));
         }
     };
     // softmax: scores s of the tile whose first key is key0 -> P^T operands pb

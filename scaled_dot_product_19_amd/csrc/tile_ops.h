@@ -41,11 +41,13 @@ __device__ __forceinline__ int swz_v(int row, int lc) {
 __device__ __forceinline__ void half_swap(float& a, float& b) {
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
-// 3-input max without the NaN-quieting copies the compiler adds around fmaxf
+// 3-input max (v_max3_f32).  Written in plain C so that the compiler sees
+// every read of its operands: the scores come straight out of MFMA
+// accumulators, and a VALU read of an MFMA result needs wait states after the
+// MFMA that only the compiler's hazard recognizer inserts (an asm v_max3_f32
+// would be issued right behind the MFMA and could read stale registers).
 __device__ __forceinline__ float max3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 __device__ __forceinline__ float half_max(float v) {
     float a = v, b = v;

@@ -59,12 +59,14 @@ def check_lse(gpu: torch.Tensor, ref: np.ndarray, what: str = "LSE"):
 
 
 def oracle_prefill(case: inputs.ThdCase, **kw):
+    kw.setdefault("nthreads", nproc_for_oracle())
     return oracle.prefill_thd(inputs.host_array(case.q), inputs.host_array(case.k),
                               inputs.host_array(case.v), case.cu_q.numpy(), case.cu_kv.numpy(),
                               case.scale, case.causal, **kw)
 
 
 def oracle_decode(pc: inputs.PagedCase, **kw):
+    kw.setdefault("nthreads", nproc_for_oracle())
     return oracle.decode_paged(inputs.host_array(pc.q), inputs.host_array(pc.k_pool),
                                inputs.host_array(pc.v_pool), pc.pt_k.numpy(), pc.pt_v.numpy(),
                                pc.seq_lens.numpy(), pc.page_size, pc.scale, pc.causal, **kw)
@@ -94,7 +96,13 @@ def thd_sample(case: inputs.ThdCase, n: int, seed: int):
 
 
 def nproc_for_oracle() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Oracle threads: the CPUs this process may run on, capped by OMP_NUM_THREADS
+    (the host's share for one GPU) and by 16."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, min(16, n))
 
 
 def finite_lse_frac(lse: np.ndarray) -> float:

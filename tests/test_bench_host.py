@@ -32,3 +32,19 @@ def test_window_prefill_flops_counts_visible_pairs(causal):
         assert bench.window_prefill_flops(lq, lk, 2, 64, 32, causal, w) == brute * 2 * 2 * 96
     assert (bench.window_prefill_flops(lq, lk, 2, 64, 64, causal, 0)
             == bench.prefill_flops(lq, lk, 2, 64, 64, causal))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_decode_visible_pairs_counts_by_brute_force(causal):
+    lens, sq = [1, 2, 5, 64], 2
+    brute = 0
+    for L in lens:
+        for t in range(sq):
+            pos = L - sq + t
+            brute += sum(1 for j in range(L) if not causal or j <= pos)
+    assert bench.decode_visible_pairs(lens, sq, causal) == brute
+
+
+def test_ms_stats_median_and_min():
+    assert bench.ms_stats([3.0, 1.0, 2.0]) == {"mean": 2.0, "median": 2.0, "min": 1.0}
+    assert bench.ms_stats([4.0, 1.0, 2.0, 3.0]) == {"mean": 2.5, "median": 2.5, "min": 1.0}

@@ -1,0 +1,228 @@
+"""Full-size parity of the four GPU workloads against the fp64 oracle.
+
+Seed 1000 + k: EVERY output row of workload k (every (token, head) of the THD
+prefills, every (sequence, token, head) of the paged decodes) is compared with
+the oracle element by element, at the workload's own size and in the launch
+configuration the benchmark times.  Seed 1100 + k: a second draw of the same
+workload at full size, compared on sampled rows.  The bar is the one of every
+parity test: O |g - o| <= 2e-2 + 2e-2 |o|, LSE |g - o| <= 1e-3 on finite rows,
+-inf exactly where the oracle has -inf (padded rows included).
+
+Also here: causal masking checked bit for bit at the decode and D = 256 shapes
+(changing a key that a row cannot see leaves that row's O and LSE identical).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from scaled_dot_product_19_amd import inputs, sdpa
+from tests.helpers import (check_lse, check_o, log, oracle_decode, oracle_prefill, sample_rows,
+                           thd_sample, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    sdpa.load()  # raises if the HIP library is missing: no fallback
+
+
+def prefill(case, lse_layout=sdpa.LSE_PACKED, lse_s_max=0, lse=None, k=None, v=None):
+    o, l = sdpa.prefill_thd(to_dev(case.q), to_dev(case.k) if k is None else k,
+                            to_dev(case.v) if v is None else v, to_dev(case.cu_q),
+                            to_dev(case.cu_kv), case.max_q, case.max_kv, case.scale, case.causal,
+                            lse=lse, lse_layout=lse_layout, lse_s_max=lse_s_max)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def decode(pc, k_pool=None, v_pool=None):
+    o, l = sdpa.decode_paged(to_dev(pc.q), to_dev(pc.k_pool) if k_pool is None else k_pool,
+                             to_dev(pc.v_pool) if v_pool is None else v_pool, to_dev(pc.pt_k),
+                             to_dev(pc.pt_v), to_dev(pc.seq_lens), pc.max_kv, pc.scale, pc.causal,
+                             num_splits=pc.num_splits)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def padded_reference(case, l_ref, s_max):
+    """The padded [B, s_max, Hq] Stats the oracle's packed rows imply: -inf past Lq_b."""
+    ref = np.full((case.batch, s_max, case.hq), -np.inf)
+    for b, L in enumerate(case.lengths_q):
+        t0 = int(case.cu_q[b])
+        ref[b, :L] = l_ref[t0:t0 + L]
+    return ref
+
+
+# ---- THD prefill D = 128 (8 sequences U[128, 4096], 32/8 heads) -------------
+
+@pytest.mark.timeout(900)
+def test_thd_prefill_d128_every_row():
+    case = inputs.thd_prefill_d128(inputs.SEED_BASE + 2)
+    log("full-size every row: %s T=%d lengths=%s" % (case.name, int(case.cu_q[-1]),
+                                                      case.lengths_q))
+    o, l = prefill(case)
+    o_ref, l_ref = oracle_prefill(case)
+    log("  max|dO|=%.3g max|dLSE|=%.3g" % (check_o(o, o_ref), check_lse(l, l_ref)))
+
+
+@pytest.mark.timeout(600)
+def test_thd_prefill_d128_second_seed_sampled():
+    seed = inputs.SEED_ALT + 2
+    case = inputs.thd_prefill_d128(seed)
+    log("full-size sampled: %s seed %d T=%d lengths=%s" % (case.name, seed, int(case.cu_q[-1]),
+                                                           case.lengths_q))
+    o, l = prefill(case)
+    toks, heads = thd_sample(case, 768, seed)
+    o_ref, l_ref = oracle_prefill(case, sel_tok=toks, sel_head=heads)
+    ti, hi = torch.from_numpy(toks).cuda(), torch.from_numpy(heads).long().cuda()
+    check_o(o[ti, hi], o_ref)
+    check_lse(l[ti, hi], l_ref)
+    assert torch.isfinite(l).all()
+
+
+# ---- paged decode D = 128 (B = 64, 32/8 heads, page 64, 8 splits) -----------
+
+@pytest.mark.timeout(600)
+def test_paged_decode_d128_every_row():
+    pc = inputs.paged_decode_d128(inputs.SEED_BASE + 3, poison=True)
+    log("full-size every row: %s pages=%d" % (pc.name, pc.k_pool.shape[0]))
+    o, l = decode(pc)
+    o_ref, l_ref = oracle_decode(pc)
+    log("  max|dO|=%.3g max|dLSE|=%.3g" % (check_o(o, o_ref), check_lse(l, l_ref)))
+
+
+@pytest.mark.timeout(600)
+def test_paged_decode_d128_second_seed_sampled():
+    seed = inputs.SEED_ALT + 3
+    pc = inputs.paged_decode_d128(seed, poison=True)
+    log("full-size sampled: %s seed %d pages=%d" % (pc.name, seed, pc.k_pool.shape[0]))
+    o, l = decode(pc)
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 512, seed, must=[0, rows - 1])
+    o_ref, l_ref = oracle_decode(pc, sel_rows=sel)
+    si = torch.from_numpy(sel).cuda()
+    check_o(o.reshape(rows, -1)[si], o_ref)
+    check_lse(l.reshape(rows)[si], l_ref)
+
+
+# ---- THD prefill D = 256 (dense 2 x 8192 and ragged {8192, 3000}, 24/2 heads) --
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ragged", [False, True])
+def test_d256_every_row_padded_lse(ragged):
+    case = (inputs.ragged_prefill_d256 if ragged else inputs.dense_prefill_d256)(
+        inputs.SEED_BASE + 4)
+    s_max = 8192
+    log("full-size every row: %s (padded LSE [2, %d, 24] on a dirty buffer)" % (case.name, s_max))
+    lse = torch.full((2, s_max, 24), 3.0, device="cuda")  # dirty: the call seeds -inf itself
+    o, l = prefill(case, lse_layout=sdpa.LSE_PADDED, lse_s_max=s_max, lse=lse)
+    o_ref, l_ref = oracle_prefill(case)
+    e_o = check_o(o, o_ref)
+    e_l = check_lse(l, padded_reference(case, l_ref, s_max), "padded LSE")
+    log("  max|dO|=%.3g max|dLSE|=%.3g" % (e_o, e_l))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("ragged", [False, True])
+def test_d256_second_seed_sampled(ragged):
+    seed = inputs.SEED_ALT + 4
+    case = (inputs.ragged_prefill_d256 if ragged else inputs.dense_prefill_d256)(seed)
+    s_max = 8192
+    log("full-size sampled: %s seed %d" % (case.name, seed))
+    lse = torch.full((2, s_max, 24), -7.0, device="cuda")
+    o, l = prefill(case, lse_layout=sdpa.LSE_PADDED, lse_s_max=s_max, lse=lse)
+    toks, heads = thd_sample(case, 512, seed)
+    o_ref, l_ref = oracle_prefill(case, sel_tok=toks, sel_head=heads)
+    ti, hi = torch.from_numpy(toks).cuda(), torch.from_numpy(heads).long().cuda()
+    check_o(o[ti, hi], o_ref)
+    b_of = np.searchsorted(case.cu_q.numpy(), toks, side="right") - 1
+    i_of = toks - case.cu_q.numpy()[b_of]
+    check_lse(l[torch.from_numpy(b_of).cuda(), torch.from_numpy(i_of).cuda(), hi], l_ref)
+    for b, L in enumerate(case.lengths_q):
+        assert torch.all(l[b, L:] == -math.inf) and torch.isfinite(l[b, :L]).all()
+
+
+# ---- absorbed-MLA-shaped decode (576/512, 128/1 heads, 2 tokens, 16 splits) ----
+
+@pytest.mark.timeout(600)
+def test_mla_decode_every_row():
+    pc = inputs.mla_decode(inputs.SEED_BASE + 5, poison=True)
+    log("full-size every row: %s pages=%d" % (pc.name, pc.k_pool.shape[0]))
+    o, l = decode(pc)
+    o_ref, l_ref = oracle_decode(pc)
+    log("  max|dO|=%.3g max|dLSE|=%.3g" % (check_o(o, o_ref), check_lse(l, l_ref)))
+
+
+@pytest.mark.timeout(600)
+def test_mla_decode_second_seed_sampled():
+    seed = inputs.SEED_ALT + 5
+    pc = inputs.mla_decode(seed, poison=True)
+    log("full-size sampled: %s seed %d pages=%d" % (pc.name, seed, pc.k_pool.shape[0]))
+    o, l = decode(pc)
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 512, seed, must=[0, rows - 1])
+    o_ref, l_ref = oracle_decode(pc, sel_rows=sel)
+    si = torch.from_numpy(sel).cuda()
+    check_o(o.reshape(rows, -1)[si], o_ref)
+    check_lse(l.reshape(rows)[si], l_ref)
+
+
+# ---- causal masking, bit for bit ---------------------------------------------
+
+def _perturb_key(pc, b, key, seed):
+    """Copies of the pools with key `key` of sequence b redrawn (K and V rows, all KV heads)."""
+    g = torch.Generator().manual_seed(seed)
+    kp, vp = pc.k_pool.clone(), pc.v_pool.clone()
+    page, slot = key // pc.page_size, key % pc.page_size
+    pk, pv = int(pc.pt_k[b, page]), int(pc.pt_v[b, page])
+    kp[pk, slot] = torch.randn(kp[pk, slot].shape, generator=g).to(kp.dtype)
+    vp[pv, slot] = torch.randn(vp[pv, slot].shape, generator=g).to(vp.dtype)
+    return kp, vp
+
+
+@pytest.mark.parametrize("shape", [
+    # (s_q, h_q, h_kv, d_qk, d_v, splits): few-row kernel (8 rows per KV head), and the
+    # absorbed-MLA wide kernel (256 rows per KV head)
+    (2, 8, 2, 128, 128, 3),
+    (2, 128, 1, 576, 512, 4),
+])
+def test_decode_two_token_causal_future_key_bitwise(shape):
+    sq, hq, hkv, dqk, dv, splits = shape
+    pc = inputs.paged_case(2101, 3, sq, hq, hkv, dqk, dv, 64, lengths=[70, 700, 1300],
+                           num_splits=splits, causal=True, poison=True, name="future_key")
+    log("decode future key: sq=%d hq=%d hkv=%d d=%d/%d splits=%d" % shape)
+    o1, l1 = decode(pc)
+    for b, L in enumerate(pc.seq_lens.tolist()):
+        # key L - 1 is visible to token 1 only (token 0 sits at position L - 2)
+        kp, vp = _perturb_key(pc, b, L - 1, 77 + b)
+        o2, l2 = decode(pc, k_pool=to_dev(kp), v_pool=to_dev(vp))
+        assert torch.equal(o1[b, 0], o2[b, 0]) and torch.equal(l1[b, 0], l2[b, 0]), \
+            "token 0 of sequence %d changed with a key it cannot see" % b
+        assert not torch.equal(l1[b, 1], l2[b, 1]), "token 1 must see key L - 1"
+        others = [x for x in range(pc.batch) if x != b]
+        assert torch.equal(o1[others], o2[others]) and torch.equal(l1[others], l2[others])
+    o_ref, l_ref = oracle_decode(pc)
+    check_o(o1, o_ref)
+    check_lse(l1, l_ref)
+
+
+def test_d256_causal_future_keys_bitwise():
+    case = inputs.thd_case(2102, hq=24, hkv=2, d_qk=256, lengths=[300, 77], name="d256_future")
+    o1, l1 = prefill(case)
+    cut = 150  # rows < cut of sequence 0 cannot see keys >= cut
+    g = torch.Generator().manual_seed(5)
+    k2, v2 = case.k.clone(), case.v.clone()
+    k2[cut:300] = torch.randn(k2[cut:300].shape, generator=g).to(torch.bfloat16)
+    v2[cut:300] = torch.randn(v2[cut:300].shape, generator=g).to(torch.bfloat16)
+    o2, l2 = prefill(case, k=to_dev(k2), v=to_dev(v2))
+    assert torch.equal(o1[:cut], o2[:cut]) and torch.equal(l1[:cut], l2[:cut])
+    assert not torch.equal(l1[cut:300], l2[cut:300])
+    assert torch.equal(o1[300:], o2[300:]) and torch.equal(l1[300:], l2[300:])
+    o_ref, l_ref = oracle_prefill(case)
+    check_o(o1, o_ref)
+    check_lse(l1, l_ref)

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 from scaled_dot_product_19_amd import inputs, sdpa
-from tests.helpers import (check_lse, check_o, log, oracle_prefill, thd_sample, to_dev)
+from tests.helpers import check_lse, check_o, log, oracle_prefill, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -182,35 +182,3 @@ def test_first_causal_row_is_v0_exactly():
         t0 = int(case.cu_q[b])
         for h in range(8):
             assert torch.equal(o[t0, h].cpu(), case.v[t0, h // 4])
-
-
-@pytest.mark.parametrize("seed", [inputs.SEED_BASE + 2])
-def test_full_size_thd_prefill_d128_sampled(seed):
-    case = inputs.thd_prefill_d128(seed)
-    log("full-size %s T=%d lengths=%s" % (case.name, int(case.cu_q[-1]), case.lengths_q))
-    o, l = run(case)
-    toks, heads = thd_sample(case, 384, seed)
-    o_ref, l_ref = oracle_prefill(case, sel_tok=toks, sel_head=heads)
-    check_o(o[torch.from_numpy(toks).cuda(), torch.from_numpy(heads).long().cuda()], o_ref)
-    check_lse(l[torch.from_numpy(toks).cuda(), torch.from_numpy(heads).long().cuda()], l_ref)
-    assert torch.isfinite(l).all()
-
-
-@pytest.mark.parametrize("ragged", [False, True])
-def test_full_size_d256_sampled(ragged):
-    case = inputs.ragged_prefill_d256() if ragged else inputs.dense_prefill_d256()
-    log("full-size %s" % case.name)
-    s_max = 8192
-    lse = torch.full((2, s_max, 24), 3.0, device="cuda")
-    o, l = run(case, lse_layout=sdpa.LSE_PADDED, lse_s_max=s_max, lse=lse)
-    toks, heads = thd_sample(case, 256, 1004)
-    o_ref, l_ref = oracle_prefill(case, sel_tok=toks, sel_head=heads)
-    check_o(o[torch.from_numpy(toks).cuda(), torch.from_numpy(heads).long().cuda()], o_ref)
-    b_of = np.searchsorted(case.cu_q.numpy(), toks, side="right") - 1
-    i_of = toks - case.cu_q.numpy()[b_of]
-    got = l[torch.from_numpy(b_of).cuda(), torch.from_numpy(i_of).cuda(),
-            torch.from_numpy(heads).long().cuda()]
-    check_lse(got, l_ref)
-    if ragged:
-        assert torch.all(l[1, 3000:] == -math.inf)
-        assert torch.isfinite(l[1, :3000]).all() and torch.isfinite(l[0]).all()
