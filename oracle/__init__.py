@@ -70,7 +70,7 @@ def _load(path: str | None = None):
     lib.oracle_decode_paged_scaled.restype = ctypes.c_int
     lib.oracle_decode_paged_scaled.argtypes = [
         ctypes.c_int, P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P, I32, I32, I32,
-        I32, I32, I32, I32, D, I32, I32, D, D, D, I64, P, P, P, P, P, I32]
+        I32, I32, I32, I32, D, I32, I32, I32, P, D, D, D, I64, P, P, P, P, P, I32]
     lib.oracle_e4m3_value.restype = D
     lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_combine.restype = None
@@ -203,8 +203,13 @@ def prefill_thd(q, k, v, cu_q, cu_kv, scale, causal, hq=None, hkv=None, sel_tok=
 
 
 def decode_paged(q, k_pool, v_pool, pt_k, pt_v, seq_lens, page_size, scale, causal,
-                 num_splits=1, sel_rows=None, want_partials=False, nthreads=0, descale=None):
+                 num_splits=1, sel_rows=None, want_partials=False, nthreads=0, descale=None,
+                 window=0, sinks=None):
     """Paged decode by definition (num_splits > 1: per-chunk partials + LSE merge).
+
+    window > 0: left sliding window W (token t at position L - sq + t sees keys
+    L - sq + t - W + 1 ..); sinks: Hq per-head sink logits (same units as scale * q.k)
+    that join the softmax denominator once (in the merge when split) and carry no value.
 
     E4M3 inputs (uint8 codes) need descale = (descale_q, descale_k, descale_v): each
     code stands for its descale times its E4M3 value (per-tensor FP8).
@@ -251,12 +256,16 @@ def decode_paged(q, k_pool, v_pool, pt_k, pt_v, seq_lens, page_size, scale, caus
     else:
         assert descale is None, "descales apply to E4M3 inputs only"
         dsc = [1.0, 1.0, 1.0]
+    sk = None
+    if sinks is not None:
+        sk = np.ascontiguousarray(sinks, dtype=np.float64)
+        assert sk.shape == (hq,)
     rc = lib.oracle_decode_paged_scaled(
         dt, _ptr(q), _ptr(k_pool), ks[0], ks[1], ks[2], _ptr(v_pool), vs[0], vs[1], vs[2],
         _ptr(pt_k), _ptr(pt_v), pt_k.shape[1], _ptr(seq_lens), B, sq, hq, hkv, dqk, dv,
-        int(page_size), float(scale), int(bool(causal)), int(num_splits), dsc[0], dsc[1],
-        dsc[2], n_sel, _ptr(sr), _ptr(o), _ptr(lse), _ptr(o_part), _ptr(lse_part),
-        int(nthreads))
+        int(page_size), float(scale), int(bool(causal)), int(num_splits), int(window), _ptr(sk),
+        dsc[0], dsc[1], dsc[2], n_sel, _ptr(sr), _ptr(o), _ptr(lse), _ptr(o_part),
+        _ptr(lse_part), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_decode_paged rejected its arguments (rc=%d)" % rc)
     if sel_rows is None:

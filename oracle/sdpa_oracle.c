@@ -334,6 +334,8 @@ typedef struct {
     int64_t k_sp, k_st, k_sh, v_sp, v_st, v_sh;
     const int32_t *pt_k, *pt_v, *seq_lens;
     int32_t table_stride, batch, sq, hq, hkv, dqk, dv, page, causal, num_splits;
+    int32_t window;            /* left window W (<= 0: none) */
+    const double* sinks;       /* [hq] sink logits, or NULL */
     double scale;
     double dq, dk, dv_scale;   /* per-tensor descales of Q, K, V (1 unless E4M3) */
     int64_t n_sel;
@@ -362,8 +364,19 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
     int32_t b = (int32_t)(row / ((int64_t)c->hq * c->sq));
     int32_t kvh = h / (c->hq / c->hkv);
     int64_t L = c->seq_lens[b];
-    /* query token tq sits at position L - sq + tq (bottom-right alignment) */
-    int64_t last = c->causal ? (L - c->sq + tq) : (L - 1);
+    /* query token tq sits at position pos = L - sq + tq (bottom-right alignment);
+       it sees keys first <= j <= last */
+    const int64_t pos = L - c->sq + tq;
+    int64_t last = c->causal ? pos : (L - 1);
+    int64_t first = 0;
+    if (c->window > 0 && pos - c->window + 1 > first) first = pos - c->window + 1;
+    /* split mode cuts the keys [base, L) into chunks, base = the start of the page
+       that holds the first key any query token of the sequence can see (0 without
+       a window) */
+    int64_t base = 0;
+    if (c->window > 0 && L - c->sq - c->window + 1 > 0)
+        base = ((L - c->sq - c->window + 1) / c->page) * c->page;
+    const double sink = c->sinks ? c->sinks[h] : -INFINITY;
     double* qrow = scratch;
     int64_t* koff = (int64_t*)(scratch + c->dqk);
     int64_t* voff = koff + c->max_lk;
@@ -372,7 +385,7 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
         qrow[d] = c->dq * load_elem(c->q, c->dtype, row * c->dqk + d);
 
     int32_t S = c->num_splits < 1 ? 1 : c->num_splits;
-    int64_t chunk = split_chunk(L, S, c->page);
+    int64_t chunk = split_chunk(L - base, S, c->page);
     double* o = c->o + unit * c->dv;
     double* lse = c->lse + unit;
     /* per-split partials: the merge below is the textbook LSE merge */
@@ -381,11 +394,12 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
     double* ll = (double*)malloc(sizeof(double) * (size_t)S);
     if (!ol || !ll) { free(ol); free(ll); *lse = NAN; return; }
     for (int32_t sp = 0; sp < S; ++sp) {
-        int64_t lo = (int64_t)sp * chunk;
+        int64_t lo = base + (int64_t)sp * chunk;
         int64_t hi = lo + chunk;
         if (S == 1) { lo = 0; hi = L; }
         if (hi > L) hi = L;
         if (hi > last + 1) hi = last + 1;
+        if (lo < first) lo = first;
         int64_t n = 0;
         for (int64_t j = lo; j < hi; ++j, ++n) {
             int64_t pg = j / c->page, slot = j % c->page;
@@ -394,8 +408,10 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
             koff[n] = kpage * c->k_sp + slot * c->k_st + (int64_t)kvh * c->k_sh;
             voff[n] = vpage * c->v_sp + slot * c->v_st + (int64_t)kvh * c->v_sh;
         }
+        /* one split: the plain definition, sink included; several: each chunk's
+           partial without the sink, which joins the merge below */
         attend_row(qrow, c->dqk, c->dv, c->kp, c->vp, koff, voff, n, c->dtype, c->dk, c->dv_scale,
-                   c->scale, -INFINITY, s,
+                   c->scale, S == 1 ? sink : -INFINITY, s,
                    ol + (size_t)sp * c->dv, ll + sp, NULL);
         if (ll[sp] > m_all) m_all = ll[sp];
         if (c->o_part) {
@@ -405,6 +421,9 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
             c->lse_part[(int64_t)sp * rows + row] = ll[sp];
         }
     }
+    /* the sink takes part in the merge as one more term of the denominator
+       with no value: a partial whose LSE is the sink logit and whose O is 0 */
+    if (S > 1 && sink > m_all) m_all = sink;
     if (S == 1) {
         for (int d = 0; d < c->dv; ++d) o[d] = ol[d];
         *lse = ll[0];
@@ -414,6 +433,7 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
     } else {
         double w_sum = 0.0;
         for (int32_t sp = 0; sp < S; ++sp) w_sum += exp(ll[sp] - m_all);
+        if (sink != -INFINITY) w_sum += exp(sink - m_all);
         double L_all = m_all + log(w_sum);
         for (int d = 0; d < c->dv; ++d) o[d] = 0.0;
         for (int32_t sp = 0; sp < S; ++sp) {
@@ -433,11 +453,19 @@ static void decode_unit(void* vctx, int64_t unit, double* scratch) {
  * seq_lens[b] = KV length, including the sq new tokens.  Query token t of
  * sequence b sits at key position seq_lens[b] - sq + t.
  *
- * num_splits <= 1: the plain definition over all visible keys.
- * num_splits  > 1: keys split into contiguous chunks (split_chunk above),
- *   each chunk's normalized partial (O_c, LSE_c) computed by the definition,
- *   then merged: M = max LSE_c, LSE = M + ln sum exp(LSE_c - M),
- *   O = sum exp(LSE_c - LSE) O_c; all-empty -> (0, -inf).
+ * Token t sees keys j < seq_lens[b] with j <= seq_lens[b] - sq + t when
+ * causal and, with a left window W > 0, j >= seq_lens[b] - sq + t - W + 1
+ * (the W keys ending at its own position).  sinks (optional): Hq per-head
+ * sink logits that join every row's softmax denominator with no value.
+ *
+ * num_splits <= 1: the plain definition over all visible keys (sink included).
+ * num_splits  > 1: keys [base, L) split into contiguous chunks (split_chunk
+ *   above; base = 0, or with a window the start of the page holding key
+ *   L - sq - W + 1, the first key any token of the sequence sees), each
+ *   chunk's normalized partial (O_c, LSE_c) computed by the definition without
+ *   the sink, then merged with the sink as one more term of no value:
+ *   M = max(LSE_c, sink), LSE = M + ln(sum exp(LSE_c - M) + exp(sink - M)),
+ *   O = sum exp(LSE_c - LSE) O_c; all-empty and no sink -> (0, -inf).
  *   o_part/lse_part (optional) receive the partials, [S, rows, Dv]/[S, rows],
  *   row = (b*sq + t)*Hq + h.
  * n_sel < 0: all rows; else only rows sel_row[r] (same row numbering).
@@ -450,10 +478,11 @@ int oracle_decode_paged_scaled(int dtype, const void* q, const void* kpool, int6
                                const int32_t* pt_v, int32_t table_stride,
                                const int32_t* seq_lens, int32_t batch, int32_t sq, int32_t hq,
                                int32_t hkv, int32_t dqk, int32_t dv, int32_t page, double scale,
-                               int32_t causal, int32_t num_splits, double descale_q,
-                               double descale_k, double descale_v, int64_t n_sel,
-                               const int64_t* sel_row, double* o, double* lse, double* o_part,
-                               double* lse_part, int32_t nthreads) {
+                               int32_t causal, int32_t num_splits, int32_t window,
+                               const double* sinks, double descale_q, double descale_k,
+                               double descale_v, int64_t n_sel, const int64_t* sel_row,
+                               double* o, double* lse, double* o_part, double* lse_part,
+                               int32_t nthreads) {
     if (batch < 0 || sq <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || page <= 0) return -1;
     if (o_part && n_sel >= 0) return -1;
     int64_t max_lk = 1;
@@ -463,8 +492,8 @@ int oracle_decode_paged_scaled(int dtype, const void* q, const void* kpool, int6
     }
     decode_ctx c = {dtype, q, kpool, vpool, k_sp, k_st, k_sh, v_sp, v_st, v_sh, pt_k, pt_v,
                     seq_lens, table_stride, batch, sq, hq, hkv, dqk, dv, page, causal,
-                    num_splits, scale, descale_q, descale_k, descale_v, n_sel, sel_row, o, lse,
-                    o_part, lse_part, max_lk};
+                    num_splits, window, sinks, scale, descale_q, descale_k, descale_v, n_sel,
+                    sel_row, o, lse, o_part, lse_part, max_lk};
     int64_t rows = (int64_t)batch * sq * hq;
     int64_t n_units = n_sel < 0 ? rows : n_sel;
     size_t scratch = (size_t)dqk + 3 * (size_t)max_lk;
@@ -483,8 +512,8 @@ int oracle_decode_paged(int dtype, const void* q, const void* kpool, int64_t k_s
     if (dtype == ORACLE_E4M3) return -1;  /* E4M3 needs its descales */
     return oracle_decode_paged_scaled(dtype, q, kpool, k_sp, k_st, k_sh, vpool, v_sp, v_st, v_sh,
                                       pt_k, pt_v, table_stride, seq_lens, batch, sq, hq, hkv,
-                                      dqk, dv, page, scale, causal, num_splits, 1.0, 1.0, 1.0,
-                                      n_sel, sel_row, o, lse, o_part, lse_part, nthreads);
+                                      dqk, dv, page, scale, causal, num_splits, 0, NULL, 1.0, 1.0,
+                                      1.0, n_sel, sel_row, o, lse, o_part, lse_part, nthreads);
 }
 
 /*

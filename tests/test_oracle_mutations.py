@@ -41,8 +41,15 @@ MUTATIONS = [
     ("v_uses_k_table", "int64_t vpage = c->pt_v[", "int64_t vpage = c->pt_k["),
     ("merge_weight_uses_max", "double w = exp(ll[sp] - L_all);",
      "double w = exp(ll[sp] - m_all);"),
-    ("decode_causal_position", "int64_t last = c->causal ? (L - c->sq + tq) : (L - 1);",
-     "int64_t last = c->causal ? (L - 1 - tq) : (L - 1);"),
+    ("decode_causal_position", "const int64_t pos = L - c->sq + tq;",
+     "const int64_t pos = L - 1 - tq;"),
+    ("decode_window_off_by_one", "if (c->window > 0 && pos - c->window + 1 > first) first = pos - c->window + 1;",
+     "if (c->window > 0 && pos - c->window > first) first = pos - c->window;"),
+    ("decode_window_ignored", "if (c->window > 0 && pos - c->window + 1 > first)",
+     "if (0 && pos - c->window + 1 > first)"),
+    ("decode_sink_in_every_split", "c->scale, S == 1 ? sink : -INFINITY, s,", "c->scale, sink, s,"),
+    ("decode_sink_dropped_from_merge", "if (sink != -INFINITY) w_sum += exp(sink - m_all);",
+     "if (0) w_sum += exp(sink - m_all);"),
     ("combine_lse_dropped_log", "double L = m + log(w_sum);", "double L = m + w_sum;"),
     ("e4m3_bias_off_by_one", "ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
     ("e4m3_subnormal_as_normal", "e == 0 ? ldexp((double)m / 8.0, -6)",
@@ -81,6 +88,12 @@ def _pin_suite():
         ("sink_brute", lambda: pins.test_window_and_sinks_brute_force_vs_torch(40, False, True)),
         ("sink_closed", pins.test_sink_closed_form_single_key),
         ("sink_empty_rows", pins.test_rows_without_keys_take_the_sink_as_lse),
+        ("decode_window_brute", lambda: pins.test_decode_window_and_sinks_brute_force_vs_torch(
+            5, 3, False, True)),
+        ("decode_sink_brute", lambda: pins.test_decode_window_and_sinks_brute_force_vs_torch(
+            0, 3, True, False)),
+        ("decode_window_one", pins.test_decode_window_one_sees_only_its_own_key),
+        ("decode_sink_empty", pins.test_decode_rows_without_keys_take_the_sink),
         ("e4m3_codes", pins.test_e4m3_values_match_torch_float8_e4m3fn),
         ("fp8_brute", lambda: pins.test_fp8_decode_brute_force_vs_torch(3, 2)),
         ("fp8_single_key", pins.test_fp8_single_key_closed_form),

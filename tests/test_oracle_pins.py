@@ -365,6 +365,120 @@ def test_rows_without_keys_take_the_sink_as_lse():
     assert np.all(np.isfinite(lse[3:]))
 
 
+# ---- paged decode with a left window and sinks --------------------------------
+
+def _brute_decode(pc, window=0, sinks=None):
+    """Independent paged-decode reference: the K/V rows gathered by torch indexing, torch
+    fp64 logits, an explicit mask (causal bound at the token's position L - sq + t, left
+    window), the sink as an extra zero-value logit column, torch.logsumexp / softmax."""
+    G = pc.hq // pc.hkv
+    k, v = _gathered_dense(pc)
+    outs = np.zeros((pc.batch, pc.sq, pc.hq, pc.v_pool.shape[3]))
+    lses = np.full((pc.batch, pc.sq, pc.hq), -np.inf)
+    off = 0
+    for b in range(pc.batch):
+        L = int(pc.seq_lens[b])
+        kb = _torch64(k[off:off + L]).repeat_interleave(G, dim=1).permute(1, 0, 2)  # [Hq, L, D]
+        vb = _torch64(v[off:off + L]).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        off += L
+        for t in range(pc.sq):
+            pos = L - pc.sq + t
+            j = torch.arange(L)
+            mask = torch.ones(L, dtype=torch.bool)
+            if pc.causal:
+                mask &= j <= pos
+            if window > 0:
+                mask &= j >= pos - window + 1
+            q = _torch64(pc.q[b, t])                                          # [Hq, D]
+            logits = pc.scale * torch.einsum("hd,hjd->hj", q, kb)
+            logits = logits.masked_fill(~mask, float("-inf"))
+            if sinks is not None:
+                logits = torch.cat([logits, torch.as_tensor(sinks, dtype=torch.float64)
+                                    .view(-1, 1)], dim=1)                     # [Hq, L + 1]
+            lse = torch.logsumexp(logits, dim=1)
+            fin = torch.isfinite(lse)
+            p = torch.zeros_like(logits)
+            p[fin] = torch.softmax(logits[fin], dim=1)
+            outs[b, t] = torch.einsum("hj,hjd->hd", p[:, :L], vb).numpy()
+            lses[b, t] = lse.numpy()
+    return outs, lses
+
+
+def _decode_oracle(pc, **kw):
+    return oracle.decode_paged(_np(pc.q), _np(pc.k_pool), _np(pc.v_pool), pc.pt_k.numpy(),
+                               pc.pt_v.numpy(), pc.seq_lens.numpy(), pc.page_size, pc.scale,
+                               pc.causal, **kw)
+
+
+@pytest.mark.parametrize("window", [0, 1, 5, 40])
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("with_sinks", [False, True])
+@pytest.mark.parametrize("causal", [True, False])
+def test_decode_window_and_sinks_brute_force_vs_torch(window, splits, with_sinks, causal):
+    # lengths cover L < s_q (token 0 sees nothing), keys inside one page and many pages
+    pc = inputs.paged_case(45, 4, 2, 4, 2, 64, 64, 16, lengths=[1, 9, 70, 130],
+                           num_splits=splits, causal=causal, poison=True, dtype=torch.float32)
+    sinks = np.array([0.3, -2.0, 5.0, -np.inf]) if with_sinks else None
+    o, lse = _decode_oracle(pc, num_splits=splits, window=window, sinks=sinks)
+    o_b, l_b = _brute_decode(pc, window=window, sinks=sinks)
+    np.testing.assert_allclose(o, o_b, rtol=1e-10, atol=1e-12)
+    fin = np.isfinite(l_b)
+    assert np.array_equal(fin, np.isfinite(lse))
+    np.testing.assert_allclose(lse[fin], l_b[fin], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("splits", [2, 5, 16])
+def test_decode_split_merge_with_window_and_sinks_equals_unsplit(splits):
+    pc = inputs.paged_case(46, 4, 3, 4, 1, 64, 64, 16, lengths=[2, 33, 100, 400])
+    sinks = np.array([1.5, -0.5, -np.inf, 9.0])
+    for window in (0, 7, 50):
+        o1, l1 = _decode_oracle(pc, num_splits=1, window=window, sinks=sinks)
+        oS, lS, op, lp = _decode_oracle(pc, num_splits=splits, window=window, sinks=sinks,
+                                        want_partials=True)
+        np.testing.assert_allclose(oS, o1, rtol=1e-13, atol=1e-14)
+        fin = np.isfinite(l1)
+        assert np.array_equal(np.isfinite(lS), fin)
+        np.testing.assert_allclose(lS[fin], l1[fin], rtol=1e-13, atol=1e-14)
+        # the partials carry no sink: merging them alone is the sink-free result
+        o0, l0 = _decode_oracle(pc, num_splits=1, window=window)
+        oc, lc = oracle.combine(op, lp)
+        np.testing.assert_allclose(oc.reshape(o0.shape), o0, rtol=1e-13, atol=1e-14)
+
+
+def test_decode_window_one_sees_only_its_own_key():
+    pc = inputs.paged_case(47, 2, 2, 2, 1, 64, 64, 16, lengths=[20, 37], dtype=torch.float32)
+    o, lse = _decode_oracle(pc, window=1)
+    k, v = _gathered_dense(pc)
+    off = 0
+    for b, L in enumerate([20, 37]):
+        for t in range(2):
+            pos = L - 2 + t
+            for h in range(2):
+                np.testing.assert_array_equal(o[b, t, h], v[off + pos, 0].double().numpy())
+                want = pc.scale * float(pc.q[b, t, h].double() @ k[off + pos, 0].double())
+                assert lse[b, t, h] == pytest.approx(want, abs=1e-12)
+        off += L
+
+
+def test_decode_wide_window_and_minus_inf_sink_change_nothing_bitwise():
+    pc = inputs.paged_case(48, 3, 2, 4, 2, 64, 64, 16, lengths=[5, 40, 77])
+    for splits in (1, 4):
+        o0, l0 = _decode_oracle(pc, num_splits=splits)
+        o1, l1 = _decode_oracle(pc, num_splits=splits, window=78, sinks=np.full(4, -np.inf))
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_decode_rows_without_keys_take_the_sink():
+    # L = 0, and L = 1 < s_q = 2 (token 0 sees no key): O = 0, LSE = sink_h
+    pc = inputs.paged_case(49, 2, 2, 2, 1, 64, 64, 16, lengths=[0, 1])
+    sinks = np.array([-1.25, 3.5])
+    for splits in (1, 3):
+        o, lse = _decode_oracle(pc, num_splits=splits, sinks=sinks)
+        assert np.all(o[0] == 0.0) and np.array_equal(lse[0], np.tile(sinks, (2, 1)))
+        assert np.all(o[1, 0] == 0.0) and np.array_equal(lse[1, 0], sinks)
+        assert np.all(np.isfinite(lse[1, 1]))
+
+
 # ---- per-tensor FP8 (E4M3) ----------------------------------------------------
 
 def _e4m3_torch(codes: torch.Tensor) -> torch.Tensor:
