@@ -43,12 +43,16 @@
  *     sequence with Lq queries and Lk keys sees key j iff j <= i + Lk - Lq
  *     (v1.28.0 "New: FROST SDPA ...", per-sequence THD bottom-right
  *     diagonals).
- *   - Thread-safe.  Mutable global state: the thread-local error detail, and
- *     the work-queue counters of the persistent prefill grid (a small
- *     static device array per GPU, 64 slots taken round robin by successive
- *     prefill calls; each launch returns its slot to zero when it ends).  Up
- *     to 64 prefill calls may therefore be in flight on one GPU at once
- *     (different streams); a 65th overlapping call would share a slot.
+ *   - Thread-safe.  Mutable global state: the thread-local error detail;
+ *     the work-queue counters of the persistent prefill and decode grids
+ *     (small static device arrays per GPU, 1024 slots each).  Each
+ *     launch takes the next slot with a launch tag of its own; a counter
+ *     still carrying another launch's tag (left behind by a launch that
+ *     never finished) is taken over rather than trusted, and a launch that
+ *     finishes returns its slot to zero, so a replayed captured launch finds
+ *     it free.  Up to 1024 prefill calls and 1024 decode calls may be in
+ *     flight on one GPU at once (different streams); a 1025th concurrent
+ *     call would share a slot with the first.
  */
 #ifndef SDPA_MI355X_H
 #define SDPA_MI355X_H
@@ -85,8 +89,9 @@ typedef enum {
                              -inf on `stream`, so rows i >= Lq_b read -inf           */
     SDPA_LSE_HEAD_MAJOR = 3 /* head-major rows [h_q, total]: lse[h * lse_s_max +
                              cu_seqlens_q[b] + i]; lse_s_max is the per-head stride,
-                             at least cu_seqlens_q[batch] (bf16 prefill only; v1.28.0
-                             release notes, Bug Fixes, head-major stats)             */
+                             at least cu_seqlens_q[batch] (bf16 and FP8 prefill:
+                             sdpa_prefill_thd, _ex, _fp8; v1.28.0 release notes, Bug
+                             Fixes, head-major stats)                                */
 } sdpa_lse_layout_t;
 
 /*

@@ -66,6 +66,7 @@ struct SmallKArgs {
     const int32_t* seq_lens;
     int32_t batch, sq, hq, hkv, group, page, page_shift, splits, rows, n_units;
     int32_t slot;  // work-queue counters used by this launch
+    uint32_t gen;  // this launch's tag on those counters (never 0)
     int64_t total_rows;
     float scale_log2;
     int32_t causal;
@@ -83,20 +84,40 @@ constexpr int kWaves = 4;
 // Work queue of the persistent decode grid: counter [slot][0] hands out
 // units (ticket t: the t-th (sequence, KV head, split) in order of
 // decreasing sequence length), counter [slot][1] counts work-groups that
-// are done; the last one returns both to 0 for the next launch that uses
-// the slot.  Launches take slots round robin (kQueueSlots calls may overlap
-// on one device).
-constexpr int kQueueSlots = 64;
+// are done; the last one returns both to 0.  Every counter word carries the
+// tag of the launch that owns it (high 32 bits) next to its count (low 32
+// bits); launches take tags 1, 2, 3, ... and slot = tag % kQueueSlots, and a
+// launch that finds a counter with another tag (0 after a reset, or left
+// behind by a launch that never finished) takes it over (own_ticket).  Up to
+// kQueueSlots decode calls may run at once on one device.
+constexpr int kQueueSlots = 1024;
 constexpr int kRankMax = 256;  // longest-first order for batches up to this size
-__device__ __align__(256) uint32_t g_decode_queue[kQueueSlots][32];
+__device__ __align__(256) uint64_t g_decode_queue[kQueueSlots][4];
 
-// Ticket from a work-queue counter: the value before adding 1.  A plain
-// one-lane atomicAdd: this file is compiled without the wave-level atomic
-// optimizer, so the compiler waits for the returned value only where it is
-// used and keeps its register reserved until then.  (An asm atomic would hide
-// the pending write from the register allocator, which could hand the
-// register to another value before the atomic returns.)
-__device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) { return atomicAdd(ctr, 1u); }
+// Ticket request on a work-queue counter: the counter word before adding 1.
+// A plain one-lane atomicAdd: this file is compiled without the wave-level
+// atomic optimizer, so the compiler waits for the returned value only where
+// it is used and keeps its register reserved until then.  (An asm atomic
+// would hide the pending write from the register allocator, which could
+// hand the register to another value before the atomic returns.)
+__device__ __forceinline__ uint64_t ticket_async(uint64_t* ctr) {
+    return atomicAdd(reinterpret_cast<unsigned long long*>(ctr), 1ull);
+}
+// The ticket that `old` (a value ticket_async returned) stands for in the
+// launch tagged gen.  A counter that still carries another tag is taken
+// over: replaced by (gen, 1), which hands out ticket 0.
+__device__ __forceinline__ uint32_t own_ticket(uint64_t* ctr, uint64_t old, uint32_t gen) {
+    auto* c = reinterpret_cast<unsigned long long*>(ctr);
+    while ((uint32_t)(old >> 32) != gen) {
+        const unsigned long long seen = old + 1;  // the word after our add, if untouched since
+        const unsigned long long prev = atomicCAS(c, seen, ((unsigned long long)gen << 32) | 1ull);
+        if (prev == seen) return 0u;
+        // another work-group of this launch took the counter over (ask again), or
+        // another request landed on the old value (retry the take-over on it)
+        old = (uint32_t)(prev >> 32) == gen ? atomicAdd(c, 1ull) : prev - 1;
+    }
+    return (uint32_t)old;
+}
 
 // Fourth word of a raw buffer resource on gfx9-family parts (CDNA): no
 // swizzle, 32-bit data format; the range check returns zeros past num_records.
@@ -138,14 +159,14 @@ struct TileRegs {
 // into next_unit during the merge; returns that unit (-1: none left).
 template <int D, bool F8, class NextOf>
 __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, bf16_t* smem, const int b,
-                                                          const int kvh, const int split, uint32_t* ctr,
+                                                          const int kvh, const int split, uint64_t* ctr,
                                                           int* next_unit, NextOf&& next_of) {
     using C = SmallCfg<D, F8>;
     constexpr int EB = C::EB;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15, g = lane >> 4;
-    uint32_t ticket = 0;
+    uint64_t ticket = 0;
     if (threadIdx.x == 0) ticket = ticket_async(ctr);
 
     // a length past the table's reach is clamped: the table is never read out of bounds
@@ -456,7 +477,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     __shared__ int next_unit;
     __shared__ int by_len[kRankMax];  // by_len[r] = sequence with the r-th largest length
-    uint32_t* const ctr = g_decode_queue[a.slot];
+    uint64_t* const ctr = g_decode_queue[a.slot];
     const int per_seq = a.hkv * a.splits;
     const bool ranked = a.batch <= kRankMax;
     if (ranked && (int)threadIdx.x < a.batch) {
@@ -469,8 +490,12 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
         }
         by_len[r] = me;
     }
-    auto next_of = [&](uint32_t t) -> int { return t < (uint32_t)a.n_units ? (int)t : -1; };
-    if (threadIdx.x == 0) next_unit = next_of(atomicAdd(&ctr[0], 1u));
+    // unit of the ticket request `raw` (-1: the queue is empty)
+    auto next_of = [&](uint64_t raw) -> int {
+        const uint32_t t = own_ticket(&ctr[0], raw, a.gen);
+        return t < (uint32_t)a.n_units ? (int)t : -1;
+    };
+    if (threadIdx.x == 0) next_unit = next_of(ticket_async(&ctr[0]));
     __syncthreads();
     int unit = next_unit;
     while (unit >= 0) {
@@ -481,10 +506,10 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
         __syncthreads();  // the merge's LDS reads are done before the next unit's V^T stores
         unit = nxt;
     }
-    if (threadIdx.x == 0 && atomicAdd(&ctr[1], 1u) == gridDim.x - 1) {
-        // every work-group has taken its last ticket
-        atomicExch(&ctr[0], 0u);
-        atomicExch(&ctr[1], 0u);
+    if (threadIdx.x == 0 && own_ticket(&ctr[1], ticket_async(&ctr[1]), a.gen) == gridDim.x - 1) {
+        // every work-group has taken its last ticket: the slot is free again
+        atomicExch(reinterpret_cast<unsigned long long*>(&ctr[0]), 0ull);
+        atomicExch(reinterpret_cast<unsigned long long*>(&ctr[1]), 0ull);
     }
 }
 
@@ -508,8 +533,12 @@ hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
         n_cu = 1;
     const int64_t slots = (int64_t)occ * n_cu;
-    static std::atomic<uint32_t> slot_seq{0};
-    a.slot = (int32_t)(slot_seq.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
+    // launch tags 1, 2, 3, ... (0 marks a free counter)
+    static std::atomic<uint32_t> launch_seq{0};
+    uint32_t gen = launch_seq.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    while (gen == 0u) gen = launch_seq.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    a.gen = gen;
+    a.slot = (int32_t)(gen % kQueueSlots);
     hipLaunchKernelGGL((decode_small_kernel<D, F8>), dim3((unsigned)(a.n_units < slots ? a.n_units : slots)), dim3(256),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();

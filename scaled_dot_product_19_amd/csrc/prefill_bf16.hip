@@ -83,6 +83,7 @@ struct PrefillKArgs {
     const float* sinks;             // [hq] sink logits (natural-log units) or nullptr
     int32_t stats_log2;             // LSE in base 2
     int32_t slot;    // work-queue counters used by this launch
+    uint32_t gen;    // this launch's tag on those counters (never 0)
     // paged mode (chunked prefill over a paged cache; see launch_prefill_paged):
     // Q [batch, sq, hq, D] dense, K/V rows through independent page tables,
     // key range split in `splits` chunks, fp32 partials when splits > 1
@@ -103,12 +104,18 @@ struct PrefillKArgs {
 // number of pairs of XCD x.  A work-group takes tickets from the queue of
 // the XCD it runs on and, once that is empty, from the other seven in turn.
 // Counter [slot][8] counts work-groups that are done; the last one returns
-// all counters to 0 for the next launch that uses the slot.  Launches take
-// slots round robin, so up to kQueueSlots prefill calls may overlap on one
-// device.
-constexpr int kQueueSlots = 64;
+// all counters of the slot to 0.
+//
+// Every counter word carries the tag of the launch that owns it (high 32
+// bits) next to its count (low 32 bits).  Launches take tags 1, 2, 3, ...
+// and slot = tag % kQueueSlots; a launch that finds a counter with another
+// tag (0 after a reset, or left behind by a launch that never finished)
+// takes it over (own_ticket), so no earlier launch can leave a slot that
+// makes a later one skip work.  Up to kQueueSlots prefill calls may run at
+// once on one device.
+constexpr int kQueueSlots = 1024;
 constexpr int kXcds = 8;
-__device__ __align__(256) uint32_t g_prefill_queue[kQueueSlots][32];
+__device__ __align__(256) uint64_t g_prefill_queue[kQueueSlots][16];
 
 constexpr float kLazyRescale = 8.f;  // log2 units the running max may lag behind
 
@@ -140,13 +147,33 @@ struct PCfg {
     static_assert(BN % 32 == 0 && D % 32 == 0 && CPR >= 8, "tile shape");
 };
 
-// Ticket from a work-queue counter: the value before adding 1.  A plain
-// one-lane atomicAdd: this file is compiled without the wave-level atomic
-// optimizer, so the compiler waits for the returned value only where it is
-// used and keeps its register reserved until then.  (An asm atomic would hide
-// the pending write from the register allocator, which could hand the
-// register to another value before the atomic returns.)
-__device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) { return atomicAdd(ctr, 1u); }
+// Ticket request on a work-queue counter: the counter word before adding 1.
+// A plain one-lane atomicAdd: this file is compiled without the wave-level
+// atomic optimizer, so the compiler waits for the returned value only where
+// it is used and keeps its register reserved until then.  (An asm atomic
+// would hide the pending write from the register allocator, which could
+// hand the register to another value before the atomic returns.)
+__device__ __forceinline__ uint64_t ticket_async(uint64_t* ctr) {
+    return atomicAdd(reinterpret_cast<unsigned long long*>(ctr), 1ull);
+}
+// The ticket that `old` (a value ticket_async returned) stands for in the
+// launch tagged gen.  A counter that still carries another tag is taken
+// over: replaced by (gen, 1), which hands out ticket 0.
+__device__ __forceinline__ uint32_t own_ticket_slow(uint64_t* ctr, uint64_t old, uint32_t gen) {
+    auto* c = reinterpret_cast<unsigned long long*>(ctr);
+    while ((uint32_t)(old >> 32) != gen) {
+        const unsigned long long seen = old + 1;  // the word after our add, if untouched since
+        const unsigned long long prev = atomicCAS(c, seen, ((unsigned long long)gen << 32) | 1ull);
+        if (prev == seen) return 0u;
+        // another work-group of this launch took the counter over (ask again), or
+        // another request landed on the old value (retry the take-over on it)
+        old = (uint32_t)(prev >> 32) == gen ? atomicAdd(c, 1ull) : prev - 1;
+    }
+    return (uint32_t)old;
+}
+__device__ __forceinline__ uint32_t own_ticket(uint64_t* ctr, uint64_t old, uint32_t gen) {
+    return (uint32_t)(old >> 32) == gen ? (uint32_t)old : own_ticket_slow(ctr, old, gen);
+}
 
 // D <= 128: two work-groups per CU (<= 256 registers per lane, 2-stage ring).
 // D = 256: one, with a 4-stage ring and the O^T accumulators in AGPRs.
@@ -159,7 +186,7 @@ __device__ __forceinline__ uint32_t ticket_async(uint32_t* ctr) { return atomicA
 template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED, bool F8>
 __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& a, const int item,
                                                             char* const lds, const uint32_t lds_base,
-                                                            uint32_t* const tctr, uint32_t& ticket) {
+                                                            uint64_t* const tctr, uint64_t& ticket) {
     static_assert(!PP || (NW == 8 && S >= 4), "ping-pong needs two wave groups and S >= 4");
     static_assert(!F8 || (PP && !PAGED && D == 128), "FP8: the D = 128 ping-pong THD kernel");
     using C = PCfg<D, BN, S, NW, F8>;
@@ -851,7 +878,7 @@ __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kern
     __shared__ int next_item;
     char* const lds = reinterpret_cast<char*>(smem);
     const uint32_t lds_base = lds_addr(smem);
-    uint32_t* const ctr = g_prefill_queue[a.slot];
+    uint64_t* const ctr = g_prefill_queue[a.slot];
     const int n_pairs = a.batch * a.n_hg * (PAGED ? a.splits : 1);
     // Only lane 0 of wave 0 talks to the queues: q is the queue it draws
     // from, tries the number of queues it has found empty.
@@ -863,34 +890,34 @@ __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kern
         const int level = (int)t / m;
         return level * n_pairs + x + kXcds * ((int)t - level * m);
     };
-    // next item after ticket t of queue q, moving on to the other queues
-    auto next_of = [&](uint32_t t) -> int {
-        int it = item_of(q, t);
-        while (it < 0 && ++tries < kXcds) {
+    // next item after the ticket request `raw` on queue q, moving on to the
+    // other queues
+    auto next_of = [&](uint64_t raw) -> int {
+        for (;;) {
+            const int it = item_of(q, own_ticket(&ctr[q], raw, a.gen));
+            if (it >= 0 || ++tries >= kXcds) return it;
             q = (q + 1) % kXcds;
-            it = item_of(q, atomicAdd(&ctr[q], 1u));
+            raw = ticket_async(&ctr[q]);
         }
-        return it;
     };
+    uint64_t ticket = 0;
     if (threadIdx.x == 0) {
         unsigned xcc;
         asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
         q = (int)(xcc % kXcds);
-        next_item = next_of(atomicAdd(&ctr[q], 1u));
+        ticket = ticket_async(&ctr[q]);
     }
-    __syncthreads();
-    int item = next_item;
-    while (item >= 0) {
-        uint32_t ticket = 0;
-        prefill_item<D, BN, S, NW, PP, CZ, PAGED, F8>(a, item, lds, lds_base, &ctr[q], ticket);
-        __syncthreads();  // every wave has read next_item of the last round
+    for (;;) {
         if (threadIdx.x == 0) next_item = next_of(ticket);
         __syncthreads();
-        item = next_item;
+        const int item = next_item;
+        if (item < 0) break;
+        prefill_item<D, BN, S, NW, PP, CZ, PAGED, F8>(a, item, lds, lds_base, &ctr[q], ticket);
+        __syncthreads();  // every wave has read next_item before it is replaced
     }
-    if (threadIdx.x == 0 && atomicAdd(&ctr[kXcds], 1u) == gridDim.x - 1) {
-        // every work-group has taken its last ticket
-        for (int x = 0; x <= kXcds; ++x) atomicExch(&ctr[x], 0u);
+    if (threadIdx.x == 0 && own_ticket(&ctr[kXcds], ticket_async(&ctr[kXcds]), a.gen) == gridDim.x - 1) {
+        // every work-group has taken its last ticket: the slot is free again
+        for (int x = 0; x <= kXcds; ++x) atomicExch(reinterpret_cast<unsigned long long*>(&ctr[x]), 0ull);
     }
 }
 
@@ -913,7 +940,13 @@ int resident_slots(K kernel, int threads, int lds_bytes) {
     return occ * n_cu;
 }
 
-std::atomic<uint32_t> g_slot_seq{0};
+// Launch tags of the prefill work queues: 1, 2, 3, ... (0 marks a free counter).
+std::atomic<uint32_t> g_launch_seq{0};
+uint32_t next_launch_tag() {
+    uint32_t g = g_launch_seq.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    while (g == 0u) g = g_launch_seq.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    return g;
+}
 
 template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED, bool F8>
 struct KernelTag {};
@@ -927,7 +960,8 @@ hipError_t launch_dz(PrefillKArgs a, int64_t n_wg, hipStream_t s) {
     if (e != hipSuccess) return e;
     const int64_t slots =
         resident_slots<KernelTag<D, BN, S, NW, PP, CZ, PAGED, F8>>(kernel, C::THREADS, C::LDS_BYTES);
-    a.slot = (int32_t)(g_slot_seq.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots);
+    a.gen = next_launch_tag();
+    a.slot = (int32_t)(a.gen % kQueueSlots);
     hipLaunchKernelGGL(kernel, dim3((unsigned)(n_wg < slots ? n_wg : slots)), dim3(C::THREADS),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
