@@ -45,7 +45,8 @@
  *     diagonals).
  *   - Thread-safe.  Mutable global state: the thread-local error detail;
  *     the work-queue counters of the persistent prefill and decode grids
- *     (small static device arrays per GPU, 1024 slots each).  Each
+ *     (small static device arrays per GPU, 1024 slots each); and the
+ *     library-owned split workspace of sdpa_decode_paged_noalloc.  Each
  *     launch takes the next slot with a launch tag of its own; a counter
  *     still carrying another launch's tag (left behind by a launch that
  *     never finished) is taken over rather than trusted, and a launch that
@@ -287,6 +288,32 @@ int sdpa_decode_paged_fp8(const void* q,
                           void* workspace, size_t workspace_bytes,
                           const float* descale_q, const float* descale_k,
                           const float* descale_v, void* o, float* lse, void* stream);
+
+/*
+ * sdpa_decode_paged for callers that cannot allocate device memory around a
+ * call (code under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, results and kernels, without the workspace
+ * arguments.  The split partials go to a library-owned device array of
+ * 32 MiB per GPU (each GPU the library runs on holds it until the process
+ * ends); a call whose split workspace (sdpa_decode_workspace_bytes) exceeds
+ * it is declined with SDPA_ERR_WORKSPACE before anything is enqueued.  The
+ * array's device address on the current device is looked up on the first
+ * call on that device (no allocation); a failed lookup returns SDPA_ERR_HIP.
+ * The call allocates nothing.  All calls on one GPU share the array and it
+ * keeps the last call's contents (nothing needs clearing: every partial the
+ * combine reads is written first), so calls that overlap on one GPU, on
+ * different streams, race on it and must not be issued.
+ * dtype: SDPA_BF16 only.
+ */
+int sdpa_decode_paged_noalloc(const void* q,
+                              const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,
+                              const void* v_pool, int64_t v_sp, int64_t v_st, int64_t v_sh,
+                              const int32_t* page_table_k, const int32_t* page_table_v,
+                              int32_t table_stride, const int32_t* seq_lens,
+                              int32_t max_seqlen_kv, int32_t batch, int32_t s_q, int32_t h_q,
+                              int32_t h_kv, int32_t d_qk, int32_t d_v, int32_t page_size,
+                              float scale, int32_t causal, int32_t num_splits,
+                              void* o, float* lse, int32_t dtype, void* stream);
 
 /*
  * LSE merge of split-KV partials (the merge the notes use but never print;

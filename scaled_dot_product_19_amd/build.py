@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libsdpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["sdpa_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_paged.hip",
-           "decode_small.hip", "decode_wide.hip", "combine.hip"]
+           "decode_small.hip", "decode_wide.hip", "combine.hip", "decode_noalloc.hip"]
 
 
 def hipcc() -> str:

@@ -258,7 +258,8 @@ static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t 
                        int32_t d_v, int32_t page_size, float scale, int32_t causal,
                        int32_t num_splits, void* workspace, size_t workspace_bytes, void* o,
                        float* lse, int32_t dtype, const float* descale_q,
-                       const float* descale_k, const float* descale_v, void* stream) {
+                       const float* descale_k, const float* descale_v, void* stream,
+                       bool use_scratch = false) {
     const bool fp8 = dtype == SDPA_FP8_E4M3;
     if (batch < 0) return fail(SDPA_ERR_SHAPE, "batch=%d < 0", batch);
     if (s_q <= 0) return fail(SDPA_ERR_SHAPE, "s_q=%d must be >= 1", s_q);
@@ -333,6 +334,21 @@ static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t 
         (lse && !aligned(lse, 4)))
         return fail(SDPA_ERR_UNSUPPORTED, "q/pools/o must be 16-byte aligned");
     const size_t need = sdpa_decode_workspace_bytes(batch, s_q, h_q, d_v, num_splits);
+    if (use_scratch) {
+        // the library-owned workspace: bounded, looked up without allocating
+        if (need > sdpa::kDecodeScratchBytes)
+            return fail(SDPA_ERR_WORKSPACE,
+                        "the split workspace of this call (%zu bytes) exceeds the library-owned "
+                        "%zu bytes; use sdpa_decode_paged with a caller workspace",
+                        need, sdpa::kDecodeScratchBytes);
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            hipError_t e = sdpa::decode_scratch(&workspace);
+            if (e != hipSuccess) return hip_fail(e, "library-owned decode workspace lookup");
+            workspace_bytes = sdpa::kDecodeScratchBytes;
+        }
+    }
     if (num_splits > 1) {
         if (workspace == nullptr)
             return fail(SDPA_ERR_WORKSPACE, "num_splits=%d needs %zu bytes of workspace, got NULL",
@@ -423,6 +439,21 @@ int sdpa_decode_paged_fp8(const void* q, const void* k_pool, int64_t k_sp, int64
                        d_qk, d_v, page_size, scale, causal, num_splits, workspace,
                        workspace_bytes, o, lse, SDPA_FP8_E4M3, descale_q, descale_k, descale_v,
                        stream);
+}
+
+int sdpa_decode_paged_noalloc(const void* q, const void* k_pool, int64_t k_sp, int64_t k_st,
+                              int64_t k_sh, const void* v_pool, int64_t v_sp, int64_t v_st,
+                              int64_t v_sh, const int32_t* page_table_k,
+                              const int32_t* page_table_v, int32_t table_stride,
+                              const int32_t* seq_lens, int32_t max_seqlen_kv, int32_t batch,
+                              int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk, int32_t d_v,
+                              int32_t page_size, float scale, int32_t causal, int32_t num_splits,
+                              void* o, float* lse, int32_t dtype, void* stream) {
+    if (dtype != SDPA_BF16) return fail(SDPA_ERR_UNSUPPORTED, "paged decode serves bf16 only");
+    return decode_impl(q, k_pool, k_sp, k_st, k_sh, v_pool, v_sp, v_st, v_sh, page_table_k,
+                       page_table_v, table_stride, seq_lens, max_seqlen_kv, batch, s_q, h_q, h_kv,
+                       d_qk, d_v, page_size, scale, causal, num_splits, nullptr, 0, o, lse,
+                       SDPA_BF16, nullptr, nullptr, nullptr, stream, /*use_scratch=*/true);
 }
 
 int sdpa_splitkv_combine(const float* o_part, const float* lse_part, int32_t num_splits,

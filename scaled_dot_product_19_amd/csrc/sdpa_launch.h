@@ -66,6 +66,11 @@ hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t sp
                           hipStream_t s);
 hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t s);
 
+// Library-owned split workspace of sdpa_decode_paged_noalloc: bytes per GPU,
+// and its device address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Decode row-group geometry shared by the launcher and the workspace query.
 bool decode_supported(int32_t dqk, int32_t dv);
 

@@ -39,10 +39,10 @@ LSE_PADDED = 2
 LSE_HEAD_MAJOR = 3
 
 # every symbol include/sdpa.h declares
-EXPORTS = ("sdpa_prefill_thd", "sdpa_prefill_thd_ex", "sdpa_prefill_thd_fp8", "sdpa_decode_workspace_bytes", "sdpa_decode_paged",
-           "sdpa_decode_paged_fp8",
-           "sdpa_splitkv_combine", "sdpa_status_string", "sdpa_last_error_detail",
-           "sdpa_version")
+EXPORTS = ("sdpa_prefill_thd", "sdpa_prefill_thd_ex", "sdpa_prefill_thd_fp8",
+           "sdpa_decode_workspace_bytes", "sdpa_decode_paged", "sdpa_decode_paged_fp8",
+           "sdpa_decode_paged_noalloc", "sdpa_splitkv_combine", "sdpa_status_string",
+           "sdpa_last_error_detail", "sdpa_version")
 
 
 class SdpaError(RuntimeError):
@@ -92,6 +92,10 @@ def load():
     lib.sdpa_decode_paged_fp8.argtypes = [P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P,
                                           I32, I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P,
                                           SZ, P, P, P, P, P, P]
+    lib.sdpa_decode_paged_noalloc.restype = ctypes.c_int
+    lib.sdpa_decode_paged_noalloc.argtypes = [P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32,
+                                              P, I32, I32, I32, I32, I32, I32, I32, I32, F, I32,
+                                              I32, P, P, I32, P]
     lib.sdpa_splitkv_combine.restype = ctypes.c_int
     lib.sdpa_splitkv_combine.argtypes = [P, P, I32, I64, I32, P, P, I32, P]
     lib.sdpa_status_string.restype = ctypes.c_char_p
@@ -276,6 +280,29 @@ def decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
         _ptr(page_table_v), int(page_table_k.shape[1]), _ptr(seq_lens), int(max_seqlen_kv), B,
         s_q, hq, hkv, dqk, dv, page, float(scale), int(bool(causal)), int(num_splits),
         _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _dtype_code(q), _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def decode_paged_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                         page_table_k: torch.Tensor, page_table_v: torch.Tensor,
+                         seq_lens: torch.Tensor, max_seqlen_kv: int, scale: float,
+                         out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                         causal: bool = True, num_splits: int = 1, stream=None):
+    """sdpa_decode_paged_noalloc: sdpa_decode_paged with the split partials in the
+    library-owned device array (no workspace argument; the caller passes out and lse).
+
+    Returns (out, lse).
+    """
+    lib = load()
+    B, s_q, hq, dqk = (int(x) for x in q.shape)
+    page, hkv, dv = int(k_pool.shape[1]), int(k_pool.shape[2]), int(v_pool.shape[3])
+    rc = lib.sdpa_decode_paged_noalloc(
+        _ptr(q), _ptr(k_pool), k_pool.stride(0), k_pool.stride(1), k_pool.stride(2),
+        _ptr(v_pool), v_pool.stride(0), v_pool.stride(1), v_pool.stride(2), _ptr(page_table_k),
+        _ptr(page_table_v), int(page_table_k.shape[1]), _ptr(seq_lens), int(max_seqlen_kv), B,
+        s_q, hq, hkv, dqk, dv, page, float(scale), int(bool(causal)), int(num_splits),
+        _ptr(out), _ptr(lse), _dtype_code(q), _stream(stream))
     _check(rc)
     return out, lse
 

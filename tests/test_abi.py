@@ -265,3 +265,23 @@ def test_combine_rejects():
     assert lib.sdpa_splitkv_combine(fake, fake, 4, 10, 128, fake, fake, 5, None) == \
         sdpa.SDPA_ERR_UNSUPPORTED
     assert lib.sdpa_splitkv_combine(None, None, 4, 0, 128, None, None, 0, None) == sdpa.SDPA_OK
+
+
+def test_decode_noalloc_declines_a_workspace_beyond_its_array():
+    lib = sdpa.load()
+    fake = ctypes.c_void_p(0x100000)
+    # B=32, 2 tokens, 128 heads, d_v 512, 16 splits: 268 MB of partials > 32 MiB
+    rc = lib.sdpa_decode_paged_noalloc(fake, fake, 64 * 576, 576, 576, fake, 64 * 512, 512, 512,
+                                       fake, fake, 256, fake, 16384, 32, 2, 128, 1, 576, 512, 64,
+                                       0.04, 1, 16, fake, fake, 0, None)
+    assert rc == sdpa.SDPA_ERR_WORKSPACE
+    assert "exceeds" in lib.sdpa_last_error_detail().decode()
+    # argument checks still come first
+    rc = lib.sdpa_decode_paged_noalloc(fake, fake, 64 * 576, 576, 576, fake, 64 * 512, 512, 512,
+                                       fake, fake, 256, fake, 16384, 32, 2, 128, 3, 576, 512, 64,
+                                       0.04, 1, 16, fake, fake, 0, None)
+    assert rc == sdpa.SDPA_ERR_SHAPE
+    rc = lib.sdpa_decode_paged_noalloc(fake, fake, 64 * 576, 576, 576, fake, 64 * 512, 512, 512,
+                                       fake, fake, 256, fake, 16384, 32, 2, 128, 1, 576, 512, 64,
+                                       0.04, 1, 16, fake, fake, 1, None)
+    assert rc == sdpa.SDPA_ERR_UNSUPPORTED
