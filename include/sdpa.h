@@ -290,6 +290,44 @@ int sdpa_decode_paged_fp8(const void* q,
                           const float* descale_v, void* o, float* lse, void* stream);
 
 /*
+ * Paged-KV decode with the mask and Stats variants: sdpa_decode_paged (dtype
+ * SDPA_BF16) or sdpa_decode_paged_fp8 (dtype SDPA_FP8_E4M3, descales as
+ * there; NULL for bf16) plus:
+ * window_left: 0 = none; W > 0 = left sliding window: query token t of
+ *   sequence b (at key position seq_lens[b] - s_q + t) sees only keys
+ *   j >= seq_lens[b] - s_q + t - W + 1, the W keys ending at its own position
+ *   when causal (left sliding windows: v1.32.0 Release Notes, "SDPA: backward
+ *   and numerical fixes"; decode with a sliding window: v1.30.0 Release Notes,
+ *   "New: decode tiles").  Negative values are rejected (SDPA_ERR_SHAPE).
+ *   With num_splits > 1 the keys cut into chunks start at the page holding
+ *   the first key any token of the sequence sees, so no chunk is spent on
+ *   keys outside every window.
+ * sinks: NULL, or device fp32 [h_q] attention-sink logits in the units of the
+ *   scaled logits: head h's sink joins every row's softmax denominator once
+ *   and carries no value (as in sdpa_prefill_thd_ex); a row with no visible
+ *   key gets O = 0 and LSE = sink_h.  With num_splits > 1 the partials carry
+ *   no sink and the merge adds it (sinks at S_q == 1 with paged KV and a
+ *   sliding window: v1.30.0 "New: decode tiles"; split-KV and paged FP8 with
+ *   sinks: v1.32.0 "SDPA: wider native forward support").
+ * stats_log2: 0 = natural-log LSE; 1 = base 2 (v1.30.0 "New: stats_use_log2").
+ *   The split workspace partials stay natural-log.
+ * Supported shapes are those of sdpa_decode_paged (bf16) or
+ * sdpa_decode_paged_fp8 (FP8), every variant with each of them.
+ */
+int sdpa_decode_paged_ex(const void* q,
+                         const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,
+                         const void* v_pool, int64_t v_sp, int64_t v_st, int64_t v_sh,
+                         const int32_t* page_table_k, const int32_t* page_table_v,
+                         int32_t table_stride, const int32_t* seq_lens, int32_t max_seqlen_kv,
+                         int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv,
+                         int32_t d_qk, int32_t d_v, int32_t page_size,
+                         float scale, int32_t causal, int32_t window_left, const float* sinks,
+                         int32_t stats_log2, int32_t num_splits,
+                         void* workspace, size_t workspace_bytes,
+                         const float* descale_q, const float* descale_k, const float* descale_v,
+                         void* o, float* lse, int32_t dtype, void* stream);
+
+/*
  * sdpa_decode_paged for callers that cannot allocate device memory around a
  * call (code under stream capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments, results and kernels, without the workspace

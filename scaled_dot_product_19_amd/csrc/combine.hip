@@ -7,7 +7,11 @@
 //   M = max_c LSE_c, LSE = M + ln sum_c exp(LSE_c - M),
 //   O = sum_c exp(LSE_c - LSE) * O_c; every split empty -> O = 0, LSE = -inf.
 // A split with LSE_c = -inf gets weight exactly 0 and its partial is not
-// read, so an empty split never contributes 0 * NaN.
+// read, so an empty split never contributes 0 * NaN.  With attention sinks
+// (decode with split-KV: v1.32.0 Release Notes, "SDPA: wider native forward
+// support", split-KV supports sinks) the sink of the row's head joins the
+// merge once, as one more term with no value: M = max(M, sink), the sum gains
+// exp(sink - M), and no partial is scaled by it.
 //
 // -inf seeding: a padded (b, s_max, h) Stats buffer under THD is filled with
 // -inf on the launch stream before the prefill writes the real rows (v1.30.0
@@ -25,7 +29,9 @@ template <bool OUT_F32>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       int splits, int64_t rows, int dv, void* o,
-                                                      float* lse, int vec) {
+                                                      float* lse, int vec,
+                                                      const float* __restrict__ sinks, int hq,
+                                                      int stats_log2) {
     __shared__ float w_s[4][kMaxSplits];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -33,14 +39,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float* w = w_s[wave];
     float lse_row = neg_inf();
     if (valid) {
-        float m = neg_inf();
+        // row = (b * s_q + t) * hq + h: the sink of head h (natural-log units)
+        const float sk = sinks != nullptr ? sinks[row % hq] : neg_inf();
+        float m = sk;
         for (int c = lane; c < splits; c += 64) m = fmaxf(m, lse_part[(int64_t)c * rows + row]);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
         if (m == neg_inf()) {
             for (int c = lane; c < splits; c += 64) w[c] = 0.f;
         } else {
-            float sum = 0.f;
+            float sum = lane == 0 ? fast_exp2((sk - m) * kLog2e) : 0.f;  // 0 without a sink
             for (int c = lane; c < splits; c += 64)
                 sum += fast_exp2((lse_part[(int64_t)c * rows + row] - m) * kLog2e);
 #pragma unroll
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                 static_cast<bf16_t*>(o)[row * dv + n] = (bf16_t)f32_to_bf16_bits(acc);
         }
     }
-    if (lse != nullptr && lane == 0) lse[row] = lse_row;
+    if (lse != nullptr && lane == 0) lse[row] = stats_log2 ? lse_row * kLog2e : lse_row;
 }
 
 __global__ void fill_kernel(float* p, int64_t n, float value) {
@@ -113,17 +121,20 @@ __global__ void fill_kernel(float* p, int64_t n, float value) {
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,
                           int64_t rows, int32_t dv, void* o, float* lse, int32_t out_f32,
-                          hipStream_t s) {
+                          hipStream_t s, const float* sinks, int32_t hq, int32_t stats_log2) {
     if (rows == 0) return hipSuccess;
     const int64_t blocks = (rows + 3) / 4;
     const int vec = (dv % 4 == 0) && reinterpret_cast<uintptr_t>(o_part) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(o) % (out_f32 ? 16 : 8) == 0;
+    if (sinks == nullptr) hq = 1;
     if (out_f32)
         hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, o_part,
-                           lse_part, (int)splits, rows, (int)dv, o, lse, vec);
+                           lse_part, (int)splits, rows, (int)dv, o, lse, vec, sinks, (int)hq,
+                           (int)stats_log2);
     else
         hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, o_part,
-                           lse_part, (int)splits, rows, (int)dv, o, lse, vec);
+                           lse_part, (int)splits, rows, (int)dv, o, lse, vec, sinks, (int)hq,
+                           (int)stats_log2);
     return hipGetLastError();
 }
 

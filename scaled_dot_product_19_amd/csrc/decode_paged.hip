@@ -42,6 +42,9 @@ struct DecodeKArgs {
     float* lse_part;
     bf16_t* o;
     float* lse;
+    int32_t window;      // left sliding window (0: none)
+    const float* sinks;  // [hq] sink logits (natural-log units) or nullptr
+    int32_t stats_log2;  // final LSE in base 2
 };
 
 constexpr int BK = 32;
@@ -67,11 +70,15 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
 
     // a length past the table's reach is clamped: the table is never read out of bounds
     const int L = min(a.seq_lens[b], a.table_stride * a.page);
-    int lo = 0, hi = L;
+    // keys [base, L) are cut into the splits; with a left window, base is the
+    // start of the page holding the first key any token of the sequence sees
+    int base = 0;
+    if (a.window > 0 && L - a.sq - a.window + 1 > 0) base = ((L - a.sq - a.window + 1) / a.page) * a.page;
+    int lo = base, hi = L;
     if (a.splits > 1) {
-        const int per = (L + a.splits - 1) / a.splits;
+        const int per = (L - base + a.splits - 1) / a.splits;
         const int chunk = ((per + a.page - 1) / a.page) * a.page;
-        lo = min(L, split * chunk);
+        lo = min(L, base + split * chunk);
         hi = min(L, lo + chunk);
     }
     const int row0_wg = rg * NW * 32;
@@ -91,6 +98,11 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
         kv_end_w = max(lo, min(hi, last_key((min(a.rows, row0 + 32) - 1) / a.group) + 1));
         nomask_end = max(lo, min(hi, last_key(row0 / a.group) + 1));
     }
+    // first key each row may see (left window): this lane's, and the largest of
+    // the wave's rows (its last token's); tiles starting below it need the mask
+    auto first_key = [&](int tok) { return a.window > 0 ? L - a.sq + tok - a.window + 1 : INT32_MIN; };
+    const int first = first_key(t);
+    const int first_w = first_key((min(a.rows, row0 + 32) - 1) / a.group);
 
     bf16x8 qf[DQK / 16];
     const int64_t grow = ((int64_t)b * a.sq + t) * a.hq + h;  // global row id
@@ -138,8 +150,9 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
             }
             const bf16_t* buf = smem + (it & 1) * G::BUF_ELEMS;
             if (key0 < kv_end_w)
-                tile_step<DQK, DV, BK>(buf, buf + G::K_ELEMS, qf, st, key0, lim,
-                                       key0 + BK > nomask_end, a.scale_log2, lane);
+                tile_step<DQK, DV, BK>(buf, buf + G::K_ELEMS, qf, st, key0, lim, first,
+                                       key0 + BK > nomask_end || key0 < first_w, a.scale_log2,
+                                       lane);
             if (more) {
                 bf16_t* nb = smem + ((it + 1) & 1) * G::BUF_ELEMS;
                 store_k_part<DQK, DV, BK, NT>(kr, nb, tid);
@@ -162,16 +175,32 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
             }
             __syncthreads();
             if (key0 < kv_end_w)
-                tile_step<DQK, DV, BK>(smem, smem + G::K_ELEMS, qf, st, key0, lim,
-                                       key0 + BK > nomask_end, a.scale_log2, lane);
+                tile_step<DQK, DV, BK>(smem, smem + G::K_ELEMS, qf, st, key0, lim, first,
+                                       key0 + BK > nomask_end || key0 < first_w, a.scale_log2,
+                                       lane);
             __syncthreads();
         }
     }
 
-    const float l_tot = row_total<DV>(st);
+    float l_tot = row_total<DV>(st);
     if (!row_ok) return;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse = l_tot > 0.f ? kLn2 * (st.m + fast_log2(l_tot)) : neg_inf();
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float m = st.m;
+    if (a.sinks != nullptr && a.splits == 1) {
+        // head h's sink joins the denominator with no value (log2 units); split
+        // partials leave it to the combine
+        const float sk = a.sinks[h] * kLog2e;
+        const float m2 = fmaxf(m, sk);
+        if (m2 != neg_inf()) {
+            const float alpha = fast_exp2(m - m2);  // 0 when no key is visible
+            l_tot = l_tot * alpha + fast_exp2(sk - m2);
+            inv = alpha / l_tot;
+            m = m2;
+        }
+    }
+    const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
+    // partials stay natural-log; the final Stats may be base 2
+    const float lse = a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
     if (a.splits > 1) {
         float* orow = a.o_part + ((int64_t)split * a.total_rows + grow) * DV;
 #pragma unroll
@@ -272,6 +301,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
     a.lse_part = da.lse_part;
     a.o = static_cast<bf16_t*>(da.o);
     a.lse = da.lse;
+    // a window of 2^30 keys covers every key the int32 lengths can describe
+    a.window = da.window > 0 ? min(da.window, 1 << 30) : 0;
+    a.sinks = da.sinks;
+    a.stats_log2 = da.stats_log2;
     a.n_rg = 1;
     if (a.n_units == 0) return hipSuccess;
     if (da.dqk == 64) return launch_dims<64, 64>(a, s);

@@ -77,6 +77,9 @@ struct SmallKArgs {
     const float* descale_q;  // F8 only: one fp32 each
     const float* descale_k;
     const float* descale_v;
+    int32_t window;          // left sliding window (0: none)
+    const float* sinks;      // [hq] sink logits (natural-log units) or nullptr
+    int32_t stats_log2;      // final LSE in base 2
 };
 
 constexpr int kWaves = 4;
@@ -171,11 +174,15 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
 
     // a length past the table's reach is clamped: the table is never read out of bounds
     const int L = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
-    int lo = 0, hi = L;
+    // keys [base, L) are cut into the splits; with a left window, base is the
+    // start of the page holding the first key any token of the sequence sees
+    int base = 0;
+    if (a.window > 0 && L - a.sq - a.window + 1 > 0) base = ((L - a.sq - a.window + 1) / a.page) * a.page;
+    int lo = base, hi = L;
     if (a.splits > 1) {
-        const int per = (L + a.splits - 1) / a.splits;
+        const int per = (L - base + a.splits - 1) / a.splits;
         const int chunk = ((per + a.page - 1) / a.page) * a.page;
-        lo = min(L, split * chunk);
+        lo = min(L, base + split * chunk);
         hi = min(L, lo + chunk);
     }
     // query column c of the tile = row c of this KV head: token c / G, head kvh*G + c % G
@@ -186,6 +193,11 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     const int lim = min(hi - 1, a.causal ? L - a.sq + tok : L - 1);
     // keys every live row sees (the first token has the earliest causal limit)
     const int nomask_end = max(lo, min(hi, a.causal ? L - a.sq + 1 : hi));
+    // first key this lane's token sees (left window), and the largest first key
+    // of the live tokens (the last token's): tiles starting below it need the
+    // lower mask
+    const int first = a.window > 0 ? L - a.sq + tok - a.window + 1 : INT32_MIN;
+    const int first_max = a.window > 0 ? L - a.window : INT32_MIN;
 
     // Q^T operand, 16 bytes per load.  bf16: lane (q = c, d-group g) holds
     // d = 32 kl + 8 g .. +8 of its row for k-step kl.  E4M3: load kl holds
@@ -335,14 +347,17 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
                 }
             }
         }
-        const bool need_mask = key0 + C::TK > nomask_end;
+        const bool need_mask = key0 + C::TK > nomask_end || key0 < first_max;
         float mt = neg_inf();
 #pragma unroll
         for (int sb = 0; sb < C::SB; ++sb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float x = s[sb][i] * scale_log2;
-                if (need_mask) x = key0 + 16 * sb + 4 * g + i > lim ? neg_inf() : x;
+                if (need_mask) {
+                    const int key = key0 + 16 * sb + 4 * g + i;
+                    x = (key > lim || key < first) ? neg_inf() : x;
+                }
                 s[sb][i] = x;
                 mt = fmaxf(mt, x);
             }
@@ -441,20 +456,38 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             M = fmaxf(M, mw[w]);
         }
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        float lse = neg_inf();
+        float tot = 0.f;
         if (M != neg_inf()) {
-            float tot = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
                 const float sc = fast_exp2(mw[w] - M);  // exactly 0 for an empty wave
                 tot += sc * red_l[w * 16 + q];
                 o += sc * *reinterpret_cast<const f32x4*>(red_o + (w * 16 + q) * D + n);
             }
-            o *= o_mul / tot;
-            lse = kLn2 * (M + fast_log2(tot));
         }
         const int t2 = q / a.group;
-        const int64_t row = ((int64_t)b * a.sq + t2) * a.hq + kvh * a.group + q % a.group;
+        const int hh = kvh * a.group + q % a.group;
+        const int64_t row = ((int64_t)b * a.sq + t2) * a.hq + hh;
+        float o_scale = o_mul;  // descale_v (1 unless FP8)
+        if (a.sinks != nullptr && a.splits == 1) {
+            // head hh's sink joins the denominator with no value (log2 units);
+            // split partials leave it to the combine
+            const float sk = a.sinks[hh] * kLog2e;
+            const float M2 = fmaxf(M, sk);
+            if (M2 != neg_inf()) {
+                const float al = fast_exp2(M - M2);  // 0 when no key is visible
+                tot = tot * al + fast_exp2(sk - M2);
+                o_scale *= al;
+                M = M2;
+            }
+        }
+        float lse = neg_inf();
+        if (tot > 0.f) {
+            o *= o_scale / tot;
+            const float lse2 = M + fast_log2(tot);
+            // partials stay natural-log; the final Stats may be base 2
+            lse = a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
+        }
         if (a.splits > 1) {
             *reinterpret_cast<f32x4*>(a.o_part + ((int64_t)split * a.total_rows + row) * D + n) = o;
             if (n == 0) a.lse_part[(int64_t)split * a.total_rows + row] = lse;
@@ -587,6 +620,11 @@ hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
     a.descale_q = da.descale_q;
     a.descale_k = da.descale_k;
     a.descale_v = da.descale_v;
+    // a window of 2^30 keys covers every key the int32 lengths can describe;
+    // the clamp keeps L - s_q + t - W + 1 in range
+    a.window = da.window > 0 ? min(da.window, 1 << 30) : 0;
+    a.sinks = da.sinks;
+    a.stats_log2 = da.stats_log2;
     if (da.fp8) {
         switch (da.dqk) {
             case 128: return launch_small_d<128, true>(a, s);

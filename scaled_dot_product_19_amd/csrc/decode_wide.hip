@@ -54,6 +54,9 @@ struct WideArgs {
     float* lse_part;  // [splits, batch*sq*hq]
     bf16_t* o;        // [batch, sq, hq, 512] when splits == 1
     float* lse;       // [batch, sq, hq] or null
+    int32_t window;   // left sliding window (0: none)
+    const float* sinks;  // [hq] sink logits (natural-log units) or null
+    int32_t stats_log2;  // final LSE in base 2
 };
 
 // LDS stage: K region A (dims 0..511 of 32 rows, pitch 1040 B: 1 KB + a
@@ -128,7 +131,9 @@ __device__ __forceinline__ uint32_t xor_add_here(uint32_t v, uint32_t x, uint32_
     return r;
 }
 
-template <int DQK, int DV>
+// VAR: a left window, sinks or base-2 Stats are requested (their masks and
+// epilogue cost registers the plain instantiation has none to spare for)
+template <int DQK, int DV, bool VAR>
 __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     using C = WCfg<DQK, DV>;
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
@@ -148,13 +153,17 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     const int kvh = bk % a.hkv;
     const int b = bk / a.hkv;
 
-    // keys of this chunk: [lo, hi)
+    // keys of this chunk: [lo, hi).  Keys [base, L) are cut into the splits;
+    // with a left window, base is the start of the page holding the first key
+    // any token of the sequence sees.
     const int L = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
-    int lo = 0, hi = L;
+    int base = 0;
+    if (VAR && a.window > 0 && L - a.sq - a.window + 1 > 0) base = ((L - a.sq - a.window + 1) / a.page) * a.page;
+    int lo = base, hi = L;
     if (a.splits > 1) {
-        const int per = (L + a.splits - 1) / a.splits;
+        const int per = (L - base + a.splits - 1) / a.splits;
         const int chunk = ((per + a.page - 1) / a.page) * a.page;
-        lo = min(L, split * chunk);
+        lo = min(L, base + split * chunk);
         hi = min(L, lo + chunk);
     }
 
@@ -174,6 +183,11 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     const int kv_end_w = wave_rows ? max(lo, end_of(r_w1)) : lo;
     const int nomask_end = wave_rows ? max(lo, end_of(r_w0)) : lo;
     const int lim = a.causal ? L - a.sq + tq : L - 1;  // last visible key of this lane
+    // first visible key of this lane (left window), and the largest of the
+    // wave's rows (its last token's): tiles starting below it need the lower mask
+    const bool win = VAR && a.window > 0;
+    const int first = win ? L - a.sq + tq - a.window + 1 : INT32_MIN;
+    const int first_w = win ? L - a.sq + r_w1 / a.group - a.window + 1 : INT32_MIN;
     const int n_tiles = (kv_end - lo + C::BN - 1) / C::BN;
 
     // ---- LDS DMA of the K/V tiles -------------------------------------------
@@ -335,9 +349,15 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         // online softmax; lane (col, half) holds keys key0 + 8 (i / 4) + 4 half + i % 4
         float mx = neg_inf();
         if (need_mask) {
+            // key = key0 + 4 half + (compile-time offset): masked above the causal
+            // bound dl or below the window's first key dlo
             const int dl = lim - key0 - 4 * half;
+            const int dlo = win ? first - key0 - 4 * half : -1;  // first is INT32_MIN without a window
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = (8 * (i >> 2) + (i & 3)) > dl ? neg_inf() : s[i];
+            for (int i = 0; i < 16; ++i) {
+                const int off = 8 * (i >> 2) + (i & 3);
+                s[i] = (off > dl || (VAR && off < dlo)) ? neg_inf() : s[i];
+            }
         }
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = max3(mx, s[i], s[i + 1]);
@@ -388,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         const DmaPlan d = plan(t + 1, ST ^ 1);
         const int key0 = lo + t * C::BN;
         if (key0 < kv_end_w) {
-            tile(lds + ST * C::STAGE_B, key0, key0 + C::BN > nomask_end,
+            tile(lds + ST * C::STAGE_B, key0, key0 + C::BN > nomask_end || (VAR && key0 < first_w),
                  [&](int j) __attribute__((always_inline)) { piece(d, j); });
         } else {
 #pragma unroll
@@ -422,11 +442,24 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         if (n_tiles > 0) issue(0, 0);
     }
 
-    // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l)
-    const float l_tot = half_sum(l);
+    // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l); with one split the sink
+    // of head h joins the denominator (split partials leave it to the combine)
+    float l_tot = half_sum(l);
     if (!row_ok) return;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const float lse = l_tot > 0.f ? kLn2 * (m + fast_log2(l_tot)) : neg_inf();
+    float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (VAR && a.sinks != nullptr && a.splits == 1) {
+        const float sk = a.sinks[h] * kLog2e;
+        const float m2 = fmaxf(m, sk);
+        if (m2 != neg_inf()) {
+            const float alpha = fast_exp2(m - m2);  // 0 when no key is visible
+            l_tot = l_tot * alpha + fast_exp2(sk - m2);
+            inv = alpha / l_tot;
+            m = m2;
+        }
+    }
+    const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
+    // partials stay natural-log; the final Stats may be base 2
+    const float lse = VAR && a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
     const int64_t row_g = (int64_t)(b * a.sq + tq) * a.hq + h;
     if (a.splits > 1) {
         const int64_t rows_all = (int64_t)a.batch * a.sq * a.hq;
@@ -498,14 +531,24 @@ hipError_t launch_decode_wide(const DecodeArgs& d, hipStream_t s) {
     a.lse_part = d.lse_part;
     a.o = static_cast<bf16_t*>(d.o);
     a.lse = d.lse;
+    // a window of 2^30 keys covers every key the int32 lengths can describe
+    a.window = d.window > 0 ? min(d.window, 1 << 30) : 0;
+    a.sinks = d.sinks;
+    a.stats_log2 = d.stats_log2;
     const int64_t n_wg = (n_g + 7) / 8 * 8 * a.n_rb;
     if (n_g == 0) return hipSuccess;
     if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-    hipError_t e = hipFuncSetAttribute((const void*)decode_wide_kernel<576, 512>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    const bool var = a.window > 0 || a.sinks != nullptr || a.stats_log2 != 0;
+    const void* kernel = var ? (const void*)decode_wide_kernel<576, 512, true>
+                             : (const void*)decode_wide_kernel<576, 512, false>;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_wide_kernel<576, 512>), dim3((unsigned)n_wg), dim3(256), (size_t)C::LDS_BYTES, s,
-                       a);
+    if (var)
+        hipLaunchKernelGGL((decode_wide_kernel<576, 512, true>), dim3((unsigned)n_wg), dim3(256),
+                           (size_t)C::LDS_BYTES, s, a);
+    else
+        hipLaunchKernelGGL((decode_wide_kernel<576, 512, false>), dim3((unsigned)n_wg), dim3(256),
+                           (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
 

@@ -216,9 +216,13 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         lk = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
         hi = lk;
         if (a.splits > 1) {
-            const int per = (lk + a.splits - 1) / a.splits;
+            // keys [base, lk) are cut into the splits; with a left window, base is
+            // the start of the page holding the first key any query token sees
+            int base = 0;
+            if (a.window > 0 && lk - lq - a.window + 1 > 0) base = ((lk - lq - a.window + 1) / a.page) * a.page;
+            const int per = (lk - base + a.splits - 1) / a.splits;
             const int chunk = ((per + a.page - 1) / a.page) * a.page;
-            lo = min(lk, split * chunk);
+            lo = min(lk, base + split * chunk);
             hi = min(lk, lo + chunk);
         }
     } else {
@@ -1063,9 +1067,11 @@ hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
     a.lse = d.lse;
     a.lse_layout = d.lse != nullptr ? 1 : 0;  // [B, s_q, Hq] = token-major
     a.lse_s_max = 0;
-    a.window = 0;
-    a.sinks = nullptr;
-    a.stats_log2 = 0;
+    // a window of 2^30 keys covers every key of any sequence the int32
+    // lengths can describe; the clamp keeps i + shift - W + 1 in range
+    a.window = d.window > 0 ? min(d.window, 1 << 30) : 0;
+    a.sinks = d.sinks;  // folded in the epilogue with one split, by the combine otherwise
+    a.stats_log2 = d.stats_log2;
     a.pt_k = d.pt_k;
     a.pt_v = d.pt_v;
     a.seq_lens = d.seq_lens;

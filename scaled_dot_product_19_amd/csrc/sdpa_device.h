@@ -232,14 +232,14 @@ __device__ __forceinline__ void row_state_init(RowState<DV>& st) {
 
 // One KV tile for one wave.
 //   ks/vt: the LDS tile; qf: the wave's Q^T operand (DQK/16 fragments);
-//   key0: absolute index of the tile's first key; lim: last key index this
-//   lane's query may see (keys > lim are masked, lim < key0 masks all);
+//   key0: absolute index of the tile's first key; lim / first: last and first
+//   key index this lane's query may see (keys > lim or < first are masked);
 //   need_mask: false when every key of the tile is visible to every row.
 template <int DQK, int DV, int BK>
 __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ ks,
                                           const bf16_t* __restrict__ vt, const bf16x8* qf,
-                                          RowState<DV>& st, int key0, int lim, bool need_mask,
-                                          float scale_log2, int lane) {
+                                          RowState<DV>& st, int key0, int lim, int first,
+                                          bool need_mask, float scale_log2, int lane) {
     using G = TileGeom<DQK, DV, BK>;
     const int col = lane & 31, half = lane >> 5;
     constexpr int NB = BK / 32;
@@ -266,7 +266,7 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ ks,
             float x = s[kb][r] * scale_log2;
             if (need_mask) {
                 int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                x = key > lim ? neg_inf() : x;
+                x = (key > lim || key < first) ? neg_inf() : x;
             }
             s[kb][r] = x;
             mt = fmaxf(mt, x);

@@ -55,15 +55,21 @@ struct DecodeArgs {
     const float* descale_q;
     const float* descale_k;
     const float* descale_v;
+    int32_t window;       // left sliding window (<= 0: none)
+    const float* sinks;   // [hq] sink logits or nullptr (folded once: in the combine when split)
+    int32_t stats_log2;   // final LSE in base 2 (split partials stay natural-log)
 };
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+// sinks (optional): [hq] sink logits merged once per row (row % hq is its head);
+// stats_log2: write the merged LSE in base 2.
 hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,
                           int64_t rows, int32_t dv, void* o, float* lse, int32_t out_f32,
-                          hipStream_t s);
+                          hipStream_t s, const float* sinks = nullptr, int32_t hq = 1,
+                          int32_t stats_log2 = 0);
 hipError_t launch_fill_neg_inf(float* p, int64_t n, hipStream_t s);
 
 // Library-owned split workspace of sdpa_decode_paged_noalloc: bytes per GPU,

@@ -41,7 +41,7 @@ LSE_HEAD_MAJOR = 3
 # every symbol include/sdpa.h declares
 EXPORTS = ("sdpa_prefill_thd", "sdpa_prefill_thd_ex", "sdpa_prefill_thd_fp8",
            "sdpa_decode_workspace_bytes", "sdpa_decode_paged", "sdpa_decode_paged_fp8",
-           "sdpa_decode_paged_noalloc", "sdpa_splitkv_combine", "sdpa_status_string",
+           "sdpa_decode_paged_ex", "sdpa_decode_paged_noalloc", "sdpa_splitkv_combine", "sdpa_status_string",
            "sdpa_last_error_detail", "sdpa_version")
 
 
@@ -92,6 +92,10 @@ def load():
     lib.sdpa_decode_paged_fp8.argtypes = [P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P,
                                           I32, I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P,
                                           SZ, P, P, P, P, P, P]
+    lib.sdpa_decode_paged_ex.restype = ctypes.c_int
+    lib.sdpa_decode_paged_ex.argtypes = [P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P,
+                                         I32, I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P,
+                                         I32, I32, P, SZ, P, P, P, P, P, I32, P]
     lib.sdpa_decode_paged_noalloc.restype = ctypes.c_int
     lib.sdpa_decode_paged_noalloc.argtypes = [P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32,
                                               P, I32, I32, I32, I32, I32, I32, I32, I32, F, I32,
@@ -280,6 +284,48 @@ def decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
         _ptr(page_table_v), int(page_table_k.shape[1]), _ptr(seq_lens), int(max_seqlen_kv), B,
         s_q, hq, hkv, dqk, dv, page, float(scale), int(bool(causal)), int(num_splits),
         _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _dtype_code(q), _stream(stream))
+    _check(rc)
+    return out, lse
+
+
+def decode_paged_ex(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                    page_table_k: torch.Tensor, page_table_v: torch.Tensor,
+                    seq_lens: torch.Tensor, max_seqlen_kv: int, scale: float,
+                    causal: bool = True, window_left: int = 0,
+                    sinks: Optional[torch.Tensor] = None, stats_log2: bool = False,
+                    num_splits: int = 1, descale: Optional[tuple] = None,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
+    """sdpa_decode_paged_ex.  bf16 q / pools, or uint8 E4M3 codes with descale =
+    (descale_q, descale_k, descale_v) one-element fp32 device tensors; sinks fp32 [Hq].
+
+    Returns (out [B, s_q, Hq, Dv] bf16, lse [B, s_q, Hq] or None).
+    """
+    lib = load()
+    fp8 = q.dtype == torch.uint8
+    if fp8 and (descale is None or len(descale) != 3):
+        raise TypeError("E4M3 codes need descale = (descale_q, descale_k, descale_v)")
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.dim() != 1):
+        raise TypeError("sinks are a float32 [Hq] tensor")
+    B, s_q, hq, dqk = (int(x) for x in q.shape)
+    page, hkv, dv = int(k_pool.shape[1]), int(k_pool.shape[2]), int(v_pool.shape[3])
+    if out is None:
+        out = torch.empty((B, s_q, hq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, s_q, hq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, s_q, hq, dv, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dq, dk, dvs = (None, None, None) if descale is None else descale
+    rc = lib.sdpa_decode_paged_ex(
+        _ptr(q), _ptr(k_pool), k_pool.stride(0), k_pool.stride(1), k_pool.stride(2),
+        _ptr(v_pool), v_pool.stride(0), v_pool.stride(1), v_pool.stride(2), _ptr(page_table_k),
+        _ptr(page_table_v), int(page_table_k.shape[1]), _ptr(seq_lens), int(max_seqlen_kv), B,
+        s_q, hq, hkv, dqk, dv, page, float(scale), int(bool(causal)), int(window_left),
+        _ptr(sinks), int(bool(stats_log2)), int(num_splits), _ptr(workspace), ws_bytes,
+        _ptr(dq), _ptr(dk), _ptr(dvs), _ptr(out), _ptr(lse),
+        SDPA_FP8_E4M3 if fp8 else _dtype_code(q), _stream(stream))
     _check(rc)
     return out, lse
 

@@ -285,3 +285,47 @@ def test_decode_noalloc_declines_a_workspace_beyond_its_array():
                                        fake, fake, 256, fake, 16384, 32, 2, 128, 1, 576, 512, 64,
                                        0.04, 1, 16, fake, fake, 1, None)
     assert rc == sdpa.SDPA_ERR_UNSUPPORTED
+
+
+def _decode_ex(**over):
+    lib = sdpa.load()
+    fake = ctypes.c_void_p(0x100000)
+    args = dict(q=fake, kp=fake, k_sp=64 * 8 * 128, k_st=8 * 128, k_sh=128, vp=fake,
+                v_sp=64 * 8 * 128, v_st=8 * 128, v_sh=128, ptk=fake, ptv=fake, ts=512,
+                seq_lens=fake, max_kv=32768, batch=64, sq=1, hq=32, hkv=8, dqk=128, dv=128,
+                page=64, scale=0.1, causal=1, window=0, sinks=None, log2=0, splits=8, ws=fake,
+                ws_bytes=1 << 40, dq=None, dk=None, dv_=None, o=fake, lse=fake, dtype=0,
+                stream=None)
+    args.update(over)
+    rc = lib.sdpa_decode_paged_ex(*args.values())
+    return rc, lib.sdpa_last_error_detail().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(window=-1), sdpa.SDPA_ERR_SHAPE),
+    (dict(log2=2), sdpa.SDPA_ERR_SHAPE),
+    (dict(dtype=1), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dtype=2), sdpa.SDPA_ERR_NULL),                      # FP8 needs its descales
+    (dict(sinks=ctypes.c_void_p(0x100002)), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(ws=None), sdpa.SDPA_ERR_WORKSPACE),
+    (dict(dqk=96, dv=96), sdpa.SDPA_ERR_UNSUPPORTED),
+    # 2^26 rows to merge: beyond the combine's grid
+    (dict(batch=1 << 20, sq=1, hq=64, hkv=64, max_kv=64, ts=1), sdpa.SDPA_ERR_SHAPE),
+])
+def test_decode_ex_rejects(over, code):
+    rc, detail = _decode_ex(**over)
+    assert rc == code, (rc, detail)
+    assert detail
+
+
+def test_combine_rejects_rows_beyond_its_grid():
+    lib = sdpa.load()
+    fake = ctypes.c_void_p(0x100000)
+    assert lib.sdpa_splitkv_combine(fake, fake, 4, 1 << 26, 128, fake, fake, 0, None) == \
+        sdpa.SDPA_ERR_SHAPE
+
+
+def test_decode_ex_declines_variants_at_d256():
+    rc, detail = _decode_ex(dqk=256, dv=256, k_sp=64 * 8 * 256, k_st=8 * 256, k_sh=256,
+                            v_sp=64 * 8 * 256, v_st=8 * 256, v_sh=256, window=37)
+    assert rc == sdpa.SDPA_ERR_UNSUPPORTED and "d = 256" in detail
