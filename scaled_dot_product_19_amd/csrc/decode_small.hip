@@ -97,6 +97,16 @@ constexpr int kQueueSlots = 1024;
 constexpr int kRankMax = 256;  // longest-first order for batches up to this size
 __device__ __align__(256) uint64_t g_decode_queue[kQueueSlots][4];
 
+// Launch tags 1, 2, 3, ... (0 marks a free counter), one sequence for every
+// instantiation of the kernel: they all share g_decode_queue, so two launches
+// in flight must never be handed the same tag and slot.
+std::atomic<uint32_t> g_decode_seq{0};
+uint32_t next_decode_tag() {
+    uint32_t g = g_decode_seq.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    while (g == 0u) g = g_decode_seq.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    return g;
+}
+
 // Ticket request on a work-queue counter: the counter word before adding 1.
 // A plain one-lane atomicAdd: this file is compiled without the wave-level
 // atomic optimizer, so the compiler waits for the returned value only where
@@ -566,10 +576,7 @@ hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
         n_cu = 1;
     const int64_t slots = (int64_t)occ * n_cu;
-    // launch tags 1, 2, 3, ... (0 marks a free counter)
-    static std::atomic<uint32_t> launch_seq{0};
-    uint32_t gen = launch_seq.fetch_add(1u, std::memory_order_relaxed) + 1u;
-    while (gen == 0u) gen = launch_seq.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    const uint32_t gen = next_decode_tag();
     a.gen = gen;
     a.slot = (int32_t)(gen % kQueueSlots);
     hipLaunchKernelGGL((decode_small_kernel<D, F8>), dim3((unsigned)(a.n_units < slots ? a.n_units : slots)), dim3(256),

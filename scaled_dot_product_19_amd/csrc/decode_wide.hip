@@ -8,22 +8,27 @@
 // the work is a dense contraction per K/V tile and runs on MFMA:
 //
 // Work-group = 4 waves = 128 query rows (row r of a KV head is query token
-// r / G, head kvh G + r % G) x one split-KV chunk of one sequence.  Per tile
-// of 32 keys (a tile never straddles a page: page_size % 32 == 0):
+// r / G, head kvh G + r % G) x one split-KV chunk of one sequence; chunks of
+// the longest sequences are dispatched first.  Per tile of 32 keys (a tile
+// never straddles a page: page_size % 32 == 0):
 //   K tile (32 x 576) and V tile (32 x 512) gathered from their pages into
 //   LDS by buffer_load_dwordx4 ... lds (lane L's 16 bytes land at M0 + 16 L),
-//   one 1 KB row per instruction, in a 2-stage ring.  Bank conflicts are
+//   one 1 KB row per instruction, in a ring of two K and two V slots that
+//   refill independently.  Bank conflicts are
 //   avoided by a 16-byte pad after dims 0..511 of each K row, an XOR swizzle
 //   of the 8 chunks of dims 512..575 (kept in a region of their own) and an
 //   XOR swizzle of the V chunks;
-//   S^T = K Q^T: 36 v_mfma_f32_32x32x16_bf16 per wave, A = K rows
-//   (ds_read_b128), B = the wave's Q^T held in registers, so each lane holds
-//   the scores of one query;
+//   S^T = K Q^T: 36 v_mfma_f32_32x32x16_bf16 per wave for its 32 rows, A = K
+//   rows (ds_read_b128), B = the wave's Q^T held in registers, so each lane
+//   holds the scores of one query;
 //   online softmax in registers (row max: 3-input max + one lane-half
-//   exchange), running max moved lazily (only when a tile's max exceeds it
-//   by more than 8 in log2 units);
-//   O^T += V^T P^T: 32 MFMAs, B = P^T straight from the score accumulators,
-//   A = V^T via ds_read_b64_tr_b16 from the row-major V tile.
+//   exchange) in a fixed per-lane frame, the chunk run a second time when a
+//   later tile's max outgrows it (the softmax frame below);
+//   P^T goes through LDS (1 KB per 32 rows x 16 keys) and each wave owns 128
+//   columns of O^T for all 128 rows: O^T += V^T P^T is 32 MFMAs per wave
+//   whose operands are each read once and used four times (A = V^T via
+//   ds_read_b64_tr_b16 from the row-major V tile, B = P^T), half the LDS
+//   reads of a wave owning whole rows.
 // The chunk's normalized partial (O_c, LSE_c) goes to the split workspace,
 // or O / LSE directly when num_splits == 1.
 #include "sdpa_device.h"
@@ -59,9 +64,11 @@ struct WideArgs {
     int32_t stats_log2;  // final LSE in base 2
 };
 
-// LDS stage: K region A (dims 0..511 of 32 rows, pitch 1040 B: 1 KB + a
-// 16-byte pad), K region B (dims 512..575, 32 rows x 128 B, chunk XOR row
-// mod 8), V (32 rows x 1 KB, chunk XOR 4 (row mod 4)).
+// LDS: two ring stages, each K region A (dims 0..511 of 32 rows, pitch
+// 1040 B: 1 KB + a 16-byte pad), K region B (dims 512..575, 32 rows x 128 B,
+// chunk XOR row mod 8), V (32 rows x 1 KB, chunk XOR 4 (row mod 4)); then
+// the P^T exchange: one 1 KB MFMA operand per (32-row block, 16-key step),
+// lane l's 16 bytes at 16 l.
 template <int DQK, int DV>
 struct WCfg {
     static constexpr int NW = 4;                    // waves, 32 query rows each
@@ -73,17 +80,21 @@ struct WCfg {
     static constexpr int V_OFF = KB_OFF + KB_B;     // V tile
     static constexpr int VROW_B = 2 * DV;
     static constexpr int STAGE_B = V_OFF + BN * VROW_B;
-    static constexpr int LDS_BYTES = 2 * STAGE_B;   // 2-stage ring
+    static constexpr int P_OFF = 2 * STAGE_B;       // P^T exchange
+    static constexpr int LDS_BYTES = P_OFF + NW * (BN / 16) * 1024;
     static constexpr int RPW = BN / NW;             // tile rows per wave (one DMA each)
     static constexpr int KK = DQK / 16;             // k-steps of S^T = K Q^T
     static constexpr int KKA = 32;                  // k-steps in region A
-    static constexpr int NB = DV / 32;              // 32-row blocks of O^T
+    static constexpr int NBW = DV / 32 / NW;        // 32-column blocks of O^T per wave
     static constexpr int NQK = KK;                  // QK MFMAs per tile
-    static constexpr int NPV = NB * (BN / 16);      // PV MFMAs per tile
     static_assert(DQK == 576 && DV == 512, "geometry below is written for the 576/512 shape");
     static_assert(BN * 8 == 64 * NW, "region B: one DMA instruction per wave");
-    static_assert(KK / 4 + (NB * (BN / 16)) / 4 == 2 * RPW + 1, "one DMA piece per four MFMAs");
+    static_assert(NBW == 4 && NW == 4, "O^T: 4 column blocks x 4 row blocks per wave");
 };
+constexpr int kTxPitch = 528;      // bytes per row of the output transpose (512 + 16)
+
+constexpr int kWideRankMax = 256;  // longest-first order for batches up to this size
+static_assert(4 * 32 * kTxPitch <= WCfg<576, 512>::P_OFF, "output transpose fits in the ring");
 
 constexpr int kWinW = 4;  // LDS operand fragments read ahead of the MFMAs
 
@@ -151,12 +162,40 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     const int split = g % a.splits;
     const int bk = g / a.splits;
     const int kvh = bk % a.hkv;
-    const int b = bk / a.hkv;
+    // the (bk / hkv)-th longest sequence (ties by index): work-groups are
+    // dispatched about in index order, so the longest chunks start first and
+    // the short ones fill the tail
+    int b = bk / a.hkv;
+    int len_b;
+    if (a.batch <= kWideRankMax) {
+        __shared__ __attribute__((aligned(16))) int lens_x[kWideRankMax];
+        __shared__ int seq_of;
+        // lengths to LDS (padded to a multiple of 4 with INT32_MIN, below any length)
+        if (tid < ((a.batch + 3) & ~3)) lens_x[tid] = tid < a.batch ? a.seq_lens[tid] : INT32_MIN;
+        __syncthreads();
+        if (tid < a.batch) {
+            const int lm = lens_x[tid];
+            int rk = 0;
+            for (int j = 0; j < a.batch; j += 4) {
+                const int4 q4 = *reinterpret_cast<const int4*>(lens_x + j);
+                rk += (q4.x > lm) || (q4.x == lm && j < tid);
+                rk += (q4.y > lm) || (q4.y == lm && j + 1 < tid);
+                rk += (q4.z > lm) || (q4.z == lm && j + 2 < tid);
+                rk += (q4.w > lm) || (q4.w == lm && j + 3 < tid);
+            }
+            if (rk == b) seq_of = tid;
+        }
+        __syncthreads();
+        b = __builtin_amdgcn_readfirstlane(seq_of);
+        len_b = __builtin_amdgcn_readfirstlane(lens_x[b]);
+    } else {
+        len_b = load_uniform(a.seq_lens, b);
+    }
 
     // keys of this chunk: [lo, hi).  Keys [base, L) are cut into the splits;
     // with a left window, base is the start of the page holding the first key
     // any token of the sequence sees.
-    const int L = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
+    const int L = min(len_b, a.table_stride * a.page);
     int base = 0;
     if (VAR && a.window > 0 && L - a.sq - a.window + 1 > 0) base = ((L - a.sq - a.window + 1) / a.page) * a.page;
     int lo = base, hi = L;
@@ -211,15 +250,20 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         pk = a.pt_k[pt_row + pg0 + i];
         pv = a.pt_v[pt_row + pg0 + i];
         pwin = first;
+        // use the ids at once: the compiler waits for them here, where the
+        // window is (re)loaded, and not (conservatively, for every pending
+        // DMA) before each later readlane of a window that arrived long ago
+        asm volatile("" ::"v"(pk), "v"(pv));
     };
     if (n_pages > 0) load_window(0);
     const bf16_t* const kbase = a.k_pool + (int64_t)kvh * a.k_sh;
     const bf16_t* const vbase = a.v_pool + (int64_t)kvh * a.v_sh;
     // The 17 DMA instructions of a tile (per wave: 8 rows of K dims 0..511,
-    // its rows of K dims 512..575, 8 rows of V) are issued one at a time
-    // between the MFMAs of the tile before (issued back to back they stall
-    // the wave while the memory pipeline takes 68 KB).  A tile at or past the
-    // end gets an empty buffer range: its DMA writes zeros and reads nothing.
+    // its rows of K dims 512..575, 8 rows of V) are issued in two bursts, V
+    // and K, each right after the barrier that frees its slot: spread between
+    // the MFMAs, the data arriving in LDS throughout slows every phase's
+    // operand reads more.  A tile at or past the end gets an empty buffer
+    // range: its DMA writes zeros and reads nothing.
     struct DmaPlan {
         u32x4 kr, vr;
         uint32_t st;
@@ -228,10 +272,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         const int key0 = lo + t * C::BN;
         const int nvalid = min(C::BN, kv_end - key0);
         const int rel = min(key0 / a.page - pg0, n_pages - 1);
-        if (rel - pwin >= 64) {  // uniform; no DMA of this wave is pending here
-            load_window(rel);
-            wait_vmcnt<0>();
-        }
+        if (rel - pwin >= 64) load_window(rel);  // uniform
         const int pkp = __builtin_amdgcn_readlane(pk, rel - pwin);
         const int pvp = __builtin_amdgcn_readlane(pv, rel - pwin);
         const int slot = key0 % a.page;
@@ -244,25 +285,34 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         d.st = lds_base + stage * C::STAGE_B;
         return d;
     };
-    constexpr int NPIECE = 2 * C::RPW + 1;
-    auto piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
+    // K of a tile is NK pieces (8 rows of dims 0..511, then the wave's rows of
+    // dims 512..575), V is NV pieces (8 rows)
+    constexpr int NK = C::RPW + 1, NV = C::RPW;
+    auto k_piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
         if (j < C::RPW) {
             const int row = wave * C::RPW + j;
             dma16(d.kr, d.st + row * C::KA_PITCH, add_here(l16, (uint32_t)row * k_st2));
-        } else if (j == C::RPW) {
-            dma16(d.kr, d.st + C::KB_OFF + wave * 1024, kb_src);
         } else {
-            const int row = wave * C::RPW + j - C::RPW - 1;
-            dma16(d.vr, d.st + C::V_OFF + row * C::VROW_B,
-                  xor_add_here(l16, 64u * (uint32_t)(row & 3), (uint32_t)row * v_st2));
+            dma16(d.kr, d.st + C::KB_OFF + wave * 1024, kb_src);
         }
     };
-    auto issue = [&](int t, int stage) __attribute__((always_inline)) {
-        const DmaPlan d = plan(t, stage);
-#pragma unroll
-        for (int j = 0; j < NPIECE; ++j) piece(d, j);
+    auto v_piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
+        const int row = wave * C::RPW + j;
+        dma16(d.vr, d.st + C::V_OFF + row * C::VROW_B,
+              xor_add_here(l16, 64u * (uint32_t)(row & 3), (uint32_t)row * v_st2));
     };
-    if (n_tiles > 0) issue(0, 0);
+    // the ring's first tiles: K and V of tile 0, K of tile 1
+    auto prologue = [&]() __attribute__((always_inline)) {
+        const DmaPlan d0 = plan(0, 0);
+#pragma unroll
+        for (int j = 0; j < NK; ++j) k_piece(d0, j);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v_piece(d0, j);
+        const DmaPlan d1 = plan(1, 1);
+#pragma unroll
+        for (int j = 0; j < NK; ++j) k_piece(d1, j);
+    };
+    if (n_tiles > 0) prologue();  // overlaps the Q load below
 
     // Q^T operand: lane (col, half) holds d = 16 kk + 8 half .. +8 of row r
     // (rows past the end read the last row and are zeroed)
@@ -294,158 +344,192 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     // 16-lane group G = l / 16 supplies row 16 kst + 4 half + (l % 16) / 4
     // (+8 for the second read) and 4 columns starting at 32 nb + 16 (G % 2) +
     // 4 (l % 4); it receives 4 consecutive keys of column 32 nb + l % 32.
-    int v_rd[4];
+    // Wave w reads the column blocks nb = 4 w + j (bytes 256 w .. of a row).
+    int v_rd[C::NBW];
     {
         const int r0 = 4 * half + (lane & 15) / 4;
         const int cg = 2 * ((lane >> 4) & 1) + (lane & 3) / 2;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-            v_rd[nb] = C::V_OFF + r0 * C::VROW_B + 16 * swz_v<64>(r0, 4 * nb + cg) + 8 * (lane & 1);
+        for (int j = 0; j < C::NBW; ++j)
+            v_rd[j] = C::V_OFF + r0 * C::VROW_B + 16 * swz_v<64>(r0, 4 * j + cg) + 8 * (lane & 1) + 256 * wave;
     }
     auto kfrag = [&](const char* st, int kk) __attribute__((always_inline)) {
         const int off = kk < C::KKA ? k_ra + 32 * kk : k_rb[kk - C::KKA];
         return *reinterpret_cast<const bf16x8*>(st + off);
     };
-    auto vfrag = [&](const char* st, int o) __attribute__((always_inline)) {
-        const int nb = o % C::NB, kst = o / C::NB;
-        const char* vp = st + v_rd[nb % 4] + (nb / 4) * 256 + kst * 16 * C::VROW_B;
+    auto vfrag = [&](const char* st, int j, int kst) __attribute__((always_inline)) {
+        const char* vp = st + v_rd[j] + kst * 16 * C::VROW_B;
         const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
         const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VROW_B));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    // P^T operand of (row block rbk, key step kst): the score-accumulator
+    // layout of wave rbk, lane l's 16 bytes at 16 l (conflict-free both ways)
+    char* const p_x = lds + C::P_OFF + 16 * lane;
+    auto pslot = [&](int rbk, int kst) __attribute__((always_inline)) {
+        return reinterpret_cast<bf16x8*>(p_x + (rbk * 2 + kst) * 1024);
+    };
 
-    f32x16 acc[C::NB];
+    // O^T accumulators of this wave: acc[j][rbk] = columns 128 w + 32 j x rows 32 rbk
+    f32x16 acc[C::NBW][C::NW];
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+    for (int j = 0; j < C::NBW; ++j)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
+        for (int rbk = 0; rbk < C::NW; ++rbk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[j][rbk][i] = 0.f;
     float m = neg_inf();      // reference max (log2 units) of this lane's query
     float l = 0.f;            // this lane half's sum of p
     float mx_all = neg_inf(); // largest tile max seen (log2 units)
 
-    // hook(j), j = 0..16, is called after every fourth MFMA (9 in S^T, 8 in O^T)
-    auto tile = [&](const char* st, int key0, bool need_mask, auto&& hook) __attribute__((always_inline)) {
-        // S^T = K Q^T
-        f32x16 s;
-        {
-            f32x16 s0, s1;
-            bf16x8 fk[kWinW];
-#pragma unroll
-            for (int w = 0; w < kWinW; ++w) fk[w] = kfrag(st, w);
-#pragma unroll
-            for (int o = 0; o < C::NQK; ++o) {
-                f32x16& d = (o & 1) ? s1 : s0;
-                if (o < 2) {
-                    qk_first(d, fk[o % kWinW], qf[o]);
-                } else {
-                    qk_next(d, fk[o % kWinW], qf[o]);
-                }
-                if (o + kWinW < C::NQK) fk[o % kWinW] = kfrag(st, o + kWinW);
-                if (o % 4 == 3) hook(o / 4);
-            }
-            qk_fence(s0, s1);
-            s = s0 + s1;
-        }
-        // online softmax; lane (col, half) holds keys key0 + 8 (i / 4) + 4 half + i % 4
-        float mx = neg_inf();
-        if (need_mask) {
-            // key = key0 + 4 half + (compile-time offset): masked above the causal
-            // bound dl or below the window's first key dlo
-            const int dl = lim - key0 - 4 * half;
-            const int dlo = win ? first - key0 - 4 * half : -1;  // first is INT32_MIN without a window
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int off = 8 * (i >> 2) + (i & 3);
-                s[i] = (off > dl || (VAR && off < dlo)) ? neg_inf() : s[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = max3(mx, s[i], s[i + 1]);
-        mx = half_max(mx);
-        const float mt = mx == neg_inf() ? neg_inf() : mx * a.c;
-        mx_all = fmaxf(mx_all, mt);
-        m = m == neg_inf() ? mt : m;  // first visible tile fixes the frame
-        const float nm = m == neg_inf() ? 0.f : -m;
+    // One tile: S^T and the softmax of this wave's 32 rows (when one of them
+    // sees a key of the tile; else P = 0), P^T to LDS, mid() (the barrier
+    // that publishes P^T), then this wave's 128 columns of O^T for all rows.
+    auto tile = [&](const char* st, int key0, bool vis, bool need_mask, auto&& mid)
+                    __attribute__((always_inline)) {
         bf16x8 pb[2];
-        float lsum = 0.f;
+        if (vis) {
+            // S^T = K Q^T
+            f32x16 s;
+            {
+                f32x16 s0, s1;
+                bf16x8 fk[kWinW];
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            float p0 = fast_exp2(__builtin_fmaf(s[i], a.c, nm));
-            float p1 = fast_exp2(__builtin_fmaf(s[i + 1], a.c, nm));
-            if (need_mask) {  // exact zeros also when c = 0 (-inf * 0 = NaN)
-                p0 = s[i] == neg_inf() ? 0.f : p0;
-                p1 = s[i + 1] == neg_inf() ? 0.f : p1;
+                for (int w = 0; w < kWinW; ++w) fk[w] = kfrag(st, w);
+#pragma unroll
+                for (int o = 0; o < C::NQK; ++o) {
+                    f32x16& d = (o & 1) ? s1 : s0;
+                    if (o < 2) {
+                        qk_first(d, fk[o % kWinW], qf[o]);
+                    } else {
+                        qk_next(d, fk[o % kWinW], qf[o]);
+                    }
+                    if (o + kWinW < C::NQK) fk[o % kWinW] = kfrag(st, o + kWinW);
+                }
+                qk_fence(s0, s1);
+                s = s0 + s1;
             }
-            lsum += p0 + p1;
-            const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-            pb[i >> 3][i & 7] = pp[0];
-            pb[i >> 3][(i & 7) + 1] = pp[1];
+            // online softmax; lane (col, half) holds keys key0 + 8 (i / 4) + 4 half + i % 4
+            float mx = neg_inf();
+            if (need_mask) {
+                // key = key0 + 4 half + (compile-time offset): masked above the causal
+                // bound dl or below the window's first key dlo
+                const int dl = lim - key0 - 4 * half;
+                const int dlo = win ? first - key0 - 4 * half : -1;  // first is INT32_MIN without a window
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 8 * (i >> 2) + (i & 3);
+                    s[i] = (off > dl || (VAR && off < dlo)) ? neg_inf() : s[i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) mx = max3(mx, s[i], s[i + 1]);
+            mx = half_max(mx);
+            const float mt = mx == neg_inf() ? neg_inf() : mx * a.c;
+            mx_all = fmaxf(mx_all, mt);
+            m = m == neg_inf() ? mt : m;  // first visible tile fixes the frame
+            const float nm = m == neg_inf() ? 0.f : -m;
+            float lsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                float p0 = fast_exp2(__builtin_fmaf(s[i], a.c, nm));
+                float p1 = fast_exp2(__builtin_fmaf(s[i + 1], a.c, nm));
+                if (need_mask) {  // exact zeros also when c = 0 (-inf * 0 = NaN)
+                    p0 = s[i] == neg_inf() ? 0.f : p0;
+                    p1 = s[i + 1] == neg_inf() ? 0.f : p1;
+                }
+                lsum += p0 + p1;
+                const bf16x2 pp = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+                pb[i >> 3][i & 7] = pp[0];
+                pb[i >> 3][(i & 7) + 1] = pp[1];
+            }
+            l += lsum;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pb[0][i] = pb[1][i] = bf16_t(0.f);
         }
-        l += lsum;
-        // O^T += V^T P^T
-        {
-            bf16x8 fv[kWinW];
+        *pslot(wave, 0) = pb[0];
+        *pslot(wave, 1) = pb[1];
+        mid();
+        // O^T += V^T P^T: per key step 4 V^T and 4 P^T operands, 16 MFMAs
 #pragma unroll
-            for (int w = 0; w < kWinW; ++w) fv[w] = vfrag(st, w);
+        for (int kst = 0; kst < C::BN / 16; ++kst) {
+            bf16x8 fv[C::NBW], fp[C::NW];
 #pragma unroll
-            for (int o = 0; o < C::NPV; ++o) {
-                acc[o % C::NB] = mfma_32x32x16(fv[o % kWinW], pb[o / C::NB], acc[o % C::NB]);
-                if (o + kWinW < C::NPV) fv[o % kWinW] = vfrag(st, o + kWinW);
-                if (o % 4 == 3) hook(C::NQK / 4 + o / 4);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kWinW, 1);
+            for (int j = 0; j < C::NBW; ++j) fv[j] = vfrag(st, j, kst);
 #pragma unroll
-            for (int o = 0; o < C::NPV; ++o) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                if (o + kWinW < C::NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-            }
+            for (int rbk = 0; rbk < C::NW; ++rbk) fp[rbk] = *pslot(rbk, kst);
+#pragma unroll
+            for (int j = 0; j < C::NBW; ++j)
+#pragma unroll
+                for (int rbk = 0; rbk < C::NW; ++rbk)
+                    acc[j][rbk] = mfma_32x32x16(fv[j], fp[rbk], acc[j][rbk]);
         }
     };
 
-    // 2-stage ring: tile t + 1 streams in while tile t is computed
+    // Ring of two K and two V slots that refill independently: tile t uses
+    // slot t % 2 of each.  V of tile t + 1 is issued right after the barrier
+    // that opens tile t (its slot held V of tile t - 1, whose O^T MFMAs every
+    // wave has passed), K of tile t + 2 right after the barrier between the
+    // softmax and O^T (its slot is the one S^T just read).  Each piece thus
+    // has about a whole tile of compute to land.  Issue order per wave:
+    // ... V(t), K(t+1), V(t+1), K(t+2) ...: when K(t) (or V(t)) is needed,
+    // the NV + NK pieces issued after it may still be in flight.
     auto step = [&](int t, auto stage) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
-        const DmaPlan d = plan(t + 1, ST ^ 1);
-        const int key0 = lo + t * C::BN;
-        if (key0 < kv_end_w) {
-            tile(lds + ST * C::STAGE_B, key0, key0 + C::BN > nomask_end || (VAR && key0 < first_w),
-                 [&](int j) __attribute__((always_inline)) { piece(d, j); });
-        } else {
+        const DmaPlan dv = plan(t + 1, ST ^ 1);
+        wait_vmcnt<NK + NV>();  // K of tile t
+        __syncthreads();        // (also: every wave is done with P^T and V of tile t - 1)
 #pragma unroll
-            for (int j = 0; j < NPIECE; ++j) piece(d, j);
-        }
-        wait_vmcnt<0>();
-        __syncthreads();
+        for (int j = 0; j < NV; ++j) v_piece(dv, j);
+        auto mid = [&]() __attribute__((always_inline)) {
+            const DmaPlan dk = plan(t + 2, ST);
+            wait_vmcnt<NK + NV>();  // V of tile t
+            __syncthreads();        // P^T of tile t is in LDS; S^T is done with K of tile t
+#pragma unroll
+            for (int j = 0; j < NK; ++j) k_piece(dk, j);
+        };
+        const int key0 = lo + t * C::BN;
+        tile(lds + ST * C::STAGE_B, key0, key0 < kv_end_w,
+             key0 + C::BN > nomask_end || (VAR && key0 < first_w), mid);
     };
-    __shared__ int rerun;
-    for (int pass = 0;; ++pass) {
-        wait_vmcnt<0>();
-        __syncthreads();
+    auto run_tiles = [&]() __attribute__((always_inline)) {
         for (int t = 0; t < n_tiles; t += 2) {
             step(t, std::integral_constant<int, 0>{});
             if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
         }
-        if (pass == 1) break;
-        // another pass if any lane of the work-group saw a tile max beyond
-        // its reference by more than kMaxExcess
-        if (tid == 0) rerun = 0;
+        // the pieces past the last tile (zeros) land before the slots are reused
+        wait_vmcnt<0>();
         __syncthreads();
-        if (__builtin_amdgcn_ballot_w64(mx_all > m + kMaxExcess) != 0 && lane == 0) rerun = 1;
-        __syncthreads();
-        if (rerun == 0) break;
+    };
+    run_tiles();
+    // Another pass if any lane of the work-group saw a tile max beyond its
+    // reference by more than kMaxExcess.  (Written out as a second copy of the
+    // loop: zeroing the accumulators on the back edge of one loop over both
+    // passes would move them out of the AGPRs.)
+    __shared__ int rerun;
+    if (tid == 0) rerun = 0;
+    __syncthreads();
+    if (__builtin_amdgcn_ballot_w64(mx_all > m + kMaxExcess) != 0 && lane == 0) rerun = 1;
+    __syncthreads();
+    if (rerun != 0) {
         m = mx_all;
         l = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
+        for (int j = 0; j < C::NBW; ++j)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
-        if (n_tiles > 0) issue(0, 0);
+            for (int rbk = 0; rbk < C::NW; ++rbk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[j][rbk][i] = 0.f;
+        if (n_tiles > 0) prologue();
+        run_tiles();
     }
 
     // epilogue: O = O^T / l, LSE = ln2 * (m + log2 l); with one split the sink
-    // of head h joins the denominator (split partials leave it to the combine)
+    // of head h joins the denominator (split partials leave it to the combine).
+    // The owner of row r's scores publishes 1 / l of it for the waves that
+    // hold its columns (the P^T exchange is free: the loop ended on a barrier).
     float l_tot = half_sum(l);
-    if (!row_ok) return;
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (VAR && a.sinks != nullptr && a.splits == 1) {
         const float sk = a.sinks[h] * kLog2e;
@@ -460,33 +544,69 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
     // partials stay natural-log; the final Stats may be base 2
     const float lse = VAR && a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
-    const int64_t row_g = (int64_t)(b * a.sq + tq) * a.hq + h;
+    const int64_t rows_all = (int64_t)a.batch * a.sq * a.hq;
+    auto row_global = [&](int rr) {  // (b, token, head) row of row rr of this KV head
+        return (int64_t)(b * a.sq + rr / a.group) * a.hq + kvh * a.group + rr % a.group;
+    };
+    if (row_ok && half == 0) {
+        const int64_t row_g = row_global(r);
+        if (a.splits > 1) {
+            a.lse_part[(int64_t)split * rows_all + row_g] = lse;
+        } else if (a.lse != nullptr) {
+            a.lse[row_g] = lse;
+        }
+    }
+    // (1 / l, output row) of every row of the block, -1 past the end
+    int2* const row_x = reinterpret_cast<int2*>(lds + C::P_OFF);
+    if (half == 0) row_x[wave * 32 + col] = make_int2(__float_as_int(inv), row_ok ? (int)row_global(r) : -1);
+    __syncthreads();
+    // O rows go out through a wave-private LDS transpose (32 rows x 128
+    // columns fp32 at a time, pitch 528 B): written in the accumulator layout
+    // (one row per lane pair), read back two whole rows per instruction, so
+    // every store writes 2 x 512 contiguous bytes (2 x 256 as bf16).
+    char* const tx = lds + wave * (32 * kTxPitch);
+    auto write_rows = [&](auto&& store) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rbk = 0; rbk < C::NW; ++rbk) {
+#pragma unroll
+            for (int j = 0; j < C::NBW; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x16& c = acc[j][rbk];
+                    const f32x4 w = {c[4 * gq], c[4 * gq + 1], c[4 * gq + 2], c[4 * gq + 3]};
+                    *reinterpret_cast<f32x4*>(tx + col * kTxPitch + 4 * (32 * j + 8 * gq + 4 * half)) = w;
+                }
+            // lane l: row 2 i + l / 32 of the block, columns 4 (l % 32) .. + 3;
+            // every read first, then the stores
+            f32x4 v[16];
+            int2 rx[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int rr_b = 2 * i + (lane >> 5);
+                v[i] = *reinterpret_cast<const f32x4*>(tx + rr_b * kTxPitch + 16 * (lane & 31));
+                rx[i] = row_x[rbk * 32 + rr_b];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float iv = __int_as_float(rx[i].x);
+                if (rx[i].y >= 0)
+                    store((int64_t)rx[i].y, 128 * wave + 4 * (lane & 31),
+                          f32x4{v[i][0] * iv, v[i][1] * iv, v[i][2] * iv, v[i][3] * iv});
+            }
+        }
+    };
     if (a.splits > 1) {
-        const int64_t rows_all = (int64_t)a.batch * a.sq * a.hq;
-        float* orow = a.o_part + ((int64_t)split * rows_all + row_g) * DV;
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int n = nb * 32 + 8 * gq + 4 * half;
-                f32x4 w = {acc[nb][4 * gq] * inv, acc[nb][4 * gq + 1] * inv, acc[nb][4 * gq + 2] * inv,
-                           acc[nb][4 * gq + 3] * inv};
-                *reinterpret_cast<f32x4*>(orow + n) = w;
-            }
-        if (half == 0) a.lse_part[(int64_t)split * rows_all + row_g] = lse;
+        float* const op = a.o_part + (int64_t)split * rows_all * DV;
+        write_rows([&](int64_t row_g, int n, f32x4 w) __attribute__((always_inline)) {
+            *reinterpret_cast<f32x4*>(op + row_g * DV + n) = w;
+        });
     } else {
-        bf16_t* orow = a.o + row_g * DV;
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int n = nb * 32 + 8 * gq + 4 * half;
-                uint2 w;
-                w.x = pack_bf16x2(acc[nb][4 * gq] * inv, acc[nb][4 * gq + 1] * inv);
-                w.y = pack_bf16x2(acc[nb][4 * gq + 2] * inv, acc[nb][4 * gq + 3] * inv);
-                *reinterpret_cast<uint2*>(orow + n) = w;
-            }
-        if (a.lse != nullptr && half == 0) a.lse[row_g] = lse;
+        write_rows([&](int64_t row_g, int n, f32x4 w) __attribute__((always_inline)) {
+            uint2 u;
+            u.x = pack_bf16x2(w[0], w[1]);
+            u.y = pack_bf16x2(w[2], w[3]);
+            *reinterpret_cast<uint2*>(a.o + row_g * DV + n) = u;
+        });
     }
 }
 
@@ -537,7 +657,8 @@ hipError_t launch_decode_wide(const DecodeArgs& d, hipStream_t s) {
     a.stats_log2 = d.stats_log2;
     const int64_t n_wg = (n_g + 7) / 8 * 8 * a.n_rb;
     if (n_g == 0) return hipSuccess;
-    if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+    // the epilogue passes output row indices as int32
+    if (n_wg > INT32_MAX || (int64_t)d.batch * d.sq * d.hq > INT32_MAX) return hipErrorInvalidValue;
     const bool var = a.window > 0 || a.sinks != nullptr || a.stats_log2 != 0;
     const void* kernel = var ? (const void*)decode_wide_kernel<576, 512, true>
                              : (const void*)decode_wide_kernel<576, 512, false>;
