@@ -330,6 +330,44 @@ def run_chunked_prefill(args, torch, inputs, sdpa, dev):
     print(json.dumps(line), flush=True)
 
 
+def context_leg(args, torch, inputs, sdpa, dev, stream):
+    """The context phase of serving: chunked prefill of 512- and 1024-token chunks against
+    64k and 128k caches (batch 2, bottom-right causal), one sdpa_decode_paged call each (the
+    prefill kernel over the page tables plus the LSE combine)."""
+    res = []
+    for chunk, cache in ((512, 65536), (1024, 65536), (512, 131072), (1024, 131072)):
+        pc = inputs.context_chunk(chunk, cache)
+        q, kp, vp = pc.q.to(dev), pc.k_pool.to(dev), pc.v_pool.to(dev)
+        ptk, ptv, sl = pc.pt_k.to(dev), pc.pt_v.to(dev), pc.seq_lens.to(dev)
+        o = torch.empty((pc.batch, pc.sq, pc.hq, 128), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((pc.batch, pc.sq, pc.hq), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, sdpa.decode_workspace_bytes(pc.batch, pc.sq, pc.hq, 128,
+                                                            pc.num_splits)),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            sdpa.decode_paged(q, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, pc.causal,
+                              num_splits=pc.num_splits, workspace=ws, out=o, lse=lse,
+                              stream=stream)
+
+        st = ms_stats(per_call_ms(torch, stream, call, args.steps, args.warmup))
+        flops = chunked_prefill_flops(pc)
+        tf = flops / (st["mean"] * 1e-3) / 1e12
+        log("%s: %.4f ms mean (median %.4f, min %.4f) -> %.1f TFLOP/s (%.1f%% of bf16 peak)"
+            % (pc.name, st["mean"], st["median"], st["min"], tf, 100 * tf / PEAK_BF16_TFLOPS))
+        res.append({"workload": pc.name, "chunk": chunk, "cache": cache,
+                    "splits": pc.num_splits, "flop": flops, "ms": st, "value": round(tf, 2),
+                    "unit": "TFLOP/s",
+                    "roofline": {"kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false, "
+                                           "true, false> + combine_kernel<false>",
+                                 "bound": "mfma", "achieved": round(tf, 2),
+                                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}})
+        del q, kp, vp, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def per_call_ms(torch, stream, call, steps, warmup, between=None):
     """Milliseconds of each of `steps` calls, from HIP events recorded on `stream` right
     before and after the call (after `warmup` untimed calls).  `between()` runs before
@@ -703,10 +741,11 @@ def main():
     ap.add_argument("--fp8-prefill", action="store_true",
                     help="time only the THD prefill workload in per-tensor FP8 E4M3 (and in "
                          "bf16 on the same GPU)")
-    ap.add_argument("--legs", default="c4,c5,c1",
+    ap.add_argument("--legs", default="c4,c5,c1,ctx",
                     help="extra workloads timed after the step, comma-separated from c4 (D=256 "
                          "dense and ragged prefill), c5 (absorbed-MLA-shaped decode), c1 (tiny "
-                         "fp32: oracle CPU seconds); empty for none")
+                         "fp32: oracle CPU seconds), ctx (context phase: 512/1024-token chunks "
+                         "against 64k/128k caches); empty for none")
     ap.add_argument("--mla-aliased", action="store_true",
                     help="time only the MLA-shaped decode over an absorbed-MLA cache (V = the "
                          "first 512 columns of the 576-wide K rows, one page table)")
@@ -849,6 +888,8 @@ def main():
         torch.cuda.empty_cache()
     if "c1" in legs:
         extra["c1_tiny_fp32"] = tiny_leg(args, torch, inputs, sdpa, dev, stream, threads)
+    if "ctx" in legs:
+        extra["context_phase"] = context_leg(args, torch, inputs, sdpa, dev, stream)
 
     line = {
         "metric": "prefill attn TFLOP/s (% MFMA peak); paged decode KV GB/s (% HBM peak)",

@@ -182,11 +182,14 @@ __device__ __forceinline__ uint32_t own_ticket(uint64_t* ctr, uint64_t old, uint
 // PP: ping-pong schedule (NW = 8, two waves per SIMD); otherwise sequential.
 // One work item: NH heads x NW / NH blocks of 32 query rows of one sequence,
 // all keys it sees.  Uniform across the work-group (every exit is taken by
-// all waves).  On return every LDS DMA of the item has landed.
-template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED, bool F8>
+// all waves).  On return every LDS DMA of the item has landed.  An item with
+// rows calls before_epilogue() once its last tile is done and before any of
+// its stores are issued.
+template <int D, int BN, int S, int NW, bool PP, bool CZ, bool PAGED, bool F8, typename Hook>
 __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& a, const int item,
                                                             char* const lds, const uint32_t lds_base,
-                                                            uint64_t* const tctr, uint64_t& ticket) {
+                                                            uint64_t* const tctr, uint64_t& ticket,
+                                                            Hook&& before_epilogue) {
     static_assert(!PP || (NW == 8 && S >= 4), "ping-pong needs two wave groups and S >= 4");
     static_assert(!F8 || (PP && !PAGED && D == 128), "FP8: the D = 128 ping-pong THD kernel");
     using C = PCfg<D, BN, S, NW, F8>;
@@ -767,6 +770,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // The DMA of tiles past the end writes zeros into LDS: let all of it land
     // before this work-group can finish and its LDS be handed to another.
     wait_vmcnt<0>();
+    before_epilogue();
 
     // epilogue: O = O^T / l written as bf16, LSE = ln2 * (m + log2 l); a
     // split of a paged call writes its normalized fp32 partial and LSE_c
@@ -911,12 +915,22 @@ __global__ __launch_bounds__(64 * NW, (D <= 128 ? 2 : 1)) void prefill_bf16_kern
         q = (int)(xcc % kXcds);
         ticket = ticket_async(&ctr[q]);
     }
+    // The next item is resolved (lane 0 of wave 0) before the current item's
+    // epilogue: waiting for the ticket there costs nothing, while after the
+    // epilogue the wait would also cover its stores (one memory counter).
+    int nxt = -1;
+    bool resolved = false;
     for (;;) {
-        if (threadIdx.x == 0) next_item = next_of(ticket);
+        if (threadIdx.x == 0) next_item = resolved ? nxt : next_of(ticket);
         __syncthreads();
         const int item = next_item;
         if (item < 0) break;
-        prefill_item<D, BN, S, NW, PP, CZ, PAGED, F8>(a, item, lds, lds_base, &ctr[q], ticket);
+        resolved = false;
+        prefill_item<D, BN, S, NW, PP, CZ, PAGED, F8>(a, item, lds, lds_base, &ctr[q], ticket,
+                                                      [&]() __attribute__((always_inline)) {
+                                                          if (threadIdx.x == 0) nxt = next_of(ticket);
+                                                          resolved = true;
+                                                      });
         __syncthreads();  // every wave has read next_item before it is replaced
     }
     if (threadIdx.x == 0 && own_ticket(&ctr[kXcds], ticket_async(&ctr[kXcds]), a.gen) == gridDim.x - 1) {

@@ -322,6 +322,21 @@ def chunked_prefill_paged(seed: int = SEED_BASE + 6, batch: int = 2, chunk: int 
                       % (batch, chunk, lo, hi, num_splits))
 
 
+def context_chunk(chunk: int, cache: int, seed: int = SEED_BASE + 10, batch: int = 2,
+                  num_splits: int = 0, poison: bool = False) -> PagedCase:
+    """The context phase of serving: a query chunk of `chunk` tokens at the end of each of
+    `batch` caches of exactly `cache` tokens, 32/8 heads, D=128, page 64, bottom-right causal
+    (512- and 1024-token chunks against 64k and 128k caches).  Splits default to enough
+    (chunk, head-group, split) work items to cover the CUs twice: 4 for 512-token chunks,
+    2 for 1024."""
+    splits = num_splits or max(1, 2048 // chunk)
+    return paged_case(seed + chunk + cache, batch=batch, sq=chunk, hq=32, hkv=8, d_qk=128,
+                      d_v=128, page_size=64, lengths=[cache] * batch, num_splits=splits,
+                      causal=True, poison=poison,
+                      name="context_chunk_bf16_b%d_c%d_h32x8_d128_p64_%d_s%d"
+                      % (batch, chunk, cache, splits))
+
+
 def mtp_decode_d128(seed: int = SEED_BASE + 7, batch: int = 4, cache: int = 131072,
                     q_tokens: int = 4, num_splits: int = 32) -> PagedCase:
     """Multi-token decode bf16 against 128k caches: batch 4, q_tokens (1 + MTP) query tokens

@@ -101,3 +101,14 @@ def test_full_size_chunked_prefill_sampled():
     sel = sample_rows(rows, 96, 7, must=[0, rows - 1])
     o, l = parity(pc, sel_rows=sel)
     assert torch.isfinite(o).all() and torch.isfinite(l).all()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("chunk,cache", [(512, 131072), (1024, 65536)])
+def test_context_phase_chunk_sampled(chunk, cache):
+    # the context phase of serving: a 512- or 1024-token chunk at the end of 64k / 128k caches
+    pc = inputs.context_chunk(chunk, cache, poison=True)
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 96, chunk + cache, must=[0, rows - 1])
+    o, l = parity(pc, sel_rows=sel)
+    assert torch.isfinite(o).all() and torch.isfinite(l).all()
