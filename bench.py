@@ -89,8 +89,14 @@ DECODE_SOURCES = ["scaled_dot_product_19_amd/csrc/decode_small.hip",
                   "scaled_dot_product_19_amd/csrc/combine.hip",
                   "scaled_dot_product_19_amd/csrc/decode_paged.hip",
                   "scaled_dot_product_19_amd/csrc/sdpa_device.h"]
+WIDE_SOURCES = ["scaled_dot_product_19_amd/csrc/decode_wide.hip",
+                "scaled_dot_product_19_amd/csrc/combine.hip",
+                "scaled_dot_product_19_amd/csrc/tile_ops.h",
+                "scaled_dot_product_19_amd/csrc/sdpa_device.h"]
 PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_thd_d128_traffic.md")
 DECODE_TRAFFIC = os.path.join(ROOT, "profiles", "paged_decode_d128_traffic.md")
+D256_TRAFFIC = os.path.join(ROOT, "profiles", "prefill_d256_traffic.md")
+WIDE_TRAFFIC = os.path.join(ROOT, "profiles", "mla_decode_wide_traffic.md")
 
 
 def sources_sha1(paths):
@@ -628,7 +634,9 @@ def d256_leg(args, torch, inputs, sdpa, dev, stream, threads, ragged):
            "roofline": {"kernel": "prefill_bf16_kernel<256, 32, 4, 4, false, false, false, false>",
                         "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                        "traffic": None}}
+                        # counters were taken on the dense workload
+                        "traffic": None if ragged else recorded_traffic(D256_TRAFFIC,
+                                                                        PREFILL_SOURCES)}}
     del q, k, v, o
     if not args.no_cpu_baseline:
         leg["cpu_baseline"] = cpu_baseline_prefill(case, args.cpu_seconds / 2, threads)
@@ -671,7 +679,8 @@ def mla_leg(args, torch, inputs, sdpa, dev, stream, threads):
            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
            "roofline": {"kernel": "decode_wide_kernel<576, 512> + combine_kernel<false>",
                         "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": recorded_traffic(WIDE_TRAFFIC, WIDE_SOURCES)}}
     del q, kp, vp
     if not args.no_cpu_baseline:
         leg["cpu_baseline"] = cpu_baseline_decode(pc, args.cpu_seconds / 2, threads)
