@@ -175,8 +175,10 @@ __device__ __forceinline__ uint32_t own_ticket(uint64_t* ctr, uint64_t old, uint
     return (uint32_t)(old >> 32) == gen ? (uint32_t)old : own_ticket_slow(ctr, old, gen);
 }
 
-// D <= 128: two work-groups per CU (<= 256 registers per lane, 2-stage ring).
-// D = 256: one, with a 4-stage ring and the O^T accumulators in AGPRs.
+// D <= 128: compiled for the register budget of two work-groups per CU (128
+// registers per lane); the 4-stage 128 KiB ring admits one work-group per CU,
+// whose 8 waves run two per SIMD.  D = 256: one 4-wave work-group per CU, one
+// wave per SIMD, with the O^T accumulators in AGPRs.
 // NW waves = 32 NW query rows per work-group, each wave 32 rows.
 // CZ: the scale is 0 (every logit is 0; masked keys need explicit zeros)
 // PP: ping-pong schedule (NW = 8, two waves per SIMD); otherwise sequential.
