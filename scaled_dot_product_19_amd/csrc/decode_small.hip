@@ -29,7 +29,8 @@
 // Release Notes, per-tensor FP8 D128 paged KV; v1.32.0 "SDPA: wider native
 // forward support", paged per-tensor FP8 D256).  A tile holds twice the keys
 // (the same 16 KB in flight); S^T = K Q^T runs on the FP8 MFMA
-// (v_mfma_f32_16x16x32_fp8_fp8, exact products, FP32 accumulate) with
+// (v_mfma_f32_16x16x32_fp8_fp8, FP32 accumulator; its dot products are not
+// fp32-exact, up to ~4e-5 of the sum of |products| off) with
 // scale * descale_q * descale_k folded into the exponent; V codes are widened
 // exactly to bf16 on their way into the V^T tile, so P V stays on the bf16
 // MFMA with P in bf16, and descale_v multiplies the normalized output.

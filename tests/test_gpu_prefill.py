@@ -175,6 +175,21 @@ def test_deterministic_and_causal_future_keys_bitwise():
     assert not torch.equal(l1[150:], l3[150:])
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_repeated_calls_are_bitwise_equal(d):
+    # identical calls give identical bits, at every head dim (the softmax must read each
+    # score accumulator only once its MFMAs are done); large logits (scale 2) included
+    for scale in (None, 2.0):
+        case = inputs.thd_case(12 + d, hq=8, hkv=2, d_qk=d, lengths=[700, 129, 65, 1],
+                               scale=scale, name="repeat_d%d" % d)
+        outs = [run(case) for _ in range(4)]
+        log("bf16 repeat: D=%d scale=%s, %d calls on lengths %s" % (d, scale, len(outs),
+                                                                     case.lengths_q))
+        for o, l in outs[1:]:
+            assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+        assert torch.isfinite(outs[0][1]).all()
+
+
 def test_first_causal_row_is_v0_exactly():
     case = inputs.thd_case(11, hq=8, hkv=2, d_qk=128, lengths=[40, 33], name="first_row")
     o, _ = run(case)

@@ -88,6 +88,56 @@ def test_scale_edges(scale):
                                name="fp8_scale"))
 
 
+# The gfx950 FP8 MFMAs do not return fp32-exact dot products: an in-bounds probe of
+# v_mfma_scale_f32_32x32x64_f8f6f4 and v_mfma_f32_16x16x32_fp8_fp8 on known E4M3 codes
+# measured errors up to 4.1e-5 of sum_d |q_d k_d| (the bf16 MFMA was exact on the same kind
+# of probe).  A logit of scale * dq * dk * sum_d q_d k_d thus carries up to
+# FP8_DOT_EPS * |scale * dq * dk| * sum_d |q_d k_d|, and the LSE (1-Lipschitz in the
+# logits) at most the largest of those over the keys a row sees.
+FP8_DOT_EPS = 2.0 ** -14
+
+
+def fp8_lse_slack(case):
+    """Per (token, head): FP8_DOT_EPS * |scale dq dk| * max over visible keys of
+    sum_d |q_d||k_d| (THD, bottom-right causal or not)."""
+    dq, dk, _ = case.descale
+    qa = case.q.view(torch.float8_e4m3fn).float().abs()
+    ka = case.k.view(torch.float8_e4m3fn).float().abs()
+    g = case.hq // case.hkv
+    out = np.zeros((int(case.cu_q[-1]), case.hq))
+    for b in range(case.batch):
+        q0, q1 = int(case.cu_q[b]), int(case.cu_q[b + 1])
+        k0, k1 = int(case.cu_kv[b]), int(case.cu_kv[b + 1])
+        lq, lk = q1 - q0, k1 - k0
+        for h in range(case.hq):
+            m = qa[q0:q1, h] @ ka[k0:k1, h // g].t()  # [lq, lk]
+            if case.causal:
+                i = torch.arange(lq)[:, None]
+                j = torch.arange(lk)[None, :]
+                m = torch.where(j <= i + lk - lq, m, torch.zeros_like(m))
+            out[q0:q1, h] = m.max(dim=1).values.numpy() if lk else 0.0
+    return FP8_DOT_EPS * abs(case.scale * dq * dk) * out
+
+
+def test_large_logits_within_the_fp8_dot_product_bound():
+    # scale 3: logits up to ~160, so the FP8 MFMA's dot-product error reaches a few 1e-3 in
+    # the LSE.  O is held to the prefill bar; the LSE to 1e-3 plus the per-row bound above.
+    case = inputs.fp8_thd_case(4005, 8, 2, 128, lengths=[1, 65, 190], scale=3.0,
+                               name="fp8_large_logits")
+    o, l = run(case)
+    o_ref, l_ref = oracle_prefill(case, descale=case.descale)
+    check_o(o, o_ref)
+    g = l.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(g), fin)
+    slack = fp8_lse_slack(case)
+    err = np.abs(g - l_ref)[fin]
+    bound = (1e-3 + slack)[fin]
+    log("fp8 large logits: max|dLSE| %.3g, max bound %.3g, max logit-scale LSE %.1f"
+        % (err.max(), bound.max(), np.abs(l_ref[fin]).max()))
+    assert np.all(err <= bound), (err.max(), bound[np.argmax(err - bound)])
+
+
 def test_negative_descale_product():
     # Q codes with flipped signs and a negated descale_q stand for the same values
     case = inputs.fp8_thd_case(4006, 8, 2, 128, lengths=[70, 129], name="fp8_neg_descale")
