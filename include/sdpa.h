@@ -114,7 +114,10 @@ typedef enum {
  *   sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key
  *   rows cu_seqlens_kv[b] .. cu_seqlens_kv[b+1]-1.
  * max_seqlen_q / max_seqlen_kv: host-known upper bounds of Lq_b / Lk_b (they
- *   size the grid; a sequence longer than its bound is only partly computed).
+ *   size the grid).  The grid covers ceil(max_seqlen_q / R) * R query rows of
+ *   every sequence (R = 64 for bf16 d 64/128 and FP8, 32 for bf16 d 256, 1 for
+ *   fp32); rows of a longer sequence past that are written as NaN (O and LSE),
+ *   never left unwritten or partly computed.
  * causal: 0 or 1 (bottom-right).  lse_layout: sdpa_lse_layout_t; lse_s_max:
  *   padded row capacity (>= max_seqlen_q) for SDPA_LSE_PADDED, the per-head
  *   stride for SDPA_LSE_HEAD_MAJOR, else ignored.
@@ -231,7 +234,10 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  * page_table_k / page_table_v: int32 [batch, table_stride]; entries past a
  *         sequence's last page are never read.
  * seq_lens int32 [batch]; max_seqlen_kv: host-known upper bound (must be
- *         <= table_stride*page_size).
+ *         <= table_stride*page_size).  A seq_lens[b] beyond the table's reach
+ *         (table_stride*page_size keys) cannot be computed: the table is read
+ *         only within its reach and every output row of sequence b is NaN (O
+ *         and LSE; its split partials too, and the merge propagates them).
  * o       [batch, s_q, h_q, d_v] dense bf16; lse [batch, s_q, h_q] fp32 or NULL.
  * Supported: dtype SDPA_BF16; (d_qk, d_v) in {(64,64), (128,128), (256,256),
  * (192,128), (576,512)}; page_size a multiple of 16; 1 <= num_splits <= 256;
@@ -354,11 +360,16 @@ int sdpa_decode_paged_noalloc(const void* q,
                               void* o, float* lse, int32_t dtype, void* stream);
 
 /*
- * LSE merge of split-KV partials (the merge the notes use but never print;
- * the textbook log-sum-exp merge is taken):
+ * LSE merge of split-KV partials: the second step of split-KV (cuDNN Frontend
+ * v1.31.0 Release Notes, "SDPA: paged KV, split-KV, and engine selection";
+ * v1.32.0 "SDPA: wider native forward support", split-KV with sinks).  The
+ * notes use the merge but never print it; the textbook log-sum-exp merge is
+ * taken:
  *   M = max_c lse_part[c,r];  LSE[r] = M + ln sum_c exp(lse_part[c,r] - M);
  *   O[r,:] = sum_c exp(lse_part[c,r] - LSE[r]) * o_part[c,r,:];
- *   every split empty (-inf) -> O[r,:] = 0, LSE[r] = -inf.
+ *   every split empty (-inf) -> O[r,:] = 0, LSE[r] = -inf;
+ *   any lse_part[c,r] NaN (a split that could not be computed) -> O[r,:] and
+ *   LSE[r] NaN.
  * o_part fp32 [num_splits, rows, d_v] (each partial already normalized),
  * lse_part fp32 [num_splits, rows] natural log; o [rows, d_v] in `dtype`
  * (SDPA_BF16 or SDPA_FP32); lse fp32 [rows] or NULL.  d_v <= 1024.

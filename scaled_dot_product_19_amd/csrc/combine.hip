@@ -42,10 +42,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         // row = (b * s_q + t) * hq + h: the sink of head h (natural-log units)
         const float sk = sinks != nullptr ? sinks[row % hq] : neg_inf();
         float m = sk;
-        for (int c = lane; c < splits; c += 64) m = fmaxf(m, lse_part[(int64_t)c * rows + row]);
+        bool bad = false;  // a NaN partial (a split that could not be computed)
+        for (int c = lane; c < splits; c += 64) {
+            const float x = lse_part[(int64_t)c * rows + row];
+            bad |= x != x;
+            m = fmaxf(m, x);
+        }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        if (m == neg_inf()) {
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+            // the row's O and LSE become NaN too (fmaxf above skips NaN)
+            lse_row = nan_f();
+            for (int c = lane; c < splits; c += 64) w[c] = nan_f();
+        } else if (m == neg_inf()) {
             for (int c = lane; c < splits; c += 64) w[c] = 0.f;
         } else {
             float sum = lane == 0 ? fast_exp2((sk - m) * kLog2e) : 0.f;  // 0 without a sink

@@ -68,7 +68,9 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
     const int bh = unit / a.splits;
     const int kvh = bh % a.hkv, b = bh / a.hkv;
 
-    // a length past the table's reach is clamped: the table is never read out of bounds
+    // a length past the table's reach is clamped (the table is never read out of
+    // bounds) and the sequence's rows are written as NaN
+    const bool trunc = a.seq_lens[b] > a.table_stride * a.page;
     const int L = min(a.seq_lens[b], a.table_stride * a.page);
     // keys [base, L) are cut into the splits; with a left window, base is the
     // start of the page holding the first key any token of the sequence sees
@@ -200,7 +202,8 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
     }
     const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
     // partials stay natural-log; the final Stats may be base 2
-    const float lse = a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
+    float lse = a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
+    if (trunc) inv = lse = nan_f();
     if (a.splits > 1) {
         float* orow = a.o_part + ((int64_t)split * a.total_rows + grow) * DV;
 #pragma unroll

@@ -183,7 +183,8 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     uint64_t ticket = 0;
     if (threadIdx.x == 0) ticket = ticket_async(ctr);
 
-    // a length past the table's reach is clamped: the table is never read out of bounds
+    // a length past the table's reach is clamped (the table is never read out of
+    // bounds) and the sequence's rows are written as NaN (see the epilogue)
     const int L = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
     // keys [base, L) are cut into the splits; with a left window, base is the
     // start of the page holding the first key any token of the sequence sees
@@ -498,6 +499,10 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             const float lse2 = M + fast_log2(tot);
             // partials stay natural-log; the final Stats may be base 2
             lse = a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
+        }
+        if (load_uniform(a.seq_lens, b) > a.table_stride * a.page) {  // truncated: NaN rows
+            o = f32x4{nan_f(), nan_f(), nan_f(), nan_f()};
+            lse = nan_f();
         }
         if (a.splits > 1) {
             *reinterpret_cast<f32x4*>(a.o_part + ((int64_t)split * a.total_rows + row) * D + n) = o;

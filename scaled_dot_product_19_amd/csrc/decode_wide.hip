@@ -195,6 +195,9 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     // keys of this chunk: [lo, hi).  Keys [base, L) are cut into the splits;
     // with a left window, base is the start of the page holding the first key
     // any token of the sequence sees.
+    // a length past the table's reach is clamped (the table is never read out of
+    // bounds) and the sequence's rows are written as NaN
+    const bool trunc = len_b > a.table_stride * a.page;
     const int L = min(len_b, a.table_stride * a.page);
     int base = 0;
     if (VAR && a.window > 0 && L - a.sq - a.window + 1 > 0) base = ((L - a.sq - a.window + 1) / a.page) * a.page;
@@ -543,7 +546,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     }
     const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
     // partials stay natural-log; the final Stats may be base 2
-    const float lse = VAR && a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
+    float lse = VAR && a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
+    if (trunc) inv = lse = nan_f();
     const int64_t rows_all = (int64_t)a.batch * a.sq * a.hq;
     auto row_global = [&](int rr) {  // (b, token, head) row of row rr of this KV head
         return (int64_t)(b * a.sq + rr / a.group) * a.hq + kvh * a.group + rr % a.group;

@@ -213,12 +213,16 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // rows [q_beg, q_beg + lq) and keys [kv_beg, kv_beg + lk) of the sequence;
     // this item sees keys [lo, hi) of it (the split's chunk when paged)
     int q_beg, lq, kv_beg, lk, lo = 0, hi;
+    bool trunc = false;  // paged: seq_lens past the table's reach (rows become NaN)
     if constexpr (PAGED) {
         q_beg = b * a.sq;
         lq = a.sq;
         kv_beg = 0;
-        // a length past the table's reach is clamped: the table is never read out of bounds
-        lk = min(load_uniform(a.seq_lens, b), a.table_stride * a.page);
+        // a length past the table's reach is clamped (the table is never read
+        // out of bounds) and the sequence's rows are written as NaN
+        const int len = load_uniform(a.seq_lens, b);
+        trunc = len > a.table_stride * a.page;
+        lk = min(len, a.table_stride * a.page);
         hi = lk;
         if (a.splits > 1) {
             // keys [base, lk) are cut into the splits; with a left window, base is
@@ -774,11 +778,39 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     wait_vmcnt<0>();
     before_epilogue();
 
+    if constexpr (!PAGED) {
+        // THD rows past the grid (a sequence longer than max_seqlen_q allows
+        // for, rounded up to whole row blocks): the item of the last row block
+        // writes them, for its heads, as NaN O and NaN LSE
+        const int cover = a.n_qtiles * 32 * nt;
+        if (qt == a.n_qtiles - 1 && lq > cover) {  // uniform
+            const int chunks = D / 8;  // 16-byte chunks of an O row
+            const int n = (lq - cover) * a.nh * chunks;
+            const uint4 nan8 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+            for (int e = tid; e < n; e += C::THREADS) {
+                const int r = cover + e / (a.nh * chunks);
+                const int hh = hg * a.nh + (e / chunks) % a.nh;
+                bf16_t* orow = a.o + (int64_t)(q_beg + r) * a.o_st + (int64_t)hh * a.o_sh;
+                *reinterpret_cast<uint4*>(orow + 8 * (e % chunks)) = nan8;
+                if (a.lse != nullptr && e % chunks == 0) {
+                    if (a.lse_layout == 1) {
+                        a.lse[(int64_t)(q_beg + r) * a.hq + hh] = nan_f();
+                    } else if (a.lse_layout == 2 && r < a.lse_s_max) {
+                        a.lse[((int64_t)b * a.lse_s_max + r) * a.hq + hh] = nan_f();
+                    } else if (a.lse_layout == 3) {
+                        a.lse[(int64_t)hh * a.lse_s_max + q_beg + r] = nan_f();
+                    }
+                }
+            }
+        }
+    }
+
     // epilogue: O = O^T / l written as bf16, LSE = ln2 * (m + log2 l); a
     // split of a paged call writes its normalized fp32 partial and LSE_c
     // (-inf and zeros when it sees no key of the row)
     float l_tot = half_sum(l);
     float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (trunc) inv = nan_f();
     if constexpr (PAGED) {
         if (a.splits > 1) {  // uniform
             if (!row_ok) return;
@@ -795,7 +827,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             }
             if (half == 0)
                 a.lse_part[(int64_t)split * a.total_rows + grow] =
-                    l_tot > 0.f ? kLn2 * (m + fast_log2(l_tot)) : neg_inf();
+                    trunc ? nan_f() : (l_tot > 0.f ? kLn2 * (m + fast_log2(l_tot)) : neg_inf());
             return;
         }
     }
@@ -868,7 +900,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     if (a.lse != nullptr && half == 0) {
         // natural log, or base 2 (the running statistics are already log2)
         const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
-        const float lse = a.stats_log2 ? lse2 : kLn2 * lse2;
+        const float lse = trunc ? nan_f() : (a.stats_log2 ? lse2 : kLn2 * lse2);
         if (a.lse_layout == 1) {
             a.lse[(int64_t)(q_beg + i) * a.hq + h] = lse;
         } else if (a.lse_layout == 2 && i < a.lse_s_max) {

@@ -52,6 +52,19 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(F32Args a) {
     const int lane = threadIdx.x;
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int q_beg = a.cu_q[b], lq = a.cu_q[b + 1] - q_beg;
+    if (i == gridDim.x - 1) {
+        // rows past the grid (a sequence longer than max_seqlen_q): NaN O and LSE
+        for (int r = i + 1; r < lq; ++r) {
+            float* orow = a.o + (int64_t)(q_beg + r) * a.o_st + (int64_t)h * a.o_sh;
+            for (int n = lane; n < a.dv; n += 64) orow[n] = nan_f();
+            if (a.lse != nullptr && lane == 0) {
+                if (a.lse_layout == 1)
+                    a.lse[(int64_t)(q_beg + r) * a.hq + h] = nan_f();
+                else if (a.lse_layout == 2 && r < a.lse_s_max)
+                    a.lse[((int64_t)b * a.lse_s_max + r) * a.hq + h] = nan_f();
+            }
+        }
+    }
     if (i >= lq) return;
     const int kv_beg = a.cu_kv[b], lk = a.cu_kv[b + 1] - kv_beg;
     const int kvh = h / a.group;

@@ -38,6 +38,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+// quiet NaN: the value of output rows a call cannot compute (a sequence longer
+// than its page table reaches, THD rows past the grid that max_seqlen_q sizes)
+__device__ __forceinline__ float nan_f() { return __builtin_nanf(""); }
 
 // 8 OCP E4M3 codes -> 8 bf16 (gfx950's FP8 conversions read OCP E4M3).
 // Every E4M3 value has at most 4 significant bits, so the top half of its
