@@ -279,9 +279,14 @@ int sdpa_decode_paged(const void* q,
  * the kernel (so a captured launch picks up new values).  Strides count
  * elements (= bytes).  Other arguments, the split workspace and its layout
  * are those of sdpa_decode_paged.
- * Supported: d_qk == d_v in {128, 256}; s_q * (h_q/h_kv) <= 16; page_size a
- * multiple of 16; K pool strides multiples of 16, V pool strides multiples of
- * 8; q and the pools 16-byte aligned.  Else SDPA_ERR_UNSUPPORTED.
+ * Supported: the (d_qk, d_v) pairs of sdpa_decode_paged ({64, 128, 256} square,
+ * (192,128), (576,512); native D64 per-tensor FP8 and Q/K 576 with V 512 are
+ * in v1.32.0 "SDPA: wider native forward support"); s_q * (h_q/h_kv) <= 512
+ * query rows per KV head (no chunked-prefill path in FP8); page_size a multiple
+ * of 16; K and V pool strides multiples of 16; q and the pools 16-byte aligned.
+ * Else SDPA_ERR_UNSUPPORTED.  d = 128 and 256 with at most 16 rows per KV head
+ * take the FP8-MFMA few-row kernel; the rest widen the codes exactly to bf16 as
+ * they are loaded and use bf16 MFMA.
  */
 int sdpa_decode_paged_fp8(const void* q,
                           const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,

@@ -24,10 +24,10 @@ namespace sdpa {
 namespace {
 
 struct DecodeKArgs {
-    const bf16_t* q;
-    const bf16_t* kp;
+    const void* q;   // bf16, or E4M3 codes (F8)
+    const void* kp;
     int64_t k_sp, k_st, k_sh;
-    const bf16_t* vp;
+    const void* vp;
     int64_t v_sp, v_st, v_sh;
     const int32_t* pt_k;
     const int32_t* pt_v;
@@ -45,11 +45,20 @@ struct DecodeKArgs {
     int32_t window;      // left sliding window (0: none)
     const float* sinks;  // [hq] sink logits (natural-log units) or nullptr
     int32_t stats_log2;  // final LSE in base 2
+    const float* descale_q;  // F8 only: one fp32 each, read on the device
+    const float* descale_k;
+    const float* descale_v;
 };
 
 constexpr int BK = 32;
 
-template <int DQK, int DV, int NW, bool PREFETCH>
+// F8: per-tensor FP8 (E4M3) Q, K and V standing for descale_{q,k,v} times
+// their codes (cuDNN Frontend v1.31.0 Release Notes, per-tensor FP8 D128 paged
+// KV; v1.32.0 "SDPA: wider native forward support", native D64 per-tensor
+// FP8, paged per-tensor FP8 D256).  Codes are widened exactly to bf16 as they
+// are loaded, so the tile and MFMA path is the bf16 one; descale_q descale_k
+// joins the logit scale and descale_v multiplies the normalized output.
+template <int DQK, int DV, int NW, bool PREFETCH, bool F8>
 __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kernel(DecodeKArgs a) {
     constexpr int NT = NW * 64;
     using G = TileGeom<DQK, DV, BK>;
@@ -108,15 +117,21 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
 
     bf16x8 qf[DQK / 16];
     const int64_t grow = ((int64_t)b * a.sq + t) * a.hq + h;  // global row id
-    load_q<DQK>(qf, a.q + grow * DQK, row_ok, lane);
+    load_q<DQK, F8>(qf, static_cast<const char*>(a.q) + grow * DQK * (F8 ? 1 : 2), row_ok, lane);
+    float scale_log2 = a.scale_log2;
+    float o_mul = 1.f;
+    if constexpr (F8) {
+        scale_log2 *= a.descale_q[0] * a.descale_k[0];
+        o_mul = a.descale_v[0];
+    }
 
     RowState<DV> st;
     row_state_init<DV>(st);
 
     const int32_t* ptk = a.pt_k + (int64_t)b * a.table_stride;
     const int32_t* ptv = a.pt_v + (int64_t)b * a.table_stride;
-    const bf16_t* kbase = a.kp + (int64_t)kvh * a.k_sh;
-    const bf16_t* vbase = a.vp + (int64_t)kvh * a.v_sh;
+    const char* kbase = static_cast<const char*>(a.kp) + (int64_t)kvh * a.k_sh * (F8 ? 1 : 2);
+    const char* vbase = static_cast<const char*>(a.vp) + (int64_t)kvh * a.v_sh * (F8 ? 1 : 2);
     auto koff = [&](int k0) {
         return [=](int j) -> int64_t {
             const int key = k0 + j;
@@ -137,8 +152,8 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
         KRegs<SH::KC> kr;
         VRegs<SH::VU> vr;
         if (n_tiles > 0) {
-            load_k_part<DQK, DV, BK, NT>(kr, kbase, tid, koff(lo));
-            load_v_part<DQK, DV, BK, NT>(vr, vbase, tid, voff(lo));
+            load_k_part<DQK, DV, BK, NT, F8>(kr, kbase, tid, koff(lo));
+            load_v_part<DQK, DV, BK, NT, F8>(vr, vbase, tid, voff(lo));
             store_k_part<DQK, DV, BK, NT>(kr, smem, tid);
             store_v_part<DQK, DV, BK, NT>(vr, smem, tid);
         }
@@ -147,13 +162,13 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
             const int key0 = lo + it * BK;
             const bool more = it + 1 < n_tiles;
             if (more) {
-                load_k_part<DQK, DV, BK, NT>(kr, kbase, tid, koff(key0 + BK));
-                load_v_part<DQK, DV, BK, NT>(vr, vbase, tid, voff(key0 + BK));
+                load_k_part<DQK, DV, BK, NT, F8>(kr, kbase, tid, koff(key0 + BK));
+                load_v_part<DQK, DV, BK, NT, F8>(vr, vbase, tid, voff(key0 + BK));
             }
             const bf16_t* buf = smem + (it & 1) * G::BUF_ELEMS;
             if (key0 < kv_end_w)
                 tile_step<DQK, DV, BK>(buf, buf + G::K_ELEMS, qf, st, key0, lim, first,
-                                       key0 + BK > nomask_end || key0 < first_w, a.scale_log2,
+                                       key0 + BK > nomask_end || key0 < first_w, scale_log2,
                                        lane);
             if (more) {
                 bf16_t* nb = smem + ((it + 1) & 1) * G::BUF_ELEMS;
@@ -167,18 +182,18 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
             const int key0 = lo + it * BK;
             {
                 KRegs<SH::KC> kr;
-                load_k_part<DQK, DV, BK, NT>(kr, kbase, tid, koff(key0));
+                load_k_part<DQK, DV, BK, NT, F8>(kr, kbase, tid, koff(key0));
                 store_k_part<DQK, DV, BK, NT>(kr, smem, tid);
             }
             {
                 VRegs<SH::VU> vr;
-                load_v_part<DQK, DV, BK, NT>(vr, vbase, tid, voff(key0));
+                load_v_part<DQK, DV, BK, NT, F8>(vr, vbase, tid, voff(key0));
                 store_v_part<DQK, DV, BK, NT>(vr, smem, tid);
             }
             __syncthreads();
             if (key0 < kv_end_w)
                 tile_step<DQK, DV, BK>(smem, smem + G::K_ELEMS, qf, st, key0, lim, first,
-                                       key0 + BK > nomask_end || key0 < first_w, a.scale_log2,
+                                       key0 + BK > nomask_end || key0 < first_w, scale_log2,
                                        lane);
             __syncthreads();
         }
@@ -203,6 +218,7 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
     const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
     // partials stay natural-log; the final Stats may be base 2
     float lse = a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
+    inv *= o_mul;  // descale_v (1 unless FP8)
     if (trunc) inv = lse = nan_f();
     if (a.splits > 1) {
         float* orow = a.o_part + ((int64_t)split * a.total_rows + grow) * DV;
@@ -237,51 +253,41 @@ __global__ __launch_bounds__(NW * 64, (DQK + DV > 512 ? 1 : 2)) void decode_kern
     }
 }
 
-template <int DQK, int DV, int NW>
+template <int DQK, int DV, int NW, bool F8>
 hipError_t launch_nw(const DecodeKArgs& a, hipStream_t s) {
     constexpr bool PREFETCH = DQK + DV <= 256;
     using G = TileGeom<DQK, DV, BK>;
     const size_t lds = (PREFETCH ? 2 : 1) * (size_t)G::BUF_BYTES;
     const int64_t n_wg = (int64_t)((a.n_units + 7) / 8) * 8 * a.n_rg;
     if (n_wg == 0) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<DQK, DV, NW, PREFETCH>,
+    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<DQK, DV, NW, PREFETCH, F8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_kernel<DQK, DV, NW, PREFETCH>), dim3((unsigned)n_wg),
+    hipLaunchKernelGGL((decode_kernel<DQK, DV, NW, PREFETCH, F8>), dim3((unsigned)n_wg),
                        dim3(NW * 64), lds, s, a);
     return hipGetLastError();
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool F8>
 hipError_t launch_dims(DecodeKArgs& a, hipStream_t s) {
     const int nw = a.rows <= 32 ? 1 : (a.rows <= 64 ? 2 : 4);
     a.n_rg = (a.rows + nw * 32 - 1) / (nw * 32);
     switch (nw) {
-        case 1: return launch_nw<DQK, DV, 1>(a, s);
-        case 2: return launch_nw<DQK, DV, 2>(a, s);
-        default: return launch_nw<DQK, DV, 4>(a, s);
+        case 1: return launch_nw<DQK, DV, 1, F8>(a, s);
+        case 2: return launch_nw<DQK, DV, 2, F8>(a, s);
+        default: return launch_nw<DQK, DV, 4, F8>(a, s);
     }
 }
 
-}  // namespace
-
-bool decode_supported(int32_t dqk, int32_t dv) {
-    return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 256 && dv == 256) ||
-           (dqk == 192 && dv == 128) || (dqk == 576 && dv == 512);
-}
-
-hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
-    if (decode_small_supported(da.dqk, da.dv, da.sq * (da.hq / da.hkv)))
-        return launch_decode_small(da, s);
-    if (prefill_paged_supported(da)) return launch_prefill_paged(da, s);
-    if (decode_wide_supported(da)) return launch_decode_wide(da, s);
+// The general decode kernel for the shapes the specialized kernels leave.
+hipError_t launch_generic(const DecodeArgs& da, hipStream_t s, bool f8) {
     DecodeKArgs a;
-    a.q = static_cast<const bf16_t*>(da.q);
-    a.kp = static_cast<const bf16_t*>(da.k_pool);
+    a.q = da.q;
+    a.kp = da.k_pool;
     a.k_sp = da.k_sp;
     a.k_st = da.k_st;
     a.k_sh = da.k_sh;
-    a.vp = static_cast<const bf16_t*>(da.v_pool);
+    a.vp = da.v_pool;
     a.v_sp = da.v_sp;
     a.v_st = da.v_st;
     a.v_sh = da.v_sh;
@@ -308,14 +314,46 @@ hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
     a.window = da.window > 0 ? min(da.window, 1 << 30) : 0;
     a.sinks = da.sinks;
     a.stats_log2 = da.stats_log2;
+    a.descale_q = f8 ? da.descale_q : nullptr;
+    a.descale_k = f8 ? da.descale_k : nullptr;
+    a.descale_v = f8 ? da.descale_v : nullptr;
     a.n_rg = 1;
     if (a.n_units == 0) return hipSuccess;
-    if (da.dqk == 64) return launch_dims<64, 64>(a, s);
-    if (da.dqk == 128) return launch_dims<128, 128>(a, s);
-    if (da.dqk == 256) return launch_dims<256, 256>(a, s);
-    if (da.dqk == 192) return launch_dims<192, 128>(a, s);
-    if (da.dqk == 576) return launch_dims<576, 512>(a, s);
+    if (f8) {
+        if (da.dqk == 64) return launch_dims<64, 64, true>(a, s);
+        if (da.dqk == 128) return launch_dims<128, 128, true>(a, s);
+        if (da.dqk == 256) return launch_dims<256, 256, true>(a, s);
+        if (da.dqk == 192) return launch_dims<192, 128, true>(a, s);
+        if (da.dqk == 576) return launch_dims<576, 512, true>(a, s);
+    } else {
+        if (da.dqk == 64) return launch_dims<64, 64, false>(a, s);
+        if (da.dqk == 128) return launch_dims<128, 128, false>(a, s);
+        if (da.dqk == 256) return launch_dims<256, 256, false>(a, s);
+        if (da.dqk == 192) return launch_dims<192, 128, false>(a, s);
+        if (da.dqk == 576) return launch_dims<576, 512, false>(a, s);
+    }
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_supported(int32_t dqk, int32_t dv) {
+    return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 256 && dv == 256) ||
+           (dqk == 192 && dv == 128) || (dqk == 576 && dv == 512);
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
+    if (decode_small_supported(da.dqk, da.dv, da.sq * (da.hq / da.hkv)))
+        return launch_decode_small(da, s);
+    if (prefill_paged_supported(da)) return launch_prefill_paged(da, s);
+    if (decode_wide_supported(da)) return launch_decode_wide(da, s);
+    return launch_generic(da, s, false);
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& da, hipStream_t s) {
+    if (decode_small_supported(da.dqk, da.dv, da.sq * (da.hq / da.hkv)))
+        return launch_decode_small(da, s);
+    return launch_generic(da, s, true);
 }
 
 }  // namespace sdpa

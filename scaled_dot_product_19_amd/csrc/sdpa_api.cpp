@@ -282,16 +282,17 @@ static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t 
     if (num_splits < 1 || num_splits > 256)
         return fail(SDPA_ERR_SHAPE, "num_splits=%d outside [1, 256]", num_splits);
     if (fp8) {
-        // per-tensor FP8: the few-row decode kernel only (HBM-streaming decode)
-        if (!sdpa::decode_small_supported(d_qk, d_v, s_q * (h_q / h_kv)))
+        // per-tensor FP8: the few-row decode kernel (HBM streaming, d 128/256,
+        // <= 16 rows per KV head), else the general decode kernel, which widens
+        // the codes to bf16 as it loads them (up to 512 rows per KV head)
+        if ((int64_t)s_q * (h_q / h_kv) > 512)
             return fail(SDPA_ERR_UNSUPPORTED,
-                        "FP8 paged decode serves d_qk == d_v in {128, 256} with s_q * (h_q / h_kv) "
-                        "<= 16 query rows per KV head; got (%d, %d), %lld rows",
-                        d_qk, d_v, (long long)s_q * (h_q / h_kv));
-        const int64_t kst[3] = {k_sp, k_st, k_sh};
-        for (int64_t x : kst)
+                        "FP8 paged decode serves up to 512 query rows per KV head; got %lld",
+                        (long long)s_q * (h_q / h_kv));
+        const int64_t st[6] = {k_sp, k_st, k_sh, v_sp, v_st, v_sh};
+        for (int64_t x : st)
             if (x % 16 != 0)
-                return fail(SDPA_ERR_UNSUPPORTED, "FP8 K pool strides must be multiples of 16");
+                return fail(SDPA_ERR_UNSUPPORTED, "FP8 K/V pool strides must be multiples of 16");
     }
     if (!fp8) {
         // more than 512 query rows per KV head: only the chunked-prefill path
@@ -417,7 +418,7 @@ static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t 
     a.sinks = sinks;
     a.stats_log2 = stats_log2;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = fp8 ? sdpa::launch_decode_small(a, s) : sdpa::launch_decode_bf16(a, s);
+    hipError_t e = fp8 ? sdpa::launch_decode_fp8(a, s) : sdpa::launch_decode_bf16(a, s);
     if (e != hipSuccess) return hip_fail(e, "paged decode launch");
     if (num_splits > 1) {
         e = sdpa::launch_combine(a.o_part, a.lse_part, num_splits, rows, d_v, o, lse, 0, s, sinks,

@@ -117,12 +117,24 @@ struct TileShare {
     static constexpr int VU = (G::V_UNITS + NTHREADS - 1) / NTHREADS;
 };
 
+// 8 elements of a row at element offset off: bf16, or (F8) 8 E4M3 codes
+// widened exactly to bf16.
+template <bool F8>
+__device__ __forceinline__ uint4 load8(const void* __restrict__ base, int64_t off) {
+    if constexpr (F8) {
+        return e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + off));
+    } else {
+        return *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(base) + off);
+    }
+}
+
 // Issue the HBM loads of one thread's share of the K tile.  koff(j) returns
 // the element offset of tile key j's K row, or -1 when key j is not to be
-// read (past the range); such rows are zero-filled.
-template <int DQK, int DV, int BK, int NTHREADS, class KOff>
+// read (past the range); such rows are zero-filled.  F8: the pool holds E4M3
+// codes (one byte per element), widened to bf16 as they arrive.
+template <int DQK, int DV, int BK, int NTHREADS, bool F8 = false, class KOff>
 __device__ __forceinline__ void load_k_part(KRegs<TileShare<DQK, DV, BK, NTHREADS>::KC>& r,
-                                            const bf16_t* __restrict__ kbase, int tid, KOff koff) {
+                                            const void* __restrict__ kbase, int tid, KOff koff) {
     using G = TileGeom<DQK, DV, BK>;
     constexpr int KC = TileShare<DQK, DV, BK, NTHREADS>::KC;
     const uint4 zero = {0u, 0u, 0u, 0u};
@@ -133,7 +145,7 @@ __device__ __forceinline__ void load_k_part(KRegs<TileShare<DQK, DV, BK, NTHREAD
         if (chunk < G::K_CHUNKS) {
             int row = chunk / (DQK / 8), cc = chunk % (DQK / 8);
             int64_t off = koff(row);
-            if (off >= 0) r.k[c] = *reinterpret_cast<const uint4*>(kbase + off + cc * 8);
+            if (off >= 0) r.k[c] = load8<F8>(kbase, off + cc * 8);
         }
     }
 }
@@ -141,9 +153,9 @@ __device__ __forceinline__ void load_k_part(KRegs<TileShare<DQK, DV, BK, NTHREAD
 // Same for the V tile: a thread loads 4 consecutive keys x 8 columns.  Rows
 // not read are zero: masked probabilities are exact zeros and must never
 // multiply NaN garbage (0 * NaN = NaN).
-template <int DQK, int DV, int BK, int NTHREADS, class VOff>
+template <int DQK, int DV, int BK, int NTHREADS, bool F8 = false, class VOff>
 __device__ __forceinline__ void load_v_part(VRegs<TileShare<DQK, DV, BK, NTHREADS>::VU>& r,
-                                            const bf16_t* __restrict__ vbase, int tid, VOff voff) {
+                                            const void* __restrict__ vbase, int tid, VOff voff) {
     using G = TileGeom<DQK, DV, BK>;
     constexpr int VU = TileShare<DQK, DV, BK, NTHREADS>::VU;
     const uint4 zero = {0u, 0u, 0u, 0u};
@@ -157,7 +169,7 @@ __device__ __forceinline__ void load_v_part(VRegs<TileShare<DQK, DV, BK, NTHREAD
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 int64_t off = voff(kq * 4 + e);
-                if (off >= 0) r.v[u][e] = *reinterpret_cast<const uint4*>(vbase + off + ncc * 8);
+                if (off >= 0) r.v[u][e] = load8<F8>(vbase, off + ncc * 8);
             }
         }
     }
@@ -309,14 +321,15 @@ __device__ __forceinline__ void tile_step(const bf16_t* __restrict__ ks,
 }
 
 // Load the wave's Q^T operand: lane (col, half) gets query row `col`'s
-// elements kk*16 + half*8 .. +8 for every kk.  Rows not present are zero.
-template <int DQK>
-__device__ __forceinline__ void load_q(bf16x8* qf, const bf16_t* qrow, bool ok, int lane) {
+// elements kk*16 + half*8 .. +8 for every kk (F8: codes widened to bf16).
+// Rows not present are zero.
+template <int DQK, bool F8 = false>
+__device__ __forceinline__ void load_q(bf16x8* qf, const void* qrow, bool ok, int lane) {
     const int half = lane >> 5;
 #pragma unroll
     for (int kk = 0; kk < DQK / 16; ++kk) {
         uint4 w = {0u, 0u, 0u, 0u};
-        if (ok) w = *reinterpret_cast<const uint4*>(qrow + kk * 16 + half * 8);
+        if (ok) w = load8<F8>(qrow, kk * 16 + half * 8);
         qf[kk] = __builtin_bit_cast(bf16x8, w);
     }
 }

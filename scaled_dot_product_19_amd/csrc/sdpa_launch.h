@@ -64,6 +64,8 @@ struct DecodeArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+// per-tensor FP8: the few-row kernel where it serves, else the general kernel
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s);
 // sinks (optional): [hq] sink logits merged once per row (row % hq is its head);
 // stats_log2: write the merged LSE in base 2.
 hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,

@@ -233,11 +233,13 @@ def fp8_thd_case(seed: int, hq: int, hkv: int, d: int, lengths: Optional[List[in
 def fp8_paged_case(seed: int, batch: int, sq: int, hq: int, hkv: int, d: int, page_size: int,
                    lo: int = 0, hi: int = 0, lengths: Optional[List[int]] = None,
                    num_splits: int = 1, causal: bool = True, scale: Optional[float] = None,
-                   poison: bool = False, name: str = "") -> PagedCase:
+                   poison: bool = False, name: str = "",
+                   d_v: Optional[int] = None) -> PagedCase:
     """Paged decode problem in per-tensor FP8 E4M3: the fp32 problem paged_case draws for
-    the same arguments, each of Q, the K pool and the V pool quantized on its own
-    (quantize_e4m3).  Poisoned slots hold the NaN code."""
-    pc = paged_case(seed, batch, sq, hq, hkv, d, d, page_size, lo=lo, hi=hi, lengths=lengths,
+    the same arguments (d_v defaults to d), each of Q, the K pool and the V pool quantized
+    on its own (quantize_e4m3).  Poisoned slots hold the NaN code."""
+    pc = paged_case(seed, batch, sq, hq, hkv, d, d if d_v is None else d_v, page_size,
+                    lo=lo, hi=hi, lengths=lengths,
                     num_splits=num_splits, causal=causal, scale=scale, dtype=torch.float32,
                     poison=poison, name=name)
     q8, dq = quantize_e4m3(pc.q)

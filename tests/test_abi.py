@@ -226,10 +226,11 @@ def _decode_fp8(**over):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(dqk=64, dv=64, k_st=8 * 64, v_st=8 * 64, k_sh=64, v_sh=64), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(dqk=576, dv=512), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(sq=4, hq=64, hkv=8), sdpa.SDPA_ERR_UNSUPPORTED),      # 32 rows per KV head
+    (dict(dqk=96, dv=96, k_st=8 * 96, v_st=8 * 96, k_sh=96, v_sh=96), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(dqk=576, dv=576), sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(sq=5, hq=128, hkv=1), sdpa.SDPA_ERR_UNSUPPORTED),     # 640 rows per KV head
     (dict(k_st=8 * 128 + 8), sdpa.SDPA_ERR_UNSUPPORTED),         # K rows need 16-byte strides
+    (dict(v_st=8 * 128 + 8), sdpa.SDPA_ERR_UNSUPPORTED),         # and V rows too
     (dict(v_st=8 * 128 + 4), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(dq=None), sdpa.SDPA_ERR_NULL),
     (dict(dv_=None), sdpa.SDPA_ERR_NULL),

@@ -1,5 +1,7 @@
 """GPU parity of sdpa_decode_paged_fp8 (per-tensor FP8 E4M3 Q/K/V, bf16 O) against the
-fp64 oracle on the same codes and descales, through the C-ABI.
+fp64 oracle on the same codes and descales, through the C-ABI: the few-row kernel (D = 128
+and 256, up to 16 query rows per KV head) and the general decode kernel (everything else up
+to 512 rows per KV head: D = 64, 192/128, 576/512, and D = 128/256 with more rows).
 
 The bar is the decode one: O within |g-o| <= 2e-2 + 2e-2|o|, LSE within 1e-3, -inf
 exactly where the oracle has -inf.  Pools are poisoned (NaN codes in unused pages and
@@ -119,3 +121,70 @@ def test_full_size_fp8_decode_sampled():
     check_o(o.reshape(rows, -1)[torch.from_numpy(sel).cuda()], o_ref)
     check_lse(l.reshape(rows)[torch.from_numpy(sel).cuda()], l_ref)
     assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
+
+
+# ---- the general decode kernel in FP8: more than 16 rows per KV head, D = 64, 192/128 and
+# the absorbed-MLA 576/512 (cuDNN Frontend v1.32.0 Release Notes, "SDPA: wider native
+# forward support": native D64 per-tensor FP8 and Q/K 576 with V 512) -------------------
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_d128_mtp_rows_past_the_few_row_kernel(splits):
+    # 4 tokens x 8 heads = 32 rows per KV head
+    pc = inputs.fp8_paged_case(3011, 3, 4, 32, 4, 128, 64, lengths=[2, 300, 1400],
+                               num_splits=splits, poison=True, name="fp8_mtp_g8")
+    o, _, _, _ = parity(pc)
+    assert torch.all(o[0, :2] == 0)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_d256_rows_past_the_few_row_kernel(splits):
+    # 4 tokens x 8 heads = 32 rows per KV head at D = 256
+    pc = inputs.fp8_paged_case(3012, 2, 4, 16, 2, 256, 32, lengths=[90, 1100],
+                               num_splits=splits, poison=True, name="fp8_d256_g8")
+    parity(pc)
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 32, 1), (3, 16, 4, 64, 3)],
+                         ids=["sq1_g4", "sq3_g4_split3"])
+def test_d64(shape):
+    sq, hq, hkv, page, splits = shape
+    pc = inputs.fp8_paged_case(3013 + sq, 3, sq, hq, hkv, 64, page, lengths=[1, 250, 1700],
+                               num_splits=splits, poison=True, name="fp8_d64")
+    parity(pc)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_d192_d128_pools(splits):
+    pc = inputs.fp8_paged_case(3017, 3, 2, 16, 2, 192, 32, lengths=[5, 333, 1200],
+                               num_splits=splits, poison=True, name="fp8_d192x128", d_v=128)
+    parity(pc)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_absorbed_mla_aliased_fp8_cache(splits):
+    # one 576-wide E4M3 pool, V = the first 512 columns of each K row (descale_v = descale_k)
+    import dataclasses
+    pc = inputs.fp8_paged_case(3018, 3, 2, 32, 1, 576, 64, lengths=[1, 700, 2000],
+                               num_splits=splits, poison=True, name="fp8_mla_aliased")
+    dq, dk, _ = pc.descale
+    pc = dataclasses.replace(pc, v_pool=pc.k_pool[..., :512], pt_v=pc.pt_k, descale=(dq, dk, dk))
+    log("fp8 aliased MLA: lens=%s splits=%d" % (pc.seq_lens.tolist(), splits))
+    kp = to_dev(pc.k_pool)
+    d_q, d_k, d_v = descales(pc)
+    o, l = sdpa.decode_paged_fp8(to_dev(pc.q), kp, kp[..., :512], to_dev(pc.pt_k),
+                                 to_dev(pc.pt_k), to_dev(pc.seq_lens), pc.max_kv, pc.scale,
+                                 d_q, d_k, d_v, causal=pc.causal, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_decode(pc, descale=pc.descale)
+    log("  max|dO|=%.3g max|dLSE|=%.3g" % (check_o(o, o_ref), check_lse(l, l_ref)))
+
+
+def test_512_rows_per_kv_head_and_past_them():
+    # 4 tokens x 128 heads over one KV head: the most rows a call serves
+    pc = inputs.fp8_paged_case(3019, 2, 4, 128, 1, 128, 64, lengths=[6, 900], num_splits=2,
+                               poison=True, name="fp8_512rows")
+    parity(pc)
+    pc5 = inputs.fp8_paged_case(3020, 1, 5, 128, 1, 128, 64, lengths=[900], name="fp8_640rows")
+    with pytest.raises(sdpa.SdpaError) as ei:
+        run(pc5)
+    assert ei.value.status == sdpa.SDPA_ERR_UNSUPPORTED

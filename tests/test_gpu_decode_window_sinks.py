@@ -1,7 +1,8 @@
 """GPU parity of sdpa_decode_paged_ex (left sliding window, attention sinks, base-2 Stats)
 against the fp64 oracle, through every paged-decode kernel: the few-row kernel (bf16 D=128,
 D=256 and per-tensor FP8), the absorbed-MLA wide kernel (576/512), the general decode
-kernel (D=64, 192/128) and the chunked-prefill path (prefill kernel over the page tables).
+kernel (bf16 D=64, 192/128; FP8 D=64 and D=128 past 16 rows per KV head) and the
+chunked-prefill path (prefill kernel over the page tables).
 """
 import math
 
@@ -72,6 +73,12 @@ def _cases():
         "general_d192_128": lambda: inputs.paged_case(
             2206, 3, 1, 8, 2, 192, 128, 32, lengths=[9, 333, 1100], poison=True,
             name="general_d192_128"),
+        "general_fp8_d64": lambda: inputs.fp8_paged_case(
+            2210, 3, 2, 8, 2, 64, 32, lengths=[1, 150, 1000], poison=True,
+            name="general_fp8_d64"),
+        "general_fp8_d128_32_rows": lambda: inputs.fp8_paged_case(
+            2211, 3, 4, 16, 2, 128, 64, lengths=[3, 420, 1300], poison=True,
+            name="general_fp8_d128_32_rows"),
         "chunked_prefill": lambda: inputs.paged_case(
             2207, 2, 128, 8, 2, 128, 128, 64, lengths=[200, 1500], poison=True,
             name="chunked_prefill"),
