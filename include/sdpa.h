@@ -222,7 +222,13 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  * The keys of each (b, KV head) are cut into num_splits contiguous chunks of
  * ceil(ceil(L/S)/page_size)*page_size keys; each chunk's normalized partial
  * (O_c, LSE_c) goes to the workspace and a second kernel merges them by LSE
- * (sdpa_splitkv_combine).  num_splits == 1 writes O/LSE directly and needs
+ * (sdpa_splitkv_combine).  One exception: with (d_qk, d_v) = (576, 512) and
+ * more than 16 query rows per KV head, when the chunks would give the GPU more
+ * than two work-groups per compute unit, m = floor(batch * h_kv * num_splits *
+ * ceil(rows / 128) / (2 * CUs)) adjacent chunks share one work-group: slot
+ * c * m holds the partial of chunks c*m .. c*m+m-1 together and the group's
+ * other slots are empty partials (LSE -inf, O not written).  The merge of all
+ * num_splits slots is the same attention either way ("fewer, longer splits").  num_splits == 1 writes O/LSE directly and needs
  * no workspace.  seq_lens need not be multiples of anything (v1.30.0 "New:
  * the FlashInfer serving path ...", split-KV kept for non-128-multiple KV max).
  *

@@ -7,7 +7,8 @@
 //   M = max_c LSE_c, LSE = M + ln sum_c exp(LSE_c - M),
 //   O = sum_c exp(LSE_c - LSE) * O_c; every split empty -> O = 0, LSE = -inf.
 // A split with LSE_c = -inf gets weight exactly 0 and its partial is not
-// read, so an empty split never contributes 0 * NaN.  With attention sinks
+// read (neither its bytes fetched nor its values used), so an empty split
+// never contributes 0 * NaN and costs no traffic.  With attention sinks
 // (decode with split-KV: v1.32.0 Release Notes, "SDPA: wider native forward
 // support", split-KV supports sinks) the sink of the row's head joins the
 // merge once, as one more term with no value: M = max(M, sink), the sum gains
@@ -33,10 +34,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ sinks, int hq,
                                                       int stats_log2) {
     __shared__ float w_s[4][kMaxSplits];
+    __shared__ float cw_s[4][kMaxSplits];  // the nonzero weights, in split order
+    __shared__ int ci_s[4][kMaxSplits];    // and their splits
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t row = (int64_t)blockIdx.x * 4 + wave;
     const bool valid = row < rows;  // no early return: every wave reaches the barrier
     float* w = w_s[wave];
+    float* cw = cw_s[wave];
+    int* ci = ci_s[wave];
+    int nz = 0;  // splits of nonzero weight (NaN counts as nonzero); uniform in the wave
     float lse_row = neg_inf();
     if (valid) {
         // row = (b * s_q + t) * hq + h: the sink of head h (natural-log units)
@@ -66,35 +72,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             for (int c = lane; c < splits; c += 64)
                 w[c] = fast_exp2((lse_part[(int64_t)c * rows + row] - lse_row) * kLog2e);
         }
+        // compact the splits whose partial is read (lane c % 64 wrote w[c])
+        const uint64_t below = (1ull << lane) - 1ull;
+        for (int c0 = 0; c0 < splits; c0 += 64) {
+            const int c = c0 + lane;
+            const bool keep = c < splits && w[c] != 0.f;
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+            if (keep) {
+                const int pos = nz + __builtin_popcountll(bal & below);
+                cw[pos] = w[c];
+                ci[pos] = c;
+            }
+            nz += __builtin_popcountll(bal);
+        }
     }
     __syncthreads();
     if (!valid) return;
     if (vec) {  // d_v % 4 == 0, o_part 16-byte and o 8/16-byte aligned
-        // 4 columns per lane and step; the loads of 8 splits are issued
-        // together (unconditionally: a split of weight 0 is dropped by a
-        // select, so its partial -- possibly never written -- cannot leak in)
+        // 4 columns per lane and step over the splits of nonzero weight
+        // only, in split order; the loads of 8 of them are issued together
         const f32x4* src = reinterpret_cast<const f32x4*>(o_part) + row * (dv / 4);
         const int64_t cstride = rows * (dv / 4);
         for (int n4 = lane; n4 < dv / 4; n4 += 64) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            int c = 0;
-            for (; c + 8 <= splits; c += 8) {
+            int k = 0;
+            for (; k + 8 <= nz; k += 8) {
                 f32x4 x[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)(c + j) * cstride + n4];
+                for (int j = 0; j < 8; ++j) x[j] = src[(int64_t)ci[k + j] * cstride + n4];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float wc = w[c + j];
-                    const f32x4 t = acc + wc * x[j];
-                    acc = wc != 0.f ? t : acc;
-                }
+                for (int j = 0; j < 8; ++j) acc = acc + cw[k + j] * x[j];
             }
-            for (; c < splits; ++c) {
-                const float wc = w[c];
-                const f32x4 x = src[(int64_t)c * cstride + n4];
-                const f32x4 t = acc + wc * x;
-                acc = wc != 0.f ? t : acc;
-            }
+            for (; k < nz; ++k) acc = acc + cw[k] * src[(int64_t)ci[k] * cstride + n4];
             if (OUT_F32) {
                 reinterpret_cast<f32x4*>(o)[row * (dv / 4) + n4] = acc;
             } else {
@@ -107,10 +116,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     } else {
         for (int n = lane; n < dv; n += 64) {
             float acc = 0.f;
-            for (int c = 0; c < splits; ++c) {
-                const float wc = w[c];
-                if (wc != 0.f) acc = fmaf(wc, o_part[((int64_t)c * rows + row) * dv + n], acc);
-            }
+            for (int k = 0; k < nz; ++k)
+                acc = fmaf(cw[k], o_part[((int64_t)ci[k] * rows + row) * dv + n], acc);
             if (OUT_F32)
                 static_cast<float*>(o)[row * dv + n] = acc;
             else

@@ -31,6 +31,15 @@
 //   reads of a wave owning whole rows.
 // The chunk's normalized partial (O_c, LSE_c) goes to the split workspace,
 // or O / LSE directly when num_splits == 1.
+//
+// Fewer, longer chunks: each work-group carries a fixed cost of about eight
+// tiles (the length rank, page ids, Q and the first K/V tiles before its
+// first MFMA; the partial's stores after its last), and one work-group per
+// CU runs at a time.  When num_splits would give more than two work-groups
+// per CU, `merge` adjacent chunks go to one work-group: it computes the
+// partial of their union into the slot of the first and marks the others
+// empty (LSE -inf, O not written; the LSE merge neither reads nor weighs
+// them), so the merge over all num_splits slots is the same attention.
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 #include "tile_ops.h"
@@ -49,6 +58,8 @@ struct WideArgs {
     int32_t table_stride;
     const int32_t* seq_lens;
     int32_t batch, sq, hq, hkv, group, page, splits;
+    int32_t merge;    // adjacent chunks per work-group (>= 1)
+    int32_t n_cg;     // ceil(splits / merge) chunk groups per (sequence, KV head)
     int32_t rows;     // s_q * group query rows per KV head
     int32_t n_rb;     // 128-row blocks per KV head
     int32_t n_g;      // batch * hkv * splits chunks
@@ -153,14 +164,14 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // chunk g = (b, kvh, split); the n_rb row blocks of a chunk are 8 work-
+    // chunk group g = (b, kvh, cg); the n_rb row blocks of a group are 8 work-
     // groups apart, i.e. on the same XCD (work-group i runs on XCD i % 8)
     const int bid = blockIdx.x;
     const int g = (bid / (8 * a.n_rb)) * 8 + bid % 8;
     const int rb = (bid / 8) % a.n_rb;
     if (g >= a.n_g) return;
-    const int split = g % a.splits;
-    const int bk = g / a.splits;
+    const int cg = g % a.n_cg;  // chunk group: chunks cg * merge .. + merge - 1
+    const int bk = g / a.n_cg;
     const int kvh = bk % a.hkv;
     // the (bk / hkv)-th longest sequence (ties by index): work-groups are
     // dispatched about in index order, so the longest chunks start first and
@@ -205,8 +216,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     if (a.splits > 1) {
         const int per = (L - base + a.splits - 1) / a.splits;
         const int chunk = ((per + a.page - 1) / a.page) * a.page;
-        lo = min(L, base + split * chunk);
-        hi = min(L, lo + chunk);
+        lo = min(L, base + cg * a.merge * chunk);
+        hi = min(L, lo + a.merge * chunk);
     }
 
     // rows of this lane / wave / work-group
@@ -552,10 +563,14 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     auto row_global = [&](int rr) {  // (b, token, head) row of row rr of this KV head
         return (int64_t)(b * a.sq + rr / a.group) * a.hq + kvh * a.group + rr % a.group;
     };
+    const int slot = cg * a.merge;  // workspace slot of the group's partial
     if (row_ok && half == 0) {
         const int64_t row_g = row_global(r);
         if (a.splits > 1) {
-            a.lse_part[(int64_t)split * rows_all + row_g] = lse;
+            a.lse_part[(int64_t)slot * rows_all + row_g] = lse;
+            // the group's other chunks are empty slots
+            for (int c = slot + 1; c < min(a.splits, slot + a.merge); ++c)
+                a.lse_part[(int64_t)c * rows_all + row_g] = neg_inf();
         } else if (a.lse != nullptr) {
             a.lse[row_g] = lse;
         }
@@ -600,7 +615,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         }
     };
     if (a.splits > 1) {
-        float* const op = a.o_part + (int64_t)split * rows_all * DV;
+        float* const op = a.o_part + (int64_t)slot * rows_all * DV;
         write_rows([&](int64_t row_g, int n, f32x4 w) __attribute__((always_inline)) {
             *reinterpret_cast<f32x4*>(op + row_g * DV + n) = w;
         });
@@ -646,7 +661,19 @@ hipError_t launch_decode_wide(const DecodeArgs& d, hipStream_t s) {
     a.splits = d.splits;
     a.rows = d.sq * a.group;
     a.n_rb = (a.rows + 127) / 128;
-    const int64_t n_g = (int64_t)d.batch * d.hkv * d.splits;
+    // chunks per work-group: enough that the grid holds about two work-groups per CU
+    a.merge = 1;
+    if (d.splits > 1) {
+        int dev = 0, n_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+            n_cu = 1;
+        const int64_t wgs = (int64_t)d.batch * d.hkv * d.splits * a.n_rb;
+        const int64_t m = wgs / (2 * (int64_t)n_cu);
+        a.merge = m < 1 ? 1 : (m > d.splits ? d.splits : (int32_t)m);
+    }
+    a.n_cg = (d.splits + a.merge - 1) / a.merge;
+    const int64_t n_g = (int64_t)d.batch * d.hkv * a.n_cg;
     a.n_g = (int32_t)n_g;
     a.c = (d.scale < 0.f ? -d.scale : d.scale) * kLog2e;
     a.q_sign = d.scale < 0.f ? 0x80008000u : 0u;

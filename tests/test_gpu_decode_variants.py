@@ -93,3 +93,47 @@ def test_absorbed_mla_aliased_cache_full_size_sampled():
     sel = sample_rows(rows, 96, 9, must=[0, rows - 1])
     kp = to_dev(pc.k_pool)
     parity(pc, sel_rows=sel, k_pool=kp, v_pool=kp[..., :512])
+
+
+# ---- fewer, longer chunks in the absorbed-MLA kernel ---------------------------------------
+# When num_splits would give more than two work-groups per CU, the 576/512 kernel gives
+# `merge` adjacent chunks to one work-group: slot cg * merge holds the partial of their union,
+# the group's other slots are empty (LSE -inf, O never written and never read by the merge).
+
+def mla_merge_factor(batch, splits, n_rb=2):
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    return max(1, min(splits, batch * splits * n_rb // (2 * n_cu)))
+
+
+@pytest.mark.parametrize("splits", [16, 17, 40])
+def test_mla_merged_chunks_partials_and_result(splits):
+    import numpy as np
+    import oracle
+    lengths = [int(x) for x in np.random.default_rng(2230 + splits).integers(1, 2600, 32)]
+    lengths[3] = 1   # a one-key sequence: every group but the first is empty
+    pc = inputs.paged_case(2230 + splits, 32, 2, 128, 1, 576, 512, 64, lengths=lengths,
+                           num_splits=splits, poison=True, name="mla_merge")
+    m = mla_merge_factor(pc.batch, splits)
+    log("MLA merged chunks: splits=%d merge=%d lens=%s" % (splits, m, lengths[:6]))
+    rows = pc.batch * pc.sq * pc.hq
+    need = sdpa.decode_workspace_bytes(pc.batch, pc.sq, pc.hq, 512, splits)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN-patterned
+    o, l = sdpa.decode_paged(to_dev(pc.q), to_dev(pc.k_pool), to_dev(pc.v_pool), to_dev(pc.pt_k),
+                             to_dev(pc.pt_v), to_dev(pc.seq_lens), pc.max_kv, pc.scale,
+                             pc.causal, num_splits=splits, workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref, op_ref, lp_ref = oracle_decode(pc, num_splits=splits, want_partials=True)
+    check_o(o, o_ref)
+    check_lse(l, l_ref)
+    o_bytes = ((splits * rows * 512 * 4 + 255) // 256) * 256
+    o_part = ws[:splits * rows * 512 * 4].view(torch.float32).view(splits, rows, 512)
+    lse_part = ws[o_bytes:o_bytes + splits * rows * 4].view(torch.float32).view(splits, rows)
+    for c0 in range(0, splits, m):
+        group = list(range(c0, min(splits, c0 + m)))
+        # the union's partial = the oracle's LSE merge of the group's chunk partials
+        og, lg = oracle.combine(op_ref[group], lp_ref[group])
+        check_lse(lse_part[c0], lg, "LSE partial of chunks %s" % group)
+        live = np.isfinite(lg)
+        check_o(o_part[c0][torch.from_numpy(live).cuda()], og[live], "O partial of chunks %s" % group)
+        for c in group[1:]:
+            assert torch.all(lse_part[c] == float("-inf")), "slot %d of a merged group" % c
