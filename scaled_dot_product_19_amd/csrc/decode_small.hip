@@ -136,6 +136,11 @@ __device__ __forceinline__ uint32_t own_ticket(uint64_t* ctr, uint64_t old, uint
 // Fourth word of a raw buffer resource on gfx9-family parts (CDNA): no
 // swizzle, 32-bit data format; the range check returns zeros past num_records.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy of the K/V loads: nontemporal (the nt bit).  Every K/V byte
+// is read once per call, so keeping it in the caches only evicts other data:
+// on an MI355X the paged decode workload ran at 75 % of HBM with nt loads
+// against 69 % without (and a plain 4.45 GB read kernel at 92 % against 80 %).
+constexpr int kStream = 2;
 
 // Load of a kernel-invariant int32 (page table, lengths) at a wave-uniform
 // index through the constant address space, so it becomes a scalar load.
@@ -296,7 +301,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
 #pragma unroll
             for (int kl = 0; kl < C::KL; ++kl)
                 r.k[sb][kl] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.k[sb], k_off + 64 * kl, 0, 0));
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.k[sb], k_off + 64 * kl, 0, kStream));
         }
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
@@ -305,10 +310,10 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             for (int e = 0; e < 4; ++e) {
                 if constexpr (F8)
                     r.v[u][e] = __builtin_bit_cast(
-                        uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.v[sb], v_off[u], e * v_st2, 0));
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.v[sb], v_off[u], e * v_st2, kStream));
                 else
                     r.v[u][e] = __builtin_bit_cast(
-                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v[sb], v_off[u], e * v_st2, 0));
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v[sb], v_off[u], e * v_st2, kStream));
             }
         }
     };

@@ -277,7 +277,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     // and K, each right after the barrier that frees its slot: spread between
     // the MFMAs, the data arriving in LDS throughout slows every phase's
     // operand reads more.  A tile at or past the end gets an empty buffer
-    // range: its DMA writes zeros and reads nothing.
+    // range: its DMA writes zeros and reads nothing.  The loads are
+    // nontemporal: 2 % faster on the MLA decode workload than cached ones.
     struct DmaPlan {
         u32x4 kr, vr;
         uint32_t st;
@@ -305,14 +306,14 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     auto k_piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
         if (j < C::RPW) {
             const int row = wave * C::RPW + j;
-            dma16(d.kr, d.st + row * C::KA_PITCH, add_here(l16, (uint32_t)row * k_st2));
+            dma16_stream(d.kr, d.st + row * C::KA_PITCH, add_here(l16, (uint32_t)row * k_st2));
         } else {
-            dma16(d.kr, d.st + C::KB_OFF + wave * 1024, kb_src);
+            dma16_stream(d.kr, d.st + C::KB_OFF + wave * 1024, kb_src);
         }
     };
     auto v_piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
         const int row = wave * C::RPW + j;
-        dma16(d.vr, d.st + C::V_OFF + row * C::VROW_B,
+        dma16_stream(d.vr, d.st + C::V_OFF + row * C::VROW_B,
               xor_add_here(l16, 64u * (uint32_t)(row & 3), (uint32_t)row * v_st2));
     };
     // the ring's first tiles: K and V of tile 0, K of tile 1

@@ -877,8 +877,11 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             const int r = j * RPI + lane / OCPR;
             const uint4 w = *reinterpret_cast<const uint4*>(ow + r * OROW_B + 16 * (rc ^ (r & (OCPR - 1))));
             if (i0 + r < lq) {
+                // nontemporal: O is not read again by this call, and cached
+                // dirty lines would be written back while later items stream
+                // K/V (2 % on the THD prefill workload)
                 bf16_t* orow = a.o + (int64_t)(q_beg + i0 + r) * a.o_st + (int64_t)h * a.o_sh;
-                *reinterpret_cast<uint4*>(orow + 8 * rc) = w;
+                __builtin_nontemporal_store(u32x4{w.x, w.y, w.z, w.w}, reinterpret_cast<u32x4*>(orow + 8 * rc));
             }
         }
     }

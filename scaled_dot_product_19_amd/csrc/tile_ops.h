@@ -88,6 +88,14 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds, int voff) {
                  : "s"(lds), "v"(voff), "s"(rsrc)
                  : "memory", "m0");
 }
+// The same with the nontemporal cache policy, for data read once per call
+// (decode K/V streams): it does not displace reused lines from the caches.
+__device__ __forceinline__ void dma16_stream(u32x4 rsrc, uint32_t lds, int voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Uniform 32-bit load through the scalar cache (read-only data).
