@@ -13,7 +13,9 @@ input already resident in HBM:
 Reported: prefill attention TFLOP/s (visible (row, key) pairs x 2 (Dqk + Dv))
 against the bf16 dense MFMA peak, and paged-decode KV GB/s against the HBM
 peak, each from HIP events recorded on the launch stream around every call
-of the timed steps.  Beside them, the fp64 CPU oracle timed on a bounded
+of the timed steps.  Every timed region starts with at least 100 ms of the
+same work, untimed, before its W warm-up steps, so the engine clock has left
+its idle state (the CPU-baseline legs leave the GPU idle for seconds).  Beside them, the fp64 CPU oracle timed on a bounded
 sample of the same workloads (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -251,6 +253,7 @@ def run_window_prefill(args, torch, inputs, sdpa, dev):
                                 lse_layout=sdpa.LSE_HEAD_MAJOR, lse_s_max=T, stats_log2=True,
                                 stream=stream)
 
+        prewarm(torch, step)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -308,6 +311,7 @@ def run_chunked_prefill(args, torch, inputs, sdpa, dev):
         sdpa.decode_paged(q, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, pc.causal,
                           num_splits=pc.num_splits, workspace=ws, out=o, lse=lse, stream=stream)
 
+    prewarm(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -378,6 +382,10 @@ def per_call_ms(torch, stream, call, steps, warmup, between=None):
     """Milliseconds of each of `steps` calls, from HIP events recorded on `stream` right
     before and after the call (after `warmup` untimed calls).  `between()` runs before
     every call, outside its events (e.g. a cache flush)."""
+    if between is None:
+        prewarm(torch, call)
+    else:
+        prewarm(torch, lambda: (between(), call()))
     for _ in range(warmup):
         if between is not None:
             between()
@@ -404,6 +412,25 @@ def ms_stats(ms):
 
 
 MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MiB MALL
+
+PREWARM_MS = 100.0  # untimed back-to-back work before every timed region
+
+
+def prewarm(torch, call, min_ms=PREWARM_MS):
+    """Run `call` back to back, untimed, for at least `min_ms` of wall time before the
+    warm-up steps.  After an idle gap (the CPU-baseline legs leave the GPU idle for seconds)
+    the engine clock takes tens of milliseconds of load to settle: on an MI355X the MLA
+    decode call ran 0.32 ms over its first 15 ms of back-to-back calls after 2 s idle and
+    0.274 ms from about 30 ms on."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        call()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= min_ms:
+                return
 
 
 def host_cpu_model():
@@ -435,6 +462,7 @@ def time_decode(torch, sdpa, pc, dev, steps, warmup, q=None, kp=None, vp=None):
         sdpa.decode_paged(q, kp, vp, ptk, ptv, sl, pc.max_kv, pc.scale, pc.causal,
                           num_splits=pc.num_splits, workspace=ws, out=o, lse=lse, stream=stream)
 
+    prewarm(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -466,6 +494,7 @@ def time_decode_fp8(torch, sdpa, pc, dev, steps, warmup):
                               causal=pc.causal, num_splits=pc.num_splits, workspace=ws, out=o,
                               lse=lse, stream=stream)
 
+    prewarm(torch, step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -543,6 +572,7 @@ def run_decode_variant(args, torch, inputs, sdpa, dev):
 
 def time_prefill(torch, steps, warmup, call):
     """Average ms of `call` (one prefill launch) over `steps` back-to-back launches."""
+    prewarm(torch, call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -827,6 +857,7 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    prewarm(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
