@@ -17,9 +17,14 @@
 //   - K goes straight from HBM into the MFMA A-operand registers
 //     (S^T = K Q^T: lane (key, d-group) loads 16 contiguous bytes of its key
 //     row), no LDS;
-//   - V is loaded row-coalesced (16 lanes read one 256-byte row), transposed
-//     in registers and written to a wave-private LDS tile V^T[n][key], from
-//     which the second MFMA (O^T += V^T P^T) reads its A operand;
+//   - V is loaded row-coalesced (16 lanes read one 256-byte row) and stored
+//     as it is to a wave-private LDS tile (rows padded by 32 bytes, so the
+//     4 rows x 32 bytes one 16-lane group reads below fall in distinct
+//     banks); the second MFMA (O^T += V^T P^T) reads its A operand with
+//     ds_read_b64_tr_b16, which hands each lane 4 consecutive keys of one
+//     column (an earlier version transposed V in registers with v_perm and
+//     wrote V^T: 16 more VALU and twice the LDS writes per 4 x 8 unit; the
+//     FP8 decode workload ran 0.496 ms with it, 0.431 ms without);
 //   - the next tile's loads are issued before the current tile is computed
 //     (register double buffer) and page ids are fetched two tiles ahead with
 //     scalar loads, so a wave keeps 16 KB in flight.
@@ -27,12 +32,13 @@
 // Per-tensor FP8 (E4M3) instantiation (F8): Q, K and V are E4M3 codes that
 // stand for descale_{q,k,v} times their values (cuDNN Frontend v1.31.0
 // Release Notes, per-tensor FP8 D128 paged KV; v1.32.0 "SDPA: wider native
-// forward support", paged per-tensor FP8 D256).  A tile holds twice the keys
-// (the same 16 KB in flight); S^T = K Q^T runs on the FP8 MFMA
+// forward support", paged per-tensor FP8 D256).  A tile holds the same keys
+// as in bf16 at D = 128 (8 KB in flight) and twice the keys at D = 256 (16 KB
+// in flight); S^T = K Q^T runs on the FP8 MFMA
 // (v_mfma_f32_16x16x32_fp8_fp8, FP32 accumulator; its dot products are not
 // fp32-exact, up to ~4e-5 of the sum of |products| off) with
 // scale * descale_q * descale_k folded into the exponent; V codes are widened
-// exactly to bf16 on their way into the V^T tile, so P V stays on the bf16
+// exactly to bf16 on their way into the V tile, so P V stays on the bf16
 // MFMA with P in bf16, and descale_v multiplies the normalized output.
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
@@ -151,14 +157,16 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t i) {
 template <int D, bool F8>
 struct SmallCfg {
     static constexpr int EB = F8 ? 1 : 2;    // bytes per stored element
-    static constexpr int TK = 8192 / (EB * D);  // keys per wave tile (8 KB of K)
+    // keys per wave tile: 8 KB of K; 4 KB for E4M3 at D = 128 (32 keys: the
+    // FP8 decode workload ran 0.416 ms with them against 0.435 ms with 64)
+    static constexpr int TK = (F8 && D <= 128 ? 4096 : 8192) / (EB * D);
     static constexpr int SB = TK / 16;       // 16-key sub-blocks per tile
     static constexpr int KK = D / 32;        // k-steps of S^T = K Q^T
     static constexpr int KL = EB * D / 64;   // 16-byte K loads per lane and sub-block
     static constexpr int NB = D / 16;        // 16-row blocks of O^T
-    static constexpr int VP = TK + 4;        // V^T LDS pitch in elements
+    static constexpr int VR = D + 16;        // V row pitch in LDS (elements): 32 bytes of pad
     static constexpr int VU = TK * D / 32 / 64;  // V units (4 keys x 8 columns) per lane
-    static constexpr int WAVE_LDS = D * VP;  // elements of one wave's V^T tile
+    static constexpr int WAVE_LDS = TK * VR;  // elements of one wave's V tile
     static constexpr int MERGE_BYTES = kWaves * 16 * D * 4 + 2 * kWaves * 16 * 4;
     static constexpr int LDS_BYTES =
         (kWaves * WAVE_LDS * 2 > MERGE_BYTES) ? kWaves * WAVE_LDS * 2 : MERGE_BYTES;
@@ -319,7 +327,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     };
     auto compute = [&](int t, const TileRegs<D, F8>& r) {
         const int key0 = lo + t * C::TK;
-        // V rows -> V^T[n][key] in this wave's LDS tile (E4M3 rows widened to bf16 first)
+        // V rows -> this wave's LDS tile, row-major (E4M3 rows widened to bf16 first)
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
             const int kt = v_kt[u];
@@ -331,21 +339,9 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
                 else
                     vr[e] = r.v[u][e];
             }
-            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[0]);
-            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[1]);
-            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[2]);
-            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[3]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint2 even, odd;
-                even.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x05040100u);
-                even.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x05040100u);
-                odd.x = __builtin_amdgcn_perm(w1[j], w0[j], 0x07060302u);
-                odd.y = __builtin_amdgcn_perm(w3[j], w2[j], 0x07060302u);
-                const int n = 8 * v_n8[u] + 2 * j;
-                *reinterpret_cast<uint2*>(vt + n * C::VP + kt) = even;
-                *reinterpret_cast<uint2*>(vt + (n + 1) * C::VP + kt) = odd;
-            }
+            for (int e = 0; e < 4; ++e)
+                *reinterpret_cast<uint4*>(vt + (kt + e) * C::VR + 8 * v_n8[u]) = vr[e];
         }
         // S^T = K Q^T: s[sb][r] is key key0 + 16 sb + 4 g + r of query c
         f32x4 s[C::SB];
@@ -399,19 +395,22 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
         l = l * alpha + lsum;
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) acc[nb] *= alpha;
-        // the V^T stores of all lanes land before any lane reads them
+        // the V stores of all lanes land before any lane reads them
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // O^T += V^T P^T: A = V^T[n = 16 nb + c][keys 16 sb + 4 g .. +4]
+        // O^T += V^T P^T: A = V^T[n = 16 nb + c][keys 16 sb + 4 g .. +4], read
+        // transposed from the row-major tile
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
 #pragma unroll
             for (int sb = 0; sb < C::SB; ++sb) {
-                const s16x4 va =
-                    *reinterpret_cast<const s16x4*>(vt + (16 * nb + c) * C::VP + 16 * sb + 4 * g);
+                // lane (c, g) addresses row 16 sb + 4 g + c / 4, columns 16 nb + 4 (c % 4)
+                // .. +3 and receives column 16 nb + c of rows 16 sb + 4 g .. +3
+                const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vt + (16 * sb + 4 * g + c / 4) * C::VR + 16 * nb + 4 * (c % 4)));
                 acc[nb] = mfma16_k16(va, pb[sb], acc[nb]);
             }
         }
-        // keep the next tile's V^T stores behind this tile's reads
+        // keep the next tile's V stores behind this tile's reads
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
 
@@ -443,7 +442,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     // ---- merge the four waves by LSE and store -----------------------------
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    __syncthreads();  // every wave is done with its V^T tile
+    __syncthreads();  // every wave is done with its V tile
     float* red_o = reinterpret_cast<float*>(smem);              // [wave][q][n]
     float* red_m = red_o + kWaves * 16 * D;                      // [wave][q]
     float* red_l = red_m + kWaves * 16;                          // [wave][q]
@@ -557,7 +556,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
         const int b = ranked ? by_len[r] : r;
         const int kvh = rem / a.splits, split = rem - (rem / a.splits) * a.splits;
         const int nxt = decode_unit<D, F8>(a, smem, b, kvh, split, &ctr[0], &next_unit, next_of);
-        __syncthreads();  // the merge's LDS reads are done before the next unit's V^T stores
+        __syncthreads();  // the merge's LDS reads are done before the next unit's V stores
         unit = nxt;
     }
     if (threadIdx.x == 0 && own_ticket(&ctr[1], ticket_async(&ctr[1]), a.gen) == gridDim.x - 1) {
