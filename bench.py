@@ -414,6 +414,7 @@ def ms_stats(ms):
 MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MiB MALL
 
 PREWARM_MS = 100.0  # untimed back-to-back work before every timed region
+PREWARM_CALLS = []  # calls each pre-warm made, in the order of the timed regions
 
 
 def prewarm(torch, call, min_ms=PREWARM_MS):
@@ -430,6 +431,7 @@ def prewarm(torch, call, min_ms=PREWARM_MS):
         if n % 8 == 0:
             torch.cuda.synchronize()
             if (time.perf_counter() - t0) * 1e3 >= min_ms:
+                PREWARM_CALLS.append(n)  # lets a kernel trace find the timed launches
                 return
 
 
@@ -698,13 +700,20 @@ def mla_leg(args, torch, inputs, sdpa, dev, stream, threads):
     gbs = comp / (st["mean"] * 1e-3) / 1e9
     tf = flops / (st["mean"] * 1e-3) / 1e12
     rows = pc.batch * pc.sq * pc.hq
-    part_bytes = 2 * pc.num_splits * rows * (512 + 1) * 4  # fp32 partials written + read back
+    # the library gives `merge` adjacent chunks to one work-group when the chunks would
+    # make more than two work-groups per CU; the other slots of a group hold an empty
+    # partial (its LSE only).  fp32 partials written + read back:
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    n_rb = (pc.sq * (pc.hq // pc.hkv) + 127) // 128
+    merge = max(1, min(pc.num_splits, pc.batch * pc.hkv * pc.num_splits * n_rb // (2 * n_cu)))
+    slots = (pc.num_splits + merge - 1) // merge
+    part_bytes = 2 * rows * (slots * 512 + pc.num_splits) * 4
     log("%s: %.4f ms mean (median %.4f, min %.4f) -> %.1f GB/s compulsory (%.1f%% of HBM), "
         "%.1f TFLOP/s (%.1f%% of bf16 MFMA)" % (pc.name, st["mean"], st["median"], st["min"], gbs,
                                                  100 * gbs / PEAK_HBM_GBS, tf,
                                                  100 * tf / PEAK_BF16_TFLOPS))
     leg = {"workload": pc.name, "kv_bytes": kv, "compulsory_bytes": comp,
-           "split_partial_bytes": part_bytes, "flop": flops, "ms": st,
+           "split_partial_bytes": part_bytes, "chunks_per_work_group": merge, "flop": flops, "ms": st,
            "value": round(kv / (st["mean"] * 1e-3) / 1e9, 1), "unit": "GB/s",
            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
            "roofline": {"kernel": "decode_wide_kernel<576, 512> + combine_kernel<false>",
@@ -989,6 +998,7 @@ def main():
         "host_cpu": {"model": host_cpu_model(), "threads_used": threads},
     }
     line.update(extra)
+    line["prewarm_calls"] = PREWARM_CALLS
     print(json.dumps(line), flush=True)
 
 
