@@ -1,5 +1,6 @@
 // decode_small.hip -- paged-KV decode for few query rows per KV head
-// (s_q * G <= 16), e.g. single-token GQA decode: the HBM-streaming case.
+// (s_q * G <= 16) at d_qk = d_v in {64, 128, 256}, e.g. single-token GQA
+// decode: the HBM-streaming case.
 //
 // Same result as decode_paged.hip (per (b, KV head, split): the normalized
 // partial O_c and its natural-log LSE_c over the chunk's visible keys, read
@@ -313,15 +314,27 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
         }
 #pragma unroll
         for (int u = 0; u < C::VU; ++u) {
-            const int sb = (64 * u) / (D / 2);   // uniform: every lane's unit is in this sub-block
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            // the 16-key sub-block of this lane's unit: one per 64 lanes for D >= 128;
+            // at D = 64 a sub-block holds 32 units, so lanes 32..63 read the next one
+            const int sb = (64 * u) / (D / 2);
+            auto vload = [&](const __amdgpu_buffer_rsrc_t& rv, int e) {
                 if constexpr (F8)
                     r.v[u][e] = __builtin_bit_cast(
-                        uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.v[sb], v_off[u], e * v_st2, kStream));
+                        uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off[u], e * v_st2, kStream));
                 else
                     r.v[u][e] = __builtin_bit_cast(
-                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v[sb], v_off[u], e * v_st2, kStream));
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[u], e * v_st2, kStream));
+            };
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (D / 2 >= 64) {
+                    vload(rs.v[sb], e);
+                } else {
+                    if (lane < 32)
+                        vload(rs.v[sb], e);
+                    else
+                        vload(rs.v[sb + 1], e);
+                }
             }
         }
     };
@@ -597,7 +610,7 @@ hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
 }  // namespace
 
 bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows) {
-    return dqk == dv && (dqk == 128 || dqk == 256) && rows <= 16;
+    return dqk == dv && (dqk == 64 || dqk == 128 || dqk == 256) && rows <= 16;
 }
 
 hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
@@ -644,12 +657,14 @@ hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
     a.stats_log2 = da.stats_log2;
     if (da.fp8) {
         switch (da.dqk) {
+            case 64: return launch_small_d<64, true>(a, s);
             case 128: return launch_small_d<128, true>(a, s);
             case 256: return launch_small_d<256, true>(a, s);
             default: return hipErrorInvalidValue;
         }
     }
     switch (da.dqk) {
+        case 64: return launch_small_d<64, false>(a, s);
         case 128: return launch_small_d<128, false>(a, s);
         case 256: return launch_small_d<256, false>(a, s);
         default: return hipErrorInvalidValue;

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from scaled_dot_product_19_amd import inputs, sdpa
-from tests.helpers import check_lse, check_o, log, oracle_decode, to_dev
+from tests.helpers import check_lse, check_o, log, oracle_decode, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +66,7 @@ def test_mla_576_512_two_tokens_causal(splits):
 
 
 @pytest.mark.parametrize("shape", [(64, 64, 4, 4, 3, False), (64, 64, 2, 1, 1, True),
+                                   (64, 64, 16, 1, 1, True), (64, 64, 32, 1, 2, True),
                                    (256, 256, 8, 2, 2, True), (128, 128, 64, 4, 1, True),
                                    (128, 128, 16, 1, 4, True)])
 def test_other_head_shapes(shape):
@@ -149,3 +150,18 @@ def test_mla_late_large_logit_takes_second_pass():
     pc.k_pool[page, key % pc.page_size, 0] = (1.5 * pc.q[0, 1, 3].float()).to(pc.k_pool.dtype)
     o, l, o_ref, l_ref = parity(pc)
     assert float(l[0, 1, 3]) > 30.0
+
+
+def test_d64_decode_workload_sampled():
+    # the paged decode workload's shape at D = 64 (B = 64, 32/8 heads, page 64,
+    # L U[512, 32768], 8 splits): the few-row kernel's D = 64 instantiation
+    pc = inputs.paged_case(inputs.SEED_BASE + 3, 64, 1, 32, 8, 64, 64, 64, lo=512, hi=32768,
+                           num_splits=8, poison=True, name="paged_decode_d64")
+    o, l = run(pc)
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 192, 64, must=[0, rows - 1])
+    o_ref, l_ref = oracle_decode(pc, sel_rows=sel)
+    si = torch.from_numpy(sel).cuda()
+    check_o(o.reshape(rows, -1)[si], o_ref)
+    check_lse(l.reshape(rows)[si], l_ref)
+    assert torch.isfinite(o.float()).all()

@@ -1,7 +1,7 @@
 """GPU parity of sdpa_decode_paged_ex (left sliding window, attention sinks, base-2 Stats)
-against the fp64 oracle, through every paged-decode kernel: the few-row kernel (bf16 D=128,
-D=256 and per-tensor FP8), the absorbed-MLA wide kernel (576/512), the general decode
-kernel (bf16 D=64, 192/128; FP8 D=64 and D=128 past 16 rows per KV head) and the
+against the fp64 oracle, through every paged-decode kernel: the few-row kernel (bf16 D=64, 128, 256 and per-tensor
+FP8), the absorbed-MLA wide kernel (576/512), the general decode kernel (bf16 D=64 past 16
+rows per KV head, 192/128; FP8 D=64 and D=128 past 16 rows per KV head) and the
 chunked-prefill path (prefill kernel over the page tables).
 """
 import math
@@ -67,9 +67,12 @@ def _cases():
         "wide_mla": lambda: inputs.paged_case(
             2204, 3, 2, 128, 1, 576, 512, 64, lengths=[3, 700, 1500], poison=True,
             name="wide_mla"),
-        "general_d64": lambda: inputs.paged_case(
+        "few_row_d64": lambda: inputs.paged_case(
             2205, 3, 3, 4, 4, 64, 64, 32, lengths=[2, 77, 900], poison=True,
-            name="general_d64"),
+            name="few_row_d64"),
+        "general_d64_32_rows": lambda: inputs.paged_case(
+            2212, 3, 4, 16, 2, 64, 64, 32, lengths=[3, 190, 1200], poison=True,
+            name="general_d64_32_rows"),
         "general_d192_128": lambda: inputs.paged_case(
             2206, 3, 1, 8, 2, 192, 128, 32, lengths=[9, 333, 1100], poison=True,
             name="general_d192_128"),
