@@ -155,20 +155,22 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p, int64_t i) {
     return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
-template <int D, bool F8>
+// D: the Q/K head dim; DV: the V/O head dim
+template <int D, bool F8, int DV = D>
 struct SmallCfg {
     static constexpr int EB = F8 ? 1 : 2;    // bytes per stored element
-    // keys per wave tile: 8 KB of K; 4 KB for E4M3 at D = 128 (32 keys: the
-    // FP8 decode workload ran 0.416 ms with them against 0.435 ms with 64)
-    static constexpr int TK = (F8 && D <= 128 ? 4096 : 8192) / (EB * D);
+    // keys per wave tile: about 8 KB of K, in whole 16-key sub-blocks; 4 KB for
+    // E4M3 at D <= 128 (32 keys at D = 128: the FP8 decode workload ran 0.416 ms
+    // with them against 0.435 ms with 64)
+    static constexpr int TK = (F8 && D <= 128 ? 4096 : 8192) / (EB * D) / 16 * 16;
     static constexpr int SB = TK / 16;       // 16-key sub-blocks per tile
     static constexpr int KK = D / 32;        // k-steps of S^T = K Q^T
     static constexpr int KL = EB * D / 64;   // 16-byte K loads per lane and sub-block
-    static constexpr int NB = D / 16;        // 16-row blocks of O^T
-    static constexpr int VR = D + 16;        // V row pitch in LDS (elements): 32 bytes of pad
-    static constexpr int VU = TK * D / 32 / 64;  // V units (4 keys x 8 columns) per lane
+    static constexpr int NB = DV / 16;       // 16-row blocks of O^T
+    static constexpr int VR = DV + 16;       // V row pitch in LDS (elements): 32 bytes of pad
+    static constexpr int VU = TK * DV / 32 / 64;  // V units (4 keys x 8 columns) per lane
     static constexpr int WAVE_LDS = TK * VR;  // elements of one wave's V tile
-    static constexpr int MERGE_BYTES = kWaves * 16 * D * 4 + 2 * kWaves * 16 * 4;
+    static constexpr int MERGE_BYTES = kWaves * 16 * DV * 4 + 2 * kWaves * 16 * 4;
     static constexpr int LDS_BYTES =
         (kWaves * WAVE_LDS * 2 > MERGE_BYTES) ? kWaves * WAVE_LDS * 2 : MERGE_BYTES;
     static_assert(SB >= 1 && VU >= 1, "tile shape");
@@ -176,20 +178,20 @@ struct SmallCfg {
 
 // One wave's registers for one tile: K operands and raw V rows (8 columns of
 // 4 keys per unit: 16 bytes a row in bf16, 8 in E4M3).
-template <int D, bool F8>
+template <int D, bool F8, int DV>
 struct TileRegs {
-    uint4 k[SmallCfg<D, F8>::SB][SmallCfg<D, F8>::KL];
-    typename std::conditional<F8, uint2, uint4>::type v[SmallCfg<D, F8>::VU][4];
+    uint4 k[SmallCfg<D, F8, DV>::SB][SmallCfg<D, F8, DV>::KL];
+    typename std::conditional<F8, uint2, uint4>::type v[SmallCfg<D, F8, DV>::VU][4];
 };
 
 // One unit: the keys of split `split` of sequence b for KV head kvh.  The
 // next unit's ticket (lane 0 of wave 0) is requested at the start and turned
 // into next_unit during the merge; returns that unit (-1: none left).
-template <int D, bool F8, class NextOf>
+template <int D, bool F8, int DV, class NextOf>
 __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, bf16_t* smem, const int b,
                                                           const int kvh, const int split, uint64_t* ctr,
                                                           int* next_unit, NextOf&& next_of) {
-    using C = SmallCfg<D, F8>;
+    using C = SmallCfg<D, F8, DV>;
     constexpr int EB = C::EB;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -273,8 +275,8 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
 #pragma unroll
     for (int u = 0; u < C::VU; ++u) {
         const int unitv = lane + 64 * u;
-        v_n8[u] = unitv % (D / 8);
-        v_kt[u] = 4 * (unitv / (D / 8));           // first key of the unit in the tile
+        v_n8[u] = unitv % (DV / 8);
+        v_kt[u] = 4 * (unitv / (DV / 8));           // first key of the unit in the tile
         v_off[u] = (v_kt[u] & 15) * v_st2 + 8 * EB * v_n8[u];
     }
 
@@ -295,7 +297,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             const int32_t pk = load_uniform(ptk, pidx);
             const int32_t pv = load_uniform(ptv, pidx);
             const int k_bytes = nvalid > 0 ? (nvalid - 1) * k_st2 + EB * D : 0;
-            const int v_bytes = nvalid > 0 ? (nvalid - 1) * v_st2 + EB * D : 0;
+            const int v_bytes = nvalid > 0 ? (nvalid - 1) * v_st2 + EB * DV : 0;
             rs.k[sb] = __builtin_amdgcn_make_buffer_rsrc(
                 (void*)(kbase + (int64_t)pk * k_sp2 + (int64_t)slot * k_st2), (short)0, k_bytes,
                 kRsrcWord3);
@@ -304,7 +306,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
                 kRsrcWord3);
         }
     };
-    auto issue = [&](const Rsrc& rs, TileRegs<D, F8>& r) {
+    auto issue = [&](const Rsrc& rs, TileRegs<D, F8, DV>& r) {
 #pragma unroll
         for (int sb = 0; sb < C::SB; ++sb) {
 #pragma unroll
@@ -316,7 +318,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
         for (int u = 0; u < C::VU; ++u) {
             // the 16-key sub-block of this lane's unit: one per 64 lanes for D >= 128;
             // at D = 64 a sub-block holds 32 units, so lanes 32..63 read the next one
-            const int sb = (64 * u) / (D / 2);
+            const int sb = (64 * u) / (DV / 2);
             auto vload = [&](const __amdgpu_buffer_rsrc_t& rv, int e) {
                 if constexpr (F8)
                     r.v[u][e] = __builtin_bit_cast(
@@ -327,7 +329,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             };
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                if constexpr (D / 2 >= 64) {
+                if constexpr (DV / 2 >= 64) {
                     vload(rs.v[sb], e);
                 } else {
                     if (lane < 32)
@@ -338,7 +340,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             }
         }
     };
-    auto compute = [&](int t, const TileRegs<D, F8>& r) {
+    auto compute = [&](int t, const TileRegs<D, F8, DV>& r) {
         const int key0 = lo + t * C::TK;
         // V rows -> this wave's LDS tile, row-major (E4M3 rows widened to bf16 first)
 #pragma unroll
@@ -432,7 +434,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     // the top: r0 holds (or is loading) tile t, ra is the resource set of
     // tile t + 4.
     {
-        TileRegs<D, F8> r0, r1;
+        TileRegs<D, F8, DV> r0, r1;
         Rsrc ra, rb;
         int t = wave;
         make_rsrc(t, rb);
@@ -457,11 +459,11 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     l += __shfl_xor(l, 32, 64);
     __syncthreads();  // every wave is done with its V tile
     float* red_o = reinterpret_cast<float*>(smem);              // [wave][q][n]
-    float* red_m = red_o + kWaves * 16 * D;                      // [wave][q]
+    float* red_m = red_o + kWaves * 16 * DV;                     // [wave][q]
     float* red_l = red_m + kWaves * 16;                          // [wave][q]
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
-        *reinterpret_cast<f32x4*>(red_o + (wave * 16 + c) * D + 16 * nb + 4 * g) = acc[nb];
+        *reinterpret_cast<f32x4*>(red_o + (wave * 16 + c) * DV + 16 * nb + 4 * g) = acc[nb];
     if (g == 0) {
         red_m[wave * 16 + c] = m;
         red_l[wave * 16 + c] = l;
@@ -474,9 +476,9 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     }
     __syncthreads();
     const int nxt = *next_unit;
-    const int items = a.rows * (D / 4);
+    const int items = a.rows * (DV / 4);
     for (int it = threadIdx.x; it < items; it += 256) {
-        const int q = it / (D / 4), n = 4 * (it % (D / 4));
+        const int q = it / (DV / 4), n = 4 * (it % (DV / 4));
         float mw[kWaves];
         float M = neg_inf();
 #pragma unroll
@@ -491,7 +493,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             for (int w = 0; w < kWaves; ++w) {
                 const float sc = fast_exp2(mw[w] - M);  // exactly 0 for an empty wave
                 tot += sc * red_l[w * 16 + q];
-                o += sc * *reinterpret_cast<const f32x4*>(red_o + (w * 16 + q) * D + n);
+                o += sc * *reinterpret_cast<const f32x4*>(red_o + (w * 16 + q) * DV + n);
             }
         }
         const int t2 = q / a.group;
@@ -522,13 +524,13 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
             lse = nan_f();
         }
         if (a.splits > 1) {
-            *reinterpret_cast<f32x4*>(a.o_part + ((int64_t)split * a.total_rows + row) * D + n) = o;
+            *reinterpret_cast<f32x4*>(a.o_part + ((int64_t)split * a.total_rows + row) * DV + n) = o;
             if (n == 0) a.lse_part[(int64_t)split * a.total_rows + row] = lse;
         } else {
             uint2 w;
             w.x = pack_bf16x2(o[0], o[1]);
             w.y = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<uint2*>(a.o + row * D + n) = w;
+            *reinterpret_cast<uint2*>(a.o + row * DV + n) = w;
             if (n == 0 && a.lse != nullptr) a.lse[row] = lse;
         }
     }
@@ -538,8 +540,8 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
 // Persistent grid: each work-group runs units until the queue is empty,
 // longest sequences first (every unit of a sequence has the same number of
 // keys but the last split).
-template <int D, bool F8>
-__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(SmallKArgs a) {
+template <int D, bool F8, int DV>
+__global__ __launch_bounds__(256, (D <= 192 ? 2 : 1)) void decode_small_kernel(SmallKArgs a) {
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     __shared__ int next_unit;
     __shared__ int by_len[kRankMax];  // by_len[r] = sequence with the r-th largest length
@@ -568,7 +570,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
         const int r = unit / per_seq, rem = unit - r * per_seq;
         const int b = ranked ? by_len[r] : r;
         const int kvh = rem / a.splits, split = rem - (rem / a.splits) * a.splits;
-        const int nxt = decode_unit<D, F8>(a, smem, b, kvh, split, &ctr[0], &next_unit, next_of);
+        const int nxt = decode_unit<D, F8, DV>(a, smem, b, kvh, split, &ctr[0], &next_unit, next_of);
         __syncthreads();  // the merge's LDS reads are done before the next unit's V stores
         unit = nxt;
     }
@@ -579,11 +581,11 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void decode_small_kernel(S
     }
 }
 
-template <int D, bool F8>
+template <int D, bool F8, int DV = D>
 hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
-    using C = SmallCfg<D, F8>;
+    using C = SmallCfg<D, F8, DV>;
     if (a.n_units == 0) return hipSuccess;
-    const void* kernel = (const void*)decode_small_kernel<D, F8>;
+    const void* kernel = (const void*)decode_small_kernel<D, F8, DV>;
     hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     // resident work-groups: per CU (computed once) x CUs of the device
@@ -602,7 +604,7 @@ hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
     const uint32_t gen = next_decode_tag();
     a.gen = gen;
     a.slot = (int32_t)(gen % kQueueSlots);
-    hipLaunchKernelGGL((decode_small_kernel<D, F8>), dim3((unsigned)(a.n_units < slots ? a.n_units : slots)), dim3(256),
+    hipLaunchKernelGGL((decode_small_kernel<D, F8, DV>), dim3((unsigned)(a.n_units < slots ? a.n_units : slots)), dim3(256),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
 }
@@ -610,7 +612,8 @@ hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
 }  // namespace
 
 bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows) {
-    return dqk == dv && (dqk == 64 || dqk == 128 || dqk == 256) && rows <= 16;
+    return ((dqk == dv && (dqk == 64 || dqk == 128 || dqk == 256)) || (dqk == 192 && dv == 128)) &&
+           rows <= 16;
 }
 
 hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
@@ -658,6 +661,7 @@ hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
     if (da.fp8) {
         switch (da.dqk) {
             case 64: return launch_small_d<64, true>(a, s);
+            case 192: return launch_small_d<192, true, 128>(a, s);
             case 128: return launch_small_d<128, true>(a, s);
             case 256: return launch_small_d<256, true>(a, s);
             default: return hipErrorInvalidValue;
@@ -665,6 +669,7 @@ hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
     }
     switch (da.dqk) {
         case 64: return launch_small_d<64, false>(a, s);
+        case 192: return launch_small_d<192, false, 128>(a, s);
         case 128: return launch_small_d<128, false>(a, s);
         case 256: return launch_small_d<256, false>(a, s);
         default: return hipErrorInvalidValue;

@@ -154,8 +154,10 @@ def test_d64(shape):
 
 
 @pytest.mark.parametrize("splits", [1, 4])
-def test_d192_d128_pools(splits):
-    pc = inputs.fp8_paged_case(3017, 3, 2, 16, 2, 192, 32, lengths=[5, 333, 1200],
+@pytest.mark.parametrize("hq", [16, 32], ids=["16_rows", "32_rows"])
+def test_d192_d128_pools(splits, hq):
+    # 2 tokens x hq / 2 heads per KV head: the few-row kernel (16 rows), the general one (32)
+    pc = inputs.fp8_paged_case(3017, 3, 2, hq, 2, 192, 32, lengths=[5, 333, 1200],
                                num_splits=splits, poison=True, name="fp8_d192x128", d_v=128)
     parity(pc)
 

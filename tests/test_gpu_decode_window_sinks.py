@@ -1,7 +1,7 @@
 """GPU parity of sdpa_decode_paged_ex (left sliding window, attention sinks, base-2 Stats)
-against the fp64 oracle, through every paged-decode kernel: the few-row kernel (bf16 D=64, 128, 256 and per-tensor
-FP8), the absorbed-MLA wide kernel (576/512), the general decode kernel (bf16 D=64 past 16
-rows per KV head, 192/128; FP8 D=64 and D=128 past 16 rows per KV head) and the
+against the fp64 oracle, through every paged-decode kernel: the few-row kernel (bf16 D=64, 128, 256, 192/128 and
+per-tensor FP8), the absorbed-MLA wide kernel (576/512), the general decode kernel (bf16 D=64
+and 192/128 past 16 rows per KV head; FP8 D=64 and D=128 past 16 rows per KV head) and the
 chunked-prefill path (prefill kernel over the page tables).
 """
 import math
@@ -73,9 +73,12 @@ def _cases():
         "general_d64_32_rows": lambda: inputs.paged_case(
             2212, 3, 4, 16, 2, 64, 64, 32, lengths=[3, 190, 1200], poison=True,
             name="general_d64_32_rows"),
-        "general_d192_128": lambda: inputs.paged_case(
+        "few_row_d192_128": lambda: inputs.paged_case(
             2206, 3, 1, 8, 2, 192, 128, 32, lengths=[9, 333, 1100], poison=True,
-            name="general_d192_128"),
+            name="few_row_d192_128"),
+        "general_d192_128_32_rows": lambda: inputs.paged_case(
+            2213, 3, 2, 32, 2, 192, 128, 32, lengths=[9, 333, 1100], poison=True,
+            name="general_d192_128_32_rows"),
         "general_fp8_d64": lambda: inputs.fp8_paged_case(
             2210, 3, 2, 8, 2, 64, 32, lengths=[1, 150, 1000], poison=True,
             name="general_fp8_d64"),
