@@ -290,9 +290,9 @@ int sdpa_decode_paged(const void* q,
  * in v1.32.0 "SDPA: wider native forward support"); s_q * (h_q/h_kv) <= 512
  * query rows per KV head (no chunked-prefill path in FP8); page_size a multiple
  * of 16; K and V pool strides multiples of 16; q and the pools 16-byte aligned.
- * Else SDPA_ERR_UNSUPPORTED.  d = 64, 128 and 256 with at most 16 rows per KV head
- * take the FP8-MFMA few-row kernel; the rest widen the codes exactly to bf16 as
- * they are loaded and use bf16 MFMA.
+ * Else SDPA_ERR_UNSUPPORTED.  Up to 64 rows per KV head (in groups of 16) at
+ * d = 64, 128, 256 or 192/128 take the FP8-MFMA few-row kernel; the rest widen
+ * the codes exactly to bf16 as they are loaded and use bf16 MFMA.
  */
 int sdpa_decode_paged_fp8(const void* q,
                           const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,

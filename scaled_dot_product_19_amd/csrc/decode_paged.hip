@@ -342,17 +342,26 @@ bool decode_supported(int32_t dqk, int32_t dv) {
            (dqk == 192 && dv == 128) || (dqk == 576 && dv == 512);
 }
 
+// The few-row kernel takes up to kSmallRowsMax rows per KV head, in groups
+// of 16 that each read the chunk's K/V (the general kernel reads it once
+// but ran 4x slower at 32 rows); its unit count must fit an int.
+static bool small_fits(const DecodeArgs& da) {
+    const int rows = da.sq * (da.hq / da.hkv);
+    return decode_small_supported(da.dqk, da.dv, rows) &&
+           (int64_t)da.batch * da.hkv * da.splits * ((rows + 15) / 16) <= INT32_MAX;
+}
+
 hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
-    if (decode_small_supported(da.dqk, da.dv, da.sq * (da.hq / da.hkv)))
-        return launch_decode_small(da, s);
+    const bool small = small_fits(da);
+    if (small && da.sq * (da.hq / da.hkv) <= 16) return launch_decode_small(da, s);
     if (prefill_paged_supported(da)) return launch_prefill_paged(da, s);
     if (decode_wide_supported(da)) return launch_decode_wide(da, s);
+    if (small) return launch_decode_small(da, s);
     return launch_generic(da, s, false);
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& da, hipStream_t s) {
-    if (decode_small_supported(da.dqk, da.dv, da.sq * (da.hq / da.hkv)))
-        return launch_decode_small(da, s);
+    if (small_fits(da)) return launch_decode_small(da, s);
     return launch_generic(da, s, true);
 }
 

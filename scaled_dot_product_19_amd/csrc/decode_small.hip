@@ -73,6 +73,7 @@ struct SmallKArgs {
     int32_t table_stride;
     const int32_t* seq_lens;
     int32_t batch, sq, hq, hkv, group, page, page_shift, splits, rows, n_units;
+    int32_t n_rg;  // groups of 16 query rows per KV head (units per chunk)
     int32_t slot;  // work-queue counters used by this launch
     uint32_t gen;  // this launch's tag on those counters (never 0)
     int64_t total_rows;
@@ -189,8 +190,8 @@ struct TileRegs {
 // into next_unit during the merge; returns that unit (-1: none left).
 template <int D, bool F8, int DV, class NextOf>
 __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, bf16_t* smem, const int b,
-                                                          const int kvh, const int split, uint64_t* ctr,
-                                                          int* next_unit, NextOf&& next_of) {
+                                                          const int kvh, const int split, const int rg,
+                                                          uint64_t* ctr, int* next_unit, NextOf&& next_of) {
     using C = SmallCfg<D, F8, DV>;
     constexpr int EB = C::EB;
     const int lane = threadIdx.x & 63;
@@ -213,14 +214,17 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
         lo = min(L, base + split * chunk);
         hi = min(L, lo + chunk);
     }
-    // query column c of the tile = row c of this KV head: token c / G, head kvh*G + c % G
-    const bool row_ok = c < a.rows;
-    const int rr = row_ok ? c : 0;
+    // query column c of the tile = row r0 + c of this KV head (row group rg): token
+    // (r0 + c) / G, head kvh*G + (r0 + c) % G
+    const int r0 = 16 * rg;
+    const int nr = min(16, a.rows - r0);  // rows of this unit
+    const bool row_ok = c < nr;
+    const int rr = r0 + (row_ok ? c : 0);
     const int tok = rr / a.group;
     const int64_t grow = ((int64_t)b * a.sq + tok) * a.hq + kvh * a.group + rr % a.group;
     const int lim = min(hi - 1, a.causal ? L - a.sq + tok : L - 1);
-    // keys every live row sees (the first token has the earliest causal limit)
-    const int nomask_end = max(lo, min(hi, a.causal ? L - a.sq + 1 : hi));
+    // keys every live row sees (the unit's first token has the earliest causal limit)
+    const int nomask_end = max(lo, min(hi, a.causal ? L - a.sq + r0 / a.group + 1 : hi));
     // first key this lane's token sees (left window), and the largest first key
     // of the live tokens (the last token's): tiles starting below it need the
     // lower mask
@@ -476,7 +480,7 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
     }
     __syncthreads();
     const int nxt = *next_unit;
-    const int items = a.rows * (DV / 4);
+    const int items = nr * (DV / 4);
     for (int it = threadIdx.x; it < items; it += 256) {
         const int q = it / (DV / 4), n = 4 * (it % (DV / 4));
         float mw[kWaves];
@@ -496,8 +500,8 @@ __device__ __attribute__((always_inline)) int decode_unit(const SmallKArgs& a, b
                 o += sc * *reinterpret_cast<const f32x4*>(red_o + (w * 16 + q) * DV + n);
             }
         }
-        const int t2 = q / a.group;
-        const int hh = kvh * a.group + q % a.group;
+        const int t2 = (r0 + q) / a.group;
+        const int hh = kvh * a.group + (r0 + q) % a.group;
         const int64_t row = ((int64_t)b * a.sq + t2) * a.hq + hh;
         float o_scale = o_mul;  // descale_v (1 unless FP8)
         if (a.sinks != nullptr && a.splits == 1) {
@@ -546,7 +550,8 @@ __global__ __launch_bounds__(256, (D <= 192 ? 2 : 1)) void decode_small_kernel(S
     __shared__ int next_unit;
     __shared__ int by_len[kRankMax];  // by_len[r] = sequence with the r-th largest length
     uint64_t* const ctr = g_decode_queue[a.slot];
-    const int per_seq = a.hkv * a.splits;
+    const int per_kvh = a.splits * a.n_rg;
+    const int per_seq = a.hkv * per_kvh;
     const bool ranked = a.batch <= kRankMax;
     if (ranked && (int)threadIdx.x < a.batch) {
         const int me = threadIdx.x;
@@ -569,8 +574,10 @@ __global__ __launch_bounds__(256, (D <= 192 ? 2 : 1)) void decode_small_kernel(S
     while (unit >= 0) {
         const int r = unit / per_seq, rem = unit - r * per_seq;
         const int b = ranked ? by_len[r] : r;
-        const int kvh = rem / a.splits, split = rem - (rem / a.splits) * a.splits;
-        const int nxt = decode_unit<D, F8, DV>(a, smem, b, kvh, split, &ctr[0], &next_unit, next_of);
+        // the row groups of a chunk take consecutive tickets (they read the same K/V)
+        const int kvh = rem / per_kvh, rem2 = rem - kvh * per_kvh;
+        const int split = rem2 / a.n_rg, rg = rem2 - split * a.n_rg;
+        const int nxt = decode_unit<D, F8, DV>(a, smem, b, kvh, split, rg, &ctr[0], &next_unit, next_of);
         __syncthreads();  // the merge's LDS reads are done before the next unit's V stores
         unit = nxt;
     }
@@ -613,7 +620,7 @@ hipError_t launch_small_d(SmallKArgs a, hipStream_t s) {
 
 bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows) {
     return ((dqk == dv && (dqk == 64 || dqk == 128 || dqk == 256)) || (dqk == 192 && dv == 128)) &&
-           rows <= 16;
+           rows <= kSmallRowsMax;
 }
 
 hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
@@ -642,7 +649,8 @@ hipError_t launch_decode_small(const DecodeArgs& da, hipStream_t s) {
         if (da.page == (1 << sh)) a.page_shift = sh;
     a.splits = da.splits;
     a.rows = da.sq * a.group;
-    a.n_units = da.batch * da.hkv * da.splits;
+    a.n_rg = (a.rows + 15) / 16;
+    a.n_units = da.batch * da.hkv * da.splits * a.n_rg;
     a.total_rows = (int64_t)da.batch * da.sq * da.hq;
     a.scale_log2 = da.scale * kLog2e;
     a.causal = da.causal;

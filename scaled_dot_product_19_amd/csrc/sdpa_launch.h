@@ -84,6 +84,8 @@ bool decode_supported(int32_t dqk, int32_t dv);
 
 // Few-row decode (s_q * G <= 16 query rows per KV head, d_qk == d_v in
 // {64, 128, 256}): the HBM-streaming kernel of decode_small.hip.
+// query rows per KV head the few-row decode kernel serves (in groups of 16)
+constexpr int kSmallRowsMax = 64;
 bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows);
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t s);
 

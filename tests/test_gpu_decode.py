@@ -67,6 +67,7 @@ def test_mla_576_512_two_tokens_causal(splits):
 
 @pytest.mark.parametrize("shape", [(64, 64, 4, 4, 3, False), (64, 64, 2, 1, 1, True),
                                    (64, 64, 16, 1, 1, True), (64, 64, 32, 1, 2, True),
+                                   (64, 64, 64, 1, 2, True),
                                    (256, 256, 8, 2, 2, True), (128, 128, 64, 4, 1, True),
                                    (128, 128, 16, 1, 4, True)])
 def test_other_head_shapes(shape):
@@ -165,3 +166,19 @@ def test_d64_decode_workload_sampled():
     check_o(o.reshape(rows, -1)[si], o_ref)
     check_lse(l.reshape(rows)[si], l_ref)
     assert torch.isfinite(o.float()).all()
+
+
+# ---- row groups: up to 64 rows per KV head take the few-row kernel in groups of 16 rows,
+# each group a unit of its own (a partial last group; causal limits per group) ----------
+
+@pytest.mark.parametrize("shape", [(17, 1, 2, 1), (3, 11, 1, 1), (4, 12, 2, 3), (4, 16, 1, 8)],
+                         ids=["17_rows", "33_rows", "48_rows", "64_rows"])
+def test_row_groups(shape):
+    sq, group, hkv, splits = shape
+    pc = inputs.paged_case(2040 + sq * group, 3, sq, group * hkv, hkv, 128, 128, 64,
+                           lengths=[2, 130, 1900], num_splits=splits, poison=True,
+                           name="row_groups")
+    log("row groups: %d rows per KV head" % (sq * group))
+    o, l, _, _ = parity(pc)
+    # sequence 0 holds 2 keys: with s_q > 2 its first token sees none
+    assert torch.all(o[0, 0] == 0) and torch.all(l[0, 0] == -math.inf)

@@ -128,8 +128,8 @@ def test_full_size_fp8_decode_sampled():
 # forward support": native D64 per-tensor FP8 and Q/K 576 with V 512) -------------------
 
 @pytest.mark.parametrize("splits", [1, 3])
-def test_d128_mtp_rows_past_the_few_row_kernel(splits):
-    # 4 tokens x 8 heads = 32 rows per KV head
+def test_d128_mtp_rows_in_two_row_groups(splits):
+    # 4 tokens x 8 heads = 32 rows per KV head: two 16-row groups of the few-row kernel
     pc = inputs.fp8_paged_case(3011, 3, 4, 32, 4, 128, 64, lengths=[2, 300, 1400],
                                num_splits=splits, poison=True, name="fp8_mtp_g8")
     o, _, _, _ = parity(pc)
@@ -137,7 +137,7 @@ def test_d128_mtp_rows_past_the_few_row_kernel(splits):
 
 
 @pytest.mark.parametrize("splits", [1, 4])
-def test_d256_rows_past_the_few_row_kernel(splits):
+def test_d256_rows_in_two_row_groups(splits):
     # 4 tokens x 8 heads = 32 rows per KV head at D = 256
     pc = inputs.fp8_paged_case(3012, 2, 4, 16, 2, 256, 32, lengths=[90, 1100],
                                num_splits=splits, poison=True, name="fp8_d256_g8")

@@ -1,8 +1,8 @@
 """GPU parity of sdpa_decode_paged_ex (left sliding window, attention sinks, base-2 Stats)
 against the fp64 oracle, through every paged-decode kernel: the few-row kernel (bf16 D=64, 128, 256, 192/128 and
-per-tensor FP8), the absorbed-MLA wide kernel (576/512), the general decode kernel (bf16 D=64
-and 192/128 past 16 rows per KV head; FP8 D=64 and D=128 past 16 rows per KV head) and the
-chunked-prefill path (prefill kernel over the page tables).
+per-tensor FP8, up to 64 rows per KV head in groups of 16), the absorbed-MLA wide kernel
+(576/512), the general decode kernel (past 64 rows per KV head) and the chunked-prefill path
+(prefill kernel over the page tables).
 """
 import math
 
@@ -70,21 +70,30 @@ def _cases():
         "few_row_d64": lambda: inputs.paged_case(
             2205, 3, 3, 4, 4, 64, 64, 32, lengths=[2, 77, 900], poison=True,
             name="few_row_d64"),
-        "general_d64_32_rows": lambda: inputs.paged_case(
+        "row_groups_d64_32_rows": lambda: inputs.paged_case(
             2212, 3, 4, 16, 2, 64, 64, 32, lengths=[3, 190, 1200], poison=True,
-            name="general_d64_32_rows"),
+            name="row_groups_d64_32_rows"),
+        "general_d64_128_rows": lambda: inputs.paged_case(
+            2214, 3, 4, 32, 1, 64, 64, 32, lengths=[3, 190, 1200], poison=True,
+            name="general_d64_128_rows"),
         "few_row_d192_128": lambda: inputs.paged_case(
             2206, 3, 1, 8, 2, 192, 128, 32, lengths=[9, 333, 1100], poison=True,
             name="few_row_d192_128"),
-        "general_d192_128_32_rows": lambda: inputs.paged_case(
+        "row_groups_d192_128_32_rows": lambda: inputs.paged_case(
             2213, 3, 2, 32, 2, 192, 128, 32, lengths=[9, 333, 1100], poison=True,
-            name="general_d192_128_32_rows"),
+            name="row_groups_d192_128_32_rows"),
+        "general_d192_128_128_rows": lambda: inputs.paged_case(
+            2215, 2, 2, 128, 2, 192, 128, 32, lengths=[9, 700], poison=True,
+            name="general_d192_128_128_rows"),
         "general_fp8_d64": lambda: inputs.fp8_paged_case(
             2210, 3, 2, 8, 2, 64, 32, lengths=[1, 150, 1000], poison=True,
             name="general_fp8_d64"),
-        "general_fp8_d128_32_rows": lambda: inputs.fp8_paged_case(
+        "row_groups_fp8_d128_32_rows": lambda: inputs.fp8_paged_case(
             2211, 3, 4, 16, 2, 128, 64, lengths=[3, 420, 1300], poison=True,
-            name="general_fp8_d128_32_rows"),
+            name="row_groups_fp8_d128_32_rows"),
+        "general_fp8_d128_128_rows": lambda: inputs.fp8_paged_case(
+            2216, 2, 4, 32, 1, 128, 64, lengths=[3, 1300], poison=True,
+            name="general_fp8_d128_128_rows"),
         "chunked_prefill": lambda: inputs.paged_case(
             2207, 2, 128, 8, 2, 128, 128, 64, lengths=[200, 1500], poison=True,
             name="chunked_prefill"),

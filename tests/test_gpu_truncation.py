@@ -70,7 +70,9 @@ DECODE = {
                                           lengths=[90, 700, 1500], name="trunc_wide"),
     "few_row_d64": lambda: inputs.paged_case(3203, 3, 1, 4, 4, 64, 64, 32,
                                              lengths=[77, 300, 900], name="trunc_few_d64"),
-    "general_d64": lambda: inputs.paged_case(3205, 3, 4, 16, 2, 64, 64, 32,
+    "row_groups_d64": lambda: inputs.paged_case(3205, 3, 4, 16, 2, 64, 64, 32,
+                                                lengths=[77, 300, 900], name="trunc_row_groups"),
+    "general_d64": lambda: inputs.paged_case(3206, 3, 4, 32, 1, 64, 64, 32,
                                              lengths=[77, 300, 900], name="trunc_general"),
     "chunked_prefill": lambda: inputs.paged_case(3204, 3, 128, 8, 2, 128, 128, 64,
                                                  lengths=[200, 700, 1500], name="trunc_chunked"),
