@@ -255,10 +255,14 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  * split-KV, and engine selection", paged D128 prefill and chunked-prefill
  * selection; the context phase of v1.28.0 "Samples, Benchmarks, and Tests",
  * 512/1024-token chunks against 64k/128k caches).  With d_qk = d_v = 128,
- * page_size % 64 == 0 and s_q of at least one prefill work item (64 tokens
- * when h_q/h_kv is a multiple of 4, 128 when it is 2 mod 4, 256 when odd) it
- * runs on the prefill kernel, which reads its 64-key K/V tiles through the
- * page tables; num_splits > 1 then writes the same partials as decode.
+ * page_size % 64 == 0, k_st, v_st < 2^22 and s_q of at least one prefill work
+ * item (64 tokens when h_q/h_kv is a multiple of 4, 128 when it is 2 mod 4,
+ * 256 when odd) it runs on the prefill kernel, which reads its 64-key K/V
+ * tiles through the page tables; num_splits > 1 then writes the same partials
+ * as decode.  With fewer tokens, a power-of-two h_q/h_kv and more than 16
+ * query rows per KV head (s_q * h_q/h_kv, e.g. multi-token decode over a wide
+ * GQA group), the same kernel takes the call with the (token, head) rows of
+ * each KV head's group folded, token-major, into its 256-row items.
  */
 int sdpa_decode_paged(const void* q,
                       const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,

@@ -6,7 +6,10 @@ causal: token i sees keys 0 .. L - s_q + i).  For d_qk = d_v = 128 and page size
 multiples of 64, once s_q covers a work item of the prefill kernel, the library runs the
 ping-pong prefill kernel with K/V tiles addressed through the two page tables (and fp32
 split partials merged by the LSE combine); these cases pin that path, including shapes the
-few-row decode kernels refuse (more than 512 query rows per KV head).
+few-row decode kernels refuse (more than 512 query rows per KV head).  With fewer tokens
+than an item holds and more than 16 query rows per KV head (a power-of-two GQA group), the
+same kernel folds the (token, head) rows of the whole group, token-major, into its 256-row
+items; the folded cases pin that mapping (partial items, several items, every group size).
 """
 import numpy as np
 import pytest
@@ -112,3 +115,53 @@ def test_context_phase_chunk_sampled(chunk, cache):
     sel = sample_rows(rows, 96, chunk + cache, must=[0, rows - 1])
     o, l = parity(pc, sel_rows=sel)
     assert torch.isfinite(o).all() and torch.isfinite(l).all()
+
+
+# Folded rows: s_q * G query rows per KV head (G a power of two, s_q below an item's token
+# count, more than 16 rows), token-major in items of 256 rows
+FOLDED = [
+    # MTP-like: 4 tokens x G 32 = 128 rows, half an item; L = 2 < s_q leaves tokens keyless
+    dict(seed=2121, sq=4, hq=32, hkv=1, lengths=[2, 190, 1200], splits=1, causal=True),
+    # 3 tokens x G 32 = 96 rows over two KV heads, three splits
+    dict(seed=2122, sq=3, hq=64, hkv=2, lengths=[0, 77, 900], splits=3, causal=True),
+    # 40 tokens x G 8 = 320 rows: a full item and a ragged one, non-causal
+    dict(seed=2123, sq=40, hq=16, hkv=2, lengths=[41, 700], splits=2, causal=False),
+    # 2 tokens x G 64 = 128 rows, causal across two tokens
+    dict(seed=2124, sq=2, hq=64, hkv=1, lengths=[1, 333], splits=1, causal=True),
+    # G 2: 33 tokens x 2 = 66 rows; G 1: 100 tokens of one head
+    dict(seed=2125, sq=33, hq=4, hkv=2, lengths=[20, 500], splits=4, causal=True),
+    dict(seed=2126, sq=100, hq=2, hkv=2, lengths=[150, 260], splits=1, causal=True),
+    # 16 tokens x G 8 = 128 rows per KV head, 4 KV heads, page 128
+    dict(seed=2127, sq=16, hq=32, hkv=4, lengths=[16, 1000, 3000], splits=8, causal=True,
+         page=128),
+    # the fewest rows that fold: 17 tokens of one head; 8 tokens x G 4 = 32 rows; 6 x 8 = 48
+    dict(seed=2129, sq=17, hq=2, hkv=2, lengths=[5, 400], splits=2, causal=True),
+    dict(seed=2130, sq=8, hq=32, hkv=8, lengths=[7, 130, 2000], splits=4, causal=True),
+    dict(seed=2131, sq=6, hq=16, hkv=2, lengths=[6, 64, 65], splits=1, causal=True),
+]
+
+
+@pytest.mark.parametrize("case", FOLDED, ids=["%d_%dx%d" % (c["seed"], c["sq"], c["hq"] // c["hkv"])
+                                              for c in FOLDED])
+def test_folded_rows(case):
+    pc = inputs.paged_case(case["seed"], len(case["lengths"]), case["sq"], case["hq"],
+                           case["hkv"], 128, 128, case.get("page", 64), lengths=case["lengths"],
+                           num_splits=case["splits"], causal=case["causal"], poison=True,
+                           name="folded_%d" % case["seed"])
+    log("folded rows: %d per KV head" % (case["sq"] * case["hq"] // case["hkv"]))
+    o, l = parity(pc)
+    if case["lengths"][0] < case["sq"] and case["causal"]:
+        # sequence 0 holds fewer keys than tokens: its first token sees none
+        assert torch.all(o[0, 0] == 0) and torch.all(l[0, 0] == -np.inf)
+
+
+@pytest.mark.timeout(600)
+def test_folded_rows_decode_workload_sampled():
+    # the paged decode workload's sequences (B = 64, 32/8 heads, D = 128, page 64,
+    # L U[512, 32768], 8 splits) with 32 query tokens: 128 folded rows per KV head
+    pc = inputs.paged_case(inputs.SEED_BASE + 3, 64, 32, 32, 8, 128, 128, 64, lo=512,
+                           hi=32768, num_splits=8, poison=True, name="folded_decode_workload")
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 256, 2128, must=[0, rows - 1])
+    o, _ = parity(pc, sel_rows=sel)
+    assert torch.isfinite(o.float()).all()

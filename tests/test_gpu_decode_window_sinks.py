@@ -2,7 +2,8 @@
 against the fp64 oracle, through every paged-decode kernel: the few-row kernel (bf16 D=64, 128, 256, 192/128 and
 per-tensor FP8, up to 64 rows per KV head in groups of 16), the absorbed-MLA wide kernel
 (576/512), the general decode kernel (past 64 rows per KV head) and the chunked-prefill path
-(prefill kernel over the page tables).
+(prefill kernel over the page tables, with its (token, head) rows folded when there are few
+tokens).
 """
 import math
 
@@ -97,6 +98,12 @@ def _cases():
         "chunked_prefill": lambda: inputs.paged_case(
             2207, 2, 128, 8, 2, 128, 128, 64, lengths=[200, 1500], poison=True,
             name="chunked_prefill"),
+        "folded_d128_128_rows": lambda: inputs.paged_case(
+            2217, 3, 4, 32, 1, 128, 128, 64, lengths=[3, 190, 1200], poison=True,
+            name="folded_d128_128_rows"),
+        "folded_d128_96_rows": lambda: inputs.paged_case(
+            2218, 2, 3, 64, 2, 128, 128, 64, lengths=[2, 900], poison=True,
+            name="folded_d128_96_rows"),
     }
 
 

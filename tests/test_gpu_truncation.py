@@ -76,6 +76,8 @@ DECODE = {
                                              lengths=[77, 300, 900], name="trunc_general"),
     "chunked_prefill": lambda: inputs.paged_case(3204, 3, 128, 8, 2, 128, 128, 64,
                                                  lengths=[200, 700, 1500], name="trunc_chunked"),
+    "folded_rows": lambda: inputs.paged_case(3207, 3, 4, 32, 1, 128, 128, 64,
+                                             lengths=[90, 700, 1500], name="trunc_folded"),
 }
 
 
