@@ -292,11 +292,18 @@ int sdpa_decode_paged(const void* q,
  * Supported: the (d_qk, d_v) pairs of sdpa_decode_paged ({64, 128, 256} square,
  * (192,128), (576,512); native D64 per-tensor FP8 and Q/K 576 with V 512 are
  * in v1.32.0 "SDPA: wider native forward support"); s_q * (h_q/h_kv) <= 512
- * query rows per KV head (no chunked-prefill path in FP8); page_size a multiple
- * of 16; K and V pool strides multiples of 16; q and the pools 16-byte aligned.
- * Else SDPA_ERR_UNSUPPORTED.  Up to 64 rows per KV head (in groups of 16) at
- * d = 64, 128, 256 or 192/128 take the FP8-MFMA few-row kernel; the rest widen
- * the codes exactly to bf16 as they are loaded and use bf16 MFMA.
+ * query rows per KV head, or any larger s_q when d_qk = d_v = 128, page_size
+ * is a multiple of 64 and k_st, v_st < 2^22 (the FP8 chunked-prefill path);
+ * page_size a multiple of 16; K and V pool strides multiples of 16; q and the
+ * pools 16-byte aligned.  Else SDPA_ERR_UNSUPPORTED.
+ * Kernels: up to 32 rows per KV head (and up to 64 off the next path) at
+ * d = 64, 128, 256 or 192/128, the FP8-MFMA few-row kernel in groups of 16
+ * rows.  Past 32 rows at d_qk = d_v = 128 with page_size % 64 == 0, the FP8
+ * prefill kernel over the page tables (FP8 MFMA for Q K^T, V codes widened
+ * to bf16 in LDS), either for s_q of at least one work item or, with fewer
+ * tokens and a power-of-two h_q/h_kv, with the (token, head) rows of each KV
+ * head's group folded into its 256-row items.  The rest widen the codes
+ * exactly to bf16 as they are loaded and use bf16 MFMA.
  */
 int sdpa_decode_paged_fp8(const void* q,
                           const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,

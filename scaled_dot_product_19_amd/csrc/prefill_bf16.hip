@@ -199,7 +199,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
                                                             uint64_t* const tctr, uint64_t& ticket,
                                                             Hook&& before_epilogue) {
     static_assert(!PP || (NW == 8 && S >= 4), "ping-pong needs two wave groups and S >= 4");
-    static_assert(!F8 || (PP && !PAGED && D == 128), "FP8: the D = 128 ping-pong THD kernel");
+    static_assert(!F8 || (PP && D == 128), "FP8: the D = 128 ping-pong kernel");
     using C = PCfg<D, BN, S, NW, F8>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -348,8 +348,10 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             // BN divides the page size and lo is a multiple of it: the tile
             // lies in one page (K and V pages looked up independently)
             const int64_t in_page = nvalid > 0 ? k0 % a.page : 0;
-            kt = a.k + (int64_t)pk_nx * a.k_sp + in_page * a.k_st + (int64_t)kvh * a.k_sh;
-            vt = a.v + (int64_t)pv_nx * a.v_sp + in_page * a.v_st + (int64_t)kvh * a.v_sh;
+            kt = reinterpret_cast<const char*>(a.k) +
+                 C::EB * ((int64_t)pk_nx * a.k_sp + in_page * a.k_st + (int64_t)kvh * a.k_sh);
+            vt = reinterpret_cast<const char*>(a.v) +
+                 C::EB * ((int64_t)pv_nx * a.v_sp + in_page * a.v_st + (int64_t)kvh * a.v_sh);
         } else {
             kt = kb0 + (int64_t)k0 * k_st2;
             vt = vb0 + (int64_t)k0 * v_st2;
@@ -834,6 +836,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
             if (!row_ok) return;
             const int64_t grow = (int64_t)(q_beg + i) * a.hq + h;
             float* prow = a.o_part + ((int64_t)split * a.total_rows + grow) * D;
+            inv *= o_mul;  // descale_v (1 unless FP8)
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
 #pragma unroll
@@ -1126,7 +1129,8 @@ bool prefill_paged_supported(const DecodeArgs& d) {
     return d.sq >= paged_item_tokens(d.hq / d.hkv) || paged_fold_lg(d) >= 0;
 }
 
-hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
+template <bool F8>
+hipError_t launch_prefill_paged_t(const DecodeArgs& d, hipStream_t s) {
     constexpr int D = 128, BN = 64, S = 4, NW = 8;
     PrefillKArgs a;
     a.q = static_cast<const bf16_t*>(d.q);
@@ -1160,8 +1164,10 @@ hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
         a.n_qtiles = (d.sq + tokens - 1) / tokens;
     }
     a.c = (d.scale < 0.f ? -d.scale : d.scale) * kLog2e;
-    a.q_sign = d.scale < 0.f ? 0x80008000u : 0u;
-    a.descale_q = a.descale_k = a.descale_v = nullptr;
+    a.q_sign = d.scale < 0.f ? (F8 ? 0x80808080u : 0x80008000u) : 0u;
+    a.descale_q = F8 ? d.descale_q : nullptr;
+    a.descale_k = F8 ? d.descale_k : nullptr;
+    a.descale_v = F8 ? d.descale_v : nullptr;
     a.causal = d.causal;
     a.lse = d.lse;
     a.lse_layout = d.lse != nullptr ? 1 : 0;  // [B, s_q, Hq] = token-major
@@ -1186,8 +1192,12 @@ hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
     const int64_t n_wg = (int64_t)a.n_qtiles * a.n_hg * a.batch * a.splits;
     if (n_wg == 0) return hipSuccess;
     if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-    return a.c == 0.f ? launch_dz<D, BN, S, NW, true, true, true>(a, n_wg, s)
-                      : launch_dz<D, BN, S, NW, true, false, true>(a, n_wg, s);
+    return a.c == 0.f ? launch_dz<D, BN, S, NW, true, true, true, F8>(a, n_wg, s)
+                      : launch_dz<D, BN, S, NW, true, false, true, F8>(a, n_wg, s);
+}
+
+hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
+    return d.fp8 ? launch_prefill_paged_t<true>(d, s) : launch_prefill_paged_t<false>(d, s);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {

@@ -282,21 +282,15 @@ static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t 
     if (num_splits < 1 || num_splits > 256)
         return fail(SDPA_ERR_SHAPE, "num_splits=%d outside [1, 256]", num_splits);
     if (fp8) {
-        // per-tensor FP8: the few-row decode kernel (HBM streaming, d 128/256,
-        // <= 16 rows per KV head), else the general decode kernel, which widens
-        // the codes to bf16 as it loads them (up to 512 rows per KV head)
-        if ((int64_t)s_q * (h_q / h_kv) > 512)
-            return fail(SDPA_ERR_UNSUPPORTED,
-                        "FP8 paged decode serves up to 512 query rows per KV head; got %lld",
-                        (long long)s_q * (h_q / h_kv));
+        // per-tensor FP8 K/V rows are DMA'd and loaded in 16-byte pieces
         const int64_t st[6] = {k_sp, k_st, k_sh, v_sp, v_st, v_sh};
         for (int64_t x : st)
             if (x % 16 != 0)
                 return fail(SDPA_ERR_UNSUPPORTED, "FP8 K/V pool strides must be multiples of 16");
     }
-    if (!fp8) {
+    {
         // more than 512 query rows per KV head: only the chunked-prefill path
-        // (prefill kernel over the page tables) serves them
+        // (prefill kernel over the page tables, bf16 or FP8) serves them
         sdpa::DecodeArgs probe{};
         probe.dqk = d_qk;
         probe.dv = d_v;

@@ -199,7 +199,9 @@ def _decode(**over):
     (dict(ws_bytes=1024), sdpa.SDPA_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x100040)), sdpa.SDPA_ERR_WORKSPACE),
     (dict(ptv=None), sdpa.SDPA_ERR_NULL),
-    (dict(hq=1024, hkv=1, sq=1), sdpa.SDPA_ERR_UNSUPPORTED),
+    # 768 rows per KV head from one token of a group that is not a power of two (folding
+    # its rows into the prefill kernel's items needs one)
+    (dict(hq=768, hkv=1, sq=1), sdpa.SDPA_ERR_UNSUPPORTED),
     # > 512 query rows per KV head: only the chunked-prefill path (D 128, page % 64) takes them
     (dict(sq=1024, page=32), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(sq=1024, dqk=64, dv=64, k_st=8 * 64, v_st=8 * 64, k_sh=64, v_sh=64),
@@ -228,7 +230,7 @@ def _decode_fp8(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(dqk=96, dv=96, k_st=8 * 96, v_st=8 * 96, k_sh=96, v_sh=96), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(dqk=576, dv=576), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(sq=5, hq=128, hkv=1), sdpa.SDPA_ERR_UNSUPPORTED),     # 640 rows per KV head
+    (dict(sq=5, hq=128, hkv=1, page=32), sdpa.SDPA_ERR_UNSUPPORTED),  # 640 rows per KV head
     (dict(k_st=8 * 128 + 8), sdpa.SDPA_ERR_UNSUPPORTED),         # K rows need 16-byte strides
     (dict(v_st=8 * 128 + 8), sdpa.SDPA_ERR_UNSUPPORTED),         # and V rows too
     (dict(v_st=8 * 128 + 4), sdpa.SDPA_ERR_UNSUPPORTED),

@@ -1,7 +1,10 @@
 """GPU parity of sdpa_decode_paged_fp8 (per-tensor FP8 E4M3 Q/K/V, bf16 O) against the
-fp64 oracle on the same codes and descales, through the C-ABI: the few-row kernel (D = 128
-and 256, up to 16 query rows per KV head) and the general decode kernel (everything else up
-to 512 rows per KV head: D = 64, 192/128, 576/512, and D = 128/256 with more rows).
+fp64 oracle on the same codes and descales, through the C-ABI: the few-row kernel (D = 64,
+128, 256 and 192/128, up to 64 query rows per KV head in groups of 16), the FP8 prefill
+kernel over the page tables (D = 128 with page sizes that are multiples of 64, past 32 rows
+per KV head and without an upper limit; with few tokens, the (token, head) rows of a
+power-of-two group are folded into its items) and the general decode kernel (the rest, up to
+512 rows per KV head, e.g. 576/512).
 
 The bar is the decode one: O within |g-o| <= 2e-2 + 2e-2|o|, LSE within 1e-3, -inf
 exactly where the oracle has -inf.  Pools are poisoned (NaN codes in unused pages and
@@ -130,7 +133,8 @@ def test_full_size_fp8_decode_sampled():
 @pytest.mark.parametrize("splits", [1, 3])
 def test_d128_mtp_rows_in_two_row_groups(splits):
     # 4 tokens x 8 heads = 32 rows per KV head: two 16-row groups of the few-row kernel
-    pc = inputs.fp8_paged_case(3011, 3, 4, 32, 4, 128, 64, lengths=[2, 300, 1400],
+    # (page 32 keeps the shape off the prefill kernel)
+    pc = inputs.fp8_paged_case(3011, 3, 4, 32, 4, 128, 32, lengths=[2, 300, 1400],
                                num_splits=splits, poison=True, name="fp8_mtp_g8")
     o, _, _, _ = parity(pc)
     assert torch.all(o[0, :2] == 0)
@@ -182,11 +186,42 @@ def test_absorbed_mla_aliased_fp8_cache(splits):
 
 
 def test_512_rows_per_kv_head_and_past_them():
-    # 4 tokens x 128 heads over one KV head: the most rows a call serves
-    pc = inputs.fp8_paged_case(3019, 2, 4, 128, 1, 128, 64, lengths=[6, 900], num_splits=2,
+    # 4 tokens x 128 heads over one KV head on 32-key pages (general kernel): the most rows
+    # it serves; past them only the prefill kernel (pages of 64k keys) takes the call
+    pc = inputs.fp8_paged_case(3019, 2, 4, 128, 1, 128, 32, lengths=[6, 900], num_splits=2,
                                poison=True, name="fp8_512rows")
     parity(pc)
-    pc5 = inputs.fp8_paged_case(3020, 1, 5, 128, 1, 128, 64, lengths=[900], name="fp8_640rows")
+    pc5 = inputs.fp8_paged_case(3020, 1, 5, 128, 1, 128, 32, lengths=[900], name="fp8_640rows")
     with pytest.raises(sdpa.SdpaError) as ei:
         run(pc5)
     assert ei.value.status == sdpa.SDPA_ERR_UNSUPPORTED
+
+
+# ---- the FP8 prefill kernel over the page tables (D = 128, pages of a multiple of 64 keys):
+# chunked prefill, and few tokens of a power-of-two GQA group with their (token, head) rows
+# folded into the 256-row items --------------------------------------------------------------
+
+FP8_PAGED_PREFILL = [
+    # (seed, batch, s_q, h_q, h_kv, page, lengths, splits, causal, scale)
+    (3021, 3, 8, 32, 4, 64, [2, 300, 1400], 1, True, None),      # folded: 64 rows
+    (3022, 3, 5, 32, 4, 64, [2, 300, 1400], 3, True, None),      # folded: 40 rows
+    (3023, 1, 5, 128, 1, 64, [900], 2, True, None),              # folded: 640 rows, 3 items
+    (3024, 2, 3, 64, 2, 128, [0, 777], 1, True, None),           # folded: 96 rows, page 128
+    (3025, 2, 100, 8, 2, 64, [120, 1500], 1, True, None),        # chunk of 100 tokens, G 4
+    (3026, 2, 100, 8, 2, 64, [120, 1500], 4, False, None),
+    (3027, 2, 16, 32, 4, 64, [40, 900], 2, True, -0.07),         # negative scale
+    (3028, 2, 16, 32, 4, 64, [40, 900], 1, True, 0.0),           # zero scale
+]
+
+
+@pytest.mark.parametrize("case", FP8_PAGED_PREFILL, ids=[str(c[0]) for c in FP8_PAGED_PREFILL])
+def test_fp8_paged_prefill_kernel(case):
+    seed, batch, sq, hq, hkv, page, lengths, splits, causal, scale = case
+    pc = inputs.fp8_paged_case(seed, batch, sq, hq, hkv, 128, page, lengths=lengths,
+                               num_splits=splits, causal=causal, scale=scale, poison=True,
+                               name="fp8_paged_prefill_%d" % seed)
+    log("fp8 paged prefill: %d rows per KV head" % (sq * hq // hkv))
+    o, l, _, _ = parity(pc)
+    assert torch.isfinite(o.float()).all()
+    if causal and lengths[0] < sq:
+        assert torch.all(o[0, 0] == 0) and torch.all(l[0, 0] == -np.inf)

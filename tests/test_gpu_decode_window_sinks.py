@@ -90,10 +90,10 @@ def _cases():
             2210, 3, 2, 8, 2, 64, 32, lengths=[1, 150, 1000], poison=True,
             name="general_fp8_d64"),
         "row_groups_fp8_d128_32_rows": lambda: inputs.fp8_paged_case(
-            2211, 3, 4, 16, 2, 128, 64, lengths=[3, 420, 1300], poison=True,
+            2211, 3, 4, 16, 2, 128, 32, lengths=[3, 420, 1300], poison=True,
             name="row_groups_fp8_d128_32_rows"),
         "general_fp8_d128_128_rows": lambda: inputs.fp8_paged_case(
-            2216, 2, 4, 32, 1, 128, 64, lengths=[3, 1300], poison=True,
+            2216, 2, 4, 32, 1, 128, 32, lengths=[3, 1300], poison=True,
             name="general_fp8_d128_128_rows"),
         "chunked_prefill": lambda: inputs.paged_case(
             2207, 2, 128, 8, 2, 128, 128, 64, lengths=[200, 1500], poison=True,
@@ -104,6 +104,12 @@ def _cases():
         "folded_d128_96_rows": lambda: inputs.paged_case(
             2218, 2, 3, 64, 2, 128, 128, 64, lengths=[2, 900], poison=True,
             name="folded_d128_96_rows"),
+        "folded_fp8_d128_64_rows": lambda: inputs.fp8_paged_case(
+            2219, 3, 8, 32, 4, 128, 64, lengths=[3, 420, 1300], poison=True,
+            name="folded_fp8_d128_64_rows"),
+        "chunked_prefill_fp8": lambda: inputs.fp8_paged_case(
+            2220, 2, 96, 8, 2, 128, 64, lengths=[100, 1500], poison=True,
+            name="chunked_prefill_fp8"),
     }
 
 
