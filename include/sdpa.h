@@ -259,10 +259,10 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  * item (64 tokens when h_q/h_kv is a multiple of 4, 128 when it is 2 mod 4,
  * 256 when odd) it runs on the prefill kernel, which reads its 64-key K/V
  * tiles through the page tables; num_splits > 1 then writes the same partials
- * as decode.  With fewer tokens, a power-of-two h_q/h_kv and more than 16
- * query rows per KV head (s_q * h_q/h_kv, e.g. multi-token decode over a wide
- * GQA group), the same kernel takes the call with the (token, head) rows of
- * each KV head's group folded, token-major, into its 256-row items.
+ * as decode.  With fewer tokens and more than 16 query rows per KV head
+ * (s_q * h_q/h_kv, e.g. multi-token decode over a wide GQA group), the same
+ * kernel takes the call with the (token, head) rows of each KV head's group
+ * folded, token-major, into its 256-row items.
  */
 int sdpa_decode_paged(const void* q,
                       const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,
@@ -301,9 +301,9 @@ int sdpa_decode_paged(const void* q,
  * rows.  Past 32 rows at d_qk = d_v = 128 with page_size % 64 == 0, the FP8
  * prefill kernel over the page tables (FP8 MFMA for Q K^T, V codes widened
  * to bf16 in LDS), either for s_q of at least one work item or, with fewer
- * tokens and a power-of-two h_q/h_kv, with the (token, head) rows of each KV
- * head's group folded into its 256-row items.  The rest widen the codes
- * exactly to bf16 as they are loaded and use bf16 MFMA.
+ * tokens, with the (token, head) rows of each KV head's group folded into
+ * its 256-row items.  The rest widen the codes exactly to bf16 as they are
+ * loaded and use bf16 MFMA.
  */
 int sdpa_decode_paged_fp8(const void* q,
                           const void* k_pool, int64_t k_sp, int64_t k_st, int64_t k_sh,

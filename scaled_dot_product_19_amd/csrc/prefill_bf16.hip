@@ -92,11 +92,11 @@ struct PrefillKArgs {
     const int32_t* seq_lens;
     int64_t k_sp, v_sp;      // page strides (elements)
     int32_t table_stride, page, sq, splits;
-    // folded rows: the item's rows are (token, head) pairs of 2^fold_lg heads,
-    // token-major (row r = token r >> fold_lg of head 2^fold_lg hg + r % 2^fold_lg),
-    // so that few query tokens of a whole GQA group still fill the 32-row
-    // blocks; 0 = one head per wave, rows = tokens
-    int32_t fold_lg = 0;
+    // folded rows: the item's rows are (token, head) pairs of `fold` heads,
+    // token-major (row r = token r / fold of head fold hg + r % fold), so that
+    // few query tokens of a whole GQA group still fill the 32-row blocks;
+    // 1 = one head per wave, rows = tokens
+    int32_t fold = 1;
     int64_t total_rows;      // batch * sq * hq
     float* o_part;           // [splits, total_rows, D]
     float* lse_part;         // [splits, total_rows]
@@ -248,9 +248,9 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
         hi = lk;
     }
     const int nt = NW / a.nh;
-    // rows of the sequence for one head (lg = 0) or one head group (folded)
-    const int lg = PAGED ? a.fold_lg : 0;
-    const int n_rows = lq << lg;
+    // rows of the sequence for one head (fg = 1) or one head group (folded)
+    const int fg = PAGED ? a.fold : 1;
+    const int n_rows = lq * fg;
     const int q0 = qt * 32 * nt;  // the item's first row
     if (q0 >= n_rows) {  // uniform across the work-group
         if (tid == 0) ticket = ticket_async(tctr);
@@ -259,13 +259,13 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     }
 
     const int hw = wave % a.nh, tb = wave / a.nh;
-    const int hb = (hg * a.nh + hw) << lg;  // the wave's head, or first head of its group
+    const int hb = (hg * a.nh + hw) * fg;  // the wave's head, or first head of its group
     const int kvh = hb / a.group;
     const int i0 = q0 + tb * 32;  // the wave's first row
     const int col = lane & 31, half = lane >> 5;
     const int ri = i0 + col;  // this lane's row: query token i of head h
-    const int i = ri >> lg;
-    const int h = hb + (ri & ((1 << lg) - 1));
+    const int i = ri / fg;
+    const int h = hb + (ri - i * fg);
     const bool row_ok = ri < n_rows;
     // a wave without rows (a folded item's or a sequence's last row block)
     // still issues its share of every tile's DMA but runs no MFMA
@@ -274,17 +274,17 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
 
     // left sliding window: row i sees keys >= i + shift - W + 1, so the item
     // starts at the first tile holding a key of its first row's window
-    if (a.window > 0) lo = max(lo, ((max(0, (q0 >> lg) + shift - a.window + 1)) / BN) * BN);
+    if (a.window > 0) lo = max(lo, ((max(0, (q0 / fg) + shift - a.window + 1)) / BN) * BN);
     // key extents within [lo, hi): the work-group's, this wave's, and this lane's
     // (from the query tokens of their first and last rows)
-    const int last_wg = (min(q0 + 32 * nt, n_rows) - 1) >> lg;
+    const int last_wg = (min(q0 + 32 * nt, n_rows) - 1) / fg;
     const int kv_end = a.causal ? max(lo, min(hi, last_wg + shift + 1)) : hi;
     int kv_end_w = lo, nomask_end = lo, kv_beg_w = lo;
     if (i0 < n_rows) {
-        const int first_w = i0 >> lg;
+        const int first_w = i0 / fg;
         // with a window, tiles that end before the wave's first visible key are skipped
         if (a.window > 0) kv_beg_w = max(lo, first_w + shift - a.window + 1);
-        const int last_w = (min(i0 + 32, n_rows) - 1) >> lg;
+        const int last_w = (min(i0 + 32, n_rows) - 1) / fg;
         kv_end_w = a.causal ? max(lo, min(hi, last_w + shift + 1)) : hi;
         nomask_end = a.causal ? max(lo, min(hi, first_w + shift + 1)) : hi;
     }
@@ -292,7 +292,7 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     // first visible key of this lane's row, and the largest of the wave's rows:
     // tiles starting below it need the lower mask
     const int first = i + shift - a.window + 1;  // used only with a window
-    const int first_w_max = a.window > 0 ? (min(i0 + 31, n_rows - 1) >> lg) + shift - a.window + 1 : INT32_MIN;
+    const int first_w_max = a.window > 0 ? (min(i0 + 31, n_rows - 1) / fg) + shift - a.window + 1 : INT32_MIN;
     // the tile starting at key0 holds keys of this wave, and needs the mask
     auto sees = [&](int key0) __attribute__((always_inline)) {
         return key0 < kv_end_w && key0 + BN > kv_beg_w;
@@ -902,8 +902,8 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
                 // nontemporal: O is not read again by this call, and cached
                 // dirty lines would be written back while later items stream
                 // K/V (2 % on the THD prefill workload)
-                bf16_t* orow = a.o + (int64_t)(q_beg + (rr >> lg)) * a.o_st +
-                               (int64_t)(hb + (rr & ((1 << lg) - 1))) * a.o_sh;
+                const int tr = rr / fg;
+                bf16_t* orow = a.o + (int64_t)(q_beg + tr) * a.o_st + (int64_t)(hb + rr - tr * fg) * a.o_sh;
                 __builtin_nontemporal_store(u32x4{w.x, w.y, w.z, w.w}, reinterpret_cast<u32x4*>(orow + 8 * rc));
             }
         }
@@ -1104,21 +1104,17 @@ int paged_item_tokens(int group) {
 }
 
 // Fewer query tokens than an item holds: the rows of a whole GQA group are
-// folded, token-major, into the item's 256 rows (power-of-two groups only, so
-// that a row splits into token and head by a shift).  Returns log2(group),
-// or -1 when the call does not fold.  Up to 16 rows per KV head the few-row
+// folded, token-major, into the item's 256 rows.  Returns the group size, or
+// 0 when the call does not fold.  Up to 16 rows per KV head the few-row
 // decode kernel reads the K/V once and is the better fit; past that it reads
 // them once per 16-row group, and the folded item (K/V read once, MFMA work
 // of 256 rows) is 1.5x faster at 32 rows and 2.8x at 64.
 constexpr int kFoldRowsMin = 17;
-int paged_fold_lg(const DecodeArgs& d) {
+int paged_fold(const DecodeArgs& d) {
     const int group = d.hq / d.hkv;
-    if (d.sq >= paged_item_tokens(group) || (group & (group - 1)) != 0) return -1;
+    if (d.sq >= paged_item_tokens(group)) return 0;
     const int64_t rows = (int64_t)d.sq * group;
-    if (rows < kFoldRowsMin || rows > (1 << 24)) return -1;
-    int lg = 0;
-    while ((1 << lg) < group) ++lg;
-    return lg;
+    return rows < kFoldRowsMin || rows > (1 << 24) ? 0 : group;
 }
 
 }  // namespace
@@ -1126,7 +1122,7 @@ int paged_fold_lg(const DecodeArgs& d) {
 bool prefill_paged_supported(const DecodeArgs& d) {
     if (d.dqk != 128 || d.dv != 128 || d.page % 64 != 0) return false;
     if (d.k_st >= (1 << 22) || d.v_st >= (1 << 22)) return false;
-    return d.sq >= paged_item_tokens(d.hq / d.hkv) || paged_fold_lg(d) >= 0;
+    return d.sq >= paged_item_tokens(d.hq / d.hkv) || paged_fold(d) > 0;
 }
 
 template <bool F8>
@@ -1149,15 +1145,15 @@ hipError_t launch_prefill_paged_t(const DecodeArgs& d, hipStream_t s) {
     a.batch = d.batch;
     a.hq = d.hq;
     a.group = d.hq / d.hkv;
-    const int lg = paged_fold_lg(d);
-    if (lg >= 0) {
+    const int fold = paged_fold(d);
+    if (fold > 0) {
         // one head group per item, its sq * group rows in blocks of 256
-        a.fold_lg = lg;
+        a.fold = fold;
         a.nh = 1;
         a.n_hg = d.hkv;
         a.n_qtiles = (int)(((int64_t)d.sq * a.group + 32 * NW - 1) / (32 * NW));
     } else {
-        a.fold_lg = 0;
+        a.fold = 1;
         a.nh = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
         a.n_hg = d.hq / a.nh;
         const int tokens = paged_item_tokens(a.group);

@@ -199,9 +199,9 @@ def _decode(**over):
     (dict(ws_bytes=1024), sdpa.SDPA_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x100040)), sdpa.SDPA_ERR_WORKSPACE),
     (dict(ptv=None), sdpa.SDPA_ERR_NULL),
-    # 768 rows per KV head from one token of a group that is not a power of two (folding
-    # its rows into the prefill kernel's items needs one)
-    (dict(hq=768, hkv=1, sq=1), sdpa.SDPA_ERR_UNSUPPORTED),
+    # 1024 rows per KV head on 32-key pages: the prefill kernel, the only path past 512
+    # rows, needs pages of a multiple of 64 keys
+    (dict(hq=1024, hkv=1, sq=1, page=32), sdpa.SDPA_ERR_UNSUPPORTED),
     # > 512 query rows per KV head: only the chunked-prefill path (D 128, page % 64) takes them
     (dict(sq=1024, page=32), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(sq=1024, dqk=64, dv=64, k_st=8 * 64, v_st=8 * 64, k_sh=64, v_sh=64),

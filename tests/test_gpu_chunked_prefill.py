@@ -7,7 +7,7 @@ multiples of 64, once s_q covers a work item of the prefill kernel, the library 
 ping-pong prefill kernel with K/V tiles addressed through the two page tables (and fp32
 split partials merged by the LSE combine); these cases pin that path, including shapes the
 few-row decode kernels refuse (more than 512 query rows per KV head).  With fewer tokens
-than an item holds and more than 16 query rows per KV head (a power-of-two GQA group), the
+than an item holds and more than 16 query rows per KV head, the
 same kernel folds the (token, head) rows of the whole group, token-major, into its 256-row
 items; the folded cases pin that mapping (partial items, several items, every group size).
 """
@@ -117,8 +117,8 @@ def test_context_phase_chunk_sampled(chunk, cache):
     assert torch.isfinite(o).all() and torch.isfinite(l).all()
 
 
-# Folded rows: s_q * G query rows per KV head (G a power of two, s_q below an item's token
-# count, more than 16 rows), token-major in items of 256 rows
+# Folded rows: s_q * G query rows per KV head (s_q below an item's token count, more than
+# 16 rows), token-major in items of 256 rows
 FOLDED = [
     # MTP-like: 4 tokens x G 32 = 128 rows, half an item; L = 2 < s_q leaves tokens keyless
     dict(seed=2121, sq=4, hq=32, hkv=1, lengths=[2, 190, 1200], splits=1, causal=True),
@@ -138,6 +138,11 @@ FOLDED = [
     dict(seed=2129, sq=17, hq=2, hkv=2, lengths=[5, 400], splits=2, causal=True),
     dict(seed=2130, sq=8, hq=32, hkv=8, lengths=[7, 130, 2000], splits=4, causal=True),
     dict(seed=2131, sq=6, hq=16, hkv=2, lengths=[6, 64, 65], splits=1, causal=True),
+    # groups that are not powers of two: 5 tokens x G 7 = 35 rows; 30 x G 6 = 180 rows
+    # (an item of 128 tokens when not folded); 3 x G 96 = 288 rows
+    dict(seed=2132, sq=5, hq=28, hkv=4, lengths=[3, 444, 1900], splits=3, causal=True),
+    dict(seed=2133, sq=30, hq=12, hkv=2, lengths=[31, 1000], splits=1, causal=True),
+    dict(seed=2134, sq=3, hq=96, hkv=1, lengths=[2, 800], splits=2, causal=True),
 ]
 
 

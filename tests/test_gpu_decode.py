@@ -170,8 +170,8 @@ def test_d64_decode_workload_sampled():
 
 # ---- row groups: up to 64 rows per KV head take the few-row kernel in groups of 16 rows,
 # each group a unit of its own (a partial last group; causal limits per group).  Page 32
-# keeps these shapes off the prefill kernel, which folds power-of-two groups past 16 rows
-# when pages are multiples of 64 ---------------------------------------------------------
+# keeps these shapes off the prefill kernel, which folds GQA groups past 16 rows when
+# pages are multiples of 64 ---------------------------------------------------------
 
 @pytest.mark.parametrize("shape", [(17, 1, 2, 1), (3, 11, 1, 1), (4, 12, 2, 3), (4, 16, 1, 8)],
                          ids=["17_rows", "33_rows", "48_rows", "64_rows"])

@@ -2,8 +2,8 @@
 fp64 oracle on the same codes and descales, through the C-ABI: the few-row kernel (D = 64,
 128, 256 and 192/128, up to 64 query rows per KV head in groups of 16), the FP8 prefill
 kernel over the page tables (D = 128 with page sizes that are multiples of 64, past 32 rows
-per KV head and without an upper limit; with few tokens, the (token, head) rows of a
-power-of-two group are folded into its items) and the general decode kernel (the rest, up to
+per KV head and without an upper limit; with few tokens, the (token, head) rows of a GQA
+group are folded into its items) and the general decode kernel (the rest, up to
 512 rows per KV head, e.g. 576/512).
 
 The bar is the decode one: O within |g-o| <= 2e-2 + 2e-2|o|, LSE within 1e-3, -inf
@@ -198,7 +198,7 @@ def test_512_rows_per_kv_head_and_past_them():
 
 
 # ---- the FP8 prefill kernel over the page tables (D = 128, pages of a multiple of 64 keys):
-# chunked prefill, and few tokens of a power-of-two GQA group with their (token, head) rows
+# chunked prefill, and few tokens of a GQA group with their (token, head) rows
 # folded into the 256-row items --------------------------------------------------------------
 
 FP8_PAGED_PREFILL = [
