@@ -367,6 +367,7 @@ hipError_t launch_decode_fp8(const DecodeArgs& da, hipStream_t s) {
     const bool small = small_fits(da);
     if (small && da.sq * (da.hq / da.hkv) <= 32) return launch_decode_small(da, s);
     if (prefill_paged_supported(da)) return launch_prefill_paged(da, s);
+    if (decode_wide_supported(da)) return launch_decode_wide(da, s);
     if (small) return launch_decode_small(da, s);
     return launch_generic(da, s, true);
 }

@@ -40,6 +40,17 @@
 // partial of their union into the slot of the first and marks the others
 // empty (LSE -inf, O not written; the LSE merge neither reads nor weighs
 // them), so the merge over all num_splits slots is the same attention.
+//
+// Per-tensor FP8 (E4M3 Q, K and V codes; F8 = true): the tiles arrive by the
+// same LDS DMA as codes, half the bytes, and the MFMAs stay bf16.  K rows
+// are 512 + 64 codes (region A: 32 chunks per row, chunk XOR row mod 8;
+// region B: 4 chunks, chunk XOR (row / 2) mod 4).  A lane's K fragment of
+// k-steps 2m and 2m + 1 is one 16-code read (d = 32 m + 16 half .. +16),
+// widened exactly to bf16 right before its two MFMAs; Q^T takes the same
+// order of d, so the contraction is unchanged.  Each wave widens its own 128
+// columns of the V codes into a bf16 V tile outside the ring (the only wave
+// that reads them), laid out as the bf16 kernel's V tile.  descale_q *
+// descale_k joins the logit scale and descale_v the output.
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 #include "tile_ops.h"
@@ -48,10 +59,10 @@ namespace sdpa {
 namespace {
 
 struct WideArgs {
-    const bf16_t* q;
-    const bf16_t* k_pool;
+    const void* q;       // bf16 or E4M3 codes
+    const void* k_pool;
     int64_t k_sp, k_st, k_sh;
-    const bf16_t* v_pool;
+    const void* v_pool;
     int64_t v_sp, v_st, v_sh;
     const int32_t* pt_k;
     const int32_t* pt_v;
@@ -73,6 +84,9 @@ struct WideArgs {
     int32_t window;   // left sliding window (0: none)
     const float* sinks;  // [hq] sink logits (natural-log units) or null
     int32_t stats_log2;  // final LSE in base 2
+    const float* descale_q;  // FP8 only: one fp32 each, read on the device
+    const float* descale_k;
+    const float* descale_v;
 };
 
 // LDS: two ring stages, each K region A (dims 0..511 of 32 rows, pitch
@@ -80,18 +94,25 @@ struct WideArgs {
 // chunk XOR row mod 8), V (32 rows x 1 KB, chunk XOR 4 (row mod 4)); then
 // the P^T exchange: one 1 KB MFMA operand per (32-row block, 16-key step),
 // lane l's 16 bytes at 16 l.
-template <int DQK, int DV>
+// FP8: region A rows of 512 codes (no pad, chunks swizzled), region B rows
+// of 64 codes, V rows of 512 codes; after the two stages the widened bf16 V
+// tile (32 rows x 1 KB, chunk XOR 4 (row mod 4) as the bf16 V tile).
+template <int DQK, int DV, bool F8>
 struct WCfg {
     static constexpr int NW = 4;                    // waves, 32 query rows each
     static constexpr int BN = 32;                   // keys per tile
-    static constexpr int KA_PITCH = 1040;
+    static constexpr int EB = F8 ? 1 : 2;           // bytes per element
+    static constexpr int KA_PITCH = F8 ? 512 : 1040;
     static constexpr int KA_B = BN * KA_PITCH;      // region A bytes
     static constexpr int KB_OFF = KA_B;             // region B
-    static constexpr int KB_B = BN * 128;
-    static constexpr int V_OFF = KB_OFF + KB_B;     // V tile
-    static constexpr int VROW_B = 2 * DV;
+    static constexpr int KB_ROW = 64 * EB;
+    static constexpr int KB_B = BN * KB_ROW;
+    static constexpr int V_OFF = KB_OFF + KB_B;     // V tile (codes for FP8)
+    static constexpr int VROW_B = EB * DV;
     static constexpr int STAGE_B = V_OFF + BN * VROW_B;
-    static constexpr int P_OFF = 2 * STAGE_B;       // P^T exchange
+    static constexpr int VB_OFF = 2 * STAGE_B;      // FP8: widened bf16 V tile
+    static constexpr int VBROW_B = 2 * DV;          // bf16 V rows, wherever they are read
+    static constexpr int P_OFF = VB_OFF + (F8 ? BN * VBROW_B : 0);  // P^T exchange
     static constexpr int LDS_BYTES = P_OFF + NW * (BN / 16) * 1024;
     static constexpr int RPW = BN / NW;             // tile rows per wave (one DMA each)
     static constexpr int KK = DQK / 16;             // k-steps of S^T = K Q^T
@@ -105,7 +126,8 @@ struct WCfg {
 constexpr int kTxPitch = 528;      // bytes per row of the output transpose (512 + 16)
 
 constexpr int kWideRankMax = 256;  // longest-first order for batches up to this size
-static_assert(4 * 32 * kTxPitch <= WCfg<576, 512>::P_OFF, "output transpose fits in the ring");
+static_assert(4 * 32 * kTxPitch <= WCfg<576, 512, false>::P_OFF, "output transpose fits in the ring");
+static_assert(4 * 32 * kTxPitch <= WCfg<576, 512, true>::P_OFF, "output transpose fits below P^T");
 
 constexpr int kWinW = 4;  // LDS operand fragments read ahead of the MFMAs
 
@@ -152,12 +174,18 @@ __device__ __forceinline__ uint32_t xor_add_here(uint32_t v, uint32_t x, uint32_
     asm volatile("v_xor_b32 %0, %1, %2\n\tv_add_u32 %0, %3, %0" : "=&v"(r) : "s"(x), "v"(v), "s"(s));
     return r;
 }
+// (v ^ x) + w + s with a per-lane w
+__device__ __forceinline__ uint32_t xor_add3_here(uint32_t v, uint32_t x, uint32_t w, uint32_t s) {
+    uint32_t r;
+    asm volatile("v_xor_b32 %0, %1, %2\n\tv_add3_u32 %0, %0, %3, %4" : "=&v"(r) : "s"(x), "v"(v), "v"(w), "s"(s));
+    return r;
+}
 
 // VAR: a left window, sinks or base-2 Stats are requested (their masks and
 // epilogue cost registers the plain instantiation has none to spare for)
-template <int DQK, int DV, bool VAR>
+template <int DQK, int DV, bool VAR, bool F8>
 __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
-    using C = WCfg<DQK, DV>;
+    using C = WCfg<DQK, DV, F8>;
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     char* const lds = reinterpret_cast<char*>(smem);
     const uint32_t lds_base = lds_addr(smem);
@@ -248,10 +276,20 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     // for K dims 0..511 (lane L: chunk L) and one for V (lane L: chunk
     // L ^ 4 (row mod 4)); one more instruction covers its 8 rows of K dims
     // 512..575 (lane L: row 8 w + L / 8, chunk (L mod 8) ^ (row mod 8)).
-    const uint32_t k_st2 = 2u * (uint32_t)a.k_st, v_st2 = 2u * (uint32_t)a.v_st;
+    // FP8: per wave 4 instructions of 2 rows each for region A (lane L: row
+    // + L / 32, physical chunk L % 32 = logical chunk (L % 32) ^ (row mod 8)),
+    // lanes 0..31 of one for its 8 rows of region B (lane L: row + L / 4,
+    // physical chunk L % 4 = logical (L % 4) ^ ((row / 2) mod 4)), and 4 of 2
+    // rows each for V (unswizzled).
+    const uint32_t k_st2 = C::EB * (uint32_t)a.k_st, v_st2 = C::EB * (uint32_t)a.v_st;
     const uint32_t l16 = 16u * (uint32_t)lane;
-    const int rb_row = wave * C::RPW + lane / 8;
-    const uint32_t kb_src = (uint32_t)rb_row * k_st2 + 1024u + 16u * (uint32_t)((lane & 7) ^ (rb_row & 7));
+    const int rb_row = wave * C::RPW + lane / (F8 ? 4 : 8);
+    const uint32_t kb_src =
+        F8 ? (uint32_t)rb_row * k_st2 + 512u + 16u * (uint32_t)((lane & 3) ^ ((rb_row >> 1) & 3))
+           : (uint32_t)rb_row * k_st2 + 1024u + 16u * (uint32_t)((lane & 7) ^ (rb_row & 7));
+    const uint32_t hl = (uint32_t)(lane >> 5);  // FP8: second row of a 2-row instruction
+    const uint32_t ka_v = 16u * (((uint32_t)lane & 31u) ^ hl), ka_w = hl * k_st2;
+    const uint32_t va_v = hl * v_st2 + 16u * ((uint32_t)lane & 31u);
     // Physical pages of the chunk's first 64 pages (lane i: page lo/page + i);
     // a chunk of more pages reloads the window when it gets there.
     const int pg0 = lo / a.page;
@@ -270,8 +308,8 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         asm volatile("" ::"v"(pk), "v"(pv));
     };
     if (n_pages > 0) load_window(0);
-    const bf16_t* const kbase = a.k_pool + (int64_t)kvh * a.k_sh;
-    const bf16_t* const vbase = a.v_pool + (int64_t)kvh * a.v_sh;
+    const char* const kbase = static_cast<const char*>(a.k_pool) + (int64_t)C::EB * kvh * a.k_sh;
+    const char* const vbase = static_cast<const char*>(a.v_pool) + (int64_t)C::EB * kvh * a.v_sh;
     // The 17 DMA instructions of a tile (per wave: 8 rows of K dims 0..511,
     // its rows of K dims 512..575, 8 rows of V) are issued in two bursts, V
     // and K, each right after the barrier that frees its slot: spread between
@@ -292,29 +330,45 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         const int pvp = __builtin_amdgcn_readlane(pv, rel - pwin);
         const int slot = key0 % a.page;
         // rows at or past nvalid fall outside the buffer range and arrive as zeros
-        const uint32_t kn = nvalid > 0 ? (uint32_t)(nvalid - 1) * k_st2 + 2u * DQK : 0u;
-        const uint32_t vn = nvalid > 0 ? (uint32_t)(nvalid - 1) * v_st2 + 2u * DV : 0u;
+        const uint32_t kn = nvalid > 0 ? (uint32_t)(nvalid - 1) * k_st2 + C::EB * DQK : 0u;
+        const uint32_t vn = nvalid > 0 ? (uint32_t)(nvalid - 1) * v_st2 + C::EB * DV : 0u;
         DmaPlan d;
-        d.kr = make_rsrc(kbase + (int64_t)pkp * a.k_sp + (int64_t)slot * a.k_st, kn);
-        d.vr = make_rsrc(vbase + (int64_t)pvp * a.v_sp + (int64_t)slot * a.v_st, vn);
+        d.kr = make_rsrc(kbase + (int64_t)C::EB * ((int64_t)pkp * a.k_sp + (int64_t)slot * a.k_st), kn);
+        d.vr = make_rsrc(vbase + (int64_t)C::EB * ((int64_t)pvp * a.v_sp + (int64_t)slot * a.v_st), vn);
         d.st = lds_base + stage * C::STAGE_B;
         return d;
     };
     // K of a tile is NK pieces (8 rows of dims 0..511, then the wave's rows of
-    // dims 512..575), V is NV pieces (8 rows)
-    constexpr int NK = C::RPW + 1, NV = C::RPW;
+    // dims 512..575), V is NV pieces (8 rows); FP8: 4 + 1 and 4
+    constexpr int NA = F8 ? C::RPW / 2 : C::RPW;  // region A pieces
+    constexpr int NK = NA + 1, NV = NA;
     auto k_piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
-        if (j < C::RPW) {
-            const int row = wave * C::RPW + j;
-            dma16_stream(d.kr, d.st + row * C::KA_PITCH, add_here(l16, (uint32_t)row * k_st2));
+        if constexpr (F8) {
+            if (j < NA) {
+                const int row = wave * C::RPW + 2 * j;
+                dma16_stream(d.kr, d.st + row * C::KA_PITCH,
+                             xor_add3_here(ka_v, 32u * (uint32_t)j, ka_w, (uint32_t)row * k_st2));
+            } else if (lane < 32) {
+                dma16_stream(d.kr, d.st + C::KB_OFF + wave * 512, kb_src);
+            }
         } else {
-            dma16_stream(d.kr, d.st + C::KB_OFF + wave * 1024, kb_src);
+            if (j < C::RPW) {
+                const int row = wave * C::RPW + j;
+                dma16_stream(d.kr, d.st + row * C::KA_PITCH, add_here(l16, (uint32_t)row * k_st2));
+            } else {
+                dma16_stream(d.kr, d.st + C::KB_OFF + wave * 1024, kb_src);
+            }
         }
     };
     auto v_piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
-        const int row = wave * C::RPW + j;
-        dma16_stream(d.vr, d.st + C::V_OFF + row * C::VROW_B,
-              xor_add_here(l16, 64u * (uint32_t)(row & 3), (uint32_t)row * v_st2));
+        if constexpr (F8) {
+            const int row = wave * C::RPW + 2 * j;
+            dma16_stream(d.vr, d.st + C::V_OFF + row * C::VROW_B, add_here(va_v, (uint32_t)row * v_st2));
+        } else {
+            const int row = wave * C::RPW + j;
+            dma16_stream(d.vr, d.st + C::V_OFF + row * C::VROW_B,
+                  xor_add_here(l16, 64u * (uint32_t)(row & 3), (uint32_t)row * v_st2));
+        }
     };
     // the ring's first tiles: K and V of tile 0, K of tile 1
     auto prologue = [&]() __attribute__((always_inline)) {
@@ -329,20 +383,47 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     };
     if (n_tiles > 0) prologue();  // overlaps the Q load below
 
+    // log2-domain logit scale and Q's sign flip; FP8 folds in descale_q *
+    // descale_k (a negative product flips Q like a negative scale)
+    float c = a.c;
+    uint32_t q_sign = a.q_sign;
+    float o_mul = 1.f;  // descale_v (1 unless FP8)
+    if constexpr (F8) {
+        const float dqk = a.descale_q[0] * a.descale_k[0];
+        c *= fabsf(dqk);
+        if (dqk < 0.f) q_sign ^= 0x80008000u;
+        o_mul = a.descale_v[0];
+    }
     // Q^T operand: lane (col, half) holds d = 16 kk + 8 half .. +8 of row r
-    // (rows past the end read the last row and are zeroed)
+    // (rows past the end read the last row and are zeroed).  FP8: k-steps 2m
+    // and 2m + 1 hold d = 32 m + 16 half .. +8 and .. +16, widened to bf16.
     bf16x8 qf[C::KK];
     {
-        const bf16_t* qrow = a.q + ((int64_t)(b * a.sq + tq) * a.hq + h) * DQK + 8 * half;
         const uint32_t keep = row_ok ? 0xffffffffu : 0u;
+        const int64_t qoff = ((int64_t)(b * a.sq + tq) * a.hq + h) * DQK;
+        if constexpr (F8) {
+            const char* qrow = static_cast<const char*>(a.q) + qoff + 16 * half;
 #pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) {
-            uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
-            w.x = (w.x & keep) ^ a.q_sign;
-            w.y = (w.y & keep) ^ a.q_sign;
-            w.z = (w.z & keep) ^ a.q_sign;
-            w.w = (w.w & keep) ^ a.q_sign;
-            qf[kk] = __builtin_bit_cast(bf16x8, w);
+            for (int mm = 0; mm < C::KK / 2; ++mm) {
+                const uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * mm);
+                uint4 lo = e4m3x8_to_bf16(uint2{w.x & keep, w.y & keep});
+                uint4 hi = e4m3x8_to_bf16(uint2{w.z & keep, w.w & keep});
+                lo = uint4{lo.x ^ q_sign, lo.y ^ q_sign, lo.z ^ q_sign, lo.w ^ q_sign};
+                hi = uint4{hi.x ^ q_sign, hi.y ^ q_sign, hi.z ^ q_sign, hi.w ^ q_sign};
+                qf[2 * mm] = __builtin_bit_cast(bf16x8, lo);
+                qf[2 * mm + 1] = __builtin_bit_cast(bf16x8, hi);
+            }
+        } else {
+            const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + qoff + 8 * half;
+#pragma unroll
+            for (int kk = 0; kk < C::KK; ++kk) {
+                uint4 w = *reinterpret_cast<const uint4*>(qrow + 16 * kk);
+                w.x = (w.x & keep) ^ q_sign;
+                w.y = (w.y & keep) ^ q_sign;
+                w.z = (w.z & keep) ^ q_sign;
+                w.w = (w.w & keep) ^ q_sign;
+                qf[kk] = __builtin_bit_cast(bf16x8, w);
+            }
         }
     }
 
@@ -360,22 +441,38 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     // (+8 for the second read) and 4 columns starting at 32 nb + 16 (G % 2) +
     // 4 (l % 4); it receives 4 consecutive keys of column 32 nb + l % 32.
     // Wave w reads the column blocks nb = 4 w + j (bytes 256 w .. of a row).
+    // FP8 K codes of k-steps 2m, 2m + 1: lane (col, half) reads logical chunk
+    // 2m + half of row col; in region A the physical chunk is that XOR
+    // (col mod 8), i.e. (half ^ (col mod 8)) ^ (2m mod 8) within the 8-chunk
+    // block m / 4; in region B (m = 16, 17) it is (2 (m - 16) + half) XOR
+    // ((col / 2) mod 4).
+    int k_ra8[4], k_rb8[2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k_ra8[e] = col * 512 + 16 * ((2 * e) ^ half ^ (col & 7));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) k_rb8[e] = C::KB_OFF + col * 64 + 16 * ((2 * e + half) ^ ((col >> 1) & 3));
     int v_rd[C::NBW];
     {
         const int r0 = 4 * half + (lane & 15) / 4;
         const int cg = 2 * ((lane >> 4) & 1) + (lane & 3) / 2;
 #pragma unroll
         for (int j = 0; j < C::NBW; ++j)
-            v_rd[j] = C::V_OFF + r0 * C::VROW_B + 16 * swz_v<64>(r0, 4 * j + cg) + 8 * (lane & 1) + 256 * wave;
+            v_rd[j] = (F8 ? C::VB_OFF : C::V_OFF) + r0 * C::VBROW_B + 16 * swz_v<64>(r0, 4 * j + cg) +
+                      8 * (lane & 1) + 256 * wave;
     }
     auto kfrag = [&](const char* st, int kk) __attribute__((always_inline)) {
         const int off = kk < C::KKA ? k_ra + 32 * kk : k_rb[kk - C::KKA];
         return *reinterpret_cast<const bf16x8*>(st + off);
     };
+    auto kraw8 = [&](const char* st, int mm) __attribute__((always_inline)) {
+        const int off = mm < 16 ? k_ra8[mm % 4] + 128 * (mm / 4) : k_rb8[mm - 16];
+        return *reinterpret_cast<const uint4*>(st + off);
+    };
+    // the bf16 V^T operands: in the stage, or (FP8) in the widened tile
     auto vfrag = [&](const char* st, int j, int kst) __attribute__((always_inline)) {
-        const char* vp = st + v_rd[j] + kst * 16 * C::VROW_B;
+        const char* vp = (F8 ? lds : st) + v_rd[j] + kst * 16 * C::VBROW_B;
         const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
-        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VROW_B));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * C::VBROW_B));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     // P^T operand of (row block rbk, key step kst): the score-accumulator
@@ -406,7 +503,31 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         if (vis) {
             // S^T = K Q^T
             f32x16 s;
-            {
+            if constexpr (F8) {
+                // 16 codes per read feed two k-steps; the widening sits right
+                // before their MFMAs (each MFMA's s_nop covers the VALU write)
+                f32x16 s0, s1;
+                constexpr int NP = C::NQK / 2, WP = kWinW / 2;
+                uint4 fr[WP];
+#pragma unroll
+                for (int w = 0; w < WP; ++w) fr[w] = kraw8(st, w);
+#pragma unroll
+                for (int mm = 0; mm < NP; ++mm) {
+                    const uint4 w = fr[mm % WP];
+                    const bf16x8 k0 = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(uint2{w.x, w.y}));
+                    const bf16x8 k1 = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(uint2{w.z, w.w}));
+                    if (mm + WP < NP) fr[mm % WP] = kraw8(st, mm + WP);
+                    if (mm == 0) {
+                        qk_first(s0, k0, qf[0]);
+                        qk_first(s1, k1, qf[1]);
+                    } else {
+                        qk_next(s0, k0, qf[2 * mm]);
+                        qk_next(s1, k1, qf[2 * mm + 1]);
+                    }
+                }
+                qk_fence(s0, s1);
+                s = s0 + s1;
+            } else {
                 f32x16 s0, s1;
                 bf16x8 fk[kWinW];
 #pragma unroll
@@ -440,15 +561,15 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; i += 2) mx = max3(mx, s[i], s[i + 1]);
             mx = half_max(mx);
-            const float mt = mx == neg_inf() ? neg_inf() : mx * a.c;
+            const float mt = mx == neg_inf() ? neg_inf() : mx * c;
             mx_all = fmaxf(mx_all, mt);
             m = m == neg_inf() ? mt : m;  // first visible tile fixes the frame
             const float nm = m == neg_inf() ? 0.f : -m;
             float lsum = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; i += 2) {
-                float p0 = fast_exp2(__builtin_fmaf(s[i], a.c, nm));
-                float p1 = fast_exp2(__builtin_fmaf(s[i + 1], a.c, nm));
+                float p0 = fast_exp2(__builtin_fmaf(s[i], c, nm));
+                float p1 = fast_exp2(__builtin_fmaf(s[i + 1], c, nm));
                 if (need_mask) {  // exact zeros also when c = 0 (-inf * 0 = NaN)
                     p0 = s[i] == neg_inf() ? 0.f : p0;
                     p1 = s[i + 1] == neg_inf() ? 0.f : p1;
@@ -466,6 +587,21 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         *pslot(wave, 0) = pb[0];
         *pslot(wave, 1) = pb[1];
         mid();
+        if constexpr (F8) {
+            // this wave's 128 columns of the V codes (every row) -> the bf16 V
+            // tile; no other wave reads or writes them.  Lane l: rows 8 i + l / 8,
+            // codes 16 (8 w + l mod 8) .. +16 -> bf16 chunks 16 w + 2 (l mod 8)
+            // and + 1, XOR 4 (row mod 4) as the reads expect.
+            const char* vc = st + C::V_OFF + 16 * (8 * wave + (lane & 7));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 8 * i + (lane >> 3);
+                const uint4 w = *reinterpret_cast<const uint4*>(vc + row * C::VROW_B);
+                char* vb = lds + C::VB_OFF + row * C::VBROW_B + 16 * ((16 * wave + 2 * (lane & 7)) ^ (4 * (row & 3)));
+                *reinterpret_cast<uint4*>(vb) = e4m3x8_to_bf16(uint2{w.x, w.y});
+                *reinterpret_cast<uint4*>(vb + 16) = e4m3x8_to_bf16(uint2{w.z, w.w});
+            }
+        }
         // O^T += V^T P^T: per key step 4 V^T and 4 P^T operands, 16 MFMAs
 #pragma unroll
         for (int kst = 0; kst < C::BN / 16; ++kst) {
@@ -556,6 +692,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
             m = m2;
         }
     }
+    inv *= o_mul;  // descale_v (1 unless FP8)
     const float lse2 = l_tot > 0.f ? m + fast_log2(l_tot) : neg_inf();
     // partials stay natural-log; the final Stats may be base 2
     float lse = VAR && a.stats_log2 && a.splits == 1 ? lse2 : kLn2 * lse2;
@@ -637,15 +774,27 @@ bool decode_wide_supported(const DecodeArgs& a) {
     return a.dqk == 576 && a.dv == 512 && rows > 16 && a.page % 32 == 0;
 }
 
+namespace {
+template <bool VAR, bool F8>
+hipError_t launch_wide_t(const WideArgs& a, int64_t n_wg, hipStream_t s) {
+    using C = WCfg<576, 512, F8>;
+    const void* kernel = (const void*)decode_wide_kernel<576, 512, VAR, F8>;
+    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_wide_kernel<576, 512, VAR, F8>), dim3((unsigned)n_wg), dim3(256),
+                       (size_t)C::LDS_BYTES, s, a);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_decode_wide(const DecodeArgs& d, hipStream_t s) {
-    using C = WCfg<576, 512>;
     WideArgs a;
-    a.q = static_cast<const bf16_t*>(d.q);
-    a.k_pool = static_cast<const bf16_t*>(d.k_pool);
+    a.q = d.q;
+    a.k_pool = d.k_pool;
     a.k_sp = d.k_sp;
     a.k_st = d.k_st;
     a.k_sh = d.k_sh;
-    a.v_pool = static_cast<const bf16_t*>(d.v_pool);
+    a.v_pool = d.v_pool;
     a.v_sp = d.v_sp;
     a.v_st = d.v_st;
     a.v_sh = d.v_sh;
@@ -687,22 +836,16 @@ hipError_t launch_decode_wide(const DecodeArgs& d, hipStream_t s) {
     a.window = d.window > 0 ? min(d.window, 1 << 30) : 0;
     a.sinks = d.sinks;
     a.stats_log2 = d.stats_log2;
+    a.descale_q = d.fp8 ? d.descale_q : nullptr;
+    a.descale_k = d.fp8 ? d.descale_k : nullptr;
+    a.descale_v = d.fp8 ? d.descale_v : nullptr;
     const int64_t n_wg = (n_g + 7) / 8 * 8 * a.n_rb;
     if (n_g == 0) return hipSuccess;
     // the epilogue passes output row indices as int32
     if (n_wg > INT32_MAX || (int64_t)d.batch * d.sq * d.hq > INT32_MAX) return hipErrorInvalidValue;
     const bool var = a.window > 0 || a.sinks != nullptr || a.stats_log2 != 0;
-    const void* kernel = var ? (const void*)decode_wide_kernel<576, 512, true>
-                             : (const void*)decode_wide_kernel<576, 512, false>;
-    hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    if (var)
-        hipLaunchKernelGGL((decode_wide_kernel<576, 512, true>), dim3((unsigned)n_wg), dim3(256),
-                           (size_t)C::LDS_BYTES, s, a);
-    else
-        hipLaunchKernelGGL((decode_wide_kernel<576, 512, false>), dim3((unsigned)n_wg), dim3(256),
-                           (size_t)C::LDS_BYTES, s, a);
-    return hipGetLastError();
+    if (d.fp8) return var ? launch_wide_t<true, true>(a, n_wg, s) : launch_wide_t<false, true>(a, n_wg, s);
+    return var ? launch_wide_t<true, false>(a, n_wg, s) : launch_wide_t<false, false>(a, n_wg, s);
 }
 
 }  // namespace sdpa

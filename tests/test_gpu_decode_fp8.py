@@ -1,10 +1,13 @@
 """GPU parity of sdpa_decode_paged_fp8 (per-tensor FP8 E4M3 Q/K/V, bf16 O) against the
-fp64 oracle on the same codes and descales, through the C-ABI: the few-row kernel (D = 64,
-128, 256 and 192/128, up to 64 query rows per KV head in groups of 16), the FP8 prefill
-kernel over the page tables (D = 128 with page sizes that are multiples of 64, past 32 rows
-per KV head and without an upper limit; with few tokens, the (token, head) rows of a GQA
-group are folded into its items) and the general decode kernel (the rest, up to
-512 rows per KV head, e.g. 576/512).
+fp64 oracle on the same codes and descales, through the C-ABI and every kernel it takes:
+- the few-row kernel (D = 64, 128, 256 and 192/128, up to 64 query rows per KV head in
+  groups of 16);
+- the FP8 prefill kernel over the page tables (D = 128 with page sizes that are multiples
+  of 64, past 32 rows per KV head and without an upper limit; with few tokens, the
+  (token, head) rows of a GQA group are folded into its items);
+- the absorbed-MLA wide kernel (576/512 past 16 rows per KV head, the codes widened to
+  bf16 in LDS and in registers);
+- the general decode kernel (the rest, up to 512 rows per KV head).
 
 The bar is the decode one: O within |g-o| <= 2e-2 + 2e-2|o|, LSE within 1e-3, -inf
 exactly where the oracle has -inf.  Pools are poisoned (NaN codes in unused pages and
@@ -195,6 +198,125 @@ def test_512_rows_per_kv_head_and_past_them():
     with pytest.raises(sdpa.SdpaError) as ei:
         run(pc5)
     assert ei.value.status == sdpa.SDPA_ERR_UNSUPPORTED
+
+
+# ---- the absorbed-MLA wide kernel in FP8 (576/512 codes, more than 16 rows per KV head,
+# pages of a multiple of 32 keys) ---------------------------------------------------------
+
+def mla8(seed, batch, sq, hq, lengths=None, page=64, splits=1, causal=True, scale=None,
+         lo=0, hi=0, name="fp8_mla"):
+    return inputs.fp8_paged_case(seed, batch, sq, hq, 1, 576, page, lo=lo, hi=hi, lengths=lengths,
+                                 num_splits=splits, causal=causal, scale=scale, poison=True,
+                                 name=name, d_v=512)
+
+
+@pytest.mark.parametrize("splits", [1, 16])
+def test_mla_wide_fp8_two_tokens_causal(splits):
+    pc = mla8(3031, 3, 2, 128, lengths=[1, 65, 700], splits=splits)
+    o, l, _, _ = parity(pc)
+    # L = 1 < s_q = 2: token 0 sees no key
+    assert torch.all(l[0, 0] == -np.inf) and torch.all(o[0, 0] == 0)
+
+
+@pytest.mark.parametrize("case", [
+    # 3 tokens x 16 heads = 48 rows (two waves without rows), page 32, two splits
+    dict(seed=3032, sq=3, hq=16, page=32, lengths=[33, 2100], splits=2, causal=True),
+    # 320 rows in 3 row blocks, page 128, lengths not multiples of a tile
+    dict(seed=3033, sq=2, hq=160, page=128, lengths=[97, 1301], splits=3, causal=True),
+    # one chunk of 71 pages (the page-id window reloads), non-causal
+    dict(seed=3034, sq=1, hq=64, page=128, lengths=[9000, 40], splits=1, causal=False),
+])
+def test_mla_wide_fp8_row_edges(case):
+    pc = mla8(case["seed"], len(case["lengths"]), case["sq"], case["hq"], lengths=case["lengths"],
+              page=case["page"], splits=case["splits"], causal=case["causal"])
+    parity(pc)
+
+
+@pytest.mark.parametrize("scale", [-0.05, 0.0])
+def test_mla_wide_fp8_negative_and_zero_scale(scale):
+    pc = mla8(3035, 2, 2, 128, lengths=[70, 500], splits=2, scale=scale)
+    parity(pc)
+
+
+def test_mla_wide_fp8_late_large_logit_takes_second_pass():
+    # as the bf16 case: key 40 of sequence 0 is 1.5 x the query of (token 1, head 3) before
+    # quantization, a logit far above the first tile's maxima, so the work-group reruns
+    # its chunk with the exact max as reference
+    import dataclasses
+    pc = inputs.paged_case(3036, 2, 2, 128, 1, 576, 512, 64, lengths=[300, 90], num_splits=2,
+                           causal=True, dtype=torch.float32, poison=True, name="fp8_mla_big")
+    key = 40
+    page = int(pc.pt_k[0, key // pc.page_size])
+    pc.k_pool[page, key % pc.page_size, 0] = 1.5 * pc.q[0, 1, 3]
+    q8, dq = inputs.quantize_e4m3(pc.q)
+    k8, dk = inputs.quantize_e4m3(pc.k_pool)
+    v8, dv = inputs.quantize_e4m3(pc.v_pool)
+    pc = dataclasses.replace(pc, q=q8, k_pool=k8, v_pool=v8, descale=(dq, dk, dv))
+    o, l, _, _ = parity(pc)
+    assert float(l[0, 1, 3]) > 30.0
+
+
+def test_mla_wide_fp8_descales_read_on_the_device():
+    import dataclasses
+    pc = mla8(3037, 2, 2, 64, lengths=[300, 1000], splits=4)
+    o1, l1 = run(pc)
+    dq, dk, dv = pc.descale
+    o2, l2 = run(dataclasses.replace(pc, descale=(dq * 2.0, dk * 0.5, dv * 2.0)))
+    assert torch.equal(o2.float(), o1.float() * 2.0)
+    assert torch.equal(l2, l1)
+
+
+def test_mla_wide_fp8_seq_lens_past_the_table_are_nan():
+    pc = mla8(3038, 3, 2, 64, lengths=[90, 700, 1500], splits=3)
+    reach = pc.pt_k.shape[1] * pc.page_size
+    lens = pc.seq_lens.clone()
+    lens[1] = reach + 5
+    dq, dk, dv = descales(pc)
+    o, l = sdpa.decode_paged_fp8(to_dev(pc.q), to_dev(pc.k_pool), to_dev(pc.v_pool),
+                                 to_dev(pc.pt_k), to_dev(pc.pt_v), to_dev(lens), reach, pc.scale,
+                                 dq, dk, dv, causal=pc.causal, num_splits=3)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1].float()).all() and torch.isnan(l[1]).all()
+    o_ref, l_ref = oracle_decode(pc, descale=pc.descale)
+    for b in (0, 2):
+        check_o(o[b], o_ref[b])
+        check_lse(l[b], l_ref[b])
+
+
+@pytest.mark.timeout(600)
+def test_mla_wide_fp8_full_size_sampled():
+    # the MLA-shaped decode workload (B = 32, 2 tokens, 128/1 heads, L U[4096, 16384],
+    # page 64, 16 splits) in per-tensor FP8
+    pc = mla8(inputs.SEED_BASE + 5, 32, 2, 128, lo=4096, hi=16384, splits=16,
+              name="fp8_mla_decode_workload")
+    o, l = run(pc)
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 256, 3039, must=[0, rows - 1])
+    o_ref, l_ref = oracle_decode(pc, sel_rows=sel, descale=pc.descale)
+    si = torch.from_numpy(sel).cuda()
+    log("fp8 MLA full size: max|dO|=%.3g max|dLSE|=%.3g" % (
+        check_o(o.reshape(rows, -1)[si], o_ref), check_lse(l.reshape(rows)[si], l_ref)))
+    assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_mla_wide_repeated_calls_are_bitwise_equal(fp8):
+    # the wide kernel's S^T MFMAs are hand-scheduled inline asm: repeated calls on the same
+    # inputs (one and several splits) must give the same bits
+    for splits in (1, 8):
+        if fp8:
+            pc = mla8(3040, 4, 2, 128, lengths=[5, 900, 2000, 3100], splits=splits)
+            outs = [run(pc) for _ in range(4)]
+        else:
+            pc = inputs.paged_case(3040, 4, 2, 128, 1, 576, 512, 64, lengths=[5, 900, 2000, 3100],
+                                   num_splits=splits, poison=True, name="mla_repeat")
+            args = [to_dev(x) for x in (pc.q, pc.k_pool, pc.v_pool, pc.pt_k, pc.pt_v, pc.seq_lens)]
+            outs = []
+            for _ in range(4):
+                outs.append(sdpa.decode_paged(*args, pc.max_kv, pc.scale, True, num_splits=splits))
+                torch.cuda.synchronize()
+        for o, l in outs[1:]:
+            assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
 
 # ---- the FP8 prefill kernel over the page tables (D = 128, pages of a multiple of 64 keys):

@@ -110,6 +110,9 @@ def _cases():
         "folded_fp8_d128_64_rows": lambda: inputs.fp8_paged_case(
             2219, 3, 8, 32, 4, 128, 64, lengths=[3, 420, 1300], poison=True,
             name="folded_fp8_d128_64_rows"),
+        "wide_mla_fp8": lambda: inputs.fp8_paged_case(
+            2222, 3, 2, 128, 1, 576, 64, lengths=[3, 700, 1500], poison=True,
+            name="wide_mla_fp8", d_v=512),
         "chunked_prefill_fp8": lambda: inputs.fp8_paged_case(
             2220, 2, 96, 8, 2, 128, 64, lengths=[100, 1500], poison=True,
             name="chunked_prefill_fp8"),
