@@ -302,8 +302,8 @@ int sdpa_decode_paged(const void* q,
  * prefill kernel over the page tables (FP8 MFMA for Q K^T, V codes widened
  * to bf16 in LDS), either for s_q of at least one work item or, with fewer
  * tokens, with the (token, head) rows of each KV head's group folded into
- * its 256-row items.  (576, 512) past 16 rows per KV head with page_size % 32
- * == 0: the absorbed-MLA wide kernel, its tiles DMA'd as codes and widened
+ * its 256-row items.  (576, 512) with page_size % 32 == 0: the absorbed-MLA
+ * wide kernel, its tiles DMA'd as codes and widened
  * exactly to bf16 (K in registers before each MFMA, V into an LDS tile).
  * The rest widen the codes exactly to bf16 as they are loaded and use bf16
  * MFMA.

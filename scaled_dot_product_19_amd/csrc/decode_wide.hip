@@ -1,6 +1,6 @@
 // decode_wide.hip -- paged-KV decode with many query rows per KV head, bf16.
 //
-// Serves s_q * G > 16 query rows per KV head with d_qk = 576, d_v = 512: the
+// Serves every s_q * G query rows per KV head with d_qk = 576, d_v = 512: the
 // absorbed-MLA decode shape with independent K/V page tables (cuDNN Frontend
 // v1.32.0 Release Notes, "SDPA: wider native forward support"; paged K/V and
 // split-KV: v1.31.0 "SDPA: paged KV, split-KV, and engine selection").  With
@@ -182,10 +182,14 @@ __device__ __forceinline__ uint32_t xor_add3_here(uint32_t v, uint32_t x, uint32
 }
 
 // VAR: a left window, sinks or base-2 Stats are requested (their masks and
-// epilogue cost registers the plain instantiation has none to spare for)
-template <int DQK, int DV, bool VAR, bool F8>
+// epilogue cost registers the plain instantiation has none to spare for).
+// NRB: 32-row blocks of O^T each wave computes: 4, or 1 when a KV head has at
+// most 32 query rows (waves 1..3 then hold no rows, and the O^T MFMAs of the
+// three empty row blocks are not issued).
+template <int DQK, int DV, bool VAR, bool F8, int NRB>
 __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     using C = WCfg<DQK, DV, F8>;
+    static_assert(NRB == 1 || NRB == C::NW, "one row block, or all of them");
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     char* const lds = reinterpret_cast<char*>(smem);
     const uint32_t lds_base = lds_addr(smem);
@@ -483,11 +487,11 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     };
 
     // O^T accumulators of this wave: acc[j][rbk] = columns 128 w + 32 j x rows 32 rbk
-    f32x16 acc[C::NBW][C::NW];
+    f32x16 acc[C::NBW][NRB];
 #pragma unroll
     for (int j = 0; j < C::NBW; ++j)
 #pragma unroll
-        for (int rbk = 0; rbk < C::NW; ++rbk)
+        for (int rbk = 0; rbk < NRB; ++rbk)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[j][rbk][i] = 0.f;
     float m = neg_inf();      // reference max (log2 units) of this lane's query
@@ -605,15 +609,15 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         // O^T += V^T P^T: per key step 4 V^T and 4 P^T operands, 16 MFMAs
 #pragma unroll
         for (int kst = 0; kst < C::BN / 16; ++kst) {
-            bf16x8 fv[C::NBW], fp[C::NW];
+            bf16x8 fv[C::NBW], fp[NRB];
 #pragma unroll
             for (int j = 0; j < C::NBW; ++j) fv[j] = vfrag(st, j, kst);
 #pragma unroll
-            for (int rbk = 0; rbk < C::NW; ++rbk) fp[rbk] = *pslot(rbk, kst);
+            for (int rbk = 0; rbk < NRB; ++rbk) fp[rbk] = *pslot(rbk, kst);
 #pragma unroll
             for (int j = 0; j < C::NBW; ++j)
 #pragma unroll
-                for (int rbk = 0; rbk < C::NW; ++rbk)
+                for (int rbk = 0; rbk < NRB; ++rbk)
                     acc[j][rbk] = mfma_32x32x16(fv[j], fp[rbk], acc[j][rbk]);
         }
     };
@@ -669,7 +673,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
 #pragma unroll
         for (int j = 0; j < C::NBW; ++j)
 #pragma unroll
-            for (int rbk = 0; rbk < C::NW; ++rbk)
+            for (int rbk = 0; rbk < NRB; ++rbk)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[j][rbk][i] = 0.f;
         if (n_tiles > 0) prologue();
@@ -724,7 +728,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     char* const tx = lds + wave * (32 * kTxPitch);
     auto write_rows = [&](auto&& store) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rbk = 0; rbk < C::NW; ++rbk) {
+        for (int rbk = 0; rbk < NRB; ++rbk) {
 #pragma unroll
             for (int j = 0; j < C::NBW; ++j)
 #pragma unroll
@@ -771,19 +775,23 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
 
 bool decode_wide_supported(const DecodeArgs& a) {
     const int rows = a.sq * (a.hq / a.hkv);
-    return a.dqk == 576 && a.dv == 512 && rows > 16 && a.page % 32 == 0;
+    return a.dqk == 576 && a.dv == 512 && rows > 0 && a.page % 32 == 0;
 }
 
 namespace {
-template <bool VAR, bool F8>
+template <bool VAR, bool F8, int NRB>
 hipError_t launch_wide_t(const WideArgs& a, int64_t n_wg, hipStream_t s) {
     using C = WCfg<576, 512, F8>;
-    const void* kernel = (const void*)decode_wide_kernel<576, 512, VAR, F8>;
+    const void* kernel = (const void*)decode_wide_kernel<576, 512, VAR, F8, NRB>;
     hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_wide_kernel<576, 512, VAR, F8>), dim3((unsigned)n_wg), dim3(256),
+    hipLaunchKernelGGL((decode_wide_kernel<576, 512, VAR, F8, NRB>), dim3((unsigned)n_wg), dim3(256),
                        (size_t)C::LDS_BYTES, s, a);
     return hipGetLastError();
+}
+template <bool VAR, bool F8>
+hipError_t launch_wide_rows(const WideArgs& a, int64_t n_wg, hipStream_t s) {
+    return a.rows <= 32 ? launch_wide_t<VAR, F8, 1>(a, n_wg, s) : launch_wide_t<VAR, F8, 4>(a, n_wg, s);
 }
 }  // namespace
 
@@ -844,8 +852,8 @@ hipError_t launch_decode_wide(const DecodeArgs& d, hipStream_t s) {
     // the epilogue passes output row indices as int32
     if (n_wg > INT32_MAX || (int64_t)d.batch * d.sq * d.hq > INT32_MAX) return hipErrorInvalidValue;
     const bool var = a.window > 0 || a.sinks != nullptr || a.stats_log2 != 0;
-    if (d.fp8) return var ? launch_wide_t<true, true>(a, n_wg, s) : launch_wide_t<false, true>(a, n_wg, s);
-    return var ? launch_wide_t<true, false>(a, n_wg, s) : launch_wide_t<false, false>(a, n_wg, s);
+    if (d.fp8) return var ? launch_wide_rows<true, true>(a, n_wg, s) : launch_wide_rows<false, true>(a, n_wg, s);
+    return var ? launch_wide_rows<true, false>(a, n_wg, s) : launch_wide_rows<false, false>(a, n_wg, s);
 }
 
 }  // namespace sdpa

@@ -133,6 +133,18 @@ def test_mla_wide_row_edges(case):
     parity(pc)
 
 
+# few rows per KV head (e.g. 16 heads of one token when the 128 heads are split over GPUs):
+# up to 32 rows the wide kernel computes one row block of O^T per wave
+@pytest.mark.parametrize("shape", [(1, 16, 64, 1, True), (1, 1, 32, 3, True), (2, 8, 64, 4, True),
+                                   (1, 32, 128, 16, False), (3, 11, 64, 2, True)],
+                         ids=["16_rows", "1_row", "2x8_rows", "32_rows", "33_rows"])
+def test_mla_few_rows(shape):
+    sq, hq, page, splits, causal = shape
+    pc = inputs.paged_case(2013, 3, sq, hq, 1, 576, 512, page, lengths=[1, 300, 2500],
+                           num_splits=splits, causal=causal, poison=True, name="mla_few_rows")
+    parity(pc)
+
+
 @pytest.mark.parametrize("scale", [-0.05, 0.0])
 def test_mla_negative_and_zero_scale(scale):
     pc = inputs.paged_case(2011, 2, 2, 128, 1, 576, 512, 64, lengths=[70, 500], num_splits=2,

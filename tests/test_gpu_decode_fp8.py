@@ -5,8 +5,8 @@ fp64 oracle on the same codes and descales, through the C-ABI and every kernel i
 - the FP8 prefill kernel over the page tables (D = 128 with page sizes that are multiples
   of 64, past 32 rows per KV head and without an upper limit; with few tokens, the
   (token, head) rows of a GQA group are folded into its items);
-- the absorbed-MLA wide kernel (576/512 past 16 rows per KV head, the codes widened to
-  bf16 in LDS and in registers);
+- the absorbed-MLA wide kernel (576/512, the codes widened to bf16 in LDS and in
+  registers);
 - the general decode kernel (the rest, up to 512 rows per KV head).
 
 The bar is the decode one: O within |g-o| <= 2e-2 + 2e-2|o|, LSE within 1e-3, -inf
@@ -230,6 +230,15 @@ def test_mla_wide_fp8_row_edges(case):
     pc = mla8(case["seed"], len(case["lengths"]), case["sq"], case["hq"], lengths=case["lengths"],
               page=case["page"], splits=case["splits"], causal=case["causal"])
     parity(pc)
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 64, 1, True), (1, 1, 32, 3, True), (2, 8, 64, 4, True),
+                                   (1, 32, 128, 16, False), (3, 11, 64, 2, True)],
+                         ids=["16_rows", "1_row", "2x8_rows", "32_rows", "33_rows"])
+def test_mla_wide_fp8_few_rows(shape):
+    sq, hq, page, splits, causal = shape
+    parity(mla8(3041, 3, sq, hq, lengths=[1, 300, 2500], page=page, splits=splits, causal=causal,
+                name="fp8_mla_few_rows"))
 
 
 @pytest.mark.parametrize("scale", [-0.05, 0.0])

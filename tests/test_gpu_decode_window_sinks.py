@@ -110,6 +110,12 @@ def _cases():
         "folded_fp8_d128_64_rows": lambda: inputs.fp8_paged_case(
             2219, 3, 8, 32, 4, 128, 64, lengths=[3, 420, 1300], poison=True,
             name="folded_fp8_d128_64_rows"),
+        "wide_mla_16_rows": lambda: inputs.paged_case(
+            2223, 3, 1, 16, 1, 576, 512, 64, lengths=[3, 700, 1500], poison=True,
+            name="wide_mla_16_rows"),
+        "wide_mla_fp8_16_rows": lambda: inputs.fp8_paged_case(
+            2224, 3, 2, 8, 1, 576, 64, lengths=[3, 700, 1500], poison=True,
+            name="wide_mla_fp8_16_rows", d_v=512),
         "wide_mla_fp8": lambda: inputs.fp8_paged_case(
             2222, 3, 2, 128, 1, 576, 64, lengths=[3, 700, 1500], poison=True,
             name="wide_mla_fp8", d_v=512),
