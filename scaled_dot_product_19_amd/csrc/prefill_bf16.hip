@@ -1096,11 +1096,15 @@ hipError_t launch_d(const PrefillArgs& pa, hipStream_t s) {
                       : launch_dz<D, BN, S, NW, PP, false, false, F8>(a, n_wg, s);
 }
 
-// Query tokens per work item of the D = 128 kernel (8 waves of 32 rows over
+// Waves (32 rows each) of the paged kernel for head dim d: the D = 128
+// ping-pong kernel has 8, the D = 256 sequential one 4.
+int paged_waves(int d) { return d == 256 ? 4 : 8; }
+
+// Query tokens per work item of the paged kernel (its waves of 32 rows over
 // NH heads of a GQA group).
-int paged_item_tokens(int group) {
+int paged_item_tokens(int group, int nw) {
     const int nh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
-    return 32 * (8 / nh);
+    return 32 * (nw / nh);
 }
 
 // Fewer query tokens than an item holds: the rows of a whole GQA group are
@@ -1112,7 +1116,7 @@ int paged_item_tokens(int group) {
 constexpr int kFoldRowsMin = 17;
 int paged_fold(const DecodeArgs& d) {
     const int group = d.hq / d.hkv;
-    if (d.sq >= paged_item_tokens(group)) return 0;
+    if (d.sq >= paged_item_tokens(group, paged_waves(d.dqk))) return 0;
     const int64_t rows = (int64_t)d.sq * group;
     return rows < kFoldRowsMin || rows > (1 << 24) ? 0 : group;
 }
@@ -1120,14 +1124,23 @@ int paged_fold(const DecodeArgs& d) {
 }  // namespace
 
 bool prefill_paged_supported(const DecodeArgs& d) {
-    if (d.dqk != 128 || d.dv != 128 || d.page % 64 != 0) return false;
+    // D = 128 (bf16 or FP8; 64-key tiles) or D = 256 (bf16; 32-key tiles):
+    // a tile must lie within one page
+    if (d.dqk != d.dv) return false;
+    if (d.dqk == 128) {
+        if (d.page % 64 != 0) return false;
+    } else if (d.dqk == 256 && !d.fp8) {
+        if (d.page % 32 != 0) return false;
+    } else {
+        return false;
+    }
     if (d.k_st >= (1 << 22) || d.v_st >= (1 << 22)) return false;
-    return d.sq >= paged_item_tokens(d.hq / d.hkv) || paged_fold(d) > 0;
+    return d.sq >= paged_item_tokens(d.hq / d.hkv, paged_waves(d.dqk)) || paged_fold(d) > 0;
 }
 
-template <bool F8>
+template <int D, int BN, int S, int NW, bool PP, bool F8>
 hipError_t launch_prefill_paged_t(const DecodeArgs& d, hipStream_t s) {
-    constexpr int D = 128, BN = 64, S = 4, NW = 8;
+    static_assert(NW == (D == 256 ? 4 : 8), "the waves paged_waves assumes");
     PrefillKArgs a;
     a.q = static_cast<const bf16_t*>(d.q);
     a.q_st = (int64_t)d.hq * D;
@@ -1156,7 +1169,7 @@ hipError_t launch_prefill_paged_t(const DecodeArgs& d, hipStream_t s) {
         a.fold = 1;
         a.nh = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0 ? 2 : 1);
         a.n_hg = d.hq / a.nh;
-        const int tokens = paged_item_tokens(a.group);
+        const int tokens = paged_item_tokens(a.group, NW);
         a.n_qtiles = (d.sq + tokens - 1) / tokens;
     }
     a.c = (d.scale < 0.f ? -d.scale : d.scale) * kLog2e;
@@ -1188,12 +1201,14 @@ hipError_t launch_prefill_paged_t(const DecodeArgs& d, hipStream_t s) {
     const int64_t n_wg = (int64_t)a.n_qtiles * a.n_hg * a.batch * a.splits;
     if (n_wg == 0) return hipSuccess;
     if (n_wg > INT32_MAX) return hipErrorInvalidValue;
-    return a.c == 0.f ? launch_dz<D, BN, S, NW, true, true, true, F8>(a, n_wg, s)
-                      : launch_dz<D, BN, S, NW, true, false, true, F8>(a, n_wg, s);
+    return a.c == 0.f ? launch_dz<D, BN, S, NW, PP, true, true, F8>(a, n_wg, s)
+                      : launch_dz<D, BN, S, NW, PP, false, true, F8>(a, n_wg, s);
 }
 
 hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
-    return d.fp8 ? launch_prefill_paged_t<true>(d, s) : launch_prefill_paged_t<false>(d, s);
+    if (d.dqk == 256) return launch_prefill_paged_t<256, 32, 4, 4, false, false>(d, s);
+    return d.fp8 ? launch_prefill_paged_t<128, 64, 4, 8, true, true>(d, s)
+                 : launch_prefill_paged_t<128, 64, 4, 8, true, false>(d, s);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {

@@ -170,3 +170,26 @@ def test_folded_rows_decode_workload_sampled():
     sel = sample_rows(rows, 256, 2128, must=[0, rows - 1])
     o, _ = parity(pc, sel_rows=sel)
     assert torch.isfinite(o.float()).all()
+
+
+# D = 256: the sequential 4-wave prefill kernel over the page tables (32-key tiles, so pages
+# of a multiple of 32 keys), items of 32 tokens x 4 heads or, folded, 128 rows
+D256 = [
+    # chunk of 40 tokens, G 4 (two items per head group), page 32, three splits
+    dict(seed=2141, sq=40, hq=8, hkv=2, page=32, lengths=[50, 900], splits=3, causal=True),
+    # folded: 2 tokens x G 16 = 32 rows; 3 x G 12 = 36; 5 x G 32 = 160 (two items)
+    dict(seed=2142, sq=2, hq=16, hkv=1, page=64, lengths=[1, 300, 1500], splits=1, causal=True),
+    dict(seed=2143, sq=3, hq=24, hkv=2, page=32, lengths=[2, 777], splits=4, causal=True),
+    dict(seed=2144, sq=5, hq=64, hkv=2, page=64, lengths=[9, 1200], splits=2, causal=False),
+]
+
+
+@pytest.mark.parametrize("case", D256, ids=[str(c["seed"]) for c in D256])
+def test_d256_paged_prefill_kernel(case):
+    pc = inputs.paged_case(case["seed"], len(case["lengths"]), case["sq"], case["hq"],
+                           case["hkv"], 256, 256, case["page"], lengths=case["lengths"],
+                           num_splits=case["splits"], causal=case["causal"], poison=True,
+                           name="d256_paged_%d" % case["seed"])
+    o, l = parity(pc)
+    if case["causal"] and case["lengths"][0] < case["sq"]:
+        assert torch.all(o[0, 0] == 0) and torch.all(l[0, 0] == -np.inf)

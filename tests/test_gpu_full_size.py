@@ -188,10 +188,12 @@ def _perturb_key(pc, b, key, seed):
 @pytest.mark.parametrize("shape", [
     # (s_q, h_q, h_kv, d_qk, d_v, splits): few-row kernel (8 rows per KV head), the
     # absorbed-MLA wide kernel (256 rows per KV head), and the prefill kernel with the
-    # (token, head) rows of a 64-head group folded (128 rows per KV head)
+    # (token, head) rows of a 64-head group folded (128 rows per KV head), and the D = 256
+    # prefill kernel with 32 folded rows
     (2, 8, 2, 128, 128, 3),
     (2, 128, 1, 576, 512, 4),
     (2, 64, 1, 128, 128, 2),
+    (2, 32, 2, 256, 256, 2),
 ])
 def test_decode_two_token_causal_future_key_bitwise(shape):
     sq, hq, hkv, dqk, dv, splits = shape
