@@ -248,8 +248,8 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  * Supported: dtype SDPA_BF16; (d_qk, d_v) in {(64,64), (128,128), (256,256),
  * (192,128), (576,512)}; page_size a multiple of 16; 1 <= num_splits <= 256;
  * s_q * (h_q/h_kv) <= 512 query rows per KV head, or any larger s_q when
- * d_qk = d_v = 128 with page_size a multiple of 64, or d_qk = d_v = 256 with
- * page_size a multiple of 32, and k_st, v_st < 2^22.
+ * d_qk = d_v = 64 or 128 with page_size a multiple of 64, or d_qk = d_v = 256
+ * with page_size a multiple of 32, and k_st, v_st < 2^22.
  *
  * Chunked prefill over the paged cache is this same call with s_q = the
  * chunk's tokens (the last s_q of each cache; v1.31.0 "SDPA: paged KV,
@@ -261,7 +261,8 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
  * 256 when odd) it runs on the prefill kernel, which reads its 64-key K/V
  * tiles through the page tables; num_splits > 1 then writes the same partials
  * as decode.  d_qk = d_v = 256 with page_size % 32 == 0 likewise runs on the
- * D = 256 prefill kernel (32-key tiles, items of 32, 64 or 128 tokens).  With fewer tokens and more than 16 query rows per KV head
+ * D = 256 prefill kernel (32-key tiles, items of 32, 64 or 128 tokens), and
+ * d_qk = d_v = 64 with page_size % 64 == 0 on the D = 64 one (64-key tiles).  With fewer tokens and more than 16 query rows per KV head
  * (s_q * h_q/h_kv, e.g. multi-token decode over a wide GQA group), the same
  * kernel takes the call with the (token, head) rows of each KV head's group
  * folded, token-major, into its 256-row items.

@@ -1124,10 +1124,10 @@ int paged_fold(const DecodeArgs& d) {
 }  // namespace
 
 bool prefill_paged_supported(const DecodeArgs& d) {
-    // D = 128 (bf16 or FP8; 64-key tiles) or D = 256 (bf16; 32-key tiles):
-    // a tile must lie within one page
+    // D = 128 (bf16 or FP8) and D = 64 (bf16) with 64-key tiles, D = 256
+    // (bf16) with 32-key tiles: a tile must lie within one page
     if (d.dqk != d.dv) return false;
-    if (d.dqk == 128) {
+    if (d.dqk == 128 || (d.dqk == 64 && !d.fp8)) {
         if (d.page % 64 != 0) return false;
     } else if (d.dqk == 256 && !d.fp8) {
         if (d.page % 32 != 0) return false;
@@ -1207,6 +1207,7 @@ hipError_t launch_prefill_paged_t(const DecodeArgs& d, hipStream_t s) {
 
 hipError_t launch_prefill_paged(const DecodeArgs& d, hipStream_t s) {
     if (d.dqk == 256) return launch_prefill_paged_t<256, 32, 4, 4, false, false>(d, s);
+    if (d.dqk == 64) return launch_prefill_paged_t<64, 64, 4, 8, true, false>(d, s);
     return d.fp8 ? launch_prefill_paged_t<128, 64, 4, 8, true, true>(d, s)
                  : launch_prefill_paged_t<128, 64, 4, 8, true, false>(d, s);
 }

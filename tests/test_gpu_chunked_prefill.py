@@ -193,3 +193,21 @@ def test_d256_paged_prefill_kernel(case):
     o, l = parity(pc)
     if case["causal"] and case["lengths"][0] < case["sq"]:
         assert torch.all(o[0, 0] == 0) and torch.all(l[0, 0] == -np.inf)
+
+
+# D = 64: the ping-pong kernel with 64-key tiles over the page tables (pages of a multiple
+# of 64 keys): a chunk of 64 tokens (G 4), and folded rows
+D64 = [
+    dict(seed=2151, sq=64, hq=8, hkv=2, page=64, lengths=[70, 900], splits=2, causal=True),
+    dict(seed=2152, sq=4, hq=32, hkv=1, page=128, lengths=[3, 500, 2000], splits=1, causal=True),
+    dict(seed=2153, sq=3, hq=12, hkv=2, page=64, lengths=[2, 640], splits=3, causal=False),
+]
+
+
+@pytest.mark.parametrize("case", D64, ids=[str(c["seed"]) for c in D64])
+def test_d64_paged_prefill_kernel(case):
+    pc = inputs.paged_case(case["seed"], len(case["lengths"]), case["sq"], case["hq"],
+                           case["hkv"], 64, 64, case["page"], lengths=case["lengths"],
+                           num_splits=case["splits"], causal=case["causal"], poison=True,
+                           name="d64_paged_%d" % case["seed"])
+    parity(pc)

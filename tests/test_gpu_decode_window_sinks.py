@@ -104,6 +104,9 @@ def _cases():
         "folded_d128_96_rows": lambda: inputs.paged_case(
             2218, 2, 3, 64, 2, 128, 128, 64, lengths=[2, 900], poison=True,
             name="folded_d128_96_rows"),
+        "folded_d64_128_rows": lambda: inputs.paged_case(
+            2225, 3, 4, 32, 1, 64, 64, 64, lengths=[3, 190, 1200], poison=True,
+            name="folded_d64_128_rows"),
         "folded_d128_g7_35_rows": lambda: inputs.paged_case(
             2221, 2, 5, 28, 4, 128, 128, 64, lengths=[4, 1100], poison=True,
             name="folded_d128_g7_35_rows"),

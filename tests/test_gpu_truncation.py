@@ -78,6 +78,8 @@ DECODE = {
                                                  lengths=[200, 700, 1500], name="trunc_chunked"),
     "folded_rows": lambda: inputs.paged_case(3207, 3, 4, 32, 1, 128, 128, 64,
                                              lengths=[90, 700, 1500], name="trunc_folded"),
+    "folded_rows_d64": lambda: inputs.paged_case(3209, 3, 4, 32, 1, 64, 64, 64,
+                                                 lengths=[77, 300, 900], name="trunc_folded_d64"),
     "folded_rows_d256": lambda: inputs.paged_case(3208, 3, 2, 32, 2, 256, 256, 32,
                                                   lengths=[90, 700, 1500], name="trunc_folded_d256"),
 }
