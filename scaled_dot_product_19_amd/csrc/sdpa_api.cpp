@@ -303,7 +303,8 @@ static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t 
         if ((int64_t)s_q * (h_q / h_kv) > 512 && !sdpa::prefill_paged_supported(probe))
             return fail(SDPA_ERR_UNSUPPORTED,
                         "s_q * (h_q / h_kv) = %lld query rows per KV head > 512 (more need "
-                        "d_qk = d_v = 128 and page_size %% 64 == 0)",
+                        "d_qk = d_v = 64 or 128 with page_size %% 64 == 0, or bf16 "
+                        "d_qk = d_v = 256 with page_size %% 32 == 0)",
                         (long long)s_q * (h_q / h_kv));
     }
     if (causal != 0 && causal != 1) return fail(SDPA_ERR_SHAPE, "causal must be 0 or 1");

@@ -202,9 +202,12 @@ def _decode(**over):
     # 1024 rows per KV head on 32-key pages: the prefill kernel, the only path past 512
     # rows, needs pages of a multiple of 64 keys
     (dict(hq=1024, hkv=1, sq=1, page=32), sdpa.SDPA_ERR_UNSUPPORTED),
-    # > 512 query rows per KV head: only the chunked-prefill path (D 128, page % 64) takes them
+    # > 512 query rows per KV head: only the chunked-prefill path (D 64 / 128 with page % 64,
+    # D 256 with page % 32) takes them
     (dict(sq=1024, page=32), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(sq=1024, dqk=64, dv=64, k_st=8 * 64, v_st=8 * 64, k_sh=64, v_sh=64),
+    (dict(sq=1024, dqk=64, dv=64, k_st=8 * 64, v_st=8 * 64, k_sh=64, v_sh=64, page=32),
+     sdpa.SDPA_ERR_UNSUPPORTED),
+    (dict(sq=1024, dqk=192, dv=128, k_st=8 * 192, v_st=8 * 128, k_sh=192, v_sh=128),
      sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(k_st=8 * 128 + 1), sdpa.SDPA_ERR_UNSUPPORTED),
 ])
