@@ -538,22 +538,47 @@ def run_decode_variant(args, torch, inputs, sdpa, dev):
                 "roofline": {"kernel": "decode_small_kernel<128, true> + combine_kernel<false>",
                              "bound": "hbm", "achieved": round(gbs, 1), "peak": peak,
                              "unit": "GB/s", "frac": round(gbs / peak, 4), "traffic": None}}
-    elif args.mtp_sweep:
-        pc = inputs.mtp_decode_d128()
+    elif args.fp8_mla:
+        # the MLA-shaped decode in per-tensor FP8, and in bf16 on the same GPU
+        pc = inputs.mla_decode_fp8()
+        ms = time_decode_fp8(torch, sdpa, pc, dev, args.steps, args.warmup)
+        kv, _ = decode_bytes(pc)
+        name = pc.name
+        del pc
+        pcb = inputs.mla_decode()
+        ms_bf16 = time_decode(torch, sdpa, pcb, dev, args.steps, args.warmup)
+        gbs = kv / ms / 1e6
+        line = {"metric": "FP8 MLA-shaped decode KV GB/s (% HBM peak)", "value": round(gbs, 1),
+                "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "fp8_e4m3",
+                "data": "synthetic (seeded N(0,1) fp32 quantized per tensor to E4M3)",
+                "config": {"workload": name, "kv_bytes": kv, "splits": 16,
+                           "bf16_ms_same_gpu": round(ms_bf16, 4),
+                           "speedup_vs_bf16": round(ms_bf16 / ms, 3)},
+                "roofline": {"kernel": "decode_wide_kernel<576, 512, false, true, 4> + combine",
+                             "bound": "hbm", "achieved": round(gbs, 1), "peak": peak,
+                             "unit": "GB/s", "frac": round(gbs / peak, 4), "traffic": None}}
+    elif args.mtp_sweep or args.gqa_mtp_sweep:
+        # q_tokens 1..4 (4..16 rows per KV head: the few-row kernel), or 8 / 16 / 32 (32 / 64
+        # / 128 rows: the prefill kernel with folded rows)
+        wide = args.gqa_mtp_sweep
+        pc = inputs.mtp_decode_d128(q_tokens=32 if wide else 4)
         kp, vp, q4 = pc.k_pool.to(dev), pc.v_pool.to(dev), pc.q.to(dev)
         kv, _ = decode_bytes(pc)
         res = []
-        for qt in (1, 2, 3, 4):
+        for qt in ((8, 16, 32) if wide else (1, 2, 3, 4)):
             ms = time_decode(torch, sdpa, pc, dev, args.steps, args.warmup,
                              q=q4[:, :qt].contiguous(), kp=kp, vp=vp)
             res.append({"q_tokens": qt, "ms": round(ms, 4), "kv_gbs": round(kv / ms / 1e6, 1),
                         "frac_hbm": round(kv / ms / 1e6 / peak, 4)})
-        line = {"metric": "multi-token decode KV GB/s (% HBM peak), q_tokens 1..4",
+        line = {"metric": "multi-token decode KV GB/s (% HBM peak), q_tokens "
+                          + ("8, 16, 32" if wide else "1..4"),
                 "value": res[0]["kv_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
                 "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16)",
-                "config": {"workload": pc.name.replace("_q4_", "_q1-4_"), "kv_bytes": kv,
-                           "splits": pc.num_splits},
+                "config": {"workload": pc.name.replace("_q32_", "_q8-32_").replace("_q4_", "_q1-4_"),
+                           "kv_bytes": kv, "splits": pc.num_splits},
                 "sweep": res}
     else:
         pc = inputs.mla_decode_aliased()
@@ -786,6 +811,10 @@ def main():
     ap.add_argument("--fp8-decode", action="store_true",
                     help="time only the paged decode workload in per-tensor FP8 E4M3 (and in "
                          "bf16 on the same GPU for the ratio)")
+    ap.add_argument("--fp8-mla", action="store_true",
+                    help="the MLA-shaped decode in per-tensor FP8 (wide kernel), bf16 beside it")
+    ap.add_argument("--gqa-mtp-sweep", action="store_true",
+                    help="multi-token decode with 8 / 16 / 32 tokens (32-128 rows per KV head)")
     ap.add_argument("--fp8-prefill", action="store_true",
                     help="time only the THD prefill workload in per-tensor FP8 E4M3 (and in "
                          "bf16 on the same GPU)")
@@ -825,7 +854,7 @@ def main():
     if args.fp8_prefill:
         run_fp8_prefill(args, torch, inputs, sdpa, dev)
         return
-    if args.mtp_sweep or args.mla_aliased or args.fp8_decode:
+    if args.mtp_sweep or args.mla_aliased or args.fp8_decode or args.fp8_mla or args.gqa_mtp_sweep:
         run_decode_variant(args, torch, inputs, sdpa, dev)
         return
 

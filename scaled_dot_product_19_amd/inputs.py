@@ -349,6 +349,16 @@ def mtp_decode_d128(seed: int = SEED_BASE + 7, batch: int = 4, cache: int = 1310
                       % (batch, q_tokens, cache, num_splits))
 
 
+def mla_decode_fp8(seed: int = SEED_BASE + 5, batch: int = 32, lo: int = 4096,
+                   hi: int = 16384) -> PagedCase:
+    """The MLA-shaped decode in per-tensor FP8 E4M3: the same draws as mla_decode (before
+    bf16 rounding), Q / K pool / V pool each quantized with its own descale."""
+    return fp8_paged_case(seed, batch=batch, sq=2, hq=128, hkv=1, d=576, page_size=64, lo=lo,
+                          hi=hi, num_splits=16, causal=True, d_v=512,
+                          name="mla_decode_fp8_b%d_sq2_h128x1_d576-512_p64_%d-%d_s16"
+                          % (batch, lo, hi))
+
+
 def mla_decode_aliased(seed: int = SEED_BASE + 8, batch: int = 32, lo: int = 4096,
                        hi: int = 16384) -> PagedCase:
     """The MLA-shaped decode over an absorbed-MLA cache: one 576-wide pool and one page table,
