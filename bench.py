@@ -332,7 +332,7 @@ def run_chunked_prefill(args, torch, inputs, sdpa, dev):
             "data": "synthetic (seeded N(0,1) bf16; cache lengths, page permutations per seed)",
             "config": {"workload": pc.name, "chunk": pc.sq, "cache_lengths": pc.seq_lens.tolist(),
                        "splits": pc.num_splits, "flop": flops},
-            "roofline": {"kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false, true>"
+            "roofline": {"kernel": "prefill_bf16_kernel<128, 64, 4, 8, true, false, true, false>"
                                    + (" + combine_kernel<false>" if pc.num_splits > 1 else ""),
                          "bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -535,7 +535,7 @@ def run_decode_variant(args, torch, inputs, sdpa, dev):
                            "cached_tokens": tokens,
                            "bf16_ms_same_gpu": round(ms_bf16, 4),
                            "speedup_vs_bf16": round(ms_bf16 / ms, 3)},
-                "roofline": {"kernel": "decode_small_kernel<128, true> + combine_kernel<false>",
+                "roofline": {"kernel": "decode_small_kernel<128, true, 128> + combine_kernel<false>",
                              "bound": "hbm", "achieved": round(gbs, 1), "peak": peak,
                              "unit": "GB/s", "frac": round(gbs / peak, 4), "traffic": None}}
     elif args.fp8_mla:
@@ -556,7 +556,7 @@ def run_decode_variant(args, torch, inputs, sdpa, dev):
                 "config": {"workload": name, "kv_bytes": kv, "splits": 16,
                            "bf16_ms_same_gpu": round(ms_bf16, 4),
                            "speedup_vs_bf16": round(ms_bf16 / ms, 3)},
-                "roofline": {"kernel": "decode_wide_kernel<576, 512, false, true, 4> + combine",
+                "roofline": {"kernel": "decode_wide_kernel<576, 512, false, true, 4> + combine_kernel<false>",
                              "bound": "hbm", "achieved": round(gbs, 1), "peak": peak,
                              "unit": "GB/s", "frac": round(gbs / peak, 4), "traffic": None}}
     elif args.mtp_sweep or args.gqa_mtp_sweep:
@@ -741,7 +741,7 @@ def mla_leg(args, torch, inputs, sdpa, dev, stream, threads):
            "split_partial_bytes": part_bytes, "chunks_per_work_group": merge, "flop": flops, "ms": st,
            "value": round(kv / (st["mean"] * 1e-3) / 1e9, 1), "unit": "GB/s",
            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
-           "roofline": {"kernel": "decode_wide_kernel<576, 512> + combine_kernel<false>",
+           "roofline": {"kernel": "decode_wide_kernel<576, 512, false, false, 4> + combine_kernel<false>",
                         "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                         "traffic": recorded_traffic(WIDE_TRAFFIC, WIDE_SOURCES)}}
@@ -1014,7 +1014,7 @@ def main():
             "traffic": recorded_traffic(PREFILL_TRAFFIC, PREFILL_SOURCES),
         },
         "roofline_decode": {
-            "kernel": "decode_small_kernel<128, false> + combine_kernel<false>",
+            "kernel": "decode_small_kernel<128, false, 128> + combine_kernel<false>",
             "bound": "hbm",
             "achieved": round(dec_comp_gbs, 1),
             "peak": PEAK_HBM_GBS,
