@@ -42,21 +42,23 @@
 // them), so the merge over all num_splits slots is the same attention.
 //
 // Per-tensor FP8 (E4M3 Q, K and V codes; F8 = true): the tiles arrive by the
-// same LDS DMA as codes, half the bytes, and the MFMAs stay bf16.  K rows
-// are 512 + 64 codes (region A: 32 chunks per row, chunk XOR row mod 8;
-// region B: 4 chunks, chunk XOR (row / 2) mod 4).  A lane's K fragment of
-// k-steps 2m and 2m + 1 is one 16-code read (d = 32 m + 16 half .. +16),
-// widened exactly to bf16 right before its two MFMAs; Q^T takes the same
-// order of d, so the contraction is unchanged.  Each wave widens its own 128
-// columns of the V codes into a bf16 V tile outside the ring (the only wave
-// that reads them), laid out as the bf16 kernel's V tile.  descale_q *
-// descale_k joins the logit scale and descale_v the output.
+// same LDS DMA as codes, half the bytes.  K rows are 512 + 64 codes (region
+// A: 32 chunks per row, chunk XOR row mod 8; region B: 4 chunks, chunk XOR
+// (row / 2) mod 4).  S^T = K Q^T runs on the FP8 MFMA (32x32x64, unit block
+// scales): 9 k-steps of 64 codes, a lane's K fragment two 16-code reads (d =
+// 64 kk + 32 half .. +32) and Q^T held as codes.  P V stays on the bf16
+// MFMA: each wave widens its own 128 columns of the V codes exactly into a
+// bf16 V tile outside the ring (the only wave that reads them), laid out as
+// the bf16 kernel's V tile.  descale_q * descale_k joins the logit scale and
+// descale_v the output.
 #include "sdpa_device.h"
 #include "sdpa_launch.h"
 #include "tile_ops.h"
 
 namespace sdpa {
 namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));  // 32 E4M3 codes
 
 struct WideArgs {
     const void* q;       // bf16 or E4M3 codes
@@ -146,6 +148,17 @@ __device__ __forceinline__ void qk_first(f32x16& d, bf16x8 a, bf16x8 b) {
 }
 __device__ __forceinline__ void qk_next(f32x16& d, bf16x8 a, bf16x8 b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// The FP8 form (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3, block scales
+// 2^0 from `sc`) under the same rules; it takes 16 passes, so the 24-wait-
+// state fence still covers the VALU reads after it.
+__device__ __forceinline__ void qk8_first(f32x16& d, i32x8 a, i32x8 b, int sc) {
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "=&v"(d) : "v"(a), "v"(b), "v"(sc));
+}
+__device__ __forceinline__ void qk8_next(f32x16& d, i32x8 a, i32x8 b, int sc) {
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+v"(d) : "v"(a), "v"(b), "v"(sc));
 }
 __device__ __forceinline__ void qk_fence(f32x16& d0, f32x16& d1) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d0), "+v"(d1));
@@ -399,23 +412,24 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         o_mul = a.descale_v[0];
     }
     // Q^T operand: lane (col, half) holds d = 16 kk + 8 half .. +8 of row r
-    // (rows past the end read the last row and are zeroed).  FP8: k-steps 2m
-    // and 2m + 1 hold d = 32 m + 16 half .. +8 and .. +16, widened to bf16.
-    bf16x8 qf[C::KK];
+    // (rows past the end read the last row and are zeroed).  FP8: the codes
+    // d = 64 kk + 32 half .. +32 of k-step kk (sign bits flipped per byte).
+    constexpr int KK8 = DQK / 64;
+    bf16x8 qf[F8 ? 1 : C::KK];
+    i32x8 qf8[F8 ? KK8 : 1];
     {
         const uint32_t keep = row_ok ? 0xffffffffu : 0u;
         const int64_t qoff = ((int64_t)(b * a.sq + tq) * a.hq + h) * DQK;
         if constexpr (F8) {
-            const char* qrow = static_cast<const char*>(a.q) + qoff + 16 * half;
+            const uint32_t sg = q_sign != 0u ? 0x80808080u : 0u;
+            const char* qrow = static_cast<const char*>(a.q) + qoff + 32 * half;
 #pragma unroll
-            for (int mm = 0; mm < C::KK / 2; ++mm) {
-                const uint4 w = *reinterpret_cast<const uint4*>(qrow + 32 * mm);
-                uint4 lo = e4m3x8_to_bf16(uint2{w.x & keep, w.y & keep});
-                uint4 hi = e4m3x8_to_bf16(uint2{w.z & keep, w.w & keep});
-                lo = uint4{lo.x ^ q_sign, lo.y ^ q_sign, lo.z ^ q_sign, lo.w ^ q_sign};
-                hi = uint4{hi.x ^ q_sign, hi.y ^ q_sign, hi.z ^ q_sign, hi.w ^ q_sign};
-                qf[2 * mm] = __builtin_bit_cast(bf16x8, lo);
-                qf[2 * mm + 1] = __builtin_bit_cast(bf16x8, hi);
+            for (int kk = 0; kk < KK8; ++kk) {
+                const uint4 w0 = *reinterpret_cast<const uint4*>(qrow + 64 * kk);
+                const uint4 w1 = *reinterpret_cast<const uint4*>(qrow + 64 * kk + 16);
+                qf8[kk] = i32x8{(int)((w0.x & keep) ^ sg), (int)((w0.y & keep) ^ sg), (int)((w0.z & keep) ^ sg),
+                                (int)((w0.w & keep) ^ sg), (int)((w1.x & keep) ^ sg), (int)((w1.y & keep) ^ sg),
+                                (int)((w1.z & keep) ^ sg), (int)((w1.w & keep) ^ sg)};
             }
         } else {
             const bf16_t* qrow = static_cast<const bf16_t*>(a.q) + qoff + 8 * half;
@@ -445,16 +459,18 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     // (+8 for the second read) and 4 columns starting at 32 nb + 16 (G % 2) +
     // 4 (l % 4); it receives 4 consecutive keys of column 32 nb + l % 32.
     // Wave w reads the column blocks nb = 4 w + j (bytes 256 w .. of a row).
-    // FP8 K codes of k-steps 2m, 2m + 1: lane (col, half) reads logical chunk
-    // 2m + half of row col; in region A the physical chunk is that XOR
-    // (col mod 8), i.e. (half ^ (col mod 8)) ^ (2m mod 8) within the 8-chunk
-    // block m / 4; in region B (m = 16, 17) it is (2 (m - 16) + half) XOR
-    // ((col / 2) mod 4).
-    int k_ra8[4], k_rb8[2];
+    // FP8 K codes of k-step kk: lane (col, half) reads logical chunks
+    // 4 kk + 2 half + e (e = 0, 1) of row col; in region A (kk < 8) the
+    // physical chunk is that XOR (col mod 8), i.e. block kk / 2 of 8 chunks
+    // and within it (4 (kk mod 2) + 2 half + e) ^ (col mod 8); in region B
+    // (kk = 8) it is (2 half + e) XOR ((col / 2) mod 4).
+    int k8a[2][2], k8b[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) k_ra8[e] = col * 512 + 16 * ((2 * e) ^ half ^ (col & 7));
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) k_rb8[e] = C::KB_OFF + col * 64 + 16 * ((2 * e + half) ^ ((col >> 1) & 3));
+        for (int e = 0; e < 2; ++e) k8a[p][e] = col * 512 + 16 * ((4 * p + 2 * half + e) ^ (col & 7));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) k8b[e] = C::KB_OFF + col * 64 + 16 * ((2 * half + e) ^ ((col >> 1) & 3));
     int v_rd[C::NBW];
     {
         const int r0 = 4 * half + (lane & 15) / 4;
@@ -468,10 +484,14 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         const int off = kk < C::KKA ? k_ra + 32 * kk : k_rb[kk - C::KKA];
         return *reinterpret_cast<const bf16x8*>(st + off);
     };
-    auto kraw8 = [&](const char* st, int mm) __attribute__((always_inline)) {
-        const int off = mm < 16 ? k_ra8[mm % 4] + 128 * (mm / 4) : k_rb8[mm - 16];
-        return *reinterpret_cast<const uint4*>(st + off);
+    auto kfrag8 = [&](const char* st, int kk) __attribute__((always_inline)) {
+        const int o0 = kk < 8 ? k8a[kk % 2][0] + 128 * (kk / 2) : k8b[0];
+        const int o1 = kk < 8 ? k8a[kk % 2][1] + 128 * (kk / 2) : k8b[1];
+        const uint4 w0 = *reinterpret_cast<const uint4*>(st + o0);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(st + o1);
+        return i32x8{(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w, (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
     };
+    const int unit_scales = 0x7f7f7f7f;  // E8M0 block scales of 2^0
     // the bf16 V^T operands: in the stage, or (FP8) in the widened tile
     auto vfrag = [&](const char* st, int j, int kst) __attribute__((always_inline)) {
         const char* vp = (F8 ? lds : st) + v_rd[j] + kst * 16 * C::VBROW_B;
@@ -508,26 +528,21 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
             // S^T = K Q^T
             f32x16 s;
             if constexpr (F8) {
-                // 16 codes per read feed two k-steps; the widening sits right
-                // before their MFMAs (each MFMA's s_nop covers the VALU write)
+                // 9 FP8 k-steps, two fragments read ahead
                 f32x16 s0, s1;
-                constexpr int NP = C::NQK / 2, WP = kWinW / 2;
-                uint4 fr[WP];
+                constexpr int W8 = 2;
+                i32x8 fk8[W8];
 #pragma unroll
-                for (int w = 0; w < WP; ++w) fr[w] = kraw8(st, w);
+                for (int w = 0; w < W8; ++w) fk8[w] = kfrag8(st, w);
 #pragma unroll
-                for (int mm = 0; mm < NP; ++mm) {
-                    const uint4 w = fr[mm % WP];
-                    const bf16x8 k0 = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(uint2{w.x, w.y}));
-                    const bf16x8 k1 = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16(uint2{w.z, w.w}));
-                    if (mm + WP < NP) fr[mm % WP] = kraw8(st, mm + WP);
-                    if (mm == 0) {
-                        qk_first(s0, k0, qf[0]);
-                        qk_first(s1, k1, qf[1]);
+                for (int o = 0; o < KK8; ++o) {
+                    f32x16& d = (o & 1) ? s1 : s0;
+                    if (o < 2) {
+                        qk8_first(d, fk8[o % W8], qf8[o], unit_scales);
                     } else {
-                        qk_next(s0, k0, qf[2 * mm]);
-                        qk_next(s1, k1, qf[2 * mm + 1]);
+                        qk8_next(d, fk8[o % W8], qf8[o], unit_scales);
                     }
+                    if (o + W8 < KK8) fk8[o % W8] = kfrag8(st, o + W8);
                 }
                 qk_fence(s0, s1);
                 s = s0 + s1;
