@@ -64,7 +64,9 @@ struct DecodeArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
-// per-tensor FP8: the few-row kernel where it serves, else the general kernel
+// per-tensor FP8: the few-row kernel up to 32 rows per KV head, the FP8 paged
+// prefill kernel (D = 128), the absorbed-MLA wide kernel (576/512), the few-row
+// kernel up to 64 rows, else the general kernel
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s);
 // sinks (optional): [hq] sink logits merged once per row (row % hq is its head);
 // stats_log2: write the merged LSE in base 2.

@@ -129,9 +129,10 @@ def test_full_size_fp8_decode_sampled():
     assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
 
 
-# ---- the general decode kernel in FP8: more than 16 rows per KV head, D = 64, 192/128 and
-# the absorbed-MLA 576/512 (cuDNN Frontend v1.32.0 Release Notes, "SDPA: wider native
-# forward support": native D64 per-tensor FP8 and Q/K 576 with V 512) -------------------
+# ---- FP8 past 16 rows per KV head: row groups of the few-row kernel, the general decode
+# kernel, D = 64, 192/128 and the absorbed-MLA 576/512 (cuDNN Frontend v1.32.0 Release
+# Notes, "SDPA: wider native forward support": native D64 per-tensor FP8 and Q/K 576 with
+# V 512) --------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("splits", [1, 3])
 def test_d128_mtp_rows_in_two_row_groups(splits):

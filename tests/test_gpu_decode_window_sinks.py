@@ -1,7 +1,8 @@
 """GPU parity of sdpa_decode_paged_ex (left sliding window, attention sinks, base-2 Stats)
 against the fp64 oracle, through every paged-decode kernel: the few-row kernel (bf16 D=64, 128, 256, 192/128 and
 per-tensor FP8, up to 64 rows per KV head in groups of 16), the absorbed-MLA wide kernel
-(576/512), the general decode kernel (past 64 rows per KV head) and the chunked-prefill path
+(576/512, any row count), the general decode kernel (past 64 rows per KV head where no other
+kernel applies) and the chunked-prefill path
 (prefill kernel over the page tables, with its (token, head) rows folded when there are few
 tokens).
 """
