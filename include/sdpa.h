@@ -209,6 +209,27 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
                                    int32_t num_splits);
 
 /*
+ * The kernel a paged decode call with these extents runs on: sdpa_decode_paged
+ * (and _ex, _noalloc) for dtype SDPA_BF16, sdpa_decode_paged_fp8 for
+ * SDPA_FP8_E4M3.  Host-only; reads no memory and makes no GPU call.  Returns
+ * one of SDPA_PATH_*, or 0 when those entry points decline the extents (the
+ * checks made here: dtype, head counts, (d_qk, d_v), page_size, num_splits,
+ * row strides, the 512-row limit; pointers, alignment, page-table and
+ * length arguments are checked only by the entry points themselves).
+ */
+enum {
+    SDPA_PATH_FEW_ROW = 1,         /* few-row streaming kernel, one 16-row group     */
+    SDPA_PATH_ROW_GROUPS = 2,      /* few-row kernel, 16-row groups (up to 64 rows)  */
+    SDPA_PATH_PREFILL = 3,         /* prefill kernel over the page tables            */
+    SDPA_PATH_PREFILL_FOLDED = 4,  /* the same with (token, head) rows folded        */
+    SDPA_PATH_WIDE = 5,            /* absorbed-MLA 576/512 MFMA kernel               */
+    SDPA_PATH_GENERAL = 6          /* general decode kernel                          */
+};
+int sdpa_decode_path(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                     int32_t d_v, int32_t page_size, int64_t k_st, int64_t v_st,
+                     int32_t num_splits, int32_t dtype);
+
+/*
  * Paged-KV decode with split-KV.
  *
  * Defines: query token t of sequence b sits at key position seq_lens[b]-s_q+t

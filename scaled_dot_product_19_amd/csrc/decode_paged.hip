@@ -351,25 +351,38 @@ static bool small_fits(const DecodeArgs& da) {
            (int64_t)da.batch * da.hkv * da.splits * ((rows + 15) / 16) <= INT32_MAX;
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) {
+// The kernel a decode call runs on (the order below is the selection order):
+// few-row kernel up to 16 rows per KV head (FP8: up to 32, in row groups
+// past 16), the paged prefill kernel (D 64 / 128 / 256 on suitable pages;
+// folded rows when the call has fewer tokens than an item), the absorbed-MLA
+// wide kernel, the few-row kernel in row groups up to kSmallRowsMax rows, and
+// the general kernel for the rest.
+DecodePath decode_path(const DecodeArgs& da) {
+    const int rows = da.sq * (da.hq / da.hkv);
     const bool small = small_fits(da);
-    if (small && da.sq * (da.hq / da.hkv) <= 16) return launch_decode_small(da, s);
-    if (prefill_paged_supported(da)) return launch_prefill_paged(da, s);
-    if (decode_wide_supported(da)) return launch_decode_wide(da, s);
-    if (small) return launch_decode_small(da, s);
-    return launch_generic(da, s, false);
+    if (small && rows <= (da.fp8 ? 32 : 16)) return rows <= 16 ? DecodePath::kFewRow : DecodePath::kRowGroups;
+    if (prefill_paged_supported(da)) return prefill_paged_folds(da) ? DecodePath::kPrefillFolded : DecodePath::kPrefill;
+    if (decode_wide_supported(da)) return DecodePath::kWide;
+    if (small) return DecodePath::kRowGroups;
+    return DecodePath::kGeneral;
 }
 
-hipError_t launch_decode_fp8(const DecodeArgs& da, hipStream_t s) {
-    // up to 32 rows per KV head two 16-row groups, each reading the codes, beat
-    // the FP8 prefill kernel's folded items (0.51 against 0.62 ms at 32 rows
-    // on B = 32 of the decode workload's sequences; 0.98 against 0.65 at 64)
-    const bool small = small_fits(da);
-    if (small && da.sq * (da.hq / da.hkv) <= 32) return launch_decode_small(da, s);
-    if (prefill_paged_supported(da)) return launch_prefill_paged(da, s);
-    if (decode_wide_supported(da)) return launch_decode_wide(da, s);
-    if (small) return launch_decode_small(da, s);
-    return launch_generic(da, s, true);
+static hipError_t launch_decode_path(const DecodeArgs& da, hipStream_t s, bool f8) {
+    switch (decode_path(da)) {
+        case DecodePath::kFewRow:
+        case DecodePath::kRowGroups: return launch_decode_small(da, s);
+        case DecodePath::kPrefill:
+        case DecodePath::kPrefillFolded: return launch_prefill_paged(da, s);
+        case DecodePath::kWide: return launch_decode_wide(da, s);
+        default: return launch_generic(da, s, f8);
+    }
 }
+
+hipError_t launch_decode_bf16(const DecodeArgs& da, hipStream_t s) { return launch_decode_path(da, s, false); }
+
+// FP8: up to 32 rows per KV head two 16-row groups, each reading the codes,
+// beat the FP8 prefill kernel's folded items (0.51 against 0.62 ms at 32 rows
+// on B = 32 of the decode workload's sequences; 0.98 against 0.65 at 64)
+hipError_t launch_decode_fp8(const DecodeArgs& da, hipStream_t s) { return launch_decode_path(da, s, true); }
 
 }  // namespace sdpa

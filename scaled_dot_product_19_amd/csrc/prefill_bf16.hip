@@ -1138,6 +1138,8 @@ bool prefill_paged_supported(const DecodeArgs& d) {
     return d.sq >= paged_item_tokens(d.hq / d.hkv, paged_waves(d.dqk)) || paged_fold(d) > 0;
 }
 
+bool prefill_paged_folds(const DecodeArgs& d) { return prefill_paged_supported(d) && paged_fold(d) > 0; }
+
 template <int D, int BN, int S, int NW, bool PP, bool F8>
 hipError_t launch_prefill_paged_t(const DecodeArgs& d, hipStream_t s) {
     static_assert(NW == (D == 256 ? 4 : 8), "the waves paged_waves assumes");

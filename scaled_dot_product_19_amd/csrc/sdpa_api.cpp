@@ -253,6 +253,31 @@ size_t sdpa_decode_workspace_bytes(int32_t batch, int32_t s_q, int32_t h_q, int3
     return o_bytes + (size_t)num_splits * rows * sizeof(float);
 }
 
+int sdpa_decode_path(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t d_qk,
+                     int32_t d_v, int32_t page_size, int64_t k_st, int64_t v_st,
+                     int32_t num_splits, int32_t dtype) {
+    const bool fp8 = dtype == SDPA_FP8_E4M3;
+    if (!fp8 && dtype != SDPA_BF16) return 0;
+    if (batch < 0 || s_q <= 0 || h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0) return 0;
+    if (!sdpa::decode_supported(d_qk, d_v) || page_size <= 0 || page_size % 16 != 0) return 0;
+    if (num_splits < 1 || num_splits > 256 || k_st < d_qk || v_st < d_v) return 0;
+    if (fp8 && (k_st % 16 != 0 || v_st % 16 != 0)) return 0;
+    sdpa::DecodeArgs a{};
+    a.batch = batch;
+    a.sq = s_q;
+    a.hq = h_q;
+    a.hkv = h_kv;
+    a.dqk = d_qk;
+    a.dv = d_v;
+    a.page = page_size;
+    a.k_st = k_st;
+    a.v_st = v_st;
+    a.splits = num_splits;
+    a.fp8 = fp8 ? 1 : 0;
+    if ((int64_t)s_q * (h_q / h_kv) > 512 && !sdpa::prefill_paged_supported(a)) return 0;
+    return (int)sdpa::decode_path(a);
+}
+
 static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t k_st,
                        int64_t k_sh, const void* v_pool, int64_t v_sp, int64_t v_st, int64_t v_sh,
                        const int32_t* page_table_k, const int32_t* page_table_v,

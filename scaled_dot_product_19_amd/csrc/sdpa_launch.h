@@ -68,6 +68,13 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 // prefill kernel (D = 128), the absorbed-MLA wide kernel (576/512), the few-row
 // kernel up to 64 rows, else the general kernel
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s);
+// The kernel both decode launchers pick for a call (values as SDPA_PATH_* in sdpa.h).
+enum class DecodePath : int32_t {
+    kFewRow = 1, kRowGroups = 2, kPrefill = 3, kPrefillFolded = 4, kWide = 5, kGeneral = 6
+};
+DecodePath decode_path(const DecodeArgs& a);
+// The paged prefill kernel would fold the call's (token, head) rows.
+bool prefill_paged_folds(const DecodeArgs& d);
 // sinks (optional): [hq] sink logits merged once per row (row % hq is its head);
 // stats_log2: write the merged LSE in base 2.
 hipError_t launch_combine(const float* o_part, const float* lse_part, int32_t splits,

@@ -40,7 +40,7 @@ LSE_HEAD_MAJOR = 3
 
 # every symbol include/sdpa.h declares
 EXPORTS = ("sdpa_prefill_thd", "sdpa_prefill_thd_ex", "sdpa_prefill_thd_fp8",
-           "sdpa_decode_workspace_bytes", "sdpa_decode_paged", "sdpa_decode_paged_fp8",
+           "sdpa_decode_workspace_bytes", "sdpa_decode_path", "sdpa_decode_paged", "sdpa_decode_paged_fp8",
            "sdpa_decode_paged_ex", "sdpa_decode_paged_noalloc", "sdpa_splitkv_combine", "sdpa_status_string",
            "sdpa_last_error_detail", "sdpa_version")
 
@@ -84,6 +84,8 @@ def load():
                                          I32, I32, I32, P, P, P, P]
     lib.sdpa_decode_workspace_bytes.restype = SZ
     lib.sdpa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.sdpa_decode_path.restype = ctypes.c_int
+    lib.sdpa_decode_path.argtypes = [I32, I32, I32, I32, I32, I32, I32, I64, I64, I32, I32]
     lib.sdpa_decode_paged.restype = ctypes.c_int
     lib.sdpa_decode_paged.argtypes = [P, P, I64, I64, I64, P, I64, I64, I64, P, P, I32, P, I32,
                                       I32, I32, I32, I32, I32, I32, I32, F, I32, I32, P, SZ, P,
@@ -148,6 +150,19 @@ def version() -> int:
 
 def decode_workspace_bytes(batch: int, s_q: int, h_q: int, d_v: int, num_splits: int) -> int:
     return int(load().sdpa_decode_workspace_bytes(batch, s_q, h_q, d_v, num_splits))
+
+
+PATH_NAMES = {1: "few_row", 2: "row_groups", 3: "prefill", 4: "prefill_folded", 5: "wide",
+              6: "general"}
+
+
+def decode_path(batch: int, s_q: int, h_q: int, h_kv: int, d_qk: int, d_v: int, page_size: int,
+                k_st: int, v_st: int, num_splits: int, fp8: bool = False) -> str:
+    """Name of the kernel sdpa_decode_paged (fp8: sdpa_decode_paged_fp8) runs for these
+    extents, or "" when the call is declined (host-only, no GPU call)."""
+    p = int(load().sdpa_decode_path(batch, s_q, h_q, h_kv, d_qk, d_v, page_size, k_st, v_st,
+                                    num_splits, SDPA_FP8_E4M3 if fp8 else SDPA_BF16))
+    return PATH_NAMES.get(p, "")
 
 
 def prefill_thd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,

@@ -107,3 +107,13 @@ def nproc_for_oracle() -> int:
 
 def finite_lse_frac(lse: np.ndarray) -> float:
     return float(np.isfinite(lse).mean()) if lse.size else math.nan
+
+
+def path_of(pc, splits=None, fp8=False):
+    """The decode kernel the library selects for a PagedCase (host-only query)."""
+    from scaled_dot_product_19_amd import sdpa
+    S = pc.num_splits if splits is None else splits
+    k_st = int(pc.k_pool.stride(1)) if pc.k_pool.dim() == 4 else pc.hkv * int(pc.q.shape[3])
+    v_st = int(pc.v_pool.stride(1)) if pc.v_pool.dim() == 4 else pc.hkv * int(pc.v_pool.shape[3])
+    return sdpa.decode_path(pc.batch, pc.sq, pc.hq, pc.hkv, int(pc.q.shape[3]),
+                            int(pc.v_pool.shape[3]), pc.page_size, k_st, v_st, S, fp8=fp8)

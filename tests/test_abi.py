@@ -335,3 +335,37 @@ def test_decode_ex_declines_variants_at_d256():
     rc, detail = _decode_ex(dqk=256, dv=256, k_sp=64 * 8 * 256, k_st=8 * 256, k_sh=256,
                             v_sp=64 * 8 * 256, v_st=8 * 256, v_sh=256, window=37)
     assert rc == sdpa.SDPA_ERR_UNSUPPORTED and "d = 256" in detail
+
+
+# Kernel selection of the paged decode entry points (host-only query, no GPU): a few-row
+# kernel, row groups, the prefill kernel over the page tables (folded rows for few
+# tokens), the absorbed-MLA wide kernel, the general kernel; "" = declined.
+@pytest.mark.parametrize("case,path", [
+    # (batch, s_q, h_q, h_kv, d_qk, d_v, page, fp8)
+    ((64, 1, 32, 8, 128, 128, 64, False), "few_row"),          # the paged decode workload
+    ((4, 4, 32, 8, 128, 128, 64, False), "few_row"),           # 16 rows
+    ((4, 8, 32, 8, 128, 128, 64, False), "prefill_folded"),    # 32 rows
+    ((4, 8, 32, 8, 128, 128, 32, False), "row_groups"),        # 32 rows, 32-key pages
+    ((4, 32, 32, 8, 128, 128, 32, False), "general"),          # 128 rows, 32-key pages
+    ((2, 1024, 32, 8, 128, 128, 64, False), "prefill"),        # chunked prefill
+    ((2, 5, 28, 4, 128, 128, 64, False), "prefill_folded"),    # G 7
+    ((2, 2, 16, 1, 256, 256, 32, False), "prefill_folded"),    # D 256, 32 rows
+    ((2, 16, 8, 2, 64, 64, 64, False), "prefill_folded"),      # D 64, 64 rows
+    ((2, 16, 8, 2, 64, 64, 128, False), "prefill_folded"),
+    ((2, 2, 64, 2, 192, 128, 64, False), "row_groups"),        # 192/128, 64 rows
+    ((2, 4, 64, 2, 192, 128, 64, False), "general"),           # 192/128, 128 rows
+    ((32, 2, 128, 1, 576, 512, 64, False), "wide"),            # the MLA-shaped workload
+    ((32, 1, 16, 1, 576, 512, 64, False), "wide"),             # 16 rows
+    ((32, 1, 16, 1, 576, 512, 16, False), "general"),          # 16-key pages
+    ((64, 1, 32, 8, 128, 128, 64, True), "few_row"),           # FP8 paged decode workload
+    ((4, 8, 32, 8, 128, 128, 64, True), "row_groups"),         # FP8 32 rows
+    ((4, 16, 32, 8, 128, 128, 64, True), "prefill_folded"),    # FP8 64 rows
+    ((2, 2, 16, 1, 256, 256, 32, True), "row_groups"),         # FP8 D 256 stays off the prefill
+    ((32, 2, 128, 1, 576, 512, 64, True), "wide"),             # FP8 MLA
+    ((2, 1024, 32, 8, 64, 64, 32, False), ""),                 # > 512 rows, 32-key pages
+    ((2, 1, 32, 8, 96, 96, 64, False), ""),                    # head dim not served
+])
+def test_decode_path_selection(case, path):
+    b, sq, hq, hkv, dqk, dv, page, fp8 = case
+    got = sdpa.decode_path(b, sq, hq, hkv, dqk, dv, page, hkv * dqk, hkv * dv, 8, fp8=fp8)
+    assert got == path, (case, got)

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from scaled_dot_product_19_amd import inputs, sdpa
-from tests.helpers import check_lse, check_o, log, oracle_decode, sample_rows, to_dev
+from tests.helpers import check_lse, check_o, log, oracle_decode, path_of, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -39,8 +39,8 @@ def run(pc, splits=None):
 
 def parity(pc, sel_rows=None):
     log("chunked prefill parity: %s lens=%s sq=%d hq=%d hkv=%d page=%d splits=%d causal=%s "
-        "scale=%g" % (pc.name, pc.seq_lens.tolist()[:8], pc.sq, pc.hq, pc.hkv, pc.page_size,
-                      pc.num_splits, pc.causal, pc.scale))
+        "scale=%g kernel=%s" % (pc.name, pc.seq_lens.tolist()[:8], pc.sq, pc.hq, pc.hkv,
+                                pc.page_size, pc.num_splits, pc.causal, pc.scale, path_of(pc)))
     o, l = run(pc)
     rows = pc.batch * pc.sq * pc.hq
     o_ref, l_ref = oracle_decode(pc, sel_rows=sel_rows)

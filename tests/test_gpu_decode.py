@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from scaled_dot_product_19_amd import inputs, sdpa
-from tests.helpers import check_lse, check_o, log, oracle_decode, sample_rows, to_dev
+from tests.helpers import check_lse, check_o, log, oracle_decode, path_of, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +31,9 @@ def run(pc: inputs.PagedCase, splits=None, workspace=None, out=None, lse=None, s
 
 def parity(pc, splits=None):
     S = pc.num_splits if splits is None else splits
-    log("decode parity: %s lens=%s sq=%d hq=%d hkv=%d d=%d/%d page=%d splits=%d" % (
+    log("decode parity: %s lens=%s sq=%d hq=%d hkv=%d d=%d/%d page=%d splits=%d kernel=%s" % (
         pc.name, pc.seq_lens.tolist()[:8], pc.sq, pc.hq, pc.hkv, pc.q.shape[3],
-        pc.v_pool.shape[3], pc.page_size, S))
+        pc.v_pool.shape[3], pc.page_size, S, path_of(pc, S)))
     o, l = run(pc, splits=S)
     o_ref, l_ref = oracle_decode(pc)
     e_o = check_o(o, o_ref)

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from scaled_dot_product_19_amd import inputs, sdpa
-from tests.helpers import check_lse, check_o, log, oracle_decode, sample_rows, to_dev
+from tests.helpers import check_lse, check_o, log, oracle_decode, path_of, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -46,9 +46,9 @@ def run(pc, splits=None):
 
 
 def parity(pc):
-    log("fp8 decode parity: %s lens=%s sq=%d hq=%d hkv=%d d=%d page=%d splits=%d descale=%s" % (
-        pc.name, pc.seq_lens.tolist()[:8], pc.sq, pc.hq, pc.hkv, pc.q.shape[3], pc.page_size,
-        pc.num_splits, pc.descale))
+    log("fp8 decode parity: %s lens=%s sq=%d hq=%d hkv=%d d=%d page=%d splits=%d descale=%s "
+        "kernel=%s" % (pc.name, pc.seq_lens.tolist()[:8], pc.sq, pc.hq, pc.hkv, pc.q.shape[3],
+                       pc.page_size, pc.num_splits, pc.descale, path_of(pc, fp8=True)))
     o, l = run(pc)
     o_ref, l_ref = oracle_decode(pc, descale=pc.descale)
     e_o = check_o(o, o_ref)

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from scaled_dot_product_19_amd import inputs, sdpa
-from tests.helpers import check_lse, check_o, log, oracle_decode, sample_rows, to_dev
+from tests.helpers import check_lse, check_o, log, oracle_decode, path_of, sample_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -41,9 +41,10 @@ def run_ex(pc, window, sinks, log2, splits, out_lse=True):
 
 def parity(pc, window, sinks, log2, splits):
     log("decode_ex parity: %s lens=%s sq=%d hq=%d hkv=%d d=%d/%d page=%d splits=%d window=%d "
-        "sinks=%s log2=%s" % (pc.name, pc.seq_lens.tolist()[:6], pc.sq, pc.hq, pc.hkv,
-                              pc.q.shape[3], pc.v_pool.shape[3], pc.page_size, splits, window,
-                              sinks is not None, log2))
+        "sinks=%s log2=%s kernel=%s" % (pc.name, pc.seq_lens.tolist()[:6], pc.sq, pc.hq, pc.hkv,
+                                        pc.q.shape[3], pc.v_pool.shape[3], pc.page_size, splits,
+                                        window, sinks is not None, log2,
+                                        path_of(pc, splits, fp8=pc.descale is not None)))
     o, l = run_ex(pc, window, sinks, log2, splits)
     o_ref, l_ref = oracle_decode(pc, num_splits=splits, window=window,
                                  sinks=None if sinks is None else sinks.double().numpy(),
