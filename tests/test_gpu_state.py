@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from scaled_dot_product_19_amd import inputs, sdpa
-from tests.helpers import check_lse, check_o, log, oracle_decode, oracle_prefill, to_dev
+from tests.helpers import path_of, check_lse, check_o, log, oracle_decode, oracle_prefill, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -23,13 +23,17 @@ def _gpu():
 
 
 def test_captured_prefill_and_decode_replayed_on_new_inputs():
-    # one prefill (padded LSE: the -inf fill kernel is captured too) and one split decode
-    # (split kernel + combine) captured once, replayed on three different inputs, with
-    # eager work between the replays
+    # one prefill (padded LSE: the -inf fill kernel is captured too), one split decode
+    # (split kernel + combine) and one multi-token decode on the paged prefill kernel
+    # (folded rows, its persistent work queue) captured once, replayed on three different
+    # inputs, with eager work between the replays
     pre = [inputs.thd_case(4100 + r, hq=8, hkv=2, d_qk=128, lengths=[100, 37, 260],
                            name="graph_prefill") for r in range(3)]
     dec = [inputs.paged_case(4200 + r, 3, 1, 32, 8, 128, 128, 64, lengths=[90, 700, 1500],
                              num_splits=4, poison=True, name="graph_decode") for r in range(3)]
+    fol = [inputs.paged_case(4300 + r, 2, 4, 32, 1, 128, 128, 64, lengths=[3, 900],
+                             num_splits=2, poison=True, name="graph_folded") for r in range(3)]
+    assert path_of(fol[0]) == "prefill_folded"
     # the captured launches read these buffers; each replay copies new inputs into them
     q, k, v = to_dev(pre[0].q), to_dev(pre[0].k), to_dev(pre[0].v)
     cu = to_dev(pre[0].cu_q)
@@ -42,12 +46,20 @@ def test_captured_prefill_and_decode_replayed_on_new_inputs():
     l_d = torch.empty((3, 1, 32), dtype=torch.float32, device="cuda")
     ws = torch.empty(sdpa.decode_workspace_bytes(3, 1, 32, 128, 4), dtype=torch.uint8,
                      device="cuda")
+    fq, fkp, fvp = to_dev(fol[0].q), to_dev(fol[0].k_pool), to_dev(fol[0].v_pool)
+    fptk, fptv, fsl = to_dev(fol[0].pt_k), to_dev(fol[0].pt_v), to_dev(fol[0].seq_lens)
+    o_f = torch.empty((2, 4, 32, 128), dtype=torch.bfloat16, device="cuda")
+    l_f = torch.empty((2, 4, 32), dtype=torch.float32, device="cuda")
+    ws_f = torch.empty(sdpa.decode_workspace_bytes(2, 4, 32, 128, 2), dtype=torch.uint8,
+                       device="cuda")
 
     def calls():
         sdpa.prefill_thd(q, k, v, cu, cu, 260, 260, pre[0].scale, True, out=o_p, lse=l_p,
                          lse_layout=sdpa.LSE_PADDED, lse_s_max=s_max)
         sdpa.decode_paged(dq, kp, vp, ptk, ptv, sl, 1500, dec[0].scale, True, num_splits=4,
                           workspace=ws, out=o_d, lse=l_d)
+        sdpa.decode_paged(fq, fkp, fvp, fptk, fptv, fsl, 900, fol[0].scale, True, num_splits=2,
+                          workspace=ws_f, out=o_f, lse=l_f)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -68,6 +80,13 @@ def test_captured_prefill_and_decode_replayed_on_new_inputs():
         vp.copy_(to_dev(dec[r].v_pool))
         ptk.copy_(to_dev(dec[r].pt_k))
         ptv.copy_(to_dev(dec[r].pt_v))
+        fq.copy_(to_dev(fol[r].q))
+        fkp.copy_(to_dev(fol[r].k_pool))
+        fvp.copy_(to_dev(fol[r].v_pool))
+        fptk.copy_(to_dev(fol[r].pt_k))
+        fptv.copy_(to_dev(fol[r].pt_v))
+        o_f.fill_(5.0)
+        l_f.fill_(5.0)
         o_p.fill_(5.0)
         l_p.fill_(5.0)
         o_d.fill_(5.0)
@@ -75,10 +94,10 @@ def test_captured_prefill_and_decode_replayed_on_new_inputs():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = [t.clone() for t in (o_p, l_p, o_d, l_d)]
+        got = [t.clone() for t in (o_p, l_p, o_d, l_d, o_f, l_f)]
         calls()  # the same calls eagerly, on the same inputs
         torch.cuda.synchronize()
-        for g, e in zip(got, (o_p, l_p, o_d, l_d)):
+        for g, e in zip(got, (o_p, l_p, o_d, l_d, o_f, l_f)):
             assert torch.equal(g, e), "replay %d differs from the eager call" % r
         o_ref, l_ref = oracle_prefill(pre[r])
         check_o(got[0], o_ref)
@@ -89,6 +108,9 @@ def test_captured_prefill_and_decode_replayed_on_new_inputs():
         od_ref, ld_ref = oracle_decode(dec[r])
         check_o(got[2], od_ref)
         check_lse(got[3], ld_ref)
+        of_ref, lf_ref = oracle_decode(fol[r])
+        check_o(got[4], of_ref)
+        check_lse(got[5], lf_ref)
 
 
 def test_many_calls_in_flight_on_four_streams():
