@@ -196,3 +196,19 @@ def test_row_groups(shape):
     o, l, _, _ = parity(pc)
     # sequence 0 holds 2 keys: with s_q > 2 its first token sees none
     assert torch.all(o[0, 0] == 0) and torch.all(l[0, 0] == -math.inf)
+
+
+@pytest.mark.timeout(600)
+def test_mla_sixteen_heads_workload_sampled():
+    # the MLA-shaped workload's sequences with 16 heads of one token (the 128 heads split
+    # over 8 GPUs): 16 rows per KV head, one row block of O^T per wave in the wide kernel
+    pc = inputs.paged_case(inputs.SEED_BASE + 5, 32, 1, 16, 1, 576, 512, 64, lo=4096, hi=16384,
+                           num_splits=16, poison=True, name="mla_decode_16_heads")
+    assert path_of(pc) == "wide"
+    o, l = run(pc)
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 192, 2014, must=[0, rows - 1])
+    o_ref, l_ref = oracle_decode(pc, sel_rows=sel)
+    si = torch.from_numpy(sel).cuda()
+    check_o(o.reshape(rows, -1)[si], o_ref)
+    check_lse(l.reshape(rows)[si], l_ref)

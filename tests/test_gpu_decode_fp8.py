@@ -357,3 +357,21 @@ def test_fp8_paged_prefill_kernel(case):
     assert torch.isfinite(o.float()).all()
     if causal and lengths[0] < sq:
         assert torch.all(o[0, 0] == 0) and torch.all(l[0, 0] == -np.inf)
+
+
+@pytest.mark.timeout(600)
+def test_fp8_folded_rows_decode_workload_sampled():
+    # the paged decode workload's sequences in FP8 (B = 64, 32/8 heads, D = 128, page 64,
+    # L U[512, 32768], 8 splits) with 16 query tokens: 64 folded rows per KV head on the FP8
+    # prefill kernel over the page tables
+    pc = inputs.fp8_paged_case(inputs.SEED_BASE + 3, 64, 16, 32, 8, 128, 64, lo=512, hi=32768,
+                               num_splits=8, poison=True, name="fp8_folded_decode_workload")
+    assert path_of(pc, fp8=True) == "prefill_folded"
+    o, l = run(pc)
+    rows = pc.batch * pc.sq * pc.hq
+    sel = sample_rows(rows, 256, 3042, must=[0, rows - 1])
+    o_ref, l_ref = oracle_decode(pc, sel_rows=sel, descale=pc.descale)
+    si = torch.from_numpy(sel).cuda()
+    check_o(o.reshape(rows, -1)[si], o_ref)
+    check_lse(l.reshape(rows)[si], l_ref)
+    assert torch.isfinite(o.float()).all()
