@@ -326,7 +326,7 @@ int sdpa_decode_paged(const void* q,
  * prefill kernel over the page tables (FP8 MFMA for Q K^T, V codes widened
  * to bf16 in LDS), either for s_q of at least one work item or, with fewer
  * tokens, with the (token, head) rows of each KV head's group folded into
- * its 256-row items.  (576, 512) with page_size % 32 == 0: the absorbed-MLA
+ * its 256-row items.  (576, 512), any page size: the absorbed-MLA
  * wide kernel, its tiles DMA'd as codes, Q K^T on the FP8 MFMA and V widened
  * exactly to bf16 in LDS for a bf16 P V.
  * The rest widen the codes exactly to bf16 as they are loaded and use bf16

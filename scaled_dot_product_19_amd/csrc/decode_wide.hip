@@ -9,10 +9,11 @@
 //
 // Work-group = 4 waves = 128 query rows (row r of a KV head is query token
 // r / G, head kvh G + r % G) x one split-KV chunk of one sequence; chunks of
-// the longest sequences are dispatched first.  Per tile of 32 keys (a tile
-// never straddles a page: page_size % 32 == 0):
+// the longest sequences are dispatched first.  Per tile of 32 keys (tiles
+// start on multiples of 16 keys and may span pages when page_size is 16):
 //   K tile (32 x 576) and V tile (32 x 512) gathered from their pages into
 //   LDS by buffer_load_dwordx4 ... lds (lane L's 16 bytes land at M0 + 16 L),
+//   each wave its own 8 rows (which lie in one page: page_size % 8 == 0),
 //   one 1 KB row per instruction, in a ring of two K and two V slots that
 //   refill independently.  Bank conflicts are
 //   avoided by a 16-byte pad after dims 0..511 of each K row, an XOR swizzle
@@ -280,7 +281,9 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     const bool wave_rows = rb * 128 + wave * 32 < a.rows;
     const int kv_end_w = wave_rows ? max(lo, end_of(r_w1)) : lo;
     const int nomask_end = wave_rows ? max(lo, end_of(r_w0)) : lo;
-    const int lim = a.causal ? L - a.sq + tq : L - 1;  // last visible key of this lane
+    // last visible key of this lane within the chunk (a chunk of 16-key pages can
+    // end inside a tile: the keys past hi are masked, not merely zero-filled)
+    const int lim = min(hi - 1, a.causal ? L - a.sq + tq : L - 1);
     // first visible key of this lane (left window), and the largest of the
     // wave's rows (its last token's): tiles starting below it need the lower mask
     const bool win = VAR && a.window > 0;
@@ -301,9 +304,12 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     const uint32_t k_st2 = C::EB * (uint32_t)a.k_st, v_st2 = C::EB * (uint32_t)a.v_st;
     const uint32_t l16 = 16u * (uint32_t)lane;
     const int rb_row = wave * C::RPW + lane / (F8 ? 4 : 8);
+    // (source offsets count from the wave's first row of the tile; the
+    // swizzles follow the row within the tile)
+    const uint32_t rb_rel = (uint32_t)(rb_row - wave * C::RPW);
     const uint32_t kb_src =
-        F8 ? (uint32_t)rb_row * k_st2 + 512u + 16u * (uint32_t)((lane & 3) ^ ((rb_row >> 1) & 3))
-           : (uint32_t)rb_row * k_st2 + 1024u + 16u * (uint32_t)((lane & 7) ^ (rb_row & 7));
+        F8 ? rb_rel * k_st2 + 512u + 16u * (uint32_t)((lane & 3) ^ ((rb_row >> 1) & 3))
+           : rb_rel * k_st2 + 1024u + 16u * (uint32_t)((lane & 7) ^ (rb_row & 7));
     const uint32_t hl = (uint32_t)(lane >> 5);  // FP8: second row of a 2-row instruction
     const uint32_t ka_v = 16u * (((uint32_t)lane & 31u) ^ hl), ka_w = hl * k_st2;
     const uint32_t va_v = hl * v_st2 + 16u * ((uint32_t)lane & 31u);
@@ -338,14 +344,18 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
         u32x4 kr, vr;
         uint32_t st;
     };
+    // Each wave moves its own 8 rows of a tile (keys key0 + 8 w ..), which lie
+    // in one page (page_size % 8 == 0 and tiles start on multiples of 16), so
+    // a tile may span pages; the wave's buffer resource starts at its first row.
     auto plan = [&](int t, int stage) __attribute__((always_inline)) {
-        const int key0 = lo + t * C::BN;
-        const int nvalid = min(C::BN, kv_end - key0);
-        const int rel = min(key0 / a.page - pg0, n_pages - 1);
-        if (rel - pwin >= 64) load_window(rel);  // uniform
+        const int keyw = lo + t * C::BN + wave * C::RPW;
+        const int nvalid = min(C::RPW, kv_end - keyw);
+        const int rel = min(keyw / a.page - pg0, n_pages - 1);
+        // uniform; the second pass of a chunk starts again below the window
+        if (rel - pwin >= 64 || rel < pwin) load_window(rel);
         const int pkp = __builtin_amdgcn_readlane(pk, rel - pwin);
         const int pvp = __builtin_amdgcn_readlane(pv, rel - pwin);
-        const int slot = key0 % a.page;
+        const int slot = keyw % a.page;
         // rows at or past nvalid fall outside the buffer range and arrive as zeros
         const uint32_t kn = nvalid > 0 ? (uint32_t)(nvalid - 1) * k_st2 + C::EB * DQK : 0u;
         const uint32_t vn = nvalid > 0 ? (uint32_t)(nvalid - 1) * v_st2 + C::EB * DV : 0u;
@@ -364,14 +374,14 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
             if (j < NA) {
                 const int row = wave * C::RPW + 2 * j;
                 dma16_stream(d.kr, d.st + row * C::KA_PITCH,
-                             xor_add3_here(ka_v, 32u * (uint32_t)j, ka_w, (uint32_t)row * k_st2));
+                             xor_add3_here(ka_v, 32u * (uint32_t)j, ka_w, (uint32_t)(2 * j) * k_st2));
             } else if (lane < 32) {
                 dma16_stream(d.kr, d.st + C::KB_OFF + wave * 512, kb_src);
             }
         } else {
             if (j < C::RPW) {
                 const int row = wave * C::RPW + j;
-                dma16_stream(d.kr, d.st + row * C::KA_PITCH, add_here(l16, (uint32_t)row * k_st2));
+                dma16_stream(d.kr, d.st + row * C::KA_PITCH, add_here(l16, (uint32_t)j * k_st2));
             } else {
                 dma16_stream(d.kr, d.st + C::KB_OFF + wave * 1024, kb_src);
             }
@@ -380,11 +390,11 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
     auto v_piece = [&](const DmaPlan& d, int j) __attribute__((always_inline)) {
         if constexpr (F8) {
             const int row = wave * C::RPW + 2 * j;
-            dma16_stream(d.vr, d.st + C::V_OFF + row * C::VROW_B, add_here(va_v, (uint32_t)row * v_st2));
+            dma16_stream(d.vr, d.st + C::V_OFF + row * C::VROW_B, add_here(va_v, (uint32_t)(2 * j) * v_st2));
         } else {
             const int row = wave * C::RPW + j;
             dma16_stream(d.vr, d.st + C::V_OFF + row * C::VROW_B,
-                  xor_add_here(l16, 64u * (uint32_t)(row & 3), (uint32_t)row * v_st2));
+                  xor_add_here(l16, 64u * (uint32_t)(row & 3), (uint32_t)j * v_st2));
         }
     };
     // the ring's first tiles: K and V of tile 0, K of tile 1
@@ -790,7 +800,7 @@ __global__ __launch_bounds__(256, 1) void decode_wide_kernel(WideArgs a) {
 
 bool decode_wide_supported(const DecodeArgs& a) {
     const int rows = a.sq * (a.hq / a.hkv);
-    return a.dqk == 576 && a.dv == 512 && rows > 0 && a.page % 32 == 0;
+    return a.dqk == 576 && a.dv == 512 && rows > 0 && a.page % 16 == 0;
 }
 
 namespace {

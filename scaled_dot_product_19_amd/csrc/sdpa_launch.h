@@ -104,7 +104,7 @@ hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t s);
 bool prefill_paged_supported(const DecodeArgs& a);
 hipError_t launch_prefill_paged(const DecodeArgs& a, hipStream_t s);
 
-// Absorbed-MLA decode (d_qk = 576, d_v = 512, page_size % 32 == 0, any
+// Absorbed-MLA decode (d_qk = 576, d_v = 512, any page size, any
 // number of query rows per KV head): the MFMA kernel of decode_wide.hip.
 bool decode_wide_supported(const DecodeArgs& a);
 hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t s);

@@ -356,7 +356,7 @@ def test_decode_ex_declines_variants_at_d256():
     ((2, 4, 64, 2, 192, 128, 64, False), "general"),           # 192/128, 128 rows
     ((32, 2, 128, 1, 576, 512, 64, False), "wide"),            # the MLA-shaped workload
     ((32, 1, 16, 1, 576, 512, 64, False), "wide"),             # 16 rows
-    ((32, 1, 16, 1, 576, 512, 16, False), "general"),          # 16-key pages
+    ((32, 1, 16, 1, 576, 512, 16, False), "wide"),             # 16-key pages
     ((64, 1, 32, 8, 128, 128, 64, True), "few_row"),           # FP8 paged decode workload
     ((4, 8, 32, 8, 128, 128, 64, True), "row_groups"),         # FP8 32 rows
     ((4, 16, 32, 8, 128, 128, 64, True), "prefill_folded"),    # FP8 64 rows

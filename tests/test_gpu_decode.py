@@ -152,6 +152,27 @@ def test_mla_negative_and_zero_scale(scale):
     parity(pc)
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_mla_16_key_pages(splits):
+    # 16-key pages: a 32-key tile spans two pages, each wave's 8 rows come from one
+    pc = inputs.paged_case(2015, 3, 2, 64, 1, 576, 512, 16, lengths=[9, 333, 2100],
+                           num_splits=splits, causal=True, poison=True, name="mla_page16")
+    assert path_of(pc) == "wide"
+    parity(pc)
+
+
+def test_mla_second_pass_reloads_the_page_window():
+    # one chunk of 188 16-key pages (the page-id window of 64 reloads twice) and a late
+    # large logit, so the work-group runs the chunk a second time from its first page
+    pc = inputs.paged_case(2016, 1, 2, 128, 1, 576, 512, 16, lengths=[3000], num_splits=1,
+                           causal=True, poison=True, name="mla_rerun_window")
+    key = 40
+    page = int(pc.pt_k[0, key // pc.page_size])
+    pc.k_pool[page, key % pc.page_size, 0] = (1.5 * pc.q[0, 1, 3].float()).to(pc.k_pool.dtype)
+    o, l, _, _ = parity(pc)
+    assert float(l[0, 1, 3]) > 30.0
+
+
 def test_mla_late_large_logit_takes_second_pass():
     # key 40 of sequence 0 is 1.5 x the query of (token 1, head 3): its logit
     # (~36 nats) exceeds the first tile's maxima by far more than 2^32, so the

@@ -202,7 +202,7 @@ def test_512_rows_per_kv_head_and_past_them():
 
 
 # ---- the absorbed-MLA wide kernel in FP8 (576/512 codes, more than 16 rows per KV head,
-# pages of a multiple of 32 keys) ---------------------------------------------------------
+# any page size) ----------------------------------------------------------------------------
 
 def mla8(seed, batch, sq, hq, lengths=None, page=64, splits=1, causal=True, scale=None,
          lo=0, hi=0, name="fp8_mla"):
@@ -264,6 +264,13 @@ def test_mla_wide_fp8_late_large_logit_takes_second_pass():
     pc = dataclasses.replace(pc, q=q8, k_pool=k8, v_pool=v8, descale=(dq, dk, dv))
     o, l, _, _ = parity(pc)
     assert float(l[0, 1, 3]) > 30.0
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_mla_wide_fp8_16_key_pages(splits):
+    pc = mla8(3043, 3, 2, 64, lengths=[9, 333, 2100], page=16, splits=splits)
+    assert path_of(pc, fp8=True) == "wide"
+    parity(pc)
 
 
 def test_mla_wide_fp8_descales_read_on_the_device():
