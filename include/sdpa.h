@@ -269,21 +269,20 @@ int sdpa_decode_path(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int3
  * Supported: dtype SDPA_BF16; (d_qk, d_v) in {(64,64), (128,128), (256,256),
  * (192,128), (576,512)}; page_size a multiple of 16; 1 <= num_splits <= 256;
  * s_q * (h_q/h_kv) <= 512 query rows per KV head, or any larger s_q when
- * d_qk = d_v = 64 or 128 with page_size a multiple of 64, or d_qk = d_v = 256
- * with page_size a multiple of 32, and k_st, v_st < 2^22.
+ * d_qk = d_v is 64, 128 or 256 and k_st, v_st < 2^22, or with (576, 512).
  *
  * Chunked prefill over the paged cache is this same call with s_q = the
  * chunk's tokens (the last s_q of each cache; v1.31.0 "SDPA: paged KV,
  * split-KV, and engine selection", paged D128 prefill and chunked-prefill
  * selection; the context phase of v1.28.0 "Samples, Benchmarks, and Tests",
  * 512/1024-token chunks against 64k/128k caches).  With d_qk = d_v = 128,
- * page_size % 64 == 0, k_st, v_st < 2^22 and s_q of at least one prefill work
- * item (64 tokens when h_q/h_kv is a multiple of 4, 128 when it is 2 mod 4,
- * 256 when odd) it runs on the prefill kernel, which reads its 64-key K/V
- * tiles through the page tables; num_splits > 1 then writes the same partials
- * as decode.  d_qk = d_v = 256 with page_size % 32 == 0 likewise runs on the
- * D = 256 prefill kernel (32-key tiles, items of 32, 64 or 128 tokens), and
- * d_qk = d_v = 64 with page_size % 64 == 0 on the D = 64 one (64-key tiles).  With fewer tokens and more than 16 query rows per KV head
+ * k_st, v_st < 2^22 and s_q of at least one prefill work item (64 tokens when
+ * h_q/h_kv is a multiple of 4, 128 when it is 2 mod 4, 256 when odd) it runs
+ * on the prefill kernel, which reads its 64-key K/V tiles through the page
+ * tables (each wave its 8 rows from the page that holds them, so any page
+ * size serves); num_splits > 1 then writes the same partials as decode.
+ * d_qk = d_v = 256 likewise runs on the D = 256 prefill kernel (32-key tiles,
+ * items of 32, 64 or 128 tokens), and d_qk = d_v = 64 on the D = 64 one.  With fewer tokens and more than 16 query rows per KV head
  * (s_q * h_q/h_kv, e.g. multi-token decode over a wide GQA group), the same
  * kernel takes the call with the (token, head) rows of each KV head's group
  * folded, token-major, into its 256-row items.
@@ -317,12 +316,12 @@ int sdpa_decode_paged(const void* q,
  * (192,128), (576,512); native D64 per-tensor FP8 and Q/K 576 with V 512 are
  * in v1.32.0 "SDPA: wider native forward support"); s_q * (h_q/h_kv) <= 512
  * query rows per KV head, or any larger s_q when d_qk = d_v = 128, page_size
- * is a multiple of 64 and k_st, v_st < 2^22 (the FP8 chunked-prefill path);
+ * and k_st, v_st < 2^22 (the FP8 chunked-prefill path);
  * page_size a multiple of 16; K and V pool strides multiples of 16; q and the
  * pools 16-byte aligned.  Else SDPA_ERR_UNSUPPORTED.
  * Kernels: up to 32 rows per KV head (and up to 64 off the next path) at
  * d = 64, 128, 256 or 192/128, the FP8-MFMA few-row kernel in groups of 16
- * rows.  Past 32 rows at d_qk = d_v = 128 with page_size % 64 == 0, the FP8
+ * rows.  Past 32 rows at d_qk = d_v = 128, the FP8
  * prefill kernel over the page tables (FP8 MFMA for Q K^T, V codes widened
  * to bf16 in LDS), either for s_q of at least one work item or, with fewer
  * tokens, with the (token, head) rows of each KV head's group folded into

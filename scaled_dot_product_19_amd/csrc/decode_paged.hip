@@ -319,6 +319,9 @@ hipError_t launch_generic(const DecodeArgs& da, hipStream_t s, bool f8) {
     a.descale_v = f8 ? da.descale_v : nullptr;
     a.n_rg = 1;
     if (a.n_units == 0) return hipSuccess;
+    // the kernel's per-work-group state is sized for 512 query rows per KV head; the
+    // entry points decline more before they get here
+    if (a.rows > 512) return hipErrorInvalidValue;
     if (f8) {
         if (da.dqk == 64) return launch_dims<64, 64, true>(a, s);
         if (da.dqk == 128) return launch_dims<128, 128, true>(a, s);

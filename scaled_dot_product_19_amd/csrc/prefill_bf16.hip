@@ -310,14 +310,22 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     const char* kb0 = reinterpret_cast<const char*>(a.k) + C::EB * ((int64_t)kv_beg * a.k_st + (int64_t)kvh * a.k_sh);
     const char* vb0 = reinterpret_cast<const char*>(a.v) + C::EB * ((int64_t)kv_beg * a.v_st + (int64_t)kvh * a.v_sh);
     const int k_st2 = C::EB * (int)a.k_st, v_st2 = C::EB * (int)a.v_st;  // byte strides
+    // Paged: a wave's instructions cover exactly its 8 rows 8 w .. 8 w + 7 of
+    // a tile, which lie in one page (page_size % 8 == 0, tiles start on
+    // multiples of 8 keys), so each wave reads through its own page and its
+    // source offsets count from its first row; the swizzle follows the row
+    // within the tile.
+    constexpr int RW = C::NI * 64 / C::CPR;  // tile rows per wave
+    static_assert(!PAGED || RW == 8, "paged DMA: 8 rows per wave");
+    const int row0 = PAGED ? RW * wave : 0;
     int k_src[C::NI], v_src[C::NI];
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
         const int p = (wave * C::NI + j) * 64 + lane;
         const int row = p / C::CPR, pc = p % C::CPR;
-        k_src[j] = row * k_st2 + 16 * swz_k<C::CPR>(row, pc);
+        k_src[j] = (row - row0) * k_st2 + 16 * swz_k<C::CPR>(row, pc);
         // an FP8 V tile stays unswizzled: it is only read row-contiguously, by the widening
-        v_src[j] = row * v_st2 + 16 * (F8 ? pc : swz_v<C::CPR>(row, pc));
+        v_src[j] = (row - row0) * v_st2 + 16 * (F8 ? pc : swz_v<C::CPR>(row, pc));
     }
     // Paged: the K and V page ids of the next tile to be issued (scalar
     // loads).  An outstanding scalar load makes every later LDS wait a full
@@ -328,8 +336,8 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     const int32_t* const ptv_b = PAGED ? a.pt_v + (int64_t)b * a.table_stride : nullptr;
     auto page_ids = [&](int t) __attribute__((always_inline)) {
         if constexpr (PAGED) {
-            const int k0 = lo + t * BN;
-            const int e = k0 < kv_end ? k0 / a.page : 0;  // a tile past the end reads no page
+            const int k0 = lo + t * BN + row0;  // the wave's first key of the tile
+            const int e = k0 < kv_end ? k0 / a.page : 0;  // rows past the end read no page
             pk_nx = load_uniform(ptk_b, e);
             pv_nx = load_uniform(ptv_b, e);
         }
@@ -340,13 +348,13 @@ __device__ __attribute__((always_inline)) void prefill_item(const PrefillKArgs& 
     auto issue = [&](int t) __attribute__((always_inline)) {
         // a tile at or past kv_end gets an empty range: its DMA writes zeros
         // and reads nothing
-        const int k0 = lo + t * BN;
-        const int nvalid = min(BN, kv_end - k0);
+        const int k0 = lo + t * BN + row0;  // paged: the wave's first key
+        const int nvalid = min(PAGED ? RW : BN, kv_end - k0);
         const void* kt;
         const void* vt;
         if constexpr (PAGED) {
-            // BN divides the page size and lo is a multiple of it: the tile
-            // lies in one page (K and V pages looked up independently)
+            // the wave's rows lie in one page (K and V pages looked up
+            // independently)
             const int64_t in_page = nvalid > 0 ? k0 % a.page : 0;
             kt = reinterpret_cast<const char*>(a.k) +
                  C::EB * ((int64_t)pk_nx * a.k_sp + in_page * a.k_st + (int64_t)kvh * a.k_sh);
@@ -1124,16 +1132,10 @@ int paged_fold(const DecodeArgs& d) {
 }  // namespace
 
 bool prefill_paged_supported(const DecodeArgs& d) {
-    // D = 128 (bf16 or FP8) and D = 64 (bf16) with 64-key tiles, D = 256
-    // (bf16) with 32-key tiles: a tile must lie within one page
-    if (d.dqk != d.dv) return false;
-    if (d.dqk == 128 || (d.dqk == 64 && !d.fp8)) {
-        if (d.page % 64 != 0) return false;
-    } else if (d.dqk == 256 && !d.fp8) {
-        if (d.page % 32 != 0) return false;
-    } else {
-        return false;
-    }
+    // D = 128 (bf16 or FP8), D = 64 and D = 256 (bf16); any page size of a
+    // multiple of 8 keys (each wave's 8 rows of a tile lie in one page)
+    if (d.dqk != d.dv || d.page % 8 != 0) return false;
+    if (!(d.dqk == 128 || (d.dqk == 64 && !d.fp8) || (d.dqk == 256 && !d.fp8))) return false;
     if (d.k_st >= (1 << 22) || d.v_st >= (1 << 22)) return false;
     return d.sq >= paged_item_tokens(d.hq / d.hkv, paged_waves(d.dqk)) || paged_fold(d) > 0;
 }

@@ -325,6 +325,7 @@ static int decode_impl(const void* q, const void* k_pool, int64_t k_sp, int64_t 
         probe.sq = s_q;
         probe.hq = h_q;
         probe.hkv = h_kv;
+        probe.fp8 = fp8 ? 1 : 0;  // the FP8 prefill kernel serves d = 128 only
         if ((int64_t)s_q * (h_q / h_kv) > 512 && !sdpa::prefill_paged_supported(probe))
             return fail(SDPA_ERR_UNSUPPORTED,
                         "s_q * (h_q / h_kv) = %lld query rows per KV head > 512 (more need "

@@ -98,9 +98,9 @@ constexpr int kSmallRowsMax = 64;
 bool decode_small_supported(int32_t dqk, int32_t dv, int32_t rows);
 hipError_t launch_decode_small(const DecodeArgs& a, hipStream_t s);
 
-// Chunked prefill over the paged cache (d_qk = d_v = 128, page_size % 64 ==
-// 0, s_q at least one work item of query tokens): the ping-pong prefill
-// kernel of prefill_bf16.hip with K/V tiles addressed through the page tables.
+// The prefill kernels over the paged cache (d_qk = d_v = 64, 128 or 256; s_q
+// of at least one work item, or folded rows past 16 per KV head): K/V tiles
+// addressed through the page tables, each wave's 8 rows from its own page.
 bool prefill_paged_supported(const DecodeArgs& a);
 hipError_t launch_prefill_paged(const DecodeArgs& a, hipStream_t s);
 

@@ -199,14 +199,10 @@ def _decode(**over):
     (dict(ws_bytes=1024), sdpa.SDPA_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x100040)), sdpa.SDPA_ERR_WORKSPACE),
     (dict(ptv=None), sdpa.SDPA_ERR_NULL),
-    # 1024 rows per KV head on 32-key pages: the prefill kernel, the only path past 512
-    # rows, needs pages of a multiple of 64 keys
-    (dict(hq=1024, hkv=1, sq=1, page=32), sdpa.SDPA_ERR_UNSUPPORTED),
-    # > 512 query rows per KV head: only the chunked-prefill path (D 64 / 128 with page % 64,
-    # D 256 with page % 32) takes them
-    (dict(sq=1024, page=32), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(sq=1024, dqk=64, dv=64, k_st=8 * 64, v_st=8 * 64, k_sh=64, v_sh=64, page=32),
-     sdpa.SDPA_ERR_UNSUPPORTED),
+    # > 512 query rows per KV head: only the paged prefill kernel (d_qk = d_v = 64, 128,
+    # 256) and the absorbed-MLA kernel take them; not 192/128 pools
+    (dict(hq=1024, hkv=1, sq=1, dqk=192, dv=128, k_st=192, v_st=128, k_sh=192, v_sh=128,
+          k_sp=64 * 192, v_sp=64 * 128), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(sq=1024, dqk=192, dv=128, k_st=8 * 192, v_st=8 * 128, k_sh=192, v_sh=128),
      sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(k_st=8 * 128 + 1), sdpa.SDPA_ERR_UNSUPPORTED),
@@ -233,7 +229,9 @@ def _decode_fp8(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(dqk=96, dv=96, k_st=8 * 96, v_st=8 * 96, k_sh=96, v_sh=96), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(dqk=576, dv=576), sdpa.SDPA_ERR_UNSUPPORTED),
-    (dict(sq=5, hq=128, hkv=1, page=32), sdpa.SDPA_ERR_UNSUPPORTED),  # 640 rows per KV head
+    # 640 rows per KV head at D = 64 (the FP8 prefill kernel is D = 128 only)
+    (dict(sq=5, hq=128, hkv=1, dqk=64, dv=64, k_st=64, v_st=64, k_sh=64, v_sh=64, k_sp=64 * 64,
+          v_sp=64 * 64), sdpa.SDPA_ERR_UNSUPPORTED),
     (dict(k_st=8 * 128 + 8), sdpa.SDPA_ERR_UNSUPPORTED),         # K rows need 16-byte strides
     (dict(v_st=8 * 128 + 8), sdpa.SDPA_ERR_UNSUPPORTED),         # and V rows too
     (dict(v_st=8 * 128 + 4), sdpa.SDPA_ERR_UNSUPPORTED),
@@ -345,8 +343,9 @@ def test_decode_ex_declines_variants_at_d256():
     ((64, 1, 32, 8, 128, 128, 64, False), "few_row"),          # the paged decode workload
     ((4, 4, 32, 8, 128, 128, 64, False), "few_row"),           # 16 rows
     ((4, 8, 32, 8, 128, 128, 64, False), "prefill_folded"),    # 32 rows
-    ((4, 8, 32, 8, 128, 128, 32, False), "row_groups"),        # 32 rows, 32-key pages
-    ((4, 32, 32, 8, 128, 128, 32, False), "general"),          # 128 rows, 32-key pages
+    ((4, 8, 32, 8, 128, 128, 32, False), "prefill_folded"),    # 32 rows, 32-key pages
+    ((4, 32, 32, 8, 128, 128, 16, False), "prefill_folded"),   # 128 rows, 16-key pages
+    ((4, 2, 64, 2, 192, 128, 16, False), "row_groups"),        # 192/128, 64 rows
     ((2, 1024, 32, 8, 128, 128, 64, False), "prefill"),        # chunked prefill
     ((2, 5, 28, 4, 128, 128, 64, False), "prefill_folded"),    # G 7
     ((2, 2, 16, 1, 256, 256, 32, False), "prefill_folded"),    # D 256, 32 rows
@@ -362,7 +361,8 @@ def test_decode_ex_declines_variants_at_d256():
     ((4, 16, 32, 8, 128, 128, 64, True), "prefill_folded"),    # FP8 64 rows
     ((2, 2, 16, 1, 256, 256, 32, True), "row_groups"),         # FP8 D 256 stays off the prefill
     ((32, 2, 128, 1, 576, 512, 64, True), "wide"),             # FP8 MLA
-    ((2, 1024, 32, 8, 64, 64, 32, False), ""),                 # > 512 rows, 32-key pages
+    ((2, 1024, 32, 8, 64, 64, 16, False), "prefill"),          # > 512 rows, 16-key pages
+    ((2, 1024, 32, 8, 192, 128, 16, False), ""),               # > 512 rows at 192/128
     ((2, 1, 32, 8, 96, 96, 64, False), ""),                    # head dim not served
 ])
 def test_decode_path_selection(case, path):

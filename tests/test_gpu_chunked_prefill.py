@@ -211,3 +211,42 @@ def test_d64_paged_prefill_kernel(case):
                            num_splits=case["splits"], causal=case["causal"], poison=True,
                            name="d64_paged_%d" % case["seed"])
     parity(pc)
+
+
+# Pages of 16 or 32 keys: a tile spans several pages and each wave of the prefill kernel
+# reads its 8 rows through the page that holds them
+SMALL_PAGES = [
+    # (seed, d, sq, hq, hkv, page, lengths, splits, causal)
+    (2161, 128, 100, 8, 2, 16, [120, 1500], 3, True),    # chunk of 100 tokens
+    (2162, 128, 8, 32, 8, 16, [7, 130, 2000], 4, True),   # folded 32 rows
+    (2163, 128, 4, 32, 1, 32, [3, 900], 1, False),        # folded 128 rows
+    (2164, 64, 64, 8, 2, 16, [70, 900], 2, True),         # D 64 chunk
+    (2165, 256, 40, 8, 2, 16, [50, 700], 3, True),        # D 256 chunk
+    (2166, 256, 2, 16, 1, 16, [1, 333], 2, True),         # D 256 folded 32 rows
+]
+
+
+@pytest.mark.parametrize("case", SMALL_PAGES, ids=[str(c[0]) for c in SMALL_PAGES])
+def test_prefill_kernel_on_small_pages(case):
+    seed, d, sq, hq, hkv, page, lengths, splits, causal = case
+    pc = inputs.paged_case(seed, len(lengths), sq, hq, hkv, d, d, page, lengths=lengths,
+                           num_splits=splits, causal=causal, poison=True,
+                           name="small_pages_%d" % seed)
+    assert path_of(pc) in ("prefill", "prefill_folded")
+    o, l = parity(pc)
+    if causal and lengths[0] < sq:
+        assert torch.all(o[0, 0] == 0) and torch.all(l[0, 0] == -np.inf)
+
+
+def test_fp8_prefill_kernel_on_16_key_pages():
+    pc = inputs.fp8_paged_case(2167, 3, 16, 32, 8, 128, 16, lengths=[10, 400, 1800],
+                               num_splits=3, poison=True, name="fp8_small_pages")
+    assert path_of(pc, fp8=True) == "prefill_folded"
+    dq, dk, dv = [torch.tensor([x], dtype=torch.float32, device="cuda") for x in pc.descale]
+    o, l = sdpa.decode_paged_fp8(to_dev(pc.q), to_dev(pc.k_pool), to_dev(pc.v_pool),
+                                 to_dev(pc.pt_k), to_dev(pc.pt_v), to_dev(pc.seq_lens),
+                                 pc.max_kv, pc.scale, dq, dk, dv, causal=True, num_splits=3)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_decode(pc, descale=pc.descale)
+    check_o(o, o_ref)
+    check_lse(l, l_ref)

@@ -202,17 +202,17 @@ def test_d64_decode_workload_sampled():
 
 
 # ---- row groups: up to 64 rows per KV head take the few-row kernel in groups of 16 rows,
-# each group a unit of its own (a partial last group; causal limits per group).  Page 32
-# keeps these shapes off the prefill kernel, which folds GQA groups past 16 rows when
-# pages are multiples of 64 ---------------------------------------------------------
+# each group a unit of its own (a partial last group; causal limits per group).  In bf16
+# that is the 192/128 pools: square head dims past 16 rows go to the prefill kernel ------
 
 @pytest.mark.parametrize("shape", [(17, 1, 2, 1), (3, 11, 1, 1), (4, 12, 2, 3), (4, 16, 1, 8)],
                          ids=["17_rows", "33_rows", "48_rows", "64_rows"])
 def test_row_groups(shape):
     sq, group, hkv, splits = shape
-    pc = inputs.paged_case(2040 + sq * group, 3, sq, group * hkv, hkv, 128, 128, 32,
+    pc = inputs.paged_case(2040 + sq * group, 3, sq, group * hkv, hkv, 192, 128, 32,
                            lengths=[2, 130, 1900], num_splits=splits, poison=True,
                            name="row_groups")
+    assert path_of(pc) == "row_groups"
     log("row groups: %d rows per KV head" % (sq * group))
     o, l, _, _ = parity(pc)
     # sequence 0 holds 2 keys: with s_q > 2 its first token sees none

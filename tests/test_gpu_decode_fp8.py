@@ -190,12 +190,13 @@ def test_absorbed_mla_aliased_fp8_cache(splits):
 
 
 def test_512_rows_per_kv_head_and_past_them():
-    # 4 tokens x 128 heads over one KV head on 32-key pages (general kernel): the most rows
-    # it serves; past them only the prefill kernel (pages of 64k keys) takes the call
-    pc = inputs.fp8_paged_case(3019, 2, 4, 128, 1, 128, 32, lengths=[6, 900], num_splits=2,
+    # 4 tokens x 128 heads over one KV head at D = 64 (general kernel): the most rows it
+    # serves; past them only the FP8 prefill kernel (D = 128) takes a call
+    pc = inputs.fp8_paged_case(3019, 2, 4, 128, 1, 64, 32, lengths=[6, 900], num_splits=2,
                                poison=True, name="fp8_512rows")
+    assert path_of(pc, fp8=True) == "general"
     parity(pc)
-    pc5 = inputs.fp8_paged_case(3020, 1, 5, 128, 1, 128, 32, lengths=[900], name="fp8_640rows")
+    pc5 = inputs.fp8_paged_case(3020, 1, 5, 128, 1, 64, 32, lengths=[900], name="fp8_640rows")
     with pytest.raises(sdpa.SdpaError) as ei:
         run(pc5)
     assert ei.value.status == sdpa.SDPA_ERR_UNSUPPORTED
@@ -336,7 +337,7 @@ def test_mla_wide_repeated_calls_are_bitwise_equal(fp8):
             assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
 
-# ---- the FP8 prefill kernel over the page tables (D = 128, pages of a multiple of 64 keys):
+# ---- the FP8 prefill kernel over the page tables (D = 128, any page size):
 # chunked prefill, and few tokens of a GQA group with their (token, head) rows
 # folded into the 256-row items --------------------------------------------------------------
 

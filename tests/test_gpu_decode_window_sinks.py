@@ -73,12 +73,12 @@ def _cases():
         "few_row_d64": lambda: inputs.paged_case(
             2205, 3, 3, 4, 4, 64, 64, 32, lengths=[2, 77, 900], poison=True,
             name="few_row_d64"),
-        "row_groups_d64_32_rows": lambda: inputs.paged_case(
+        "folded_d64_32_rows_page32": lambda: inputs.paged_case(
             2212, 3, 4, 16, 2, 64, 64, 32, lengths=[3, 190, 1200], poison=True,
-            name="row_groups_d64_32_rows"),
-        "general_d64_128_rows": lambda: inputs.paged_case(
+            name="folded_d64_32_rows_page32"),
+        "folded_d64_128_rows_page32": lambda: inputs.paged_case(
             2214, 3, 4, 32, 1, 64, 64, 32, lengths=[3, 190, 1200], poison=True,
-            name="general_d64_128_rows"),
+            name="folded_d64_128_rows_page32"),
         "few_row_d192_128": lambda: inputs.paged_case(
             2206, 3, 1, 8, 2, 192, 128, 32, lengths=[9, 333, 1100], poison=True,
             name="few_row_d192_128"),
@@ -94,9 +94,12 @@ def _cases():
         "row_groups_fp8_d128_32_rows": lambda: inputs.fp8_paged_case(
             2211, 3, 4, 16, 2, 128, 32, lengths=[3, 420, 1300], poison=True,
             name="row_groups_fp8_d128_32_rows"),
-        "general_fp8_d128_128_rows": lambda: inputs.fp8_paged_case(
+        "folded_fp8_d128_128_rows_page32": lambda: inputs.fp8_paged_case(
             2216, 2, 4, 32, 1, 128, 32, lengths=[3, 1300], poison=True,
-            name="general_fp8_d128_128_rows"),
+            name="folded_fp8_d128_128_rows_page32"),
+        "general_fp8_d64_128_rows": lambda: inputs.fp8_paged_case(
+            2226, 2, 4, 32, 1, 64, 32, lengths=[3, 1300], poison=True,
+            name="general_fp8_d64_128_rows"),
         "chunked_prefill": lambda: inputs.paged_case(
             2207, 2, 128, 8, 2, 128, 128, 64, lengths=[200, 1500], poison=True,
             name="chunked_prefill"),

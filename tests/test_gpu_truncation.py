@@ -70,10 +70,14 @@ DECODE = {
                                           lengths=[90, 700, 1500], name="trunc_wide"),
     "few_row_d64": lambda: inputs.paged_case(3203, 3, 1, 4, 4, 64, 64, 32,
                                              lengths=[77, 300, 900], name="trunc_few_d64"),
-    "row_groups_d64": lambda: inputs.paged_case(3205, 3, 4, 16, 2, 64, 64, 32,
-                                                lengths=[77, 300, 900], name="trunc_row_groups"),
-    "general_d64": lambda: inputs.paged_case(3206, 3, 4, 32, 1, 64, 64, 32,
-                                             lengths=[77, 300, 900], name="trunc_general"),
+    "row_groups_d192_128": lambda: inputs.paged_case(3205, 3, 4, 16, 2, 192, 128, 32,
+                                                     lengths=[77, 300, 900],
+                                                     name="trunc_row_groups"),
+    "general_d192_128": lambda: inputs.paged_case(3206, 3, 4, 32, 1, 192, 128, 32,
+                                                  lengths=[77, 300, 900], name="trunc_general"),
+    "folded_d64_page32": lambda: inputs.paged_case(3210, 3, 4, 32, 1, 64, 64, 32,
+                                                   lengths=[77, 300, 900],
+                                                   name="trunc_folded_d64_page32"),
     "chunked_prefill": lambda: inputs.paged_case(3204, 3, 128, 8, 2, 128, 128, 64,
                                                  lengths=[200, 700, 1500], name="trunc_chunked"),
     "folded_rows": lambda: inputs.paged_case(3207, 3, 4, 32, 1, 128, 128, 64,
